@@ -1,0 +1,443 @@
+"""CPU oracle for the DeepSeek-V4-style sparse-attention decode step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this module:
+only the tests, the smoke check and the benchmark's CPU-baseline leg use it.
+It shares no code with the HIP library (no headers, tables, helpers or
+generators); it reads the same input *bytes* and recomputes every step the
+plain way, in float64 where floating point is involved.
+
+Sources (web pages; cited by page and by the function or section on it):
+
+* [ops]     tokenspeed "DeepSeek V4 attention kernel boundaries"
+            (runtime/layers/attention/deepseek_v4_ops.py page)
+* [model]   tokenspeed DeepSeek V4 model page (runtime/models/deepseek_v4.py)
+* [backend] tokenspeed DeepSeek V4 attention backend page
+            (runtime/layers/attention/backends/deepseek_v4.py)
+* [vllm]    vLLM "vllm.models.deepseek_v41.common.ops" API page
+
+Readings taken where the pages are silent (each is listed in the design doc):
+
+* indexer score  = sum_h w[t,h] * ReLU(q[t,h] . k_s)      (parity unpinned vs pages)
+* top-k ties go to the lower row id; output is ascending by row id, -1 padded
+* KV scales are fp32 per 64 nope elements (the pages use ue8m0 there)
+* sparse_topk_lens counts the valid compressed entries, which are packed to
+  the left of the compressed segment in top-k order; the rest is -1
+* a row whose page id is negative, past the table or past the pool is invalid
+  (fail closed) and is dropped
+* attention values are the whole dequantized row (Dv = Dn + Dr); the sink is
+  one extra logit with a zero value vector
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# O2: element codecs
+# ---------------------------------------------------------------------------
+
+
+def e4m3fn_value(byte: int) -> float:
+    """Value of one OCP FP8 E4M3 ("fn") byte.
+
+    Sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is
+    subnormal (m/8 * 2^-6); there are no infinities and S.1111.111 is NaN, so
+    the largest finite magnitude is 448.  gfx950 uses this OCP encoding, not
+    the FNUZ one ([vllm] ``dequantize_and_gather_k_cache``, use_fnuz note).
+    """
+    sign = -1.0 if byte & 0x80 else 1.0
+    exp = (byte >> 3) & 0xF
+    man = byte & 0x7
+    if exp == 0xF and man == 0x7:
+        return math.nan
+    if exp == 0:
+        return sign * (man / 8.0) * 2.0 ** (1 - 7)
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+E4M3_VALUES = np.array([e4m3fn_value(b) for b in range(256)], dtype=np.float64)
+
+# [ops] ``_e2m1_values``: magnitudes of the 3 low bits, sign in bit 3.
+E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def e2m1_value(nibble: int) -> float:
+    mag = E2M1_MAGNITUDES[nibble & 0x7]
+    return -mag if nibble & 0x8 else mag
+
+
+E2M1_VALUES = np.array([e2m1_value(n) for n in range(16)], dtype=np.float64)
+
+
+def e8m0_value(byte: int) -> float:
+    """[ops] ``read_deepseek_v4_indexer_mxfp4_cache``: scale = 2^(b - 127)."""
+    return math.ldexp(1.0, int(byte) - 127)
+
+
+def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 is the upper half of an IEEE binary32; returns float64."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def float32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round binary32 values to bfloat16, nearest-even; returns uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = ((u[nan] >> np.uint64(16)) | np.uint64(0x40)).astype(np.uint16)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O1: token geometry
+# ---------------------------------------------------------------------------
+
+
+def token_positions(query_start_loc, seq_lens, token_to_req) -> np.ndarray:
+    """Position of every token in its request.
+
+    [backend] ``_decode_positions_from_metadata``:
+    ``pos = seq_len - query_len + (t - query_start)`` for the token's request,
+    where seq_len counts this step's query tokens.
+    """
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    sl = np.asarray(seq_lens, dtype=np.int64)
+    req = np.asarray(token_to_req, dtype=np.int64)
+    t = np.arange(req.shape[0], dtype=np.int64)
+    if req.size:
+        if not np.all((qsl[req] <= t) & (t < qsl[req + 1])):
+            raise ValueError("token_to_req disagrees with query_start_loc")
+    qlen = qsl[req + 1] - qsl[req]
+    return sl[req] - qlen + (t - qsl[req])
+
+
+def compressed_len(pos: np.ndarray, ratio: int) -> np.ndarray:
+    """Compressed rows visible to a token at ``pos``: floor((pos + 1) / ratio).
+
+    A compressed row is complete once ``(pos + 1) % ratio == 0`` ([ops]
+    compressor helpers; [model] indexer prefill ``row_lens``; [backend]
+    dense compressed indices).
+    """
+    return np.maximum(np.asarray(pos, dtype=np.int64) + 1, 0) // int(ratio)
+
+
+# ---------------------------------------------------------------------------
+# O5/O6: slot mapping, window ids, sparse index rows
+# ---------------------------------------------------------------------------
+
+
+def logical_to_slot(bt_row, logical: int, block_size: int, num_pages: int) -> int:
+    """Paged lookup ``bt[logical // B] * B + logical % B``, or -1 (fail closed).
+
+    [vllm] ``compute_global_topk_indices_and_lens`` (block-table lookup),
+    [backend] dense compressed indices (``safe_page_ids``; invalid -> -1).
+    """
+    if logical < 0:
+        return -1
+    col = logical // block_size
+    if col >= len(bt_row):
+        return -1
+    page = int(bt_row[col])
+    if page < 0 or page >= num_pages:
+        return -1
+    return page * block_size + logical % block_size
+
+
+def build_sparse_indices(
+    query_start_loc, seq_lens, token_to_req, replay_start,
+    swa_bt, swa_block_size, swa_num_pages,
+    comp_bt, comp_block_size, comp_num_pages,
+    topk_local, topk, window_size, compress_ratio, padded_topk,
+):
+    """One int32 row per token: ``window_size`` window slots then ``padded_topk``
+    compressed slots, plus the count of valid compressed slots.
+
+    Window columns ([vllm] ``build_flashinfer_mixed_sparse_indices``; [backend]
+    ``_update_decode_swa_metadata``): positions ``lo..pos`` ascending with
+    ``lo = max(pos - W + 1, replay_start[r], 0)`` mapped through the window
+    table, then -1.  Compressed columns ([vllm]
+    ``compute_global_topk_indices_and_lens``; [backend]
+    ``_decode_compressed_attention_indices_and_lens``): each local id of the
+    token's top-k row (or ``0..n_c-1`` when ``topk_local`` is None, the dense
+    ratio-128 path) that is ``< n_c`` and maps to a backed page, in order,
+    packed left; then -1.
+    """
+    pos = token_positions(query_start_loc, seq_lens, token_to_req)
+    req = np.asarray(token_to_req, dtype=np.int64)
+    replay = np.zeros(len(seq_lens), np.int64) if replay_start is None else np.asarray(replay_start)
+    T = req.shape[0]
+    W, P = int(window_size), int(padded_topk)
+    out = np.full((T, W + P), -1, dtype=np.int32)
+    lens = np.zeros(T, dtype=np.int32)
+    nc_all = compressed_len(pos, compress_ratio)
+    for t in range(T):
+        r = int(req[t])
+        p = int(pos[t])
+        lo = max(p - W + 1, int(replay[r]), 0)
+        for j, q in enumerate(range(lo, p + 1)):
+            out[t, j] = logical_to_slot(swa_bt[r], q, swa_block_size, swa_num_pages)
+        nc = int(nc_all[t])
+        if topk_local is None:
+            cand = range(min(nc, P))
+        else:
+            cand = [int(x) for x in topk_local[t, :topk]]
+        n = 0
+        for l in cand:
+            if l < 0 or l >= nc:
+                continue
+            s = logical_to_slot(comp_bt[r], l, comp_block_size, comp_num_pages)
+            if s < 0:
+                continue
+            out[t, W + n] = s
+            n += 1
+        lens[t] = n
+    return out, lens
+
+
+# ---------------------------------------------------------------------------
+# O7: latent row dequantization
+# ---------------------------------------------------------------------------
+
+
+def dequant_rows(kv_pages: dict, slots, block_size: int, d_nope: int, d_rope: int) -> np.ndarray:
+    """bf16 bits [n, Dn+Dr] of the rows at ``slots``; slot -1 gives a zero row.
+
+    [ops] ``dequantize_deepseek_v4_fp8_ds_mla_cache``: values of row ``o`` of
+    page ``g`` start at ``g*stride + o*(Dn + 2*Dr)``; its scales start at
+    ``g*stride + B*(Dn + 2*Dr) + o*scale_bytes``.  Each nope element is
+    ``bf16_rne(fp32(e4m3(v)) * scale[d // 64])`` (one binary32 multiply); the
+    rope tail is stored bf16 and copied.  Scales here are fp32 (4 bytes each).
+    """
+    slots = np.asarray(slots, dtype=np.int64)
+    row_b = d_nope + 2 * d_rope
+    nsc = d_nope // 64
+    out = np.zeros((slots.shape[0], d_nope + d_rope), dtype=np.uint16)
+    for i, s in enumerate(slots):
+        if s < 0:
+            continue
+        page = kv_pages[int(s) // block_size]
+        o = int(s) % block_size
+        vals = page[o * row_b: (o + 1) * row_b]
+        sbase = block_size * row_b + o * 4 * nsc
+        scales = page[sbase: sbase + 4 * nsc].view(np.float32)
+        nope32 = E4M3_VALUES[vals[:d_nope]].astype(np.float32)
+        prod = nope32 * np.repeat(scales, 64)  # binary32 multiply
+        out[i, :d_nope] = float32_to_bf16_bits(prod)
+        out[i, d_nope:] = vals[d_nope:].view(np.uint16)
+    return out
+
+
+def gather_dequant(kv_swa: dict, kv_comp: dict, sparse_indices, sparse_topk_lens,
+                   window_size, block_size_swa, block_size_comp, d_nope, d_rope) -> np.ndarray:
+    """[T, W+P, Dn+Dr] bf16 bits: every attended column dequantized, others zero.
+
+    Window columns read the window cache; compressed columns ``W..W+lens-1``
+    read the compressed cache; -1 and columns past ``lens`` are zero rows.
+    """
+    si = np.asarray(sparse_indices)
+    T, width = si.shape
+    W = int(window_size)
+    out = np.zeros((T, width, d_nope + d_rope), dtype=np.uint16)
+    for t in range(T):
+        out[t, :W] = dequant_rows(kv_swa, si[t, :W], block_size_swa, d_nope, d_rope)
+        n = int(min(max(sparse_topk_lens[t], 0), width - W))
+        out[t, W: W + n] = dequant_rows(kv_comp, si[t, W: W + n], block_size_comp, d_nope, d_rope)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O3/O4: indexer scores and top-k
+# ---------------------------------------------------------------------------
+
+
+def mxfp4_decode(packed: np.ndarray, exps: np.ndarray) -> np.ndarray:
+    """[n, D/2] packed E2M1 + [n, D/32] e8m0 -> float64 [n, D].
+
+    [ops] ``read_deepseek_v4_indexer_mxfp4_cache``: the low nibble is the
+    even element, the high nibble the odd one; every 32 elements share one
+    power-of-two scale.
+    """
+    packed = np.asarray(packed, dtype=np.uint8)
+    n, half = packed.shape
+    vals = np.empty((n, 2 * half), dtype=np.float64)
+    vals[:, 0::2] = E2M1_VALUES[packed & 0xF]
+    vals[:, 1::2] = E2M1_VALUES[packed >> 4]
+    scale = np.ldexp(1.0, np.asarray(exps, dtype=np.int64) - 127)
+    return vals * np.repeat(scale, 32, axis=1)
+
+
+def read_index_keys(idx_pages: dict, bt_row, rows: int, block_size: int, dim: int, num_pages: int):
+    """Keys of compressed rows ``0..rows-1`` through the indexer table.
+
+    Returns (keys float64 [rows, dim], valid bool [rows]); a row whose page is
+    unbacked is invalid and its key is zero.
+    """
+    vb, sb = dim // 2, dim // 32
+    keys = np.zeros((rows, dim), dtype=np.float64)
+    valid = np.zeros(rows, dtype=bool)
+    for c in range((rows + block_size - 1) // block_size):
+        lo, hi = c * block_size, min(rows, (c + 1) * block_size)
+        if c >= len(bt_row):
+            break
+        page_id = int(bt_row[c])
+        if page_id < 0 or page_id >= num_pages:
+            continue
+        page = idx_pages[page_id]
+        n = hi - lo
+        packed = page[: block_size * vb].reshape(block_size, vb)[:n]
+        exps = page[block_size * vb: block_size * (vb + sb)].reshape(block_size, sb)[:n]
+        keys[lo:hi] = mxfp4_decode(packed, exps)
+        valid[lo:hi] = True
+    return keys, valid
+
+
+def indexer_scores(q_values, q_scales, weights, keys) -> np.ndarray:
+    """score[s] = sum_h w[h] * max(q_h . k_s, 0), float64.
+
+    Per token, each indexer head's MXFP4 query is dotted with every compressed
+    row's MXFP4 key, and the per-head logits are combined with the folded
+    weights ([model] ``_deepseek_v4_indexer_topk_from_cache_deepgemm_decode``;
+    [vllm] ``fused_indexer_q_rope_quant``: MXFP4 weights carry
+    softmax_scale * head_scale).  The ReLU combination is this build's reading.
+    """
+    q = mxfp4_decode(q_values, q_scales)  # [Hi, Di]
+    dots = q @ keys.T  # [Hi, n]
+    return np.asarray(weights, dtype=np.float64) @ np.maximum(dots, 0.0)
+
+
+def topk_select(scores: np.ndarray, valid: np.ndarray, k: int) -> np.ndarray:
+    """Ids of the ``min(k, #valid)`` largest scores (ties: lower id), ascending,
+    -1 padded to ``k`` ([model] ``_deepseek_v4_indexer_topk_from_logits``:
+    the output starts filled with -1)."""
+    ids = np.nonzero(valid)[0]
+    out = np.full(k, -1, dtype=np.int32)
+    if ids.size == 0 or k == 0:
+        return out
+    order = np.lexsort((ids, -scores[ids]))
+    chosen = np.sort(ids[order[:k]])
+    out[: chosen.size] = chosen
+    return out
+
+
+def indexer_topk(query_start_loc, seq_lens, token_to_req, q_values, q_scales, weights,
+                 idx_pages, idx_bt, idx_block_size, idx_dim, idx_num_pages, compress_ratio, topk,
+                 tokens=None, return_scores=False):
+    """Top-k local compressed-row ids for each token (all, or ``tokens``)."""
+    pos = token_positions(query_start_loc, seq_lens, token_to_req)
+    nc = compressed_len(pos, compress_ratio)
+    req = np.asarray(token_to_req, dtype=np.int64)
+    tokens = range(req.shape[0]) if tokens is None else tokens
+    out = np.full((len(tokens), topk), -1, dtype=np.int32)
+    scores_out = []
+    for i, t in enumerate(tokens):
+        n = int(nc[t])
+        keys, valid = read_index_keys(idx_pages, idx_bt[req[t]], n, idx_block_size, idx_dim, idx_num_pages)
+        sc = indexer_scores(q_values[t], q_scales[t], weights[t], keys) if n else np.zeros(0)
+        out[i] = topk_select(sc, valid, topk)
+        scores_out.append((sc, valid))
+    return (out, scores_out) if return_scores else out
+
+
+# ---------------------------------------------------------------------------
+# O8: attention
+# ---------------------------------------------------------------------------
+
+
+def attend(q_bits: np.ndarray, row_bits: np.ndarray, softmax_scale: float, sink=None):
+    """Softmax attention of every head over the given rows (float64).
+
+    ``o_h = sum_j exp(l_hj - m) x_j / (sum_j exp(l_hj - m) + exp(sink_h - m))``
+    with ``l_hj = c * q_h . x_j`` over the full row, ``m`` the max of the
+    logits and the sink ([backend] ``forward_deepseek_v4_decode``: values are
+    the whole row, ``head_dim_v = head_dim``; [model] attention: scale
+    ``head_dim^-1/2``, per-head sink).  Returns (o [H, D], lse [H]); with no
+    rows and no sink, o = 0 and lse = -inf.
+    """
+    q = bf16_bits_to_float(q_bits)  # [H, D]
+    H = q.shape[0]
+    if row_bits.shape[0] == 0 and sink is None:
+        return np.zeros((H, row_bits.shape[1]), np.float64), np.full(H, -np.inf)
+    x = bf16_bits_to_float(row_bits)  # [n, D]
+    logits = softmax_scale * (q @ x.T)  # [H, n]
+    s = None if sink is None else np.asarray(sink, dtype=np.float64)
+    m = logits.max(axis=1) if logits.shape[1] else np.full(H, -np.inf)
+    if s is not None:
+        m = np.maximum(m, s)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(logits - m_safe[:, None])
+    z = e.sum(axis=1)
+    if s is not None:
+        z = z + np.exp(s - m_safe)
+    o = (e @ x) / np.where(z > 0, z, 1.0)[:, None]
+    o[z == 0] = 0.0
+    with np.errstate(divide="ignore"):
+        lse = m_safe + np.log(z)
+    return o, lse
+
+
+def sparse_mla_decode(q_bits, kv_swa, kv_comp, sparse_indices, sparse_topk_lens, window_size,
+                      block_size_swa, block_size_comp, d_nope, d_rope, softmax_scale,
+                      attn_sink=None, tokens=None):
+    """Attention of every head of each token over its attended columns.
+
+    Attended columns: window columns ``0..W-1`` with slot >= 0 and compressed
+    columns ``W..W+lens-1`` with slot >= 0, each one key ([backend]
+    ``forward_deepseek_v4_decode``: window ids bounded by their lengths plus
+    extra (compressed) ids bounded by ``extra_topk_length``).
+    Returns float64 (o [n, H, Dn+Dr], lse [n, H]).
+    """
+    si = np.asarray(sparse_indices)
+    W = int(window_size)
+    tokens = range(si.shape[0]) if tokens is None else tokens
+    H = q_bits.shape[1]
+    D = d_nope + d_rope
+    o = np.zeros((len(tokens), H, D), np.float64)
+    lse = np.zeros((len(tokens), H), np.float64)
+    for i, t in enumerate(tokens):
+        swa = si[t, :W]
+        n = int(min(max(int(sparse_topk_lens[t]), 0), si.shape[1] - W))
+        comp = si[t, W: W + n]
+        rows = np.concatenate([
+            dequant_rows(kv_swa, swa[swa >= 0], block_size_swa, d_nope, d_rope),
+            dequant_rows(kv_comp, comp[comp >= 0], block_size_comp, d_nope, d_rope),
+        ])
+        o[i], lse[i] = attend(q_bits[t], rows, softmax_scale, attn_sink)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Whole step
+# ---------------------------------------------------------------------------
+
+
+def step(view, cfg, padded_topk, kv_num_pages, idx_num_pages, softmax_scale, tokens=None, attn_sink=None):
+    """Indexer -> top-k -> index build -> attention for one layer.
+
+    ``view`` holds numpy inputs (see the workload host view); ``cfg`` gives
+    the shape parameters.  Returns a dict of every intermediate.
+    """
+    T = len(view.token_to_req)
+    all_tokens = list(range(T)) if tokens is None else list(tokens)
+    if cfg.topk > 0:
+        tk = np.full((T, cfg.topk), -1, np.int32)
+        sel = indexer_topk(view.query_start_loc, view.seq_lens, view.token_to_req,
+                           view.idx_q_values, view.idx_q_scales, view.idx_weights,
+                           view.idx_pages, view.idx_bt, cfg.idx_block, cfg.idx_dim, idx_num_pages,
+                           cfg.ratio, cfg.topk, tokens=all_tokens)
+        tk[all_tokens] = sel
+    else:
+        tk = None
+    si, lens = build_sparse_indices(
+        view.query_start_loc, view.seq_lens, view.token_to_req, view.replay_start,
+        view.swa_bt, cfg.block, kv_num_pages, view.comp_bt, cfg.block, kv_num_pages,
+        tk, cfg.topk, cfg.window, cfg.ratio, padded_topk)
+    o, lse = sparse_mla_decode(view.q, view.kv_pages, view.kv_pages, si, lens, cfg.window,
+                               cfg.block, cfg.block, cfg.d_nope, cfg.d_rope, softmax_scale,
+                               attn_sink=attn_sink, tokens=all_tokens)
+    return {"topk": tk, "sparse_indices": si, "lens": lens, "out": o, "lse": lse, "tokens": all_tokens}

@@ -1,0 +1,383 @@
+"""Pins of the CPU oracle against facts outside itself (CPU only).
+
+Each test checks one oracle step against a library routine, a value printed
+on the pages (fixtures under tests/golden/), a closed form, an invariant or
+brute force, chosen so a plausible slip (wrong nibble order, wrong scale
+block, dropped ReLU, off-by-one window, transposed operand) fails one of them.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sad_oracle as O
+from sparse_attention_decode_build_amd import workloads as WL
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# --------------------------------------------------------------------------- codecs
+
+
+def test_e4m3_matches_torch_cast_all_bytes():
+    b = torch.arange(256, dtype=torch.uint8)
+    ref = b.view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    mine = O.E4M3_VALUES
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert mine[0x7E] == 448.0 and mine[0xFE] == -448.0  # largest finite
+    assert mine[0x01] == 2.0 ** -9  # smallest subnormal
+
+
+def test_e2m1_matches_printed_table():
+    for nib, val in _golden("e2m1_table.txt"):
+        v = float(val)
+        got = O.e2m1_value(int(nib))
+        assert got == v and math.copysign(1, got) == math.copysign(1, v) or (v == 0 and got == 0)
+
+
+def test_fp8_max_and_blocks_match_pages():
+    consts = {k: float(v) for k, v in _golden("format_constants.txt")}
+    assert consts["fp8_max"] == float(torch.finfo(torch.float8_e4m3fn).max)
+    assert consts["fp8_max"] == max(O.E4M3_VALUES[~np.isnan(O.E4M3_VALUES)])
+    assert WL.FP8_BLOCK == consts["fp8_block"] and WL.MX_BLOCK == consts["mxfp4_block"]
+
+
+def test_e8m0_is_power_of_two():
+    for b in range(255):
+        assert O.e8m0_value(b) == math.ldexp(1.0, b - 127)
+
+
+def test_bf16_rne_matches_torch_cast():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(1_000_000).astype(np.float32) * np.float32(3.0)
+    # exact ties (low 16 bits 0x8000) with both parities, plus specials
+    u = rng.integers(0, 2**32, 20000, dtype=np.uint64).astype(np.uint32)
+    ties = ((u & np.uint32(0xFFFF0000)) | np.uint32(0x8000)).view(np.float32)
+    ties = ties[np.isfinite(ties)]
+    specials = np.array([0.0, -0.0, 1e-40, -1e-40, 3.0e38, np.inf, -np.inf], np.float32)
+    x = np.concatenate([x, ties, specials])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.float32_to_bf16_bits(x), ref)
+    back = O.bf16_bits_to_float(ref)
+    assert np.array_equal(back, torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
+
+
+def test_mxfp4_nibble_order_and_block_scale():
+    # low nibble is the even element, high nibble the odd one; one scale per 32
+    packed = np.zeros((1, 32), np.uint8)
+    packed[0, 0] = 0x2F  # element0 = nibble 0xF = -6, element1 = nibble 0x2 = 1.0
+    packed[0, 16] = 0x71  # element32 = 0.5, element33 = 6
+    exps = np.array([[127 + 1, 127 - 2]], np.uint8)  # block0 x2, block1 x1/4
+    v = O.mxfp4_decode(packed, exps)
+    assert v[0, 0] == -12.0 and v[0, 1] == 2.0
+    assert v[0, 32] == 0.5 * 0.25 and v[0, 33] == 6.0 * 0.25
+    assert np.count_nonzero(v) == 4
+
+
+def test_mxfp4_encoder_roundtrip_within_half_step():
+    # write side (workload encoder) and read side (oracle) were written apart;
+    # the decoded value must be the nearest grid point at the block's scale.
+    x = torch.randn(512, 64, generator=torch.Generator().manual_seed(1))
+    packed, exps = WL.encode_mxfp4(x)
+    v = O.mxfp4_decode(packed.numpy(), exps.numpy())
+    xs = x.double().numpy()
+    scale = np.repeat(np.ldexp(1.0, exps.numpy().astype(np.int64) - 127), 32, axis=1)
+    grid = np.array(sorted(set(abs(g) for g in O.E2M1_VALUES)))
+    y = np.abs(xs) / scale
+    nearest = np.min(np.abs(y[..., None] - grid), axis=-1)
+    assert np.all(np.abs(np.abs(v) / scale - y) <= nearest + 1e-12)
+    assert np.all(np.abs(xs) / scale <= 6.0 + 1e-9)
+
+
+# --------------------------------------------------------------------------- dequant
+
+
+def _one_page_cache(rows_bf16, B, Dn, Dr):
+    cfg = WL.Config(name="t", seed=0, window=1, ratio=1, topk=1, heads=1, d_nope=Dn, d_rope=Dr,
+                    idx_heads=1, idx_dim=64, block=B, idx_block=B)
+    page = WL._kv_page_bytes(cfg, rows_bf16)
+    return {7: page[0].numpy()}, cfg
+
+
+def test_dequant_roundtrip_bound_and_idempotence():
+    B, Dn, Dr = 16, 128, 32
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(B, Dn + Dr, generator=g)
+    x[3, :64] *= 1e-3  # small block: exercises subnormal codes
+    x[5, 64:128] = 0.0  # all-zero block: amax clamped
+    x = x.to(torch.bfloat16)
+    pages, _ = _one_page_cache(x, B, Dn, Dr)
+    slots = np.arange(7 * B, 8 * B)
+    got = O.dequant_rows(pages, slots, B, Dn, Dr)
+    xh = O.bf16_bits_to_float(got)
+    xr = x.double().numpy()
+    scale = np.repeat(
+        np.maximum(np.abs(xr[:, :Dn]).reshape(B, -1, 64).max(-1), 1e-4) / 448.0, 64, axis=1)
+    err = np.abs(xh[:, :Dn] - xr[:, :Dn])
+    assert np.all(err <= (2 ** -4 + 2 ** -8) * np.abs(xr[:, :Dn]) + 2 ** -9 * scale * 1.0001)
+    assert np.array_equal(got[:, Dn:], x[:, Dn:].view(torch.int16).numpy().view(np.uint16))
+    # idempotence: re-encoding the dequantized value with the stored scale gives the same byte
+    page = pages[7]
+    row_b = Dn + 2 * Dr
+    sc = page[B * row_b:].view(np.float32).reshape(B, Dn // 64)
+    codes = np.stack([page[o * row_b: o * row_b + Dn] for o in range(B)])
+    re = torch.from_numpy(
+        (xh[:, :Dn] / np.repeat(sc.astype(np.float64), 64, axis=1)).astype(np.float32)
+    ).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(re, codes)
+
+
+def test_dequant_reads_the_addressed_row_and_scale_block():
+    # closed form on a hand-built page: row o, block b holds byte 0x38 (=1.0) and
+    # scale (o + 1) * 2^b, so every dequantized element is exactly (o + 1) * 2^b.
+    B, Dn, Dr = 16, 128, 32
+    row_b = Dn + 2 * Dr
+    page = np.zeros(B * (row_b + 4 * (Dn // 64)), np.uint8)
+    for o in range(B):
+        page[o * row_b: o * row_b + Dn] = 0x38
+        sc = np.array([(o + 1) * 2.0 ** b for b in range(Dn // 64)], np.float32)
+        page[B * row_b + o * 8: B * row_b + o * 8 + 8] = sc.view(np.uint8)
+    got = O.bf16_bits_to_float(O.dequant_rows({2: page}, [2 * B + 5, -1, 2 * B], B, Dn, Dr))
+    assert np.all(got[0, :64] == 6.0) and np.all(got[0, 64:Dn] == 12.0)
+    assert np.all(got[1] == 0.0)
+    assert np.all(got[2, :64] == 1.0) and np.all(got[2, 64:Dn] == 2.0)
+
+
+# --------------------------------------------------------------------------- geometry / indices
+
+
+def test_positions_closed_form():
+    qsl = [0, 1, 4, 4, 6]
+    seq = [10, 3, 7, 2]
+    t2r = [0, 1, 1, 1, 3, 3]
+    pos = O.token_positions(qsl, seq, t2r)
+    assert pos.tolist() == [9, 0, 1, 2, 0, 1]
+    assert O.compressed_len(np.array([0, 2, 3, 4, 7, 127]), 4).tolist() == [0, 0, 1, 1, 2, 32]
+    with pytest.raises(ValueError):
+        O.token_positions([0, 1], [5], [0, 0])
+
+
+def _random_batch(rng, R=6, B=4, W=5, ratio=4, topk=6, P=8, pages=200):
+    q_lens = rng.integers(0, 5, R)
+    seq = np.array([int(rng.integers(ql, ql + 40)) if ql else int(rng.integers(1, 40)) for ql in q_lens])
+    qsl = np.concatenate([[0], np.cumsum(q_lens)])
+    t2r = np.repeat(np.arange(R), q_lens)
+    replay = rng.integers(0, 20, R)
+    cols = (seq.max() + B - 1) // B + 1
+    perm = rng.permutation(pages)
+    swa_bt = perm[: R * cols].reshape(R, cols).astype(np.int32)
+    comp_bt = perm[R * cols: 2 * R * cols].reshape(R, cols).astype(np.int32)
+    swa_bt[rng.random(swa_bt.shape) < 0.15] = -1  # unbacked pages
+    comp_bt[rng.random(comp_bt.shape) < 0.15] = -1
+    comp_bt[0, 0] = pages + 5  # past the pool: invalid
+    T = int(q_lens.sum())
+    topk_local = rng.integers(-2, 14, (T, topk + 2)).astype(np.int32)
+    return dict(qsl=qsl, seq=seq, t2r=t2r, replay=replay, swa_bt=swa_bt, comp_bt=comp_bt,
+                topk_local=topk_local, B=B, W=W, ratio=ratio, topk=topk, P=P, pages=pages)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sparse_indices_match_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    b = _random_batch(rng)
+    dense = seed % 2 == 1
+    tk = None if dense else b["topk_local"]
+    si, lens = O.build_sparse_indices(
+        b["qsl"], b["seq"], b["t2r"], b["replay"], b["swa_bt"], b["B"], b["pages"],
+        b["comp_bt"], b["B"], b["pages"], tk, b["topk"], b["W"], b["ratio"], b["P"])
+    # independent walk: enumerate every position of the request, keep the window
+    for t, r in enumerate(b["t2r"]):
+        qlen = b["qsl"][r + 1] - b["qsl"][r]
+        p = b["seq"][r] - qlen + (t - b["qsl"][r])
+        keep = [x for x in range(0, p + 1) if x > p - b["W"] and x >= b["replay"][r]]
+        exp_swa = []
+        for x in keep:
+            page = b["swa_bt"][r][x // b["B"]] if x // b["B"] < b["swa_bt"].shape[1] else -1
+            exp_swa.append(int(page) * b["B"] + x % b["B"] if 0 <= page < b["pages"] else -1)
+        exp_swa += [-1] * (b["W"] - len(exp_swa))
+        assert si[t, : b["W"]].tolist() == exp_swa
+        nc = (p + 1) // b["ratio"]
+        cand = list(range(min(nc, b["P"]))) if dense else b["topk_local"][t, : b["topk"]].tolist()
+        exp_c = []
+        for l in cand:
+            if 0 <= l < nc:
+                page = b["comp_bt"][r][l // b["B"]]
+                if 0 <= page < b["pages"]:
+                    exp_c.append(int(page) * b["B"] + l % b["B"])
+        assert lens[t] == len(exp_c)
+        assert si[t, b["W"]:].tolist() == exp_c + [-1] * (b["P"] - len(exp_c))
+
+
+def test_window_is_last_w_positions_clipped_by_replay():
+    B, W = 4, 6
+    bt = np.arange(10, dtype=np.int32)[None, :]  # identity table: slot == position
+    for p in range(0, 30):
+        for replay in (0, 3, p, p + 1):
+            si, lens = O.build_sparse_indices([0, 1], [p + 1], [0], [replay], bt, B, 100, bt, B, 100,
+                                              None, 0, W, 4, 64)
+            want = list(range(max(p - W + 1, replay, 0), p + 1))
+            assert si[0, :W].tolist() == want + [-1] * (W - len(want))
+            assert lens[0] == min((p + 1) // 4, 64)
+
+
+# --------------------------------------------------------------------------- indexer / top-k
+
+
+def _mx_query(rng, H, D):
+    x = torch.from_numpy(rng.standard_normal((H, D)).astype(np.float32))
+    v, e = WL.encode_mxfp4(x)
+    return v.numpy(), e.numpy()
+
+
+def test_scores_one_hot_query_reads_single_key_element():
+    rng = np.random.default_rng(5)
+    D = 64
+    keys = torch.from_numpy(rng.standard_normal((10, D)).astype(np.float32))
+    kv, ke = WL.encode_mxfp4(keys)
+    kd = O.mxfp4_decode(kv.numpy(), ke.numpy())
+    for i in (0, 1, 31, 32, 63):
+        q = np.zeros((1, D // 2), np.uint8)
+        q[0, i // 2] = 0x2 << (4 * (i % 2))  # element i = 1.0
+        qe = np.full((1, D // 32), 127, np.uint8)
+        s = O.indexer_scores(q, qe, np.array([1.0]), kd)
+        assert np.array_equal(s, np.maximum(kd[:, i], 0.0))
+
+
+def test_scores_relu_per_head_and_invariants():
+    rng = np.random.default_rng(6)
+    H, D, n = 4, 64, 50
+    qv, qe = _mx_query(rng, H, D)
+    neg = qv ^ np.uint8(0x88)  # flip both sign bits: q -> -q
+    keys = O.mxfp4_decode(*[a.numpy() for a in WL.encode_mxfp4(torch.randn(n, D))])
+    w = rng.standard_normal(H)
+    s_pos = O.indexer_scores(qv, qe, w, keys)
+    s_neg = O.indexer_scores(neg, qe, w, keys)
+    qd = O.mxfp4_decode(qv, qe)
+    dots = qd @ keys.T
+    # relu applied per head: s(q) + s(-q) = sum_h w_h |q_h . k|
+    assert np.allclose(s_pos + s_neg, w @ np.abs(dots), rtol=1e-12, atol=1e-12)
+    assert np.allclose(s_pos - s_neg, w @ dots, rtol=1e-12, atol=1e-12)
+    # head permutation invariance, weight homogeneity
+    perm = rng.permutation(H)
+    assert np.allclose(O.indexer_scores(qv[perm], qe[perm], w[perm], keys), s_pos, rtol=1e-12)
+    assert np.array_equal(O.indexer_scores(qv, qe, 2 * w, keys), 2 * s_pos)
+    # every per-head dot product is exact in binary32 (any summation order)
+    assert np.array_equal(dots.astype(np.float32).astype(np.float64), dots)
+
+
+def test_topk_brute_force():
+    rng = np.random.default_rng(7)
+    for trial in range(200):
+        n = int(rng.integers(0, 30))
+        k = int(rng.integers(1, 12))
+        scores = np.round(rng.standard_normal(n), 1)  # many ties
+        valid = rng.random(n) < 0.8
+        got = O.topk_select(scores, valid, k)
+        cand = [i for i in range(n) if valid[i]]
+        chosen = []
+        for _ in range(min(k, len(cand))):
+            best = max(cand, key=lambda i: (scores[i], -i))
+            chosen.append(best)
+            cand.remove(best)
+        want = sorted(chosen) + [-1] * (k - len(chosen))
+        assert got.tolist() == want
+
+
+def test_topk_special_cases():
+    s = np.array([3.0, 1.0, 2.0])
+    assert O.topk_select(s, np.ones(3, bool), 5).tolist() == [0, 1, 2, -1, -1]
+    assert O.topk_select(s, np.ones(3, bool), 1).tolist() == [0]
+    assert O.topk_select(np.zeros(6), np.ones(6, bool), 3).tolist() == [0, 1, 2]
+    assert O.topk_select(np.zeros(0), np.zeros(0, bool), 2).tolist() == [-1, -1]
+
+
+# --------------------------------------------------------------------------- attention
+
+
+def _bf16_bits(x):
+    return torch.as_tensor(x, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_attend_matches_library_softmax():
+    from scipy.special import logsumexp, softmax
+
+    rng = np.random.default_rng(8)
+    H, n, D = 5, 37, 24
+    q = _bf16_bits(rng.standard_normal((H, D)))
+    x = _bf16_bits(rng.standard_normal((n, D)))
+    sink = rng.standard_normal(H)
+    qf, xf = O.bf16_bits_to_float(q), O.bf16_bits_to_float(x)
+    c = D ** -0.5
+    o, lse = O.attend(q, x, c, sink)
+    logits = np.concatenate([c * qf @ xf.T, sink[:, None]], axis=1)
+    p = softmax(logits, axis=1)
+    assert np.allclose(o, p[:, :n] @ xf, rtol=1e-12, atol=1e-14)
+    assert np.allclose(lse, logsumexp(logits, axis=1), rtol=1e-12)
+    o2, _ = O.attend(q, x, c, np.full(H, -np.inf))
+    o3, _ = O.attend(q, x, c, None)
+    assert np.allclose(o2, o3, rtol=1e-14, atol=0)
+
+
+def test_attend_degenerate_cases():
+    rng = np.random.default_rng(9)
+    q = _bf16_bits(rng.standard_normal((3, 16)))
+    x0 = _bf16_bits(rng.standard_normal((1, 16)))
+    o, _ = O.attend(q, x0, 0.25)
+    assert np.array_equal(o, np.repeat(O.bf16_bits_to_float(x0), 3, axis=0))  # single key
+    o, _ = O.attend(q, np.repeat(x0, 9, axis=0), 0.25)
+    assert np.allclose(o, np.repeat(O.bf16_bits_to_float(x0), 3, axis=0), rtol=1e-14)  # identical keys
+    o, lse = O.attend(q, np.zeros((0, 16), np.uint16), 0.25)
+    assert np.all(o == 0) and np.all(lse == -np.inf)  # empty set
+
+
+def test_sparse_equals_dense_when_everything_is_selected():
+    """topk >= n_c and window >= seq_len: the sparse step equals dense attention
+    over every compressed row and every position, computed by torch SDPA in
+    float64 over rows reached by walking the block tables directly."""
+    cfg = WL.with_overrides(WL.CONFIGS["tiny"], window=256, topk=64)
+    wl = WL.make_workload(cfg, "cpu")
+    v = WL.host_view(wl)
+    P = wl.padded_topk
+    res = O.step(v, cfg, P, wl.kv_pool.shape[0], wl.idx_pool.shape[0], wl.softmax_scale)
+    # the whole history was selected
+    assert res["lens"][0] == 64 and np.all(res["sparse_indices"][0] >= 0)
+    rows_swa = [O.logical_to_slot(v.swa_bt[0], p, cfg.block, 10**9) for p in range(256)]
+    rows_cmp = [O.logical_to_slot(v.comp_bt[0], l, cfg.block, 10**9) for l in range(64)]
+    rows = O.dequant_rows(v.kv_pages, rows_swa + rows_cmp, cfg.block, cfg.d_nope, cfg.d_rope)
+    x = torch.from_numpy(O.bf16_bits_to_float(rows))[None, None]  # [1,1,n,D]
+    q = torch.from_numpy(O.bf16_bits_to_float(v.q[0]))[None, :, None, :]  # [1,H,1,D]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, x.expand(1, cfg.heads, -1, -1), x.expand(1, cfg.heads, -1, -1), scale=wl.softmax_scale)
+    assert np.allclose(res["out"][0], ref[0, :, 0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_sparse_attention_ignores_padding_and_invalid_columns():
+    cfg = WL.CONFIGS["tiny"]
+    wl = WL.make_workload(cfg, "cpu")
+    v = WL.host_view(wl)
+    P = wl.padded_topk
+    res = O.step(v, cfg, P, wl.kv_pool.shape[0], wl.idx_pool.shape[0], wl.softmax_scale)
+    si = res["sparse_indices"].copy()
+    lens = res["lens"]
+    W = cfg.window
+    # garbage past lens and -1 anywhere must not change the result
+    si2 = si.copy()
+    si2[0, W + lens[0]:] = si[0, W]  # a valid slot, but past lens
+    o2, _ = O.sparse_mla_decode(v.q, v.kv_pages, v.kv_pages, si2, lens, W, cfg.block, cfg.block,
+                                cfg.d_nope, cfg.d_rope, wl.softmax_scale)
+    assert np.array_equal(o2, res["out"])
