@@ -1,0 +1,249 @@
+/*
+ * sad.h - C ABI of libsad.so, the MI355X (gfx950) sparse-attention decode step.
+ *
+ * The step (DeepSeek-V4 style sparse MLA decode) has five parts:
+ *   1. indexer scoring of each query token against MXFP4 keys of its request's
+ *      compressed rows,
+ *   2. per-token top-k over those scores,
+ *   3. local->global slot mapping through paged block tables, merged with the
+ *      sliding-window (SWA) slot ids into one sparse_indices row + a length,
+ *   4. dequantize-and-gather of the selected rows of a paged FP8 latent cache,
+ *   5. MLA attention of all query heads over the gathered rows.
+ * Parts 1+2 are indexer_score_topk, part 3 is build_sparse_indices, part 4 is
+ * gather_dequant_kv (standalone; also fused into part 5), part 5 is
+ * sparse_mla_decode.
+ *
+ * Sources (web pages; cited by page and function):
+ *   [ops]     tokenspeed "DeepSeek V4 attention kernel boundaries" page
+ *             (runtime/layers/attention/deepseek_v4_ops.py)
+ *   [model]   tokenspeed DeepSeek V4 model page (runtime/models/deepseek_v4.py)
+ *   [backend] tokenspeed DeepSeek V4 attention backend page
+ *   [vllm]    vLLM vllm.models.deepseek_v41.common.ops API page
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked "host".  Structs are passed
+ *     by host pointer and read on the host during the call only.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream).  No call allocates device memory, copies,
+ *     synchronizes or reads device data on the host, so every call may be
+ *     captured into a HIP graph.
+ *   - The caller owns every buffer; outputs and workspaces are caller
+ *     preallocated (the pages never allocate under graph capture: [model]
+ *     top-k buffer, [backend] SWA metadata).  The library keeps no state but
+ *     a thread-local error string.
+ *   - Return codes: SAD_OK; SAD_EINVAL (null required pointer, negative or
+ *     inconsistent size); SAD_EUNSUPPORTED (a dimension or block size outside
+ *     the supported set); SAD_EWORKSPACE (workspace too small); SAD_ELAUNCH
+ *     (the HIP launch failed).  sad_last_error() describes the last non-OK
+ *     return on the calling thread.  num_tokens == 0 returns SAD_OK and
+ *     launches nothing ([ops] empty-input early returns).
+ *   - Device data the host cannot check without a sync (stale ids, -1 pages,
+ *     ids past a table or past the pool) is handled fail closed ([model]
+ *     SWA slot sanitizing): any id that does not resolve to a row of the pool
+ *     becomes -1 and is masked; -1 means "no row" everywhere ([vllm] "-1 = skip").
+ *
+ * Cache formats:
+ *   sad_kv_cache (latent rows; [ops] dequantize_deepseek_v4_fp8_ds_mla_cache
+ *   page addressing with fp32 instead of ue8m0 scales): page g starts at
+ *   pool + g*page_stride and holds block_size rows.  Row o's values are at
+ *   byte o*(d_nope + 2*d_rope): d_nope FP8 e4m3fn (OCP) bytes then d_rope
+ *   bf16.  Row o's scales are at byte block_size*(d_nope + 2*d_rope) + o*4*(d_nope/64):
+ *   d_nope/64 fp32, one per 64 nope elements.  Row value: nope[d] =
+ *   bf16_rne(float(e4m3(v[d])) * scale[d/64]), rope copied.  A slot is
+ *   page*block_size + row.
+ *
+ *   sad_mxfp4_cache (indexer keys; [ops] read_deepseek_v4_indexer_mxfp4_cache):
+ *   page g holds block_size rows: first block_size*dim/2 bytes of packed E2M1
+ *   (row-major, low nibble = even element), then block_size*dim/32 e8m0
+ *   exponents (value 2^(b-127), one per 32 elements).
+ */
+#ifndef SAD_H
+#define SAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SAD_OK = 0,
+  SAD_EINVAL = 1,
+  SAD_EUNSUPPORTED = 2,
+  SAD_EWORKSPACE = 3,
+  SAD_ELAUNCH = 4
+};
+
+/* Paged FP8 latent KV cache (see "Cache formats").  Supported (d_nope, d_rope):
+ * (128, 32) and (512, 64); block_size 16 or 64; page_stride a multiple of 16 and
+ * >= block_size*(d_nope + 2*d_rope + 4*d_nope/64); num_pages*block_size < 2^31. */
+typedef struct {
+  const void* pool;    /* device, uint8 [num_pages * page_stride] */
+  int64_t page_stride; /* bytes between consecutive pages */
+  int64_t num_pages;   /* page ids outside [0, num_pages) are invalid */
+  int32_t block_size;  /* rows per page */
+  int32_t d_nope;      /* FP8 part of the row */
+  int32_t d_rope;      /* bf16 part of the row */
+} sad_kv_cache;
+
+/* Paged MXFP4 indexer-key cache.  dim 64 or 128; block_size 16 or 64;
+ * page_stride a multiple of 16 and >= block_size*(dim/2 + dim/32). */
+typedef struct {
+  const void* pool;
+  int64_t page_stride;
+  int64_t num_pages;
+  int32_t block_size;
+  int32_t dim;
+} sad_mxfp4_cache;
+
+/* Ragged batch ([backend] init_forward_metadata / _decode_positions_from_metadata).
+ * Token t belongs to request r = token_to_req[t] with query_start_loc[r] <= t <
+ * query_start_loc[r+1]; seq_lens[r] counts this step's query tokens, so the
+ * token's position is p = seq_lens[r] - (qsl[r+1]-qsl[r]) + (t - qsl[r]) and it
+ * sees n_c = floor((p+1)/compress_ratio) compressed rows ([model] indexer
+ * row_lens).  A token whose request id is out of range, or whose position is
+ * negative, sees nothing. */
+typedef struct {
+  const int32_t* query_start_loc; /* device [num_reqs + 1] */
+  const int32_t* seq_lens;        /* device [num_reqs] */
+  const int32_t* token_to_req;    /* device [num_tokens] */
+  int32_t num_reqs;
+  int32_t num_tokens;
+} sad_batch;
+
+/*
+ * build_sparse_indices - one sparse_indices row per token plus sparse_topk_lens.
+ *
+ * Defined by [vllm] build_flashinfer_mixed_sparse_indices (window columns first,
+ * then compressed columns; replay_start lower-bounds the window) and
+ * compute_global_topk_indices_and_lens (local id -> page*B + row, count of
+ * valid entries), [backend] _update_decode_swa_metadata (window = last
+ * window_size positions) and the dense branch of
+ * _decode_compressed_attention_indices_and_lens (ratio-128 layers attend to
+ * every compressed row).
+ *
+ * Row t of sparse_indices ([num_tokens, window_size + padded_topk] int32, row
+ * stride window_size + padded_topk):
+ *   columns [0, window_size): the slots of positions lo..p in ascending order,
+ *     lo = max(p - window_size + 1, replay_start[r], 0), mapped through
+ *     swa_bt[r][pos / swa_block_size]; then -1.  A position whose page is
+ *     unbacked (< 0, past swa_bt_cols or past swa_num_pages) gives -1 in its column.
+ *   columns [window_size, window_size + padded_topk): candidates are
+ *     topk_local[t][0..topk) (local compressed-row ids, -1 = none), or, when
+ *     topk_local is NULL (dense mode), 0..min(n_c, padded_topk)-1.  A candidate
+ *     l is kept when 0 <= l < n_c and comp_bt[r][l / comp_block_size] is a valid
+ *     page; kept candidates are written in candidate order as page*B + l%B,
+ *     packed to the left; the rest of the segment is -1.
+ *   sparse_topk_lens[t] = number of kept candidates.
+ * Integer-only; bit-exact.  padded_topk must be >= topk and a multiple of 64;
+ * topk_stride >= topk.  Block tables are int32 [num_reqs, cols] with row stride
+ * *_bt_stride (elements).  replay_start may be NULL (all 0).
+ */
+int build_sparse_indices(const sad_batch* batch, const int32_t* replay_start,
+                         const int32_t* swa_bt, int64_t swa_bt_stride, int32_t swa_bt_cols,
+                         int32_t swa_block_size, int64_t swa_num_pages,
+                         const int32_t* comp_bt, int64_t comp_bt_stride, int32_t comp_bt_cols,
+                         int32_t comp_block_size, int64_t comp_num_pages,
+                         const int32_t* topk_local, int64_t topk_stride, int32_t topk,
+                         int32_t window_size, int32_t compress_ratio, int32_t padded_topk,
+                         int32_t* sparse_indices, int32_t* sparse_topk_lens, void* stream);
+
+/*
+ * indexer_score_topk - indexer scores and per-token top-k local ids.
+ *
+ * Defined by [model] _deepseek_v4_indexer_topk_from_cache_deepgemm_decode (per
+ * token, MXFP4 query heads against every paged MXFP4 key of the token's
+ * request, weighted into one fp32 logit per compressed row) and
+ * _deepseek_v4_indexer_topk_from_logits (top-k over the first n_c logits,
+ * output prefilled with -1); weights are pre-folded as w * Di^-1/2 * Hi^-1/2
+ * ([vllm] fused_indexer_q_rope_quant, MXFP4 path).
+ *
+ * For token t of request r and each compressed row s < n_c(t) whose key page
+ * idx_bt[r][s / block_size] is valid:
+ *     score[s] = sum_h weights[t,h] * max(dot(q[t,h], key[s]), 0)
+ * (the per-head ReLU is this library's reading of the unprinted combination).
+ * q·key products are exact in fp32; the head sum is fp32.
+ * topk_local[t][0..m) = the m = min(topk, #valid rows) highest-scoring row ids
+ * in ASCENDING id order (ties at the threshold go to the lower id);
+ * topk_local[t][m..topk) = -1.
+ *
+ *   q_values  [num_tokens, num_idx_heads, dim/2] u8 packed E2M1 (low nibble even)
+ *   q_scales  [num_tokens, num_idx_heads, dim/32] u8 e8m0
+ *   weights   [num_tokens, num_idx_heads] fp32 (pre-folded)
+ *   idx_bt    int32 [num_reqs, idx_bt_cols], row stride idx_bt_stride
+ *   topk_local out int32 [num_tokens, topk]
+ *   logits_debug NULL, or out fp32 [num_tokens, logits_stride]: score[s] for
+ *     valid rows s < n_c(t), -inf for invalid rows s < n_c(t) (others untouched);
+ *     requires logits_stride >= idx_bt_cols*block_size.
+ *   workspace  >= indexer_score_topk_workspace_size(num_tokens, idx_bt_cols*block_size, topk)
+ * num_idx_heads in [1, 64]; topk in [1, 65536]; idx_bt_cols*block_size <= 32768.
+ */
+int indexer_score_topk(const sad_batch* batch, const uint8_t* q_values, const uint8_t* q_scales,
+                       const float* weights, int32_t num_idx_heads, const sad_mxfp4_cache* keys,
+                       const int32_t* idx_bt, int64_t idx_bt_stride, int32_t idx_bt_cols,
+                       int32_t compress_ratio, int32_t topk, int32_t* topk_local,
+                       float* logits_debug, int64_t logits_stride, void* workspace,
+                       size_t workspace_bytes, void* stream);
+size_t indexer_score_topk_workspace_size(int32_t num_tokens, int32_t max_ctx_rows, int32_t topk);
+
+/*
+ * gather_dequant_kv - dequantized rows of every attended column.
+ *
+ * Defined by [ops] dequantize_deepseek_v4_fp8_ds_mla_cache (slot -> page row,
+ * one fp32 multiply per FP8 element, bf16 rounding, slot -1 -> zero row) and
+ * [vllm] dequantize_and_gather_k_cache.
+ * out[t][c] ([num_tokens, window_size + padded_topk, d_nope + d_rope] bf16) is
+ * the dequantized row at slot sparse_indices[t][c] for window columns
+ * c < window_size (read from `swa`) and for compressed columns
+ * window_size <= c < window_size + sparse_topk_lens[t] (read from `comp`); it
+ * is all zeros for slot -1, for slots that do not resolve to a row of the pool,
+ * and for compressed columns past sparse_topk_lens[t].  Bit-exact.
+ * `swa` and `comp` must have the same (d_nope, d_rope); they may share a pool.
+ */
+int gather_dequant_kv(const sad_kv_cache* swa, const sad_kv_cache* comp,
+                      const int32_t* sparse_indices, const int32_t* sparse_topk_lens,
+                      int32_t num_tokens, int32_t window_size, int32_t padded_topk,
+                      uint16_t* out_bf16, void* stream);
+
+/*
+ * sparse_mla_decode - attention of every query head over the attended rows.
+ *
+ * Defined by [backend] forward_deepseek_v4_decode (FlashMLA sparse decode over
+ * window ids bounded by their lengths plus compressed ids bounded by
+ * extra_topk_length, FP8 cache, head_dim_v = head_dim, per-head attention
+ * sink) and [model] DeepseekV4Attention (softmax scale = head_dim^-1/2).
+ * For token t and head h, over the attended columns j (window columns with a
+ * valid slot, compressed columns < sparse_topk_lens[t] with a valid slot) with
+ * x_j the dequantized row (d_nope + d_rope values, as in gather_dequant_kv):
+ *     l_j = softmax_scale * dot(q[t,h], x_j)
+ *     out[t,h] = sum_j exp(l_j) x_j / (sum_j exp(l_j) + exp(attn_sink[h]))
+ *     lse[t,h] = log(sum_j exp(l_j) + exp(attn_sink[h]))      (natural log)
+ * (sink terms absent when attn_sink is NULL).  With nothing attended and no
+ * sink, out = 0 and lse = -inf.  fp32 softmax and accumulation (bf16 MFMA
+ * operands), bf16 out.
+ *   q_bf16  [num_tokens, num_heads, d_nope + d_rope] bf16
+ *   out_bf16 [num_tokens, num_heads, d_nope + d_rope] bf16
+ *   lse      NULL or fp32 [num_tokens, num_heads]
+ *   workspace >= sparse_mla_decode_workspace_size(num_tokens, num_heads,
+ *                window_size + padded_topk, d_nope + d_rope)
+ * num_heads in {8, 16, ..., 128} (a multiple of 8, <= 128); (d_nope, d_rope)
+ * = (512, 64) or (128, 32).
+ */
+int sparse_mla_decode(const uint16_t* q_bf16, int32_t num_tokens, int32_t num_heads,
+                      const sad_kv_cache* swa, const sad_kv_cache* comp,
+                      const int32_t* sparse_indices, const int32_t* sparse_topk_lens,
+                      int32_t window_size, int32_t padded_topk, float softmax_scale,
+                      const float* attn_sink, uint16_t* out_bf16, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+size_t sparse_mla_decode_workspace_size(int32_t num_tokens, int32_t num_heads,
+                                        int32_t max_row_width, int32_t dv);
+
+/* Description of the last non-OK return on the calling thread ("" if none). */
+const char* sad_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAD_H */

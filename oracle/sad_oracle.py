@@ -149,11 +149,22 @@ def logical_to_slot(bt_row, logical: int, block_size: int, num_pages: int) -> in
     return page * block_size + logical % block_size
 
 
+def _slots(bt_row, logical, block_size, num_pages):
+    """Vector form of ``logical_to_slot`` for an array of logical rows."""
+    logical = np.asarray(logical, dtype=np.int64)
+    bt_row = np.asarray(bt_row, dtype=np.int64)
+    col = np.where(logical >= 0, logical // block_size, 0)
+    inside = (logical >= 0) & (col < bt_row.shape[0])
+    page = np.where(inside, bt_row[np.minimum(col, max(bt_row.shape[0] - 1, 0))] if bt_row.size else -1, -1)
+    ok = inside & (page >= 0) & (page < num_pages)
+    return np.where(ok, page * block_size + logical % block_size, -1)
+
+
 def build_sparse_indices(
     query_start_loc, seq_lens, token_to_req, replay_start,
     swa_bt, swa_block_size, swa_num_pages,
     comp_bt, comp_block_size, comp_num_pages,
-    topk_local, topk, window_size, compress_ratio, padded_topk,
+    topk_local, topk, window_size, compress_ratio, padded_topk, tokens=None,
 ):
     """One int32 row per token: ``window_size`` window slots then ``padded_topk``
     compressed slots, plus the count of valid compressed slots.
@@ -166,37 +177,32 @@ def build_sparse_indices(
     ``_decode_compressed_attention_indices_and_lens``): each local id of the
     token's top-k row (or ``0..n_c-1`` when ``topk_local`` is None, the dense
     ratio-128 path) that is ``< n_c`` and maps to a backed page, in order,
-    packed left; then -1.
+    packed left; then -1.  ``tokens`` restricts the output rows to those tokens.
     """
     pos = token_positions(query_start_loc, seq_lens, token_to_req)
     req = np.asarray(token_to_req, dtype=np.int64)
     replay = np.zeros(len(seq_lens), np.int64) if replay_start is None else np.asarray(replay_start)
-    T = req.shape[0]
+    tokens = list(range(req.shape[0])) if tokens is None else list(tokens)
     W, P = int(window_size), int(padded_topk)
-    out = np.full((T, W + P), -1, dtype=np.int32)
-    lens = np.zeros(T, dtype=np.int32)
+    out = np.full((len(tokens), W + P), -1, dtype=np.int32)
+    lens = np.zeros(len(tokens), dtype=np.int32)
     nc_all = compressed_len(pos, compress_ratio)
-    for t in range(T):
+    for i, t in enumerate(tokens):
         r = int(req[t])
         p = int(pos[t])
         lo = max(p - W + 1, int(replay[r]), 0)
-        for j, q in enumerate(range(lo, p + 1)):
-            out[t, j] = logical_to_slot(swa_bt[r], q, swa_block_size, swa_num_pages)
+        window = np.arange(lo, p + 1)
+        out[i, : window.size] = _slots(swa_bt[r], window, swa_block_size, swa_num_pages)
         nc = int(nc_all[t])
         if topk_local is None:
-            cand = range(min(nc, P))
+            cand = np.arange(min(nc, P))
         else:
-            cand = [int(x) for x in topk_local[t, :topk]]
-        n = 0
-        for l in cand:
-            if l < 0 or l >= nc:
-                continue
-            s = logical_to_slot(comp_bt[r], l, comp_block_size, comp_num_pages)
-            if s < 0:
-                continue
-            out[t, W + n] = s
-            n += 1
-        lens[t] = n
+            cand = np.asarray(topk_local[t, :topk], dtype=np.int64)
+        cand = cand[(cand >= 0) & (cand < nc)]
+        slots = _slots(comp_bt[r], cand, comp_block_size, comp_num_pages)
+        slots = slots[slots >= 0]
+        out[i, W: W + slots.size] = slots
+        lens[i] = slots.size
     return out, lens
 
 

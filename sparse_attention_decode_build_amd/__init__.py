@@ -1,1 +1,19 @@
-"""MI355X-native sparse-attention decode step (DeepSeek-V4 style)."""
+"""MI355X-native sparse-attention decode step (DeepSeek-V4 style).
+
+The hot path lives in libsad.so (HIP kernels for gfx950, C ABI in include/sad.h);
+this package holds its ctypes binding, its build script and the seeded synthetic
+workloads used by the benchmark.
+"""
+
+from ._lib import (  # noqa: F401
+    IndexerCache,
+    KvCache,
+    build_sparse_indices,
+    gather_dequant_kv,
+    indexer_score_topk,
+    indexer_score_topk_workspace_size,
+    last_error,
+    load,
+    sparse_mla_decode,
+    sparse_mla_decode_workspace_size,
+)

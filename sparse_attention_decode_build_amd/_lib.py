@@ -1,0 +1,258 @@
+"""ctypes binding of libsad.so (argument marshalling only).
+
+Every function here takes torch device tensors, checks shapes/dtypes, passes raw
+pointers plus the current HIP stream to the C ABI declared in include/sad.h and
+raises on a non-OK return.  All computation happens in the HIP kernels; there is no
+fallback: if libsad.so is missing or fails to load, every entry point raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsad.so")
+
+SAD_OK, SAD_EINVAL, SAD_EUNSUPPORTED, SAD_EWORKSPACE, SAD_ELAUNCH = range(5)
+_ERR = {1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "ELAUNCH"}
+
+c_i32, c_i64, c_ptr, c_size, c_f32 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_float)
+
+
+class SadKvCache(ctypes.Structure):
+    _fields_ = [("pool", c_ptr), ("page_stride", c_i64), ("num_pages", c_i64),
+                ("block_size", c_i32), ("d_nope", c_i32), ("d_rope", c_i32)]
+
+
+class SadMxfp4Cache(ctypes.Structure):
+    _fields_ = [("pool", c_ptr), ("page_stride", c_i64), ("num_pages", c_i64),
+                ("block_size", c_i32), ("dim", c_i32)]
+
+
+class SadBatch(ctypes.Structure):
+    _fields_ = [("query_start_loc", c_ptr), ("seq_lens", c_ptr), ("token_to_req", c_ptr),
+                ("num_reqs", c_i32), ("num_tokens", c_i32)]
+
+
+_SIGNATURES = {
+    "build_sparse_indices": (c_i32, [ctypes.POINTER(SadBatch), c_ptr, c_ptr, c_i64, c_i32, c_i32, c_i64,
+                                     c_ptr, c_i64, c_i32, c_i32, c_i64, c_ptr, c_i64, c_i32, c_i32,
+                                     c_i32, c_i32, c_ptr, c_ptr, c_ptr]),
+    "indexer_score_topk": (c_i32, [ctypes.POINTER(SadBatch), c_ptr, c_ptr, c_ptr, c_i32,
+                                   ctypes.POINTER(SadMxfp4Cache), c_ptr, c_i64, c_i32, c_i32, c_i32,
+                                   c_ptr, c_ptr, c_i64, c_ptr, c_size, c_ptr]),
+    "indexer_score_topk_workspace_size": (c_size, [c_i32, c_i32, c_i32]),
+    "gather_dequant_kv": (c_i32, [ctypes.POINTER(SadKvCache), ctypes.POINTER(SadKvCache), c_ptr, c_ptr,
+                                  c_i32, c_i32, c_i32, c_ptr, c_ptr]),
+    "sparse_mla_decode": (c_i32, [c_ptr, c_i32, c_i32, ctypes.POINTER(SadKvCache),
+                                  ctypes.POINTER(SadKvCache), c_ptr, c_ptr, c_i32, c_i32, c_f32, c_ptr,
+                                  c_ptr, c_ptr, c_ptr, c_size, c_ptr]),
+    "sparse_mla_decode_workspace_size": (c_size, [c_i32, c_i32, c_i32, c_i32]),
+    "sad_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsad.so (once) and declare the C signatures; raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it first (python -m sparse_attention_decode_build_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().sad_last_error().decode()
+
+
+def _check(name: str, rc: int) -> None:
+    if rc != SAD_OK:
+        raise RuntimeError(f"{name} failed with SAD_{_ERR.get(rc, rc)}: {last_error()}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, name, dim=None, device=None):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must be {dim}-D, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+@dataclass
+class KvCache:
+    """A paged FP8 latent cache: uint8 pool [pages, page_bytes] + its geometry."""
+
+    pool: torch.Tensor
+    block_size: int
+    d_nope: int
+    d_rope: int
+
+    def c(self) -> SadKvCache:
+        _need(self.pool, torch.uint8, "kv pool", dim=2)
+        return SadKvCache(self.pool.data_ptr(), self.pool.stride(0), self.pool.shape[0],
+                          self.block_size, self.d_nope, self.d_rope)
+
+
+@dataclass
+class IndexerCache:
+    """A paged MXFP4 indexer-key cache: uint8 pool [pages, page_bytes] + geometry."""
+
+    pool: torch.Tensor
+    block_size: int
+    dim: int
+
+    def c(self) -> SadMxfp4Cache:
+        _need(self.pool, torch.uint8, "indexer pool", dim=2)
+        return SadMxfp4Cache(self.pool.data_ptr(), self.pool.stride(0), self.pool.shape[0],
+                             self.block_size, self.dim)
+
+
+def _batch(query_start_loc, seq_lens, token_to_req) -> SadBatch:
+    for t, nm in ((query_start_loc, "query_start_loc"), (seq_lens, "seq_lens"),
+                  (token_to_req, "token_to_req")):
+        _need(t, torch.int32, nm, dim=1)
+    if query_start_loc.numel() != seq_lens.numel() + 1:
+        raise ValueError("query_start_loc must have num_reqs + 1 entries")
+    return SadBatch(query_start_loc.data_ptr(), seq_lens.data_ptr(), token_to_req.data_ptr(),
+                    seq_lens.numel(), token_to_req.numel())
+
+
+def build_sparse_indices(query_start_loc, seq_lens, token_to_req, replay_start, swa_bt, swa_block_size,
+                         swa_num_pages, comp_bt, comp_block_size, comp_num_pages, topk_local, topk,
+                         window_size, compress_ratio, padded_topk, out=None, lens=None, stream=None):
+    """Window + compressed slot ids per token -> (sparse_indices [T, W+P], lens [T])."""
+    lib = load()
+    b = _batch(query_start_loc, seq_lens, token_to_req)
+    T = b.num_tokens
+    dev = token_to_req.device
+    for t, nm in ((swa_bt, "swa_bt"), (comp_bt, "comp_bt")):
+        _need(t, torch.int32, nm, dim=2)
+    if replay_start is not None:
+        _need(replay_start, torch.int32, "replay_start", dim=1)
+    if topk_local is not None:
+        _need(topk_local, torch.int32, "topk_local", dim=2)
+    if out is None:
+        out = torch.empty((T, window_size + padded_topk), dtype=torch.int32, device=dev)
+    if lens is None:
+        lens = torch.empty((T,), dtype=torch.int32, device=dev)
+    rc = lib.build_sparse_indices(
+        ctypes.byref(b), _p(replay_start), _p(swa_bt), swa_bt.stride(0), swa_bt.shape[1],
+        swa_block_size, swa_num_pages, _p(comp_bt), comp_bt.stride(0), comp_bt.shape[1],
+        comp_block_size, comp_num_pages, _p(topk_local),
+        topk_local.stride(0) if topk_local is not None else 0, topk, window_size, compress_ratio,
+        padded_topk, _p(out), _p(lens), _stream(stream))
+    _check("build_sparse_indices", rc)
+    return out, lens
+
+
+def indexer_score_topk_workspace_size(num_tokens, max_ctx_rows, topk) -> int:
+    return load().indexer_score_topk_workspace_size(num_tokens, max_ctx_rows, topk)
+
+
+def indexer_score_topk(query_start_loc, seq_lens, token_to_req, q_values, q_scales, weights,
+                       keys: IndexerCache, idx_bt, compress_ratio, topk, out=None, logits_debug=None,
+                       workspace=None, stream=None):
+    """MXFP4 indexer scores + per-token top-k -> topk_local [T, topk] (ascending ids, -1 pad)."""
+    lib = load()
+    b = _batch(query_start_loc, seq_lens, token_to_req)
+    T = b.num_tokens
+    _need(q_values, torch.uint8, "q_values", dim=3)
+    _need(q_scales, torch.uint8, "q_scales", dim=3)
+    _need(weights, torch.float32, "weights", dim=2)
+    _need(idx_bt, torch.int32, "idx_bt", dim=2)
+    num_heads = q_values.shape[1]
+    if out is None:
+        out = torch.empty((T, topk), dtype=torch.int32, device=q_values.device)
+    max_rows = idx_bt.shape[1] * keys.block_size
+    if workspace is None:
+        ws = lib.indexer_score_topk_workspace_size(T, max_rows, topk)
+        workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=q_values.device)
+    if logits_debug is not None:
+        _need(logits_debug, torch.float32, "logits_debug", dim=2)
+    kc = keys.c()
+    rc = lib.indexer_score_topk(
+        ctypes.byref(b), _p(q_values), _p(q_scales), _p(weights), num_heads, ctypes.byref(kc),
+        _p(idx_bt), idx_bt.stride(0), idx_bt.shape[1], compress_ratio, topk, _p(out),
+        _p(logits_debug), logits_debug.stride(0) if logits_debug is not None else 0,
+        _p(workspace), workspace.numel(), _stream(stream))
+    _check("indexer_score_topk", rc)
+    return out
+
+
+def gather_dequant_kv(swa: KvCache, comp: KvCache, sparse_indices, sparse_topk_lens, window_size,
+                      padded_topk, out=None, stream=None):
+    """Dequantized bf16 rows of every attended column -> [T, W+P, Dn+Dr]."""
+    lib = load()
+    _need(sparse_indices, torch.int32, "sparse_indices", dim=2)
+    _need(sparse_topk_lens, torch.int32, "sparse_topk_lens", dim=1)
+    T = sparse_indices.shape[0]
+    if sparse_indices.shape[1] != window_size + padded_topk:
+        raise ValueError("sparse_indices must be [T, window_size + padded_topk]")
+    if out is None:
+        out = torch.empty((T, window_size + padded_topk, swa.d_nope + swa.d_rope), dtype=torch.bfloat16,
+                          device=sparse_indices.device)
+    s, c = swa.c(), comp.c()
+    rc = lib.gather_dequant_kv(ctypes.byref(s), ctypes.byref(c), _p(sparse_indices),
+                               _p(sparse_topk_lens), T, window_size, padded_topk, _p(out),
+                               _stream(stream))
+    _check("gather_dequant_kv", rc)
+    return out
+
+
+def sparse_mla_decode_workspace_size(num_tokens, num_heads, max_row_width, dv) -> int:
+    return load().sparse_mla_decode_workspace_size(num_tokens, num_heads, max_row_width, dv)
+
+
+def sparse_mla_decode(q, swa: KvCache, comp: KvCache, sparse_indices, sparse_topk_lens, window_size,
+                      padded_topk, softmax_scale, attn_sink=None, out=None, lse=None, workspace=None,
+                      stream=None):
+    """Sparse MLA attention of every head -> out [T, H, Dn+Dr] bf16 (and lse [T, H] if given)."""
+    lib = load()
+    _need(q, torch.bfloat16, "q", dim=3)
+    _need(sparse_indices, torch.int32, "sparse_indices", dim=2)
+    _need(sparse_topk_lens, torch.int32, "sparse_topk_lens", dim=1)
+    T, H, D = q.shape
+    if attn_sink is not None:
+        _need(attn_sink, torch.float32, "attn_sink", dim=1)
+    if out is None:
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=q.device)
+    if lse is not None:
+        _need(lse, torch.float32, "lse", dim=2)
+    if workspace is None:
+        ws = lib.sparse_mla_decode_workspace_size(T, H, window_size + padded_topk, D)
+        workspace = torch.empty((max(ws, 16),), dtype=torch.uint8, device=q.device) if ws else None
+    s, c = swa.c(), comp.c()
+    rc = lib.sparse_mla_decode(_p(q), T, H, ctypes.byref(s), ctypes.byref(c), _p(sparse_indices),
+                               _p(sparse_topk_lens), window_size, padded_topk, softmax_scale,
+                               _p(attn_sink), _p(out), _p(lse), _p(workspace),
+                               workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check("sparse_mla_decode", rc)
+    return out

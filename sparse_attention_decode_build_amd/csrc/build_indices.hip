@@ -1,0 +1,128 @@
+// build_sparse_indices: window slots + compressed slots per token (integer only).
+//
+// [vllm] build_flashinfer_mixed_sparse_indices / compute_global_topk_indices_and_lens,
+// [backend] _update_decode_swa_metadata and the dense branch of
+// _decode_compressed_attention_indices_and_lens.  One workgroup per token row;
+// kept compressed candidates are compacted in candidate order with a ballot scan.
+#include "sad_internal.h"
+
+namespace sad {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void build_sparse_indices_kernel(
+    sad_batch b, const int32_t* __restrict__ replay, const int32_t* __restrict__ swa_bt,
+    int64_t swa_stride, int swa_cols, int swa_block, int64_t swa_pages,
+    const int32_t* __restrict__ comp_bt, int64_t comp_stride, int comp_cols, int comp_block,
+    int64_t comp_pages, const int32_t* __restrict__ topk_local, int64_t topk_stride, int topk,
+    int window, int ratio, int padded, int32_t* __restrict__ out, int32_t* __restrict__ lens) {
+  __shared__ int wave_count[kThreads / 64];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int32_t* row = out + (int64_t)t * (window + padded);
+
+  TokenGeom g;
+  const bool ok = token_geometry(b, t, ratio, g);
+
+  // Window columns: positions lo..pos ascending, then -1.
+  int lo = 0;
+  if (ok) {
+    lo = g.pos - window + 1;
+    if (replay != nullptr) lo = max(lo, replay[g.req]);
+    lo = max(lo, 0);
+  }
+  const int32_t* swa_row = ok ? swa_bt + (int64_t)g.req * swa_stride : nullptr;
+  for (int j = tid; j < window; j += kThreads) {
+    const int p = lo + j;
+    int s = -1;
+    if (ok && p <= g.pos) s = page_slot(swa_row, swa_cols, swa_block, swa_pages, p);
+    row[j] = s;
+  }
+
+  // Compressed columns: kept candidates packed left in candidate order.
+  const int ncand = !ok ? 0 : (topk_local != nullptr ? topk : min(g.n_comp, padded));
+  const int32_t* comp_row = ok ? comp_bt + (int64_t)g.req * comp_stride : nullptr;
+  const int32_t* cand_row = topk_local != nullptr ? topk_local + (int64_t)t * topk_stride : nullptr;
+  int base = 0;
+  for (int c0 = 0; c0 < ncand; c0 += kThreads) {
+    const int c = c0 + tid;
+    int s = -1;
+    if (c < ncand) {
+      const int l = cand_row != nullptr ? cand_row[c] : c;
+      if (l >= 0 && l < g.n_comp) s = page_slot(comp_row, comp_cols, comp_block, comp_pages, l);
+    }
+    const uint64_t m = __ballot(s >= 0);
+    const int below = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_count[wave] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    int total = base;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      const int cw = wave_count[w];
+      if (w < wave) off += cw;
+      total += cw;
+    }
+    if (s >= 0) row[window + off + below] = s;
+    base = total;
+    __syncthreads();
+  }
+  for (int j = base + tid; j < padded; j += kThreads) row[window + j] = -1;
+  if (tid == 0) lens[t] = base;
+}
+
+}  // namespace
+}  // namespace sad
+
+using namespace sad;
+
+extern "C" int build_sparse_indices(const sad_batch* batch, const int32_t* replay_start,
+                                    const int32_t* swa_bt, int64_t swa_bt_stride,
+                                    int32_t swa_bt_cols, int32_t swa_block_size,
+                                    int64_t swa_num_pages, const int32_t* comp_bt,
+                                    int64_t comp_bt_stride, int32_t comp_bt_cols,
+                                    int32_t comp_block_size, int64_t comp_num_pages,
+                                    const int32_t* topk_local, int64_t topk_stride, int32_t topk,
+                                    int32_t window_size, int32_t compress_ratio,
+                                    int32_t padded_topk, int32_t* sparse_indices,
+                                    int32_t* sparse_topk_lens, void* stream) {
+  clear_error();
+  SAD_CHECK(batch != nullptr, SAD_EINVAL, "build_sparse_indices: batch is NULL");
+  const int T = batch->num_tokens;
+  SAD_CHECK(T >= 0 && batch->num_reqs >= 0, SAD_EINVAL,
+            "build_sparse_indices: negative num_tokens/num_reqs");
+  SAD_CHECK(window_size >= 0 && padded_topk >= 0 && topk >= 0, SAD_EINVAL,
+            "build_sparse_indices: negative window_size/padded_topk/topk");
+  SAD_CHECK(padded_topk % 64 == 0, SAD_EINVAL,
+            "build_sparse_indices: padded_topk (%d) must be a multiple of 64", padded_topk);
+  SAD_CHECK(compress_ratio >= 1, SAD_EINVAL, "build_sparse_indices: compress_ratio must be >= 1");
+  SAD_CHECK(topk_local == nullptr || (topk <= padded_topk && topk_stride >= topk), SAD_EINVAL,
+            "build_sparse_indices: need topk <= padded_topk and topk_stride >= topk");
+  SAD_CHECK(swa_block_size >= 1 && comp_block_size >= 1, SAD_EINVAL,
+            "build_sparse_indices: block sizes must be >= 1");
+  SAD_CHECK(swa_bt_cols >= 0 && comp_bt_cols >= 0 && swa_num_pages >= 0 && comp_num_pages >= 0,
+            SAD_EINVAL, "build_sparse_indices: negative table/pool size");
+  SAD_CHECK(swa_num_pages * (int64_t)swa_block_size <= INT32_MAX &&
+                comp_num_pages * (int64_t)comp_block_size <= INT32_MAX,
+            SAD_EINVAL, "build_sparse_indices: slots must fit int32 (num_pages*block_size)");
+  SAD_CHECK(swa_bt_stride >= swa_bt_cols && comp_bt_stride >= comp_bt_cols, SAD_EINVAL,
+            "build_sparse_indices: table stride smaller than its column count");
+  SAD_CHECK((int64_t)T * (window_size + padded_topk) < ((int64_t)1 << 40), SAD_EINVAL,
+            "build_sparse_indices: output too large");
+  if (T == 0) return SAD_OK;
+  SAD_CHECK(batch->query_start_loc && batch->seq_lens && batch->token_to_req, SAD_EINVAL,
+            "build_sparse_indices: batch arrays must be non-NULL");
+  SAD_CHECK(swa_bt != nullptr && comp_bt != nullptr, SAD_EINVAL,
+            "build_sparse_indices: block tables must be non-NULL");
+  SAD_CHECK(sparse_indices != nullptr && sparse_topk_lens != nullptr, SAD_EINVAL,
+            "build_sparse_indices: outputs must be non-NULL");
+  hipLaunchKernelGGL(build_sparse_indices_kernel, dim3(T), dim3(kThreads), 0,
+                     (hipStream_t)stream, *batch, replay_start, swa_bt, swa_bt_stride, swa_bt_cols,
+                     swa_block_size, swa_num_pages, comp_bt, comp_bt_stride, comp_bt_cols,
+                     comp_block_size, comp_num_pages, topk_local, topk_stride, topk, window_size,
+                     compress_ratio, padded_topk, sparse_indices, sparse_topk_lens);
+  return check_launch("build_sparse_indices");
+}

@@ -1,0 +1,394 @@
+// indexer_score_topk: MXFP4 indexer scores and per-token top-k local row ids.
+//
+// [model] _deepseek_v4_indexer_topk_from_cache_deepgemm_decode (per token, every
+// indexer head's MXFP4 query against each paged MXFP4 key of the request, weighted
+// into one fp32 logit per compressed row) and _deepseek_v4_indexer_topk_from_logits
+// (top-k of the first n_c logits, -1 prefilled).  The head combination
+// sum_h w_h * ReLU(q_h . k) is this library's reading of the unprinted formula.
+//
+// Scoring: v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1 and the e8m0
+// block exponents as the hardware scales: one lane carries 32 elements of one row
+// together with that block's exponent, which is exactly the MXFP4 block of the
+// cache, so a 128-dim key is one MFMA per 16 heads x 16 keys.  FP4 x FP4 products
+// scaled by powers of two are exact in fp32, so every per-head dot is exact.
+//
+// Top-k: one 1024-thread workgroup per token holds the token's keys in registers
+// (order-preserving uint32 transform), finds the exact k-th largest key with four
+// 8-bit radix passes over per-wave LDS histograms, then compacts the winners in
+// row order (ties at the threshold go to the lower row id), so the output is
+// ascending.
+#include "sad_internal.h"
+
+namespace sad {
+namespace {
+
+// ------------------------------------------------------------------ scoring
+
+constexpr int kScoreThreads = 256;
+constexpr int kScoreChunk = 1024;  // compressed rows per workgroup
+
+struct IdxDesc {
+  const uint8_t* pool;
+  int64_t stride;
+  int64_t num_pages;
+  int block;
+};
+
+template <int DIM>
+__global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
+    sad_batch b, const uint8_t* __restrict__ qv, const uint8_t* __restrict__ qs,
+    const float* __restrict__ wts, int num_heads, IdxDesc kc, const int32_t* __restrict__ bt,
+    int64_t bt_stride, int bt_cols, int ratio, float* __restrict__ logits, int64_t logits_stride,
+    float* __restrict__ dbg, int64_t dbg_stride) {
+  constexpr int VB = DIM / 2;    // packed value bytes per row
+  constexpr int SB = DIM / 32;   // exponent bytes per row
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  TokenGeom g;
+  if (!token_geometry(b, t, ratio, g)) return;
+  const int n_rows = min(g.n_comp, bt_cols * kc.block);
+  const int s_begin = blockIdx.x * kScoreChunk;
+  if (s_begin >= n_rows) return;
+  const int s_end = min(s_begin + kScoreChunk, n_rows);
+
+  // A operands: 16 heads x 128 dims per tile; lane (m = lane%16, grp = lane/16)
+  // holds dims [32*grp, 32*grp+32) of head 16*ht + m and that block's exponent.
+  const int m = lane & 15;
+  const int grp = lane >> 4;
+  i32x8_t qa[4];
+  int qsc[4];
+  float wl[4][4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const int h = ht * 16 + m;
+    qa[ht] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    qsc[ht] = 127;
+    if (h < num_heads && grp < SB) {
+      const int4 v = *reinterpret_cast<const int4*>(qv + ((int64_t)t * num_heads + h) * VB + 16 * grp);
+      qa[ht][0] = v.x;
+      qa[ht][1] = v.y;
+      qa[ht][2] = v.z;
+      qa[ht][3] = v.w;
+      qsc[ht] = qs[((int64_t)t * num_heads + h) * SB + grp];
+    }
+    // this lane's outputs are heads 16*ht + 4*grp + j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ho = ht * 16 + 4 * grp + j;
+      wl[ht][j] = ho < num_heads ? wts[(int64_t)t * num_heads + ho] : 0.0f;
+    }
+  }
+  const int32_t* bt_row = bt + (int64_t)g.req * bt_stride;
+  float* lrow = logits + (int64_t)t * logits_stride;
+  float* drow = dbg != nullptr ? dbg + (int64_t)t * dbg_stride : nullptr;
+
+  // Each wave takes 16-row groups; two groups in flight per iteration.
+  for (int s0 = s_begin + wave * 16; s0 < s_end; s0 += 2 * 4 * 16) {
+    i32x8_t kb[2];
+    int ksc[2];
+    bool kval[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int sg = s0 + u * 4 * 16;
+      kb[u] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      ksc[u] = 127;
+      kval[u] = false;
+      if (sg < s_end) {
+        const int col = sg / kc.block;  // 16 | block, so the group sits in one page
+        const int page = bt_row[col];
+        kval[u] = page >= 0 && (int64_t)page < kc.num_pages;
+        if (kval[u] && grp < SB) {
+          const int ro = sg - col * kc.block + m;
+          const uint8_t* pg = kc.pool + (int64_t)page * kc.stride;
+          const int4 v = *reinterpret_cast<const int4*>(pg + (int64_t)ro * VB + 16 * grp);
+          kb[u][0] = v.x;
+          kb[u][1] = v.y;
+          kb[u][2] = v.z;
+          kb[u][3] = v.w;
+          ksc[u] = pg[(int64_t)kc.block * VB + (int64_t)ro * SB + grp];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int sg = s0 + u * 4 * 16;
+      if (sg >= s_end) break;
+      float part = 0.0f;
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        if (ht * 16 >= num_heads) break;
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        // format 4 = E2M1 for both operands; scales are e8m0 in byte 0
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kb[u], acc, 4, 4, 0, qsc[ht],
+                                                              0, ksc[u]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part += wl[ht][j] * fmaxf(acc[j], 0.0f);
+      }
+      // lanes m, m+16, m+32, m+48 hold the 4 head groups of row sg + m
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      if (lane < 16 && sg + lane < s_end) {
+        const float v = kval[u] ? part : -INFINITY;
+        lrow[sg + lane] = v;
+        if (drow != nullptr) drow[sg + lane] = v;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ top-k
+
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+
+__device__ inline uint32_t order_key(float f) {
+  // -inf and NaN mark rows that are not candidates
+  if (!(f > -INFINITY)) return 0u;
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum over the workgroup (all threads must call); returns the
+// exclusive prefix and writes the total to *total.
+__device__ inline int block_excl_scan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  int off = 0;
+  int tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const int c = sh[w];
+    if (w < wave) off += c;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + incl - v;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
+    sad_batch b, int ratio, int max_rows, const float* __restrict__ logits, int64_t logits_stride,
+    int k, int32_t* __restrict__ out) {
+  __shared__ int hist[kTopkWaves][256];
+  __shared__ int scan_sh[kTopkWaves];
+  __shared__ int pick[2];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int32_t* orow = out + (int64_t)t * k;
+  TokenGeom g;
+  const bool ok = token_geometry(b, t, ratio, g);
+  const int n = ok ? min(g.n_comp, max_rows) : 0;
+  if (n == 0) {
+    for (int j = tid; j < k; j += kTopkThreads) orow[j] = -1;
+    return;
+  }
+  const float* lrow = logits + (int64_t)t * logits_stride;
+  const int base = tid * KPT;
+  uint32_t key[KPT];
+  int nvalid_local = 0;
+#pragma unroll
+  for (int i = 0; i < KPT; i += 4) {
+    float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (base + i + 3 < n) {
+      v = *reinterpret_cast<const float4*>(lrow + base + i);
+    } else {
+      if (base + i + 0 < n) v.x = lrow[base + i + 0];
+      if (base + i + 1 < n) v.y = lrow[base + i + 1];
+      if (base + i + 2 < n) v.z = lrow[base + i + 2];
+    }
+    key[i + 0] = order_key(v.x);
+    key[i + 1] = order_key(v.y);
+    key[i + 2] = order_key(v.z);
+    key[i + 3] = order_key(v.w);
+  }
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) nvalid_local += key[i] != 0u;
+  int nvalid;
+  (void)block_excl_scan(nvalid_local, scan_sh, &nvalid);
+
+  uint32_t thr = 0u;  // keys > thr are taken, plus `need` keys == thr in row order
+  int need = 0;
+  if (nvalid > k) {
+    uint32_t prefix = 0u, pmask = 0u;
+    int kk = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int j = tid; j < kTopkWaves * 256; j += kTopkThreads) (&hist[0][0])[j] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        if ((key[i] & pmask) == prefix) atomicAdd(&hist[wave][(key[i] >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane owns bins 4*lane .. 4*lane+3; suffix sums from the top bin down
+        int c[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          int s = 0;
+          for (int w = 0; w < kTopkWaves; ++w) s += hist[w][4 * lane + q];
+          c[q] = s;
+        }
+        const int lane_sum = c[0] + c[1] + c[2] + c[3];
+        // inclusive suffix over lanes: sum of lane_sum for lanes >= this lane
+        int suf = lane_sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_down(suf, off, 64);
+          if (lane + off < 64) suf += o;
+        }
+        int above = suf - lane_sum;  // keys in bins of higher lanes
+#pragma unroll
+        for (int q = 3; q >= 0; --q) {
+          if (above < kk && kk <= above + c[q]) {
+            pick[0] = 4 * lane + q;
+            pick[1] = above;
+          }
+          above += c[q];
+        }
+      }
+      __syncthreads();
+      const int d = pick[0];
+      kk -= pick[1];
+      prefix |= (uint32_t)d << shift;
+      pmask |= 255u << shift;
+      __syncthreads();
+    }
+    thr = prefix;
+    need = kk;
+  }
+
+  // rank of equal keys in row order, then compaction of the winners in row order
+  int eq_local = 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) eq_local += (key[i] == thr && thr != 0u);
+  int dummy;
+  const int eq_before = block_excl_scan(eq_local, scan_sh, &dummy);
+  int sel_local = 0;
+  {
+    int run = eq_before;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      bool s = key[i] > thr;
+      if (key[i] == thr && thr != 0u) {
+        s = run < need;
+        ++run;
+      }
+      sel_local += s;
+    }
+  }
+  int total;
+  int pos = block_excl_scan(sel_local, scan_sh, &total);
+  {
+    int run = eq_before;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      bool s = key[i] > thr;
+      if (key[i] == thr && thr != 0u) {
+        s = run < need;
+        ++run;
+      }
+      if (s) orow[pos++] = base + i;
+    }
+  }
+  for (int j = total + tid; j < k; j += kTopkThreads) orow[j] = -1;
+}
+
+}  // namespace
+}  // namespace sad
+
+using namespace sad;
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+extern "C" size_t indexer_score_topk_workspace_size(int32_t num_tokens, int32_t max_ctx_rows,
+                                                    int32_t topk) {
+  (void)topk;
+  if (num_tokens <= 0 || max_ctx_rows <= 0) return 0;
+  const size_t stride = (size_t)((max_ctx_rows + 3) / 4 * 4);
+  return align256((size_t)num_tokens * stride * sizeof(float));
+}
+
+extern "C" int indexer_score_topk(const sad_batch* batch, const uint8_t* q_values,
+                                  const uint8_t* q_scales, const float* weights,
+                                  int32_t num_idx_heads, const sad_mxfp4_cache* keys,
+                                  const int32_t* idx_bt, int64_t idx_bt_stride, int32_t idx_bt_cols,
+                                  int32_t compress_ratio, int32_t topk, int32_t* topk_local,
+                                  float* logits_debug, int64_t logits_stride, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  clear_error();
+  SAD_CHECK(batch != nullptr && keys != nullptr, SAD_EINVAL, "indexer_score_topk: NULL batch/keys");
+  const int T = batch->num_tokens;
+  SAD_CHECK(T >= 0 && batch->num_reqs >= 0, SAD_EINVAL, "indexer_score_topk: negative sizes");
+  SAD_CHECK(keys->dim == 64 || keys->dim == 128, SAD_EUNSUPPORTED,
+            "indexer_score_topk: dim %d unsupported (64 or 128)", keys->dim);
+  SAD_CHECK(keys->block_size == 16 || keys->block_size == 64, SAD_EUNSUPPORTED,
+            "indexer_score_topk: block_size %d unsupported (16 or 64)", keys->block_size);
+  SAD_CHECK(num_idx_heads >= 1 && num_idx_heads <= 64, SAD_EUNSUPPORTED,
+            "indexer_score_topk: num_idx_heads %d unsupported (1..64)", num_idx_heads);
+  SAD_CHECK(topk >= 1 && topk <= 65536, SAD_EINVAL, "indexer_score_topk: topk must be in [1, 65536]");
+  SAD_CHECK(compress_ratio >= 1, SAD_EINVAL, "indexer_score_topk: compress_ratio must be >= 1");
+  SAD_CHECK(idx_bt_cols >= 0 && idx_bt_stride >= idx_bt_cols, SAD_EINVAL,
+            "indexer_score_topk: bad table shape");
+  const int64_t need_stride = (int64_t)keys->block_size * (keys->dim / 2 + keys->dim / 32);
+  SAD_CHECK(keys->page_stride >= need_stride && keys->page_stride % 16 == 0, SAD_EINVAL,
+            "indexer_score_topk: page_stride must be a multiple of 16 and >= %lld",
+            (long long)need_stride);
+  SAD_CHECK(keys->num_pages >= 0, SAD_EINVAL, "indexer_score_topk: negative num_pages");
+  const int64_t max_rows64 = (int64_t)idx_bt_cols * keys->block_size;
+  SAD_CHECK(max_rows64 <= 32 * kTopkThreads, SAD_EUNSUPPORTED,
+            "indexer_score_topk: idx_bt_cols*block_size = %lld exceeds 32768 rows",
+            (long long)max_rows64);
+  const int max_rows = (int)max_rows64;
+  SAD_CHECK(logits_debug == nullptr || logits_stride >= max_rows, SAD_EINVAL,
+            "indexer_score_topk: logits_stride must be >= idx_bt_cols*block_size");
+  if (T == 0) return SAD_OK;
+  SAD_CHECK(batch->query_start_loc && batch->seq_lens && batch->token_to_req, SAD_EINVAL,
+            "indexer_score_topk: batch arrays must be non-NULL");
+  SAD_CHECK(q_values && q_scales && weights && idx_bt && topk_local && keys->pool, SAD_EINVAL,
+            "indexer_score_topk: NULL pointer argument");
+  SAD_CHECK(((uintptr_t)q_values & 15) == 0 && ((uintptr_t)keys->pool & 15) == 0, SAD_EINVAL,
+            "indexer_score_topk: q_values and the key pool must be 16-byte aligned");
+  const size_t ws_need = indexer_score_topk_workspace_size(T, max_rows, topk);
+  SAD_CHECK(workspace_bytes >= ws_need && (ws_need == 0 || workspace != nullptr), SAD_EWORKSPACE,
+            "indexer_score_topk: workspace needs %zu bytes, got %zu", ws_need, workspace_bytes);
+  SAD_CHECK(((uintptr_t)workspace & 15) == 0, SAD_EINVAL,
+            "indexer_score_topk: workspace must be 16-byte aligned");
+  const int64_t ws_stride = (max_rows + 3) / 4 * 4;
+  float* logits = reinterpret_cast<float*>(workspace);
+  IdxDesc kd{(const uint8_t*)keys->pool, keys->page_stride, keys->num_pages, keys->block_size};
+  hipStream_t st = (hipStream_t)stream;
+  if (max_rows > 0) {
+    const dim3 grid((max_rows + kScoreChunk - 1) / kScoreChunk, T);
+    if (keys->dim == 128) {
+      hipLaunchKernelGGL((indexer_score_kernel<128>), grid, dim3(kScoreThreads), 0, st, *batch,
+                         q_values, q_scales, weights, num_idx_heads, kd, idx_bt, idx_bt_stride,
+                         idx_bt_cols, compress_ratio, logits, ws_stride, logits_debug,
+                         logits_stride);
+    } else {
+      hipLaunchKernelGGL((indexer_score_kernel<64>), grid, dim3(kScoreThreads), 0, st, *batch,
+                         q_values, q_scales, weights, num_idx_heads, kd, idx_bt, idx_bt_stride,
+                         idx_bt_cols, compress_ratio, logits, ws_stride, logits_debug,
+                         logits_stride);
+    }
+    int rc = check_launch("indexer_score_topk(score)");
+    if (rc != SAD_OK) return rc;
+  }
+  if (max_rows <= 4 * kTopkThreads) {
+    hipLaunchKernelGGL((topk_kernel<4>), dim3(T), dim3(kTopkThreads), 0, st, *batch,
+                       compress_ratio, max_rows, logits, ws_stride, topk, topk_local);
+  } else if (max_rows <= 16 * kTopkThreads) {
+    hipLaunchKernelGGL((topk_kernel<16>), dim3(T), dim3(kTopkThreads), 0, st, *batch,
+                       compress_ratio, max_rows, logits, ws_stride, topk, topk_local);
+  } else {
+    hipLaunchKernelGGL((topk_kernel<32>), dim3(T), dim3(kTopkThreads), 0, st, *batch,
+                       compress_ratio, max_rows, logits, ws_stride, topk, topk_local);
+  }
+  return check_launch("indexer_score_topk(topk)");
+}

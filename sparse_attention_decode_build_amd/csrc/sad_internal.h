@@ -1,0 +1,125 @@
+// Internal helpers shared by the libsad.so translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sad.h"
+
+namespace sad {
+
+// ---- host-side error reporting -------------------------------------------------
+
+void set_error(const char* fmt, ...);
+void clear_error();
+int check_launch(const char* what);
+// Host-side validation of a latent KV cache descriptor (SAD_OK or an error code).
+int check_kv_cache(const sad_kv_cache* c, const char* what);
+
+#define SAD_CHECK(cond, code, ...)   \
+  do {                               \
+    if (!(cond)) {                   \
+      ::sad::set_error(__VA_ARGS__); \
+      return (code);                 \
+    }                                \
+  } while (0)
+
+// Number of compute units the launch heuristics assume (MI355X: 256 CUs in 8 XCDs).
+constexpr int kNumCUs = 256;
+
+// ---- vector types -----------------------------------------------------------------
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2_t;
+
+// ---- token geometry ---------------------------------------------------------------
+
+// Request, position and number of visible compressed rows of token t.
+// ([backend] _decode_positions_from_metadata; [model] indexer row_lens.)
+struct TokenGeom {
+  int req;
+  int pos;
+  int n_comp;
+};
+
+// Returns false when the token sees nothing (bad request id or negative position).
+__device__ inline bool token_geometry(const sad_batch& b, int t, int ratio, TokenGeom& g) {
+  const int r = b.token_to_req[t];
+  g.req = r;
+  g.pos = -1;
+  g.n_comp = 0;
+  if (r < 0 || r >= b.num_reqs) return false;
+  const int q0 = b.query_start_loc[r];
+  const int q1 = b.query_start_loc[r + 1];
+  const int p = b.seq_lens[r] - (q1 - q0) + (t - q0);
+  if (p < 0) return false;
+  g.pos = p;
+  g.n_comp = (p + 1) / ratio;
+  return true;
+}
+
+// Paged lookup: logical row -> slot, or -1 when the page is not a valid pool page.
+__device__ inline int page_slot(const int32_t* bt_row, int cols, int block, int64_t num_pages,
+                                int logical) {
+  if (logical < 0) return -1;
+  const int col = logical / block;
+  if (col >= cols) return -1;
+  const int page = bt_row[col];
+  if (page < 0 || (int64_t)page >= num_pages) return -1;
+  return page * block + (logical - col * block);
+}
+
+// A slot resolves to a row of the pool iff 0 <= slot / block < num_pages.
+__device__ inline bool slot_ok(int slot, int block, int64_t num_pages) {
+  return slot >= 0 && (int64_t)(slot / block) < num_pages;
+}
+
+// ---- wave / block reductions ------------------------------------------------------
+
+__device__ inline int wave_lane() { return __lane_id(); }
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ inline int wave_incl_scan(int v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ inline int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ---- element conversions ------------------------------------------------------------
+
+// Round a float to bf16 bits, nearest-even (finite inputs).
+__device__ inline uint16_t f32_to_bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ inline float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// OCP e4m3fn byte -> float (exact).  gfx950's conversion instruction decodes OCP
+// FP8; byte selects which of the 4 bytes of `word` is converted.
+template <int kByte>
+__device__ inline float e4m3_to_f32(uint32_t word) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)word, kByte);
+}
+
+}  // namespace sad

@@ -450,19 +450,22 @@ class HostView:
     idx_pages: dict
 
 
-def host_view(wl: Workload, layer: int = 0, pages: str = "all") -> HostView:
+def host_view(wl: Workload, layer: int = 0, reqs=None) -> HostView:
     """Copy one layer to host numpy arrays.
 
-    Only pages the layer's tables reference are copied (the pools may be far
-    larger than host memory should hold).
+    Only the pages referenced by the block tables of ``reqs`` (default: every
+    request) are copied; the pools may be far larger than host memory.
     """
     L = wl.layers[layer]
 
     def np_(t):
         return t.detach().cpu().numpy()
 
-    kv_ids = sorted(set(L.kv_pages))
-    idx_ids = sorted(set(L.idx_pages))
+    rows = slice(None) if reqs is None else torch.as_tensor(sorted(set(reqs)), device=L.swa_bt.device)
+    kv_ids = torch.cat([L.swa_bt[rows].flatten(), L.comp_bt[rows].flatten()])
+    kv_ids = sorted(set(kv_ids[kv_ids >= 0].cpu().tolist()))
+    idx_ids = L.idx_bt[rows].flatten()
+    idx_ids = sorted(set(idx_ids[idx_ids >= 0].cpu().tolist()))
     kv_pages = {}
     idx_pages = {}
     chunk = 4096

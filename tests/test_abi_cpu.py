@@ -1,0 +1,120 @@
+"""libsad.so loads, exports every function include/sad.h declares, and rejects bad
+arguments on the host (no kernel launch, so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_attention_decode_build_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from sparse_attention_decode_build_amd.build import build
+
+        build()
+    return L.load()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "sad.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert {"build_sparse_indices", "indexer_score_topk", "gather_dequant_kv", "sparse_mla_decode"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+FAKE = 4096  # a non-NULL, 16-byte aligned pointer value that is never dereferenced on the host
+
+
+def _batch(T, R=1):
+    return L.SadBatch(FAKE, FAKE, FAKE, R, T)
+
+
+def _kv(d_nope=512, d_rope=64, block=64, stride=None, pages=10):
+    stride = stride if stride is not None else block * (d_nope + 2 * d_rope + 4 * (d_nope // 64))
+    return L.SadKvCache(FAKE, stride, pages, block, d_nope, d_rope)
+
+
+def _call_build(lib, batch, padded=64, topk=16, window=32, stride=16, ratio=4):
+    return lib.build_sparse_indices(
+        ctypes.byref(batch) if batch is not None else None, None, FAKE, 4, 4, 16, 100, FAKE, 4, 4, 16,
+        100, FAKE, stride, topk, window, ratio, padded, FAKE, FAKE, None)
+
+
+def test_build_sparse_indices_errors(lib):
+    assert _call_build(lib, None) == L.SAD_EINVAL
+    assert "batch" in L.last_error()
+    assert _call_build(lib, _batch(0)) == L.SAD_OK  # empty batch: no launch
+    assert L.last_error() == ""
+    assert _call_build(lib, _batch(3), padded=60) == L.SAD_EINVAL  # not a multiple of 64
+    assert _call_build(lib, _batch(3), topk=128, padded=64) == L.SAD_EINVAL  # topk > padded
+    assert _call_build(lib, _batch(3), stride=8) == L.SAD_EINVAL  # topk_stride < topk
+    assert _call_build(lib, _batch(3), ratio=0) == L.SAD_EINVAL
+    assert _call_build(lib, _batch(-1)) == L.SAD_EINVAL
+
+
+def _call_indexer(lib, T=2, dim=128, heads=64, block=64, cols=4, topk=16, ws_bytes=1 << 30, ratio=4):
+    keys = L.SadMxfp4Cache(FAKE, block * (dim // 2 + dim // 32), 10, block, dim)
+    b = _batch(T)
+    return lib.indexer_score_topk(ctypes.byref(b), FAKE, FAKE, FAKE, heads, ctypes.byref(keys), FAKE,
+                                  cols, cols, ratio, topk, FAKE, None, 0, FAKE, ws_bytes, None)
+
+
+def test_indexer_errors(lib):
+    assert _call_indexer(lib, T=0) == L.SAD_OK
+    assert _call_indexer(lib, dim=96) == L.SAD_EUNSUPPORTED
+    assert _call_indexer(lib, heads=65) == L.SAD_EUNSUPPORTED
+    assert _call_indexer(lib, block=32) == L.SAD_EUNSUPPORTED
+    assert _call_indexer(lib, cols=1024) == L.SAD_EUNSUPPORTED  # 65536 rows > 32768
+    assert _call_indexer(lib, topk=0) == L.SAD_EINVAL
+    assert _call_indexer(lib, ws_bytes=16) == L.SAD_EWORKSPACE
+    assert "workspace" in L.last_error()
+    need = lib.indexer_score_topk_workspace_size(128, 16384, 2048)
+    assert need == 128 * 16384 * 4
+    assert lib.indexer_score_topk_workspace_size(0, 16384, 2048) == 0
+
+
+def test_gather_errors(lib):
+    s, c = _kv(), _kv()
+    assert lib.gather_dequant_kv(ctypes.byref(s), ctypes.byref(c), FAKE, FAKE, 0, 128, 2048, FAKE, None) == L.SAD_OK
+    bad = _kv(d_nope=256)
+    assert lib.gather_dequant_kv(ctypes.byref(bad), ctypes.byref(c), FAKE, FAKE, 4, 128, 2048, FAKE, None) == L.SAD_EUNSUPPORTED
+    small = _kv(stride=1024)
+    assert lib.gather_dequant_kv(ctypes.byref(small), ctypes.byref(c), FAKE, FAKE, 4, 128, 2048, FAKE, None) == L.SAD_EINVAL
+    tiny = _kv(d_nope=128, d_rope=32, block=16)
+    assert lib.gather_dequant_kv(ctypes.byref(tiny), ctypes.byref(c), FAKE, FAKE, 4, 128, 2048, FAKE, None) == L.SAD_EINVAL
+    huge = _kv(pages=1 << 30)
+    assert lib.gather_dequant_kv(ctypes.byref(huge), ctypes.byref(c), FAKE, FAKE, 4, 128, 2048, FAKE, None) == L.SAD_EINVAL
+
+
+def _call_attn(lib, T=128, H=128, ws=None, ws_bytes=0, W=128, P=2048):
+    s, c = _kv(), _kv()
+    return lib.sparse_mla_decode(FAKE, T, H, ctypes.byref(s), ctypes.byref(c), FAKE, FAKE, W, P, 0.04, None,
+                                 FAKE, None, ws, ws_bytes, None)
+
+
+def test_attention_errors(lib):
+    assert _call_attn(lib, T=0) == L.SAD_OK
+    assert _call_attn(lib, H=7) == L.SAD_EUNSUPPORTED
+    assert _call_attn(lib, H=256) == L.SAD_EUNSUPPORTED
+    # few tokens -> split columns -> partials need a workspace
+    need = lib.sparse_mla_decode_workspace_size(8, 128, 128 + 8192, 576)
+    assert need > 0
+    assert _call_attn(lib, T=8, P=8192) == L.SAD_EWORKSPACE
+    assert "workspace" in L.last_error()
+    assert lib.sparse_mla_decode_workspace_size(16448, 128, 2176, 576) == 0

@@ -1,0 +1,298 @@
+"""GPU parity: every step of the HIP path, called through the C ABI, against the CPU
+oracle on the same seeded input bytes.
+
+Bars: bit-exact for sparse_indices, lens and dequantized rows; top-k sets equal except
+swaps among scores within 1e-5 relative of the oracle's k-th score; indexer logits
+within 1e-5 relative (the per-head dots are exact, only the fp32 head sum rounds);
+attention output within max-abs 5e-3 (bf16 out, fp32 accumulate) and lse within 1e-3.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_decode_build_amd as sad
+from oracle import sad_oracle as O
+from sparse_attention_decode_build_amd import workloads as WL
+
+from gpu_helpers import (bf16_to_f64, check_topk, free, gpu_attention, gpu_build, gpu_indexer, log,
+                         oracle_attention, oracle_build, oracle_topk, sample_tokens)
+
+pytestmark = pytest.mark.gpu
+
+ATOL_OUT = 5e-3
+ATOL_LSE = 1e-3
+
+EDGE = WL.Config(
+    name="edge", seed=5, window=32, ratio=4, topk=16, heads=16, d_nope=128, d_rope=32, idx_heads=4,
+    idx_dim=64, block=16, idx_block=16,
+    # p=0 (n_c=0); n_c=0; n_c=1; a 40-token prefill from position 0 with replay 10;
+    # a decode whose window is clipped to one position; a longer decode
+    groups=((1, 1, 1, 0), (1, 1, 3, 0), (1, 1, 4, 0), (1, 40, 40, 10), (1, 1, 100, 99), (1, 1, 300, 0)),
+    swa_backing="all",
+)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sad.load()
+    torch.manual_seed(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _wl(cfg, **kw):
+    log(f"[case] workload {cfg if isinstance(cfg, str) else cfg.name} {kw}")
+    return WL.make_workload(cfg, "cuda", **kw)
+
+
+def _full_check(wl, view, tokens, sink=None, check_gather=True):
+    """Indexer/top-k, index build, gather and attention of `tokens` vs the oracle."""
+    cfg = wl.cfg
+    T = wl.num_tokens
+    torch.cuda.synchronize()
+    # ---- indexer + top-k
+    if not cfg.dense:
+        log("[step] indexer_score_topk")
+        topk_g, logits = gpu_indexer(wl)
+        torch.cuda.synchronize()
+        topk_g = topk_g.cpu().numpy()
+        logits = logits.cpu().numpy()
+        tk_o, scores = oracle_topk(wl, view, tokens)
+        swaps = 0
+        for i, t in enumerate(tokens):
+            sc, valid = scores[i]
+            n = sc.shape[0]
+            lg = logits[t, :n]
+            assert np.all(np.isneginf(lg[~valid])), "invalid rows must score -inf"
+            if valid.any():
+                ref = sc[valid]
+                scale = max(np.abs(ref).max(), 1e-30)
+                assert np.max(np.abs(lg[valid] - ref)) <= 1e-5 * scale, f"logits token {t}"
+            swaps += check_topk(topk_g[t], sc, valid, cfg.topk)
+        log(f"[ok] indexer/top-k on {len(tokens)} tokens, {swaps} near-tie swaps")
+        # oracle top-k for every token feeds the index build (tokens not sampled get
+        # the GPU-independent oracle result too when cheap)
+        tk_full = np.full((T, cfg.topk), -1, np.int32)
+        tk_full[tokens] = tk_o
+    else:
+        tk_full = None
+    # ---- build_sparse_indices on the oracle's top-k: bit-exact
+    log("[step] build_sparse_indices")
+    tk_dev = torch.from_numpy(tk_full).cuda() if tk_full is not None else None
+    si_g, lens_g = gpu_build(wl, tk_dev)
+    torch.cuda.synchronize()
+    si_o, lens_o = oracle_build(wl, view, tk_full, tokens=tokens)
+    assert np.array_equal(si_g.cpu().numpy()[tokens], si_o)
+    assert np.array_equal(lens_g.cpu().numpy()[tokens], lens_o)
+    log("[ok] build_sparse_indices bit-exact")
+    si_full = np.full((T, si_o.shape[1]), -1, np.int32)
+    lens_full = np.zeros(T, np.int32)
+    si_full[tokens] = si_o
+    lens_full[tokens] = lens_o
+    # ---- gather + dequant: bit-exact
+    if check_gather:
+        log("[step] gather_dequant_kv")
+        kv, _ = _caches(wl)
+        sub = tokens[: min(len(tokens), 16)]
+        si_sub = si_g[torch.as_tensor(sub, device="cuda")].contiguous()
+        lens_sub = lens_g[torch.as_tensor(sub, device="cuda")].contiguous()
+        rows_g = sad.gather_dequant_kv(kv, kv, si_sub, lens_sub, cfg.window, wl.padded_topk)
+        torch.cuda.synchronize()
+        rows_o = O.gather_dequant(view.kv_pages, view.kv_pages, si_o[: len(sub)], lens_o[: len(sub)],
+                                  cfg.window, cfg.block, cfg.block, cfg.d_nope, cfg.d_rope)
+        got = rows_g.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, rows_o)
+        log(f"[ok] gather_dequant_kv bit-exact on {len(sub)} tokens")
+    # ---- attention on the (bit-identical) index rows
+    log("[step] sparse_mla_decode")
+    sink_dev = None if sink is None else torch.from_numpy(sink.astype(np.float32)).cuda()
+    out_g, lse_g = gpu_attention(wl, si_g, lens_g, sink=sink_dev, with_lse=True)
+    torch.cuda.synchronize()
+    o_o, lse_o = oracle_attention(wl, view, si_full, lens_full, tokens, sink=sink)
+    got = bf16_to_f64(out_g)[tokens]
+    err = np.abs(got - o_o)
+    rms = float(np.sqrt(np.mean((got - o_o) ** 2)) / max(np.sqrt(np.mean(o_o ** 2)), 1e-30))
+    log(f"[ok?] attention max-abs {err.max():.3e} rel-rms {rms:.3e}")
+    assert err.max() <= ATOL_OUT
+    lg = lse_g.cpu().numpy()[tokens]
+    fin = np.isfinite(lse_o)
+    assert np.array_equal(np.isfinite(lg), fin)
+    assert np.max(np.abs(lg[fin] - lse_o[fin]), initial=0.0) <= ATOL_LSE
+    return si_g, lens_g, out_g
+
+
+def _caches(wl):
+    cfg = wl.cfg
+    return (sad.KvCache(wl.kv_pool, cfg.block, cfg.d_nope, cfg.d_rope),
+            sad.IndexerCache(wl.idx_pool, cfg.idx_block, cfg.idx_dim))
+
+
+# ---------------------------------------------------------------------------- small
+
+
+@pytest.mark.parametrize("name", ["tiny", "b32_8k"])
+def test_small_config_every_step(name):
+    wl = _wl(name)
+    view = WL.host_view(wl)
+    _full_check(wl, view, list(range(wl.num_tokens)))
+    free(wl)
+
+
+def test_tiny_sparse_equals_dense_selfcheck():
+    cfg = WL.with_overrides(WL.CONFIGS["tiny"], window=256, topk=64)
+    wl = _wl(cfg)
+    view = WL.host_view(wl)
+    _, lens, out = _full_check(wl, view, [0])
+    assert int(lens[0]) == 64
+
+
+@pytest.mark.parametrize("name", ["tiny", "b32_8k"])
+def test_peaky_queries(name):
+    wl = _wl(name, q_scale=4.0)
+    view = WL.host_view(wl)
+    _full_check(wl, view, list(range(wl.num_tokens)), check_gather=False)
+    free(wl)
+
+
+def test_attention_sink_and_lse():
+    wl = _wl("tiny")
+    view = WL.host_view(wl)
+    rng = np.random.default_rng(11)
+    sink = rng.standard_normal(wl.cfg.heads) * 2.0
+    _full_check(wl, view, [0], sink=sink, check_gather=False)
+
+
+def test_edge_batch():
+    wl = _wl(EDGE)
+    view = WL.host_view(wl)
+    _full_check(wl, view, list(range(wl.num_tokens)))
+    free(wl)
+
+
+def test_edge_fail_closed_tables():
+    """Unbacked pages, ids past the pool and random local ids (incl. -1 and >= n_c)."""
+    wl = _wl(EDGE)
+    cfg = wl.cfg
+    L = wl.layers[0]
+    g = torch.Generator(device="cpu").manual_seed(3)
+    holes = torch.rand(L.swa_bt.shape, generator=g) < 0.2
+    L.swa_bt[holes.cuda()] = -1
+    holes = torch.rand(L.comp_bt.shape, generator=g) < 0.2
+    L.comp_bt[holes.cuda()] = -1
+    L.comp_bt[0, 0] = wl.kv_pool.shape[0] + 3  # past the pool
+    view = WL.host_view(wl)
+    T = wl.num_tokens
+    tk = torch.randint(-3, 80, (T, cfg.topk + 5), generator=g, dtype=torch.int32)
+    si_g, lens_g = sad.build_sparse_indices(
+        wl.query_start_loc, wl.seq_lens, wl.token_to_req, wl.replay_start, L.swa_bt, cfg.block,
+        wl.kv_pool.shape[0], L.comp_bt, cfg.block, wl.kv_pool.shape[0], tk.cuda(), cfg.topk,
+        cfg.window, cfg.ratio, wl.padded_topk)
+    torch.cuda.synchronize()
+    si_o, lens_o = oracle_build(wl, view, tk.numpy())
+    assert np.array_equal(si_g.cpu().numpy(), si_o)
+    assert np.array_equal(lens_g.cpu().numpy(), lens_o)
+    # attention over rows with holes
+    out_g, _ = gpu_attention(wl, si_g, lens_g)
+    torch.cuda.synchronize()
+    o_o, _ = oracle_attention(wl, view, si_o, lens_o, list(range(T)))
+    assert np.abs(bf16_to_f64(out_g) - o_o).max() <= ATOL_OUT
+
+
+def test_nothing_attended_gives_zero_and_neg_inf_lse():
+    wl = _wl("tiny")
+    cfg = wl.cfg
+    T = wl.num_tokens
+    si = torch.full((T, cfg.window + wl.padded_topk), -1, dtype=torch.int32, device="cuda")
+    lens = torch.zeros(T, dtype=torch.int32, device="cuda")
+    out, lse = gpu_attention(wl, si, lens, with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+    assert torch.all(torch.isneginf(lse)).item()
+
+
+def test_empty_batch_is_a_no_op():
+    wl = _wl("tiny")
+    cfg = wl.cfg
+    e32 = torch.empty(0, dtype=torch.int32, device="cuda")
+    L = wl.layers[0]
+    si, lens = sad.build_sparse_indices(torch.zeros(1, dtype=torch.int32, device="cuda"), e32, e32, None,
+                                        L.swa_bt[:0], cfg.block, 1, L.comp_bt[:0], cfg.block, 1, None, 0,
+                                        cfg.window, cfg.ratio, wl.padded_topk)
+    assert si.shape == (0, cfg.window + wl.padded_topk)
+    kv, _ = _caches(wl)
+    out = sad.sparse_mla_decode(L.q[:0], kv, kv, si, lens, cfg.window, wl.padded_topk, 0.1)
+    assert out.shape[0] == 0
+
+
+def test_dequant_every_e4m3_code_bit_exact():
+    """A page whose rows hold every finite e4m3 byte, with assorted fp32 scales."""
+    cfg = WL.CONFIGS["tiny"]
+    B, Dn, Dr = cfg.block, cfg.d_nope, cfg.d_rope
+    rowb = Dn + 2 * Dr
+    codes = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)  # 254 finite codes
+    page = np.zeros(cfg.kv_page_bytes, np.uint8)
+    rng = np.random.default_rng(2)
+    for o in range(B):
+        page[o * rowb: o * rowb + Dn] = np.roll(np.resize(codes, Dn), 7 * o)
+        page[o * rowb + Dn: (o + 1) * rowb] = rng.integers(0, 256, 2 * Dr, dtype=np.uint8) & 0x3F
+        sc = (rng.random(Dn // 64) * 3 + 1e-3).astype(np.float32) * np.float32(2.0 ** (o - 8))
+        page[B * rowb + o * 4 * (Dn // 64): B * rowb + (o + 1) * 4 * (Dn // 64)] = sc.view(np.uint8)
+    pool = torch.from_numpy(np.stack([page, page])).cuda()
+    kv = sad.KvCache(pool, B, Dn, Dr)
+    si = torch.tensor([[B + o for o in range(B)] + [-1] * 16], dtype=torch.int32, device="cuda")
+    W = B
+    lens = torch.tensor([0], dtype=torch.int32, device="cuda")
+    got = sad.gather_dequant_kv(kv, kv, si, lens, W, 16)
+    torch.cuda.synchronize()
+    want = O.gather_dequant({1: page}, {1: page}, si.cpu().numpy(), [0], W, B, B, Dn, Dr)
+    assert np.array_equal(got.view(torch.int16).cpu().numpy().view(np.uint16), want)
+
+
+def test_deterministic():
+    wl = _wl("b32_8k")
+    topk_a, _ = gpu_indexer(wl, logits=False)
+    topk_b, _ = gpu_indexer(wl, logits=False)
+    si_a, lens_a = gpu_build(wl, topk_a)
+    out_a, _ = gpu_attention(wl, si_a, lens_a)
+    out_b, _ = gpu_attention(wl, si_a, lens_a)
+    torch.cuda.synchronize()
+    assert torch.equal(topk_a, topk_b)
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    free(wl)
+
+
+# ---------------------------------------------------------------------------- full size
+
+
+@pytest.mark.slow
+def test_b128_64k_full_size_sampled():
+    """128 requests at 64K context over a ~196 GB pool: all tokens run on the GPU in
+    the benchmark's launch configuration; index rows are compared on every token and
+    the oracle recomputes scores, top-k, rows and attention for sampled tokens."""
+    wl = _wl("b128_64k")
+    tokens = [0, 17, 63, 127]
+    view = WL.host_view(wl, reqs=tokens)
+    all_view = view
+    _full_check(wl, all_view, tokens)
+    free(wl)
+
+
+@pytest.mark.slow
+def test_mixed_batch_sampled():
+    wl = _wl("mixed")
+    tokens = sample_tokens(wl, n_decode=4, n_prefill=8)
+    reqs = sorted(set(wl.token_to_req.cpu().numpy()[tokens].tolist()))
+    view = WL.host_view(wl, reqs=reqs)
+    _full_check(wl, view, tokens)
+    free(wl)
+
+
+@pytest.mark.slow
+def test_dense_1m_full():
+    wl = _wl("dense_1m")
+    view = WL.host_view(wl)
+    _full_check(wl, view, list(range(wl.num_tokens)))
+    free(wl)
