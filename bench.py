@@ -1,0 +1,256 @@
+"""Benchmark of the sparse-attention decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: indexer_score_topk (MXFP4
+scoring + top-k) -> build_sparse_indices -> sparse_mla_decode (fused gather + FP8
+dequant + MLA attention), all through the C ABI of libsad.so on one HIP stream.
+
+Workload: 128 requests x 1 decode token at 64K context (window 128, compress ratio 4
+-> 16384 compressed rows, top-2048, 128 heads, latent 512 FP8 + 64 bf16, indexer 64
+heads x 128 MXFP4, page size 64), pages shuffled over a ~196 GB KV pool and a ~3.9 GB
+indexer pool.  Several independent layers (own pages, queries and tables) are
+rotated step by step so the 256 MB MALL cannot serve a step from the previous one.
+Inputs are resident in HBM before timing starts.
+
+Prints one JSON line (rank 0) with tokens/s, per-kernel times, roofline objects for
+the attention kernel (HBM and MFMA views) and the CPU oracle's throughput on a
+bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_attention_decode_build_amd as sad  # noqa: E402
+from sparse_attention_decode_build_amd import _lib as L  # noqa: E402
+from sparse_attention_decode_build_amd import workloads as WL  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+WORKLOAD = WL.HEADLINE
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_b128_64k_traffic.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Step:
+    """Pre-marshalled C-ABI calls for one layer (no Python work in the timed loop)."""
+
+    def __init__(self, wl: WL.Workload, layer: int):
+        cfg = wl.cfg
+        lay = wl.layers[layer]
+        self.lib = L.load()
+        T, dev = wl.num_tokens, wl.device
+        self.batch = L.SadBatch(wl.query_start_loc.data_ptr(), wl.seq_lens.data_ptr(),
+                                wl.token_to_req.data_ptr(), wl.num_reqs, T)
+        self.kv = L.SadKvCache(wl.kv_pool.data_ptr(), wl.kv_pool.stride(0), wl.kv_pool.shape[0],
+                               cfg.block, cfg.d_nope, cfg.d_rope)
+        self.idx = L.SadMxfp4Cache(wl.idx_pool.data_ptr(), wl.idx_pool.stride(0), wl.idx_pool.shape[0],
+                                   cfg.idx_block, cfg.idx_dim)
+        self.topk = torch.empty((T, cfg.topk), dtype=torch.int32, device=dev)
+        self.si = torch.empty((T, cfg.window + wl.padded_topk), dtype=torch.int32, device=dev)
+        self.lens = torch.empty((T,), dtype=torch.int32, device=dev)
+        self.out = torch.empty((T, cfg.heads, cfg.dqk), dtype=torch.bfloat16, device=dev)
+        max_rows = lay.idx_bt.shape[1] * cfg.idx_block
+        ws_i = self.lib.indexer_score_topk_workspace_size(T, max_rows, cfg.topk)
+        self.ws_i = torch.empty((max(ws_i, 16),), dtype=torch.uint8, device=dev)
+        ws_a = self.lib.sparse_mla_decode_workspace_size(T, cfg.heads, cfg.window + wl.padded_topk, cfg.dqk)
+        self.ws_a = torch.empty((max(ws_a, 16),), dtype=torch.uint8, device=dev)
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        n_pages = wl.kv_pool.shape[0]
+        self.args_idx = (ctypes.byref(self.batch), p(lay.idx_q_values), p(lay.idx_q_scales),
+                         p(lay.idx_weights), cfg.idx_heads, ctypes.byref(self.idx), p(lay.idx_bt),
+                         lay.idx_bt.stride(0), lay.idx_bt.shape[1], cfg.ratio, cfg.topk, p(self.topk),
+                         None, 0, p(self.ws_i), self.ws_i.numel(), stream)
+        self.args_build = (ctypes.byref(self.batch), p(wl.replay_start), p(lay.swa_bt), lay.swa_bt.stride(0),
+                           lay.swa_bt.shape[1], cfg.block, n_pages, p(lay.comp_bt), lay.comp_bt.stride(0),
+                           lay.comp_bt.shape[1], cfg.block, n_pages, p(self.topk), self.topk.stride(0),
+                           cfg.topk, cfg.window, cfg.ratio, wl.padded_topk, p(self.si), p(self.lens), stream)
+        self.args_attn = (p(lay.q), T, cfg.heads, ctypes.byref(self.kv), ctypes.byref(self.kv), p(self.si),
+                          p(self.lens), cfg.window, wl.padded_topk, ctypes.c_float(wl.softmax_scale), None,
+                          p(self.out), None, p(self.ws_a), self.ws_a.numel(), stream)
+
+    def run(self, ev=None):
+        lib = self.lib
+        if ev is not None:
+            ev[0].record()
+        rc = lib.indexer_score_topk(*self.args_idx)
+        if ev is not None:
+            ev[1].record()
+        rc |= lib.build_sparse_indices(*self.args_build)
+        if ev is not None:
+            ev[2].record()
+        rc |= lib.sparse_mla_decode(*self.args_attn)
+        if ev is not None:
+            ev[3].record()
+        if rc:
+            raise RuntimeError(f"step failed: {L.last_error()}")
+
+
+def algorithmic_bytes(wl: WL.Workload) -> dict:
+    """Bytes the method must move per step (each FP8/MXFP4 row once, q, out, indices)."""
+    cfg = wl.cfg
+    seq = wl.seq_lens.cpu().numpy().astype(np.int64)
+    qsl = wl.query_start_loc.cpu().numpy().astype(np.int64)
+    t2r = wl.token_to_req.cpu().numpy().astype(np.int64)
+    pos = seq[t2r] - (qsl[t2r + 1] - qsl[t2r]) + (np.arange(len(t2r)) - qsl[t2r])
+    nc = (pos + 1) // cfg.ratio
+    rows = np.minimum(pos + 1, cfg.window) + np.minimum(nc, cfg.topk)  # attended rows per token
+    row_b = cfg.d_nope + 2 * cfg.d_rope + 4 * (cfg.d_nope // 64)
+    idx_row = cfg.idx_dim // 2 + cfg.idx_dim // 32
+    W, P, H, D = cfg.window, wl.padded_topk, cfg.heads, cfg.dqk
+    attn = rows * row_b + (W + P) * 4 + 4 + 2 * H * D + 2 * H * D
+    indexer = (nc * idx_row + (nc + cfg.idx_block - 1) // cfg.idx_block * 4
+               + cfg.idx_heads * idx_row + 4 * cfg.idx_heads + 4 * cfg.topk)
+    build = 4 * cfg.topk + 4 * (W + P)
+    flops = 2 * H * (D + D) * rows  # QK + PV
+    return {"attention": int(attn.sum()), "indexer": int(indexer.sum()), "build": int(build * len(t2r)),
+            "attention_flops": int(flops.sum()), "rows": int(rows.sum())}
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from committed rocprofv3 PMC runs, or None when
+    the kernel source changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    src = open(os.path.join(ROOT, "sparse_attention_decode_build_amd", "csrc", "attention.hip"), "rb").read()
+    sha = hashlib.sha256(src).hexdigest()
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("attention.hip sha256") != sha:
+        return None
+    try:
+        return float(vals["bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl: WL.Workload, budget_s: float) -> dict:
+    """The CPU oracle, as it stands, on the first tokens of layer 0 (whole step each)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import sad_oracle as O
+
+    cfg = wl.cfg
+    T = wl.num_tokens
+
+    def run(tokens):
+        view = WL.host_view(wl, 0, reqs=wl.token_to_req[tokens].cpu().tolist())
+        t0 = time.perf_counter()
+        O.step(view, cfg, wl.padded_topk, wl.kv_pool.shape[0], wl.idx_pool.shape[0], wl.softmax_scale,
+               tokens=tokens)
+        return time.perf_counter() - t0
+
+    t1 = run([0])
+    n = int(max(2, min(T, budget_s / max(t1, 1e-3))))
+    tokens = list(range(n))
+    dt = run(tokens)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole step (indexer, top-k, index build, attention) of tokens 0..{n - 1} "
+                      f"of layer 0 of the same {WORKLOAD} workload, float64 numpy oracle, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=4, help="independent layers rotated per step")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the step is data-parallel "
+              "over requests and needs no collectives; run with --gpus 1", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    sad.load()
+    t0 = time.perf_counter()
+    wl = WL.make_workload(WORKLOAD, "cuda", num_layers=args.layers)
+    torch.cuda.synchronize()
+    log(f"[bench] workload {WORKLOAD} built in {time.perf_counter() - t0:.1f} s "
+        f"(kv pool {wl.kv_pool.numel() / 1e9:.1f} GB, {args.layers} layers)")
+    steps = [Step(wl, i) for i in range(args.layers)]
+    for i in range(args.warmup):
+        steps[i % args.layers].run()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        steps[i % args.layers].run(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    seg = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(K)])
+    ms_step = wall * 1e3 / K
+    ms_idx, ms_build, ms_attn = seg.mean(axis=0)
+    T = wl.num_tokens
+    ab = algorithmic_bytes(wl)
+    attn_gbs = ab["attention"] / (ms_attn * 1e-3) / 1e9
+    attn_tflops = ab["attention_flops"] / (ms_attn * 1e-3) / 1e12
+    idx_gbs = ab["indexer"] / (ms_idx * 1e-3) / 1e9
+    traffic = measured_traffic()
+    cfg = wl.cfg
+    result = {
+        "metric": "sparse-attn decode tokens/s/GPU at 64K ctx; achieved HBM GB/s % of peak",
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: {wl.num_reqs} requests x 1 decode token, seq_len 65536, "
+                               f"window {cfg.window}, compress_ratio {cfg.ratio}, topk {cfg.topk}, "
+                               f"{cfg.heads} heads, latent {cfg.d_nope} fp8 + {cfg.d_rope} bf16, indexer "
+                               f"{cfg.idx_heads}x{cfg.idx_dim} mxfp4, page {cfg.block}, kv pool "
+                               f"{wl.kv_pool.numel() / 1e9:.1f} GB",
+                   "tokens_per_step": T, "layers_rotated": args.layers},
+        "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "kernel": "sparse_mla_decode (sparse_mla_kernel)"},
+        "roofline_hbm": {"bound": "hbm", "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": attn_gbs / PEAK_HBM_GBS, "traffic": traffic,
+                         "kernel": "sparse_mla_decode (sparse_mla_kernel)"},
+        "kernels_ms": {"indexer_score_topk": ms_idx, "build_sparse_indices": ms_build,
+                       "sparse_mla_decode": ms_attn},
+        "algorithmic_bytes_per_step": {"attention": ab["attention"], "indexer": ab["indexer"],
+                                       "build": ab["build"]},
+        "indexer_hbm_gbs": idx_gbs,
+        "step_hbm_frac": (ab["attention"] + ab["indexer"] + ab["build"]) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

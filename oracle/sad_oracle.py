@@ -355,7 +355,8 @@ def indexer_topk(query_start_loc, seq_lens, token_to_req, q_values, q_scales, we
 # ---------------------------------------------------------------------------
 
 
-def attend(q_bits: np.ndarray, row_bits: np.ndarray, softmax_scale: float, sink=None):
+def attend(q_bits: np.ndarray, row_bits: np.ndarray, softmax_scale: float, sink=None,
+           return_mass: bool = False):
     """Softmax attention of every head over the given rows (float64).
 
     ``o_h = sum_j exp(l_hj - m) x_j / (sum_j exp(l_hj - m) + exp(sink_h - m))``
@@ -363,12 +364,14 @@ def attend(q_bits: np.ndarray, row_bits: np.ndarray, softmax_scale: float, sink=
     logits and the sink ([backend] ``forward_deepseek_v4_decode``: values are
     the whole row, ``head_dim_v = head_dim``; [model] attention: scale
     ``head_dim^-1/2``, per-head sink).  Returns (o [H, D], lse [H]); with no
-    rows and no sink, o = 0 and lse = -inf.
+    rows and no sink, o = 0 and lse = -inf.  With ``return_mass`` also returns
+    ``sum_j p_j |x_j|`` per head and dim, the scale of any per-weight rounding error.
     """
     q = bf16_bits_to_float(q_bits)  # [H, D]
     H = q.shape[0]
     if row_bits.shape[0] == 0 and sink is None:
-        return np.zeros((H, row_bits.shape[1]), np.float64), np.full(H, -np.inf)
+        zero = np.zeros((H, row_bits.shape[1]), np.float64)
+        return (zero, np.full(H, -np.inf), zero) if return_mass else (zero, np.full(H, -np.inf))
     x = bf16_bits_to_float(row_bits)  # [n, D]
     logits = softmax_scale * (q @ x.T)  # [H, n]
     s = None if sink is None else np.asarray(sink, dtype=np.float64)
@@ -380,23 +383,29 @@ def attend(q_bits: np.ndarray, row_bits: np.ndarray, softmax_scale: float, sink=
     z = e.sum(axis=1)
     if s is not None:
         z = z + np.exp(s - m_safe)
-    o = (e @ x) / np.where(z > 0, z, 1.0)[:, None]
+    zs = np.where(z > 0, z, 1.0)[:, None]
+    o = (e @ x) / zs
     o[z == 0] = 0.0
     with np.errstate(divide="ignore"):
         lse = m_safe + np.log(z)
+    if return_mass:
+        mass = (e @ np.abs(x)) / zs
+        mass[z == 0] = 0.0
+        return o, lse, mass
     return o, lse
 
 
 def sparse_mla_decode(q_bits, kv_swa, kv_comp, sparse_indices, sparse_topk_lens, window_size,
                       block_size_swa, block_size_comp, d_nope, d_rope, softmax_scale,
-                      attn_sink=None, tokens=None):
+                      attn_sink=None, tokens=None, return_mass=False):
     """Attention of every head of each token over its attended columns.
 
     Attended columns: window columns ``0..W-1`` with slot >= 0 and compressed
     columns ``W..W+lens-1`` with slot >= 0, each one key ([backend]
     ``forward_deepseek_v4_decode``: window ids bounded by their lengths plus
     extra (compressed) ids bounded by ``extra_topk_length``).
-    Returns float64 (o [n, H, Dn+Dr], lse [n, H]).
+    Returns float64 (o [n, H, Dn+Dr], lse [n, H]) and, with ``return_mass``, the
+    per-output absolute mass ``sum_j p_j |x_j|`` [n, H, Dn+Dr].
     """
     si = np.asarray(sparse_indices)
     W = int(window_size)
@@ -405,6 +414,7 @@ def sparse_mla_decode(q_bits, kv_swa, kv_comp, sparse_indices, sparse_topk_lens,
     D = d_nope + d_rope
     o = np.zeros((len(tokens), H, D), np.float64)
     lse = np.zeros((len(tokens), H), np.float64)
+    mass = np.zeros((len(tokens), H, D), np.float64) if return_mass else None
     for i, t in enumerate(tokens):
         swa = si[t, :W]
         n = int(min(max(int(sparse_topk_lens[t]), 0), si.shape[1] - W))
@@ -413,8 +423,11 @@ def sparse_mla_decode(q_bits, kv_swa, kv_comp, sparse_indices, sparse_topk_lens,
             dequant_rows(kv_swa, swa[swa >= 0], block_size_swa, d_nope, d_rope),
             dequant_rows(kv_comp, comp[comp >= 0], block_size_comp, d_nope, d_rope),
         ])
-        o[i], lse[i] = attend(q_bits[t], rows, softmax_scale, attn_sink)
-    return o, lse
+        if return_mass:
+            o[i], lse[i], mass[i] = attend(q_bits[t], rows, softmax_scale, attn_sink, return_mass=True)
+        else:
+            o[i], lse[i] = attend(q_bits[t], rows, softmax_scale, attn_sink)
+    return (o, lse, mass) if return_mass else (o, lse)
 
 
 # ---------------------------------------------------------------------------

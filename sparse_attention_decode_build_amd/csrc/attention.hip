@@ -300,7 +300,8 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[mt][r] = 0.0f;
   float m_run = -INFINITY;
-  float l_run = 0.0f;
+  float l_run = 0.0f;  // sum of the bf16-rounded weights (normalizes O)
+  float l_lse = 0.0f;  // sum of the fp32 weights (log-sum-exp)
 
   // Prologue: rows of the first two tiles, DMA of the first.
   if (tile_begin < tile_end) {
@@ -383,6 +384,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
       const float alpha = upd ? exp2f(m_run - tmax) : 1.0f;  // exp2(-inf) = 0
       if (upd) m_run = tmax;
       l_run *= alpha;
+      l_lse *= alpha;
 #pragma unroll
       for (int mt = 0; mt < MTMAX; ++mt)
 #pragma unroll
@@ -392,9 +394,12 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     bf16x8_t pb[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = exp2f(s[r] - m_use);
-      l_run += p;
-      pb[r >> 3][r & 7] = (__bf16)p;
+      // normalize by the same rounded weights the PV MFMA multiplies with
+      const float pf = exp2f(s[r] - m_use);
+      const __bf16 p = (__bf16)pf;
+      l_run += (float)p;
+      l_lse += pf;
+      pb[r >> 3][r & 7] = p;
     }
     // ---- O^T += V^T P^T over this wave's output dims
 #pragma unroll
@@ -418,13 +423,16 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
 
   if (!block_active || head >= num_heads) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_exp = l_lse + __shfl_xor(l_lse, 32, 64);
   // lane (n, h) holds O^T rows (dims) dim0 + 32mt + 8(r/4) + 4h + r%4 for head n
   if (num_splits == 1) {
     const float s2 = sink != nullptr ? sink[head] * kLog2e : -INFINITY;
     const float mm = fmaxf(m_run, s2);
     const float mref = mm == -INFINITY ? 0.0f : mm;
     const float so = exp2f(m_run - mref);
-    const float den = l_tot * so + exp2f(s2 - mref);
+    const float es = exp2f(s2 - mref);
+    const float den = l_tot * so + es;
+    const float den_lse = l_exp * so + es;
     const float f = den > 0.0f ? so / den : 0.0f;
     uint16_t* orow = out + ((int64_t)t * num_heads + head) * DQK + dim0;
 #pragma unroll
@@ -439,7 +447,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
         }
       }
     if (lse_out != nullptr && h == 0 && dh == 0)
-      lse_out[(int64_t)t * num_heads + head] = den > 0.0f ? (mref + log2f(den)) * kLn2 : -INFINITY;
+      lse_out[(int64_t)t * num_heads + head] = den_lse > 0.0f ? (mref + log2f(den_lse)) * kLn2 : -INFINITY;
   } else {
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     float* prow = part_o + (((int64_t)split * num_tokens + t) * num_heads + head) * DQK + dim0;
@@ -455,7 +463,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
       }
     if (h == 0 && dh == 0)
       part_lse[((int64_t)split * num_tokens + t) * num_heads + head] =
-          l_tot > 0.0f ? m_run + log2f(l_tot) : -INFINITY;
+          l_exp > 0.0f ? m_run + log2f(l_exp) : -INFINITY;
   }
 }
 

@@ -462,10 +462,11 @@ def host_view(wl: Workload, layer: int = 0, reqs=None) -> HostView:
         return t.detach().cpu().numpy()
 
     rows = slice(None) if reqs is None else torch.as_tensor(sorted(set(reqs)), device=L.swa_bt.device)
+    # only ids that name a page of the pool (tables may hold -1 or stale ids past it)
     kv_ids = torch.cat([L.swa_bt[rows].flatten(), L.comp_bt[rows].flatten()])
-    kv_ids = sorted(set(kv_ids[kv_ids >= 0].cpu().tolist()))
+    kv_ids = sorted(set(kv_ids[(kv_ids >= 0) & (kv_ids < wl.kv_pool.shape[0])].cpu().tolist()))
     idx_ids = L.idx_bt[rows].flatten()
-    idx_ids = sorted(set(idx_ids[idx_ids >= 0].cpu().tolist()))
+    idx_ids = sorted(set(idx_ids[(idx_ids >= 0) & (idx_ids < wl.idx_pool.shape[0])].cpu().tolist()))
     kv_pages = {}
     idx_pages = {}
     chunk = 4096

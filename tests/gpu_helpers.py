@@ -75,12 +75,12 @@ def oracle_build(wl: WL.Workload, view, topk_local, tokens=None):
                                   wl.padded_topk, tokens=tokens)
 
 
-def oracle_attention(wl: WL.Workload, view, si, lens, tokens, sink=None, q_bits=None):
+def oracle_attention(wl: WL.Workload, view, si, lens, tokens, sink=None, q_bits=None, return_mass=False):
     cfg = wl.cfg
     q_bits = view.q if q_bits is None else q_bits
     return O.sparse_mla_decode(q_bits, view.kv_pages, view.kv_pages, si, lens, cfg.window, cfg.block,
                                cfg.block, cfg.d_nope, cfg.d_rope, wl.softmax_scale, attn_sink=sink,
-                               tokens=tokens)
+                               tokens=tokens, return_mass=return_mass)
 
 
 def check_topk(gpu_row: np.ndarray, scores: np.ndarray, valid: np.ndarray, k: int, rel: float = 1e-5):
