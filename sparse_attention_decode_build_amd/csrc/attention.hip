@@ -13,15 +13,16 @@
 //     split.  The two waves of a head block add their partial S^T through LDS;
 //   * the workgroups of one token's head groups are numbered 8 apart so they run on the
 //     same XCD at the same time and the second read of each row hits that XCD's L2;
-//   * columns are taken 32 at a time.  The raw cache bytes of tile i+1 are copied
-//     HBM -> LDS by direct global-to-LDS loads (no VGPRs) while tile i is computed;
-//     the row addresses of tile i+2 are resolved meanwhile;
+//   * the workgroup's index columns are staged in LDS once; columns are then taken 32
+//     at a time.  The raw cache bytes of tiles i+1..i+3 are in flight HBM -> LDS as
+//     direct global-to-LDS loads (no VGPRs) while tile i is computed; each lane carries
+//     one row of every tile, so it computes one row address per tile;
 //   * tile i is dequantized from LDS (fp32 multiply by the row's block scale, bf16
-//     rounding) into two LDS copies: key-major K[32][D] for S^T = K Q^T, dim-major
-//     V^T[D][32] for O^T += V^T P^T;
+//     rounding) into one key-major, XOR-swizzled bf16 tile K[32][D].  S^T = K Q^T reads
+//     it with 16-byte fragment loads; O^T += V^T P^T reads the same tile transposed
+//     (ds_read_b64_tr_b16), so no second copy is written;
 //   * S^T puts one head per lane, so the online softmax needs only a swap with lane^32,
-//     and the probabilities already sit in the B-operand layout of the PV MFMA (the key
-//     order inside V^T rows is permuted to match);
+//     and the probabilities already sit in the B-operand layout of the PV MFMA;
 //   * splits of one token write (o / l, log2-sum-exp) partials that a second kernel
 //     merges, with the sink, when more than one split is used.
 // Barriers are raw s_barrier with explicit LDS waits so that the in-flight LDS DMA of
@@ -39,17 +40,44 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;              // attended columns per tile
+constexpr int kStages = 4;             // raw tiles in the LDS ring (DMA runs 3 tiles ahead)
+constexpr int kMaxSiCols = 4352;       // index columns one workgroup stages in LDS (17 KB)
 constexpr float kRescaleSlack = 8.0f;  // keep the running max until exceeded by 2^8
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// s_waitcnt immediates (gfx9 encoding): lgkmcnt(0) only; vmcnt(0) only.
+// s_waitcnt immediate (gfx9 encoding) waiting for lgkmcnt(0) only.
 constexpr int kWaitLgkm0 = 0xC07F;
-constexpr int kWaitVm0 = 0x0F70;
 
 __device__ inline void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __builtin_amdgcn_s_barrier();
+}
+
+// Source of the DMA for columns that are not attended: reading zeros makes their
+// dequantized rows exactly zero with no masking in the dequant.
+__device__ __align__(16) uint8_t kZeroRow[1024];
+
+// Direct global -> LDS loads.  They are issued as inline asm so that the compiler
+// neither tracks them nor inserts its own waits for them (its LDS-DMA alias tracking
+// is lost across the tile loop and would drain every in-flight tile); the kernel waits
+// for them explicitly with vmcnt, which counts vector-memory ops in issue order.  The
+// LDS destination of lane i is m0 + 16*i (dwordx4) or m0 + 4*i (dword).
+__device__ inline void dma_x4(const void* src, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_wave_base), "v"(src) : "memory", "m0");
+}
+__device__ inline void dma_x1(const void* src, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(lds_wave_base), "v"(src) : "memory", "m0");
+}
+template <int N>
+__device__ inline void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+template <typename T>
+__device__ inline uint32_t lds_addr(const T* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T*)p;
 }
 
 struct KvDesc {
@@ -57,7 +85,16 @@ struct KvDesc {
   int64_t stride;
   int64_t num_pages;
   int block;
+  int block_shift;  // log2(block)
 };
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+__device__ inline uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
 
 template <int DN, int DR>
 struct Shape {
@@ -69,158 +106,114 @@ struct Shape {
   static constexpr int MT1 = MT - MT0;
   static constexpr int KS0 = 2 * MT0;       // QK k-steps (16 dims) of dim half 0
   static constexpr int KS1 = 2 * MT1;
-  static constexpr int KROW = DQK + 8;      // padded K-major row (bf16 elements)
-  static constexpr int CPR = ROWB / 16;     // 16-byte chunks per row
-  static constexpr int VAL_LOADS = (kTile * CPR + kThreads - 1) / kThreads;  // per wave
-  static constexpr int NOPE_UNITS = (kTile / 8) * (DN / 4);  // 8 keys x 4 fp8 dims
-  static constexpr int NU = (NOPE_UNITS + kThreads - 1) / kThreads;
-  static constexpr int ROPE_UNITS = (kTile / 4) * (DR / 4);  // 4 keys x 4 bf16 dims
-  static_assert(ROWB % 16 == 0, "rows are whole 16-byte chunks");
+  static constexpr int KCH = DQK / 8 + 1;  // 16-byte chunks per K row in LDS (odd: one pad chunk)
+  static constexpr int CPR = ROWB / 16;               // 16-byte chunks of a cached row
+  static constexpr int VAL_LOADS = (CPR + 7) / 8;     // value DMAs per wave per tile
+  static constexpr int DMA_PER_TILE = VAL_LOADS + 1;  // + one scale DMA
+  static constexpr int RAW_V = VAL_LOADS * kWaves * 64 * 16;  // [chunk][row][16 B], padded
+  static constexpr int RAW_S = kThreads;                      // fp32 [row][NSC], padded
+  static constexpr int NOPE_U = DN / 16 / kWaves;  // 16-byte fp8 chunks per wave (2 rows each)
+  static constexpr int ROPE_CH = DR / 8;           // 16-byte bf16 chunks of the rope part
+  static_assert(ROWB % 16 == 0 && DN % 64 == 0, "rows are whole chunks, 64-element scale blocks");
+  static_assert((DN / 16) % kWaves == 0, "fp8 chunks split evenly over the waves");
   static_assert(kTile * NSC <= kThreads, "one scale dword per thread");
-  static_assert(ROPE_UNITS <= kThreads, "one rope unit per thread");
+  static_assert(ROPE_CH <= 2 * kWaves, "at most one rope chunk per thread");
   static_assert(DQK % 32 == 0, "output dims in 32-row MFMA tiles");
 };
 
-
-// Keys of the 8-key V^T chunk c (chunk c = 2*ks + h feeds k-step ks, lane half h):
-// position e (0..7) holds key 16*(c/2) + 8*(e/4) + 4*(c%2) + e%4, which is the key the
-// S^T accumulator register 8*ks + e of a lane in half h belongs to.
-__device__ inline int chunk_key(int c, int e) {
-  return 16 * (c >> 1) + 8 * (e >> 2) + 4 * (c & 1) + (e & 3);
+// Element offset of (key, dim) in the K tile.  Rows hold an odd number of 16-byte
+// chunks (one pad chunk), so consecutive keys start 16 bytes apart modulo 128: the QK
+// fragment reads (8 keys, same chunk) and the transposing PV reads (8 keys x 64 bytes)
+// both spread over all LDS banks, and every fragment address is a per-lane base plus
+// a compile-time offset.
+template <int KCH>
+__device__ inline int kt_off(int key, int dim) {
+  return key * KCH * 8 + dim;
 }
 
-// Physical 16-byte chunk of V^T row d holding logical chunk c (the rotation spreads LDS
-// banks for both the fragment reads (8 consecutive rows) and the dequant writes).
-__device__ inline int vt_chunk(int d, int c) { return (c + (d >> 1) + (d >> 3)) & 3; }
-
-__device__ inline uint32_t pack_bf16(float a, float b) {
-  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+// Row values / scales of one attended column, or the zero row when the column is not
+// attended (past ncols, slot -1, page outside the pool).
+__device__ inline void col_row(int col, int ncols, int window, const int32_t* si_lds, int col_base,
+                               const KvDesc& swa, const KvDesc& comp, int rowb, int nsc,
+                               const uint8_t** vals, const uint8_t** scales) {
+  *vals = kZeroRow;
+  *scales = kZeroRow;
+  if (col >= ncols) return;
+  const int slot = si_lds[col - col_base];
+  const KvDesc& kv = col < window ? swa : comp;
+  if (slot < 0) return;
+  const int page = slot >> kv.block_shift;
+  if ((int64_t)page >= kv.num_pages) return;
+  const int ro = slot & (kv.block - 1);
+  const uint8_t* pg = kv.pool + (int64_t)page * kv.stride;
+  *vals = pg + ro * rowb;
+  *scales = pg + (kv.block * rowb + ro * 4 * nsc);
 }
 
-// Row base pointers of one tile (values, scales); nullptr = column not attended.
-__device__ inline void resolve_rows(const uint8_t** rowv, const uint8_t** rows, int tile0,
-                                    int ncols, int window, const int32_t* si_row,
-                                    const KvDesc& swa, const KvDesc& comp, int rowb, int nsc) {
-  const int r = threadIdx.x;
-  if (r >= kTile) return;
-  const int col = tile0 + r;
-  const uint8_t* pv = nullptr;
-  const uint8_t* ps = nullptr;
-  if (col < ncols) {
-    const int slot = si_row[col];
-    const KvDesc& kv = col < window ? swa : comp;
-    if (slot_ok(slot, kv.block, kv.num_pages)) {
-      const int page = slot / kv.block;
-      const int ro = slot - page * kv.block;
-      const uint8_t* pg = kv.pool + (int64_t)page * kv.stride;
-      pv = pg + (int64_t)ro * rowb;
-      ps = pg + (int64_t)kv.block * rowb + (int64_t)ro * 4 * nsc;
-    }
-  }
-  rowv[r] = pv;
-  rows[r] = ps;
-}
-
-// Copy one tile's raw rows (values and fp32 scales) HBM -> LDS with direct loads.
-// Unattended rows read a harmless dummy address; their data is zeroed on dequant.
+// Copy one tile's raw rows HBM -> LDS.  Values go chunk-major ([chunk][row][16 B]), so
+// lane l of every value DMA carries row l%32 and only one row address is needed per
+// lane; scales go row-major ([row][NSC] fp32).  Every wave issues exactly DMA_PER_TILE
+// loads with all lanes active (padding lanes read the zero row into padding LDS), so
+// a wave's vmcnt advances by a known amount per tile.
 template <int DN, int DR>
-__device__ inline void dma_tile(uint8_t* raw_v, float* raw_s, const uint8_t* const* rowv,
-                                const uint8_t* const* rows, const void* dummy) {
+__device__ inline void dma_tile(int lane, int wave, uint8_t (&raw_v)[Shape<DN, DR>::RAW_V],
+                                float (&raw_s)[Shape<DN, DR>::RAW_S], int tile0, int ncols,
+                                int window, const int32_t* si_lds, int col_base, const KvDesc& swa,
+                                const KvDesc& comp) {
   using S = Shape<DN, DR>;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const uint8_t* vrow;
+  const uint8_t* srow;
+  col_row(tile0 + (lane & 31), ncols, window, si_lds, col_base, swa, comp, S::ROWB, S::NSC, &vrow, &srow);
+  const uint32_t vbase = lds_addr(raw_v);
 #pragma unroll
   for (int j = 0; j < S::VAL_LOADS; ++j) {
-    const int q0 = (j * kWaves + wave) * 64;
-    const int q = q0 + lane;
-    if (q0 < kTile * S::CPR) {
-      if (q < kTile * S::CPR) {
-        const int row = q / S::CPR;
-        const int c16 = q - row * S::CPR;
-        const uint8_t* base = rowv[row];
-        const void* src = base != nullptr ? (const void*)(base + 16 * c16) : dummy;
-        __builtin_amdgcn_global_load_lds(src, raw_v + q0 * 16, 16, 0, 0);
-      }
-    }
+    const int jj = j * kWaves + wave;         // wave-uniform
+    const int c16 = 2 * jj + (lane >> 5);     // chunk carried by this lane
+    const uint8_t* src = c16 < S::CPR ? vrow + 16 * c16 : kZeroRow;
+    dma_x4(src, __builtin_amdgcn_readfirstlane(vbase + jj * 1024));
   }
-  {
-    const int q0 = wave * 64;
-    const int q = q0 + lane;
-    if (q0 < kTile * S::NSC) {
-      if (q < kTile * S::NSC) {
-        const int row = q / S::NSC;
-        const uint8_t* base = rows[row];
-        const void* src = base != nullptr ? (const void*)(base + 4 * (q - row * S::NSC)) : dummy;
-        __builtin_amdgcn_global_load_lds(src, raw_s + q0, 4, 0, 0);
-      }
-    }
-  }
+  const int q = wave * 64 + lane;
+  const int srow_i = q / S::NSC;
+  const uint8_t* vr2;
+  const uint8_t* sr2;
+  col_row(tile0 + srow_i, srow_i < kTile ? ncols : 0, window, si_lds, col_base, swa, comp, S::ROWB, S::NSC,
+          &vr2, &sr2);
+  const uint8_t* ssrc = srow_i < kTile ? sr2 + 4 * (q - srow_i * S::NSC) : kZeroRow;
+  dma_x1(ssrc, __builtin_amdgcn_readfirstlane(lds_addr(raw_s) + wave * 256));
 }
 
-// Dequantize the raw tile in LDS into the K-major and V^T copies.
+// Dequantize the raw tile into the swizzled bf16 K tile: fp8 elements become
+// bf16_rne(float(e4m3) * scale), rope elements are copied.  Lane (key = lane%32,
+// h = lane/32) of wave w converts 8-element halves of the wave's fp8 chunks.
 template <int DN, int DR>
-__device__ inline void dequant_tile(const uint8_t* raw_v, const float* raw_s, uint32_t valid,
-                                    uint16_t* kt, uint16_t* vt) {
+__device__ inline void dequant_tile(int lane, int wave, const uint8_t (&raw_v)[Shape<DN, DR>::RAW_V],
+                                    const float (&raw_s)[Shape<DN, DR>::RAW_S],
+                                    uint16_t (&kt)[kTile * Shape<DN, DR>::KCH * 8]) {
   using S = Shape<DN, DR>;
-  const int tid = threadIdx.x;
+  const int key = lane & 31;
+  const int h = lane >> 5;
 #pragma unroll
-  for (int u = 0; u < S::NU; ++u) {
-    const int unit = tid + u * kThreads;
-    if (unit < S::NOPE_UNITS) {
-      const int c = unit / (DN / 4);
-      const int dg = unit - c * (DN / 4);
-      uint32_t packed[8][2];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = chunk_key(c, e);
-        const bool ok = (valid >> key) & 1u;
-        const uint32_t w = ok ? *reinterpret_cast<const uint32_t*>(raw_v + key * S::ROWB + 4 * dg) : 0u;
-        const float sc = ok ? raw_s[key * S::NSC + (4 * dg) / 64] : 0.0f;
-        packed[e][0] = pack_bf16(e4m3_to_f32<0>(w) * sc, e4m3_to_f32<1>(w) * sc);
-        packed[e][1] = pack_bf16(e4m3_to_f32<2>(w) * sc, e4m3_to_f32<3>(w) * sc);
-        *reinterpret_cast<uint2*>(kt + key * S::KROW + 4 * dg) = make_uint2(packed[e][0], packed[e][1]);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 4 * dg + j;
-        // bf16 of dim j for keys e = 0..7: low or high half of packed[e][j/2]
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        uint4 w;
-        w.x = __builtin_amdgcn_perm(packed[1][j >> 1], packed[0][j >> 1], sel);
-        w.y = __builtin_amdgcn_perm(packed[3][j >> 1], packed[2][j >> 1], sel);
-        w.z = __builtin_amdgcn_perm(packed[5][j >> 1], packed[4][j >> 1], sel);
-        w.w = __builtin_amdgcn_perm(packed[7][j >> 1], packed[6][j >> 1], sel);
-        *reinterpret_cast<uint4*>(vt + d * kTile + 8 * vt_chunk(d, c)) = w;
-      }
-    }
+  for (int u = 0; u < S::NOPE_U; ++u) {
+    const int c16 = wave * S::NOPE_U + u;
+    const int d0 = 16 * c16 + 8 * h;
+    const uint2 raw = *reinterpret_cast<const uint2*>(raw_v + (c16 * 32 + key) * 16 + 8 * h);
+    const float sc = raw_s[key * S::NSC + (16 * c16) / 64];
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.x, false) * sc;
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.x, true) * sc;
+    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.y, false) * sc;
+    const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.y, true) * sc;
+    uint4 w;
+    w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2_t));
+    w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2_t));
+    w.z = __builtin_bit_cast(uint32_t, __builtin_convertvector(c, bf16x2_t));
+    w.w = __builtin_bit_cast(uint32_t, __builtin_convertvector(d, bf16x2_t));
+    *reinterpret_cast<uint4*>(kt + kt_off<S::KCH>(key, d0)) = w;
   }
-  if (tid < S::ROPE_UNITS) {
-    const int kq = tid / (DR / 4);
-    const int dg = tid - kq * (DR / 4);
-    // keys 4kq..4kq+3 = chunk c = 2*(kq/4) + kq%2, positions 4*((kq/2)%2) .. +3
-    const int c = 2 * (kq >> 2) + (kq & 1);
-    const int pos0 = 4 * ((kq >> 1) & 1);
-    uint2 r[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = 4 * kq + j;
-      r[j] = ((valid >> key) & 1u) ? *reinterpret_cast<const uint2*>(raw_v + key * S::ROWB + DN + 8 * dg)
-                                   : make_uint2(0u, 0u);
-      *reinterpret_cast<uint2*>(kt + key * S::KROW + DN + 4 * dg) = r[j];
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d = DN + 4 * dg + e;
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t a0 = (e < 2) ? r[0].x : r[0].y;
-      const uint32_t a1 = (e < 2) ? r[1].x : r[1].y;
-      const uint32_t a2 = (e < 2) ? r[2].x : r[2].y;
-      const uint32_t a3 = (e < 2) ? r[3].x : r[3].y;
-      uint2 w;
-      w.x = __builtin_amdgcn_perm(a1, a0, sel);
-      w.y = __builtin_amdgcn_perm(a3, a2, sel);
-      *reinterpret_cast<uint2*>(vt + d * kTile + 8 * vt_chunk(d, c) + pos0) = w;
-    }
+  const int rc = 2 * wave + h;  // rope chunk of this lane
+  if (rc < S::ROPE_CH) {
+    const int c16 = DN / 16 + rc;
+    const uint4 w = *reinterpret_cast<const uint4*>(raw_v + (c16 * 32 + key) * 16);
+    *reinterpret_cast<uint4*>(kt + kt_off<S::KCH>(key, DN + 8 * rc)) = w;
   }
 }
 
@@ -237,19 +230,18 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   constexpr int DQK = S::DQK;
   constexpr int KSMAX = S::KS0;
   constexpr int MTMAX = S::MT0;
-  // Distinct LDS objects, so the compiler can tell the DMA targets from the buffers
-  // that are read while a DMA is in flight.
-  __shared__ __align__(16) uint8_t raw_v0[kTile * S::ROWB];
-  __shared__ __align__(16) uint8_t raw_v1[kTile * S::ROWB];
-  __shared__ __align__(16) float raw_s0[kTile * S::NSC];
-  __shared__ __align__(16) float raw_s1[kTile * S::NSC];
-  __shared__ __align__(16) uint16_t kt[kTile * S::KROW];
-  __shared__ __align__(16) uint16_t vt[DQK * kTile];
+  constexpr int NV = S::DMA_PER_TILE;
+  __shared__ __align__(16) uint8_t raw_v0[S::RAW_V];
+  __shared__ __align__(16) uint8_t raw_v1[S::RAW_V];
+  __shared__ __align__(16) uint8_t raw_v2[S::RAW_V];
+  __shared__ __align__(16) uint8_t raw_v3[S::RAW_V];
+  __shared__ __align__(16) float raw_s0[S::RAW_S];
+  __shared__ __align__(16) float raw_s1[S::RAW_S];
+  __shared__ __align__(16) float raw_s2[S::RAW_S];
+  __shared__ __align__(16) float raw_s3[S::RAW_S];
+  __shared__ __align__(16) uint16_t kt[kTile * S::KCH * 8];
   __shared__ __align__(16) float xbuf[kWaves * 16 * 64];
-  __shared__ const uint8_t* rowv0[kTile];
-  __shared__ const uint8_t* rowv1[kTile];
-  __shared__ const uint8_t* rows0[kTile];
-  __shared__ const uint8_t* rows1[kTile];
+  __shared__ __align__(16) int32_t si_lds[kMaxSiCols];  // this split's sparse_indices columns
 
   // Block -> (token, split, head group): the head groups of one (token, split) are
   // 8 blocks apart, i.e. on the same XCD and dispatched together.
@@ -264,11 +256,11 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int n = lane & 31;  // head within the wave's block / key row within a fragment
-  const int h = lane >> 5;  // lane half
-  const int hb = wave >> 1;  // head block of this wave
-  const int dh = wave & 1;   // dim half of this wave
+  const int wave = tid >> 6;  // wave-uniform
+  const int n = lane & 31;    // head within the wave's block / key row within a fragment
+  const int h = lane >> 5;    // lane half
+  const int hb = wave >> 1;   // head block of this wave
+  const int dh = wave & 1;    // dim half of this wave
   const int head = hg * 64 + hb * 32 + n;
   const bool block_active = hg * 64 + hb * 32 < num_heads;
   const int ks_n = dh == 0 ? S::KS0 : S::KS1;  // k-steps of this wave's dims
@@ -282,8 +274,13 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   const int per = (ntiles + num_splits - 1) / num_splits;
   const int tile_begin = split * per;
   const int tile_end = min(ntiles, tile_begin + per);
+  const int col_base = tile_begin * kTile;
+  const int col_end = min(ncols, tile_end * kTile);
   const uint16_t* qrow = q + ((int64_t)t * num_heads + min(head, num_heads - 1)) * DQK;
-  const void* dummy = q + (int64_t)t * num_heads * DQK;  // >= 16 readable bytes
+
+  // Stage this split's index columns in LDS (the tile loop then issues no global
+  // loads besides the row DMA).
+  for (int c = col_base + tid; c < col_end; c += kThreads) si_lds[c - col_base] = si_row[c];
 
   // Q^T fragments: lane (head n, half h) holds dims dim0 + [16kk + 8h, 16kk + 8h + 8).
   bf16x8_t qf[KSMAX];
@@ -293,7 +290,6 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     if (kk < ks_n && head < num_heads)
       qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + dim0 + 16 * kk + 8 * h);
   }
-
   f32x16_t acc_o[MTMAX];
 #pragma unroll
   for (int mt = 0; mt < MTMAX; ++mt)
@@ -303,47 +299,58 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   float l_run = 0.0f;  // sum of the bf16-rounded weights (normalizes O)
   float l_lse = 0.0f;  // sum of the fp32 weights (log-sum-exp)
 
-  // Prologue: rows of the first two tiles, DMA of the first.
-  if (tile_begin < tile_end) {
-    resolve_rows(rowv0, rows0, tile_begin * kTile, ncols, window, si_row, swa, comp, S::ROWB, S::NSC);
-    resolve_rows(rowv1, rows1, (tile_begin + 1) * kTile, ncols, window, si_row, swa, comp, S::ROWB,
-                 S::NSC);
-    lds_barrier();
-    dma_tile<DN, DR>(raw_v0, raw_s0, rowv0, rows0, dummy);
-  }
+  // Q fragments and index columns landed (a wait the compiler sees, so it does not
+  // re-check the Q loads inside the tile loop)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  lds_barrier();  // si_lds complete
+  // Prologue: DMA of the first three tiles.
+  if (tile_begin < tile_end)
+    dma_tile<DN, DR>(lane, wave, raw_v0, raw_s0, tile_begin * kTile, ncols, window, si_lds, col_base, swa, comp);
+  if (tile_begin + 1 < tile_end)
+    dma_tile<DN, DR>(lane, wave, raw_v1, raw_s1, (tile_begin + 1) * kTile, ncols, window, si_lds, col_base, swa,
+                     comp);
+  if (tile_begin + 2 < tile_end)
+    dma_tile<DN, DR>(lane, wave, raw_v2, raw_s2, (tile_begin + 2) * kTile, ncols, window, si_lds, col_base, swa,
+                     comp);
 
-  // One tile step; the tag selects the LDS staging buffer holding this tile.
-  auto step = [&](int tile, auto cur_tag) __attribute__((always_inline)) {
-    constexpr bool CUR1 = decltype(cur_tag)::value;
-    uint8_t* raw_v = CUR1 ? raw_v1 : raw_v0;
-    float* raw_s = CUR1 ? raw_s1 : raw_s0;
-    uint8_t* nraw_v = CUR1 ? raw_v0 : raw_v1;
-    float* nraw_s = CUR1 ? raw_s0 : raw_s1;
-    const uint8_t** rowv = CUR1 ? rowv1 : rowv0;
-    const uint8_t** rows = CUR1 ? rows1 : rows0;
-    const uint8_t** nrowv = CUR1 ? rowv0 : rowv1;
-    const uint8_t** nrows = CUR1 ? rows0 : rows1;
+  // One tile step; the tag selects the ring slot holding this tile.
+  auto step = [&](int tile, auto slot_tag) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_tag)::value;
+    auto& raw_v = SL == 0 ? raw_v0 : (SL == 1 ? raw_v1 : (SL == 2 ? raw_v2 : raw_v3));
+    auto& raw_s = SL == 0 ? raw_s0 : (SL == 1 ? raw_s1 : (SL == 2 ? raw_s2 : raw_s3));
+    // tile + 3 goes to the slot tile - 1 used
+    auto& nraw_v = SL == 0 ? raw_v3 : (SL == 1 ? raw_v0 : (SL == 2 ? raw_v1 : raw_v2));
+    auto& nraw_s = SL == 0 ? raw_s3 : (SL == 1 ? raw_s0 : (SL == 2 ? raw_s1 : raw_s2));
     const int tile0 = tile * kTile;
+    // Per-lane indices are recomputed in every step from an opaque copy of the lane id:
+    // hoisting them out of the tile loop would keep dozens of registers live.
+    int lane_s = lane;
+    asm volatile("" : "+v"(lane_s));
+    const int n_s = lane_s & 31;
+    const int h_s = lane_s >> 5;
 
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's DMA of this tile landed
-    lds_barrier();  // all waves' DMA landed; the previous tile's compute is done
-    if (tile + 1 < tile_end) dma_tile<DN, DR>(nraw_v, nraw_s, nrowv, nrows, dummy);
-    if (tile + 2 < tile_end)
-      resolve_rows(rowv, rows, tile0 + 2 * kTile, ncols, window, si_row, swa, comp, S::ROWB, S::NSC);
+    // This wave's DMA of this tile landed; the DMAs of the next tiles may be in flight.
+    const int ahead = min(tile_end - 1 - tile, kStages - 2);
+    if (ahead >= 2)
+      wait_vmem<2 * NV>();
+    else if (ahead == 1)
+      wait_vmem<NV>();
+    else
+      wait_vmem<0>();
+    lds_barrier();  // every wave's DMA of this tile landed; the previous tile's compute is done
+    if (tile + 3 < tile_end)
+      dma_tile<DN, DR>(lane_s, wave, nraw_v, nraw_s, tile0 + 3 * kTile, ncols, window, si_lds, col_base, swa,
+                       comp);
     // validity of this tile's 32 columns, one bit per key
     uint32_t valid_mask;
     {
-      bool ok = false;
-      const int col = tile0 + n;
-      if (col < ncols) {
-        const int slot = si_row[col];
-        const KvDesc& kv = col < window ? swa : comp;
-        ok = slot_ok(slot, kv.block, kv.num_pages);
-      }
-      valid_mask = (uint32_t)__ballot(ok);
+      const uint8_t* vr;
+      const uint8_t* sr;
+      col_row(tile0 + n_s, ncols, window, si_lds, col_base, swa, comp, S::ROWB, S::NSC, &vr, &sr);
+      valid_mask = (uint32_t)__ballot(vr != kZeroRow);
     }
-    dequant_tile<DN, DR>(raw_v, raw_s, valid_mask, kt, vt);
-    lds_barrier();  // K / V^T copies complete
+    dequant_tile<DN, DR>(lane_s, wave, raw_v, raw_s, kt);
+    lds_barrier();  // K tile complete
 
     // ---- partial S^T = K Q^T over this wave's dims: lane (head n, half h) gets
     //      keys 8*(r/4) + 4h + r%4, r = 0..15
@@ -355,33 +362,37 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
       for (int kk = 0; kk < KSMAX; ++kk) {
         if (kk < ks_n) {
           const bf16x8_t a =
-              *reinterpret_cast<const bf16x8_t*>(kt + n * S::KROW + dim0 + 16 * kk + 8 * h);
+              *reinterpret_cast<const bf16x8_t*>(kt + kt_off<S::KCH>(n_s, dim0 + 16 * kk + 8 * h_s));
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
         }
       }
     }
     // ---- add the partner wave's half: S = S(dims half 0) + S(dims half 1)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) xbuf[(wave * 16 + r) * 64 + lane] = s[r];
+    for (int r = 0; r < 16; ++r) xbuf[(wave * 16 + r) * 64 + lane_s] = s[r];
     lds_barrier();
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float other = xbuf[((wave ^ 1) * 16 + r) * 64 + lane];
+      const float other = xbuf[((wave ^ 1) * 16 + r) * 64 + lane_s];
       s[r] = dh == 0 ? s[r] + other : other + s[r];
     }
     if (!block_active) return;
-    // ---- online softmax (log2 domain, lazy rescaling); identical in both dim halves
+    // ---- online softmax (log2 domain, lazy rescaling); identical in both dim halves.
+    //      Masking is skipped for fully attended tiles (the common case).
+    if (valid_mask != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * h_s + (r & 3);
+        s[r] = ((valid_mask >> key) & 1u) ? s[r] : -INFINITY;
+      }
+    }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * h + (r & 3);
-      s[r] = ((valid_mask >> key) & 1u) ? s[r] * scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, s[r]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
     const bool upd = tmax > m_run + kRescaleSlack;  // also true when m_run is -inf
     if (__ballot(upd) != 0ull) {
-      const float alpha = upd ? exp2f(m_run - tmax) : 1.0f;  // exp2(-inf) = 0
+      const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;  // exp2(-inf) = 0
       if (upd) m_run = tmax;
       l_run *= alpha;
       l_lse *= alpha;
@@ -395,30 +406,43 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       // normalize by the same rounded weights the PV MFMA multiplies with
-      const float pf = exp2f(s[r] - m_use);
+      const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -m_use));
       const __bf16 p = (__bf16)pf;
       l_run += (float)p;
       l_lse += pf;
       pb[r >> 3][r & 7] = p;
     }
-    // ---- O^T += V^T P^T over this wave's output dims
+    // ---- O^T += V^T P^T over this wave's output dims.  The V^T fragment (lane: dim
+    //      32mt + lane%32, 8 keys) comes from the key-major tile through two transposing
+    //      reads: in each 16-lane group, lane (a = i/4, b = i%4) points at key a of the
+    //      4-key set and dims 4b..4b+3, and lane j receives dim j of all 4 keys.
+    const int g = lane_s >> 4;
+    const int ia = (lane_s & 15) >> 2;
+    const int ib = lane_s & 3;
 #pragma unroll
     for (int mt = 0; mt < MTMAX; ++mt) {
       if (mt < mt_n) {
-        const int d = dim0 + 32 * mt + n;
+        const int dim = dim0 + 32 * mt + 16 * (g & 1) + 4 * ib;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8_t a =
-              *reinterpret_cast<const bf16x8_t*>(vt + d * kTile + 8 * vt_chunk(d, 2 * ks + h));
+          const int key0 = 16 * ks + 4 * (g >> 1) + ia;
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(kt + kt_off<S::KCH>(key0, dim)));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(kt + kt_off<S::KCH>(key0 + 8, dim)));
+          const bf16x8_t a = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc_o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], acc_o[mt], 0, 0, 0);
         }
       }
     }
   };
 
-  for (int tile = tile_begin; tile < tile_end; tile += 2) {
-    step(tile, std::false_type{});
-    if (tile + 1 < tile_end) step(tile + 1, std::true_type{});
+  for (int tile = tile_begin; tile < tile_end; tile += kStages) {
+    step(tile, std::integral_constant<int, 0>{});
+    if (tile + 1 < tile_end) step(tile + 1, std::integral_constant<int, 1>{});
+    if (tile + 2 < tile_end) step(tile + 2, std::integral_constant<int, 2>{});
+    if (tile + 3 < tile_end) step(tile + 3, std::integral_constant<int, 3>{});
   }
 
   if (!block_active || head >= num_heads) return;
@@ -439,11 +463,11 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     for (int mt = 0; mt < MTMAX; ++mt)
       if (mt < mt_n) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int gg = 0; gg < 4; ++gg) {
           uint2 w;
-          w.x = pack_bf16(acc_o[mt][4 * g + 0] * f, acc_o[mt][4 * g + 1] * f);
-          w.y = pack_bf16(acc_o[mt][4 * g + 2] * f, acc_o[mt][4 * g + 3] * f);
-          *reinterpret_cast<uint2*>(orow + 32 * mt + 8 * g + 4 * h) = w;
+          w.x = pack_bf16(acc_o[mt][4 * gg + 0] * f, acc_o[mt][4 * gg + 1] * f);
+          w.y = pack_bf16(acc_o[mt][4 * gg + 2] * f, acc_o[mt][4 * gg + 3] * f);
+          *reinterpret_cast<uint2*>(orow + 32 * mt + 8 * gg + 4 * h) = w;
         }
       }
     if (lse_out != nullptr && h == 0 && dh == 0)
@@ -455,10 +479,10 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     for (int mt = 0; mt < MTMAX; ++mt)
       if (mt < mt_n) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 w = make_float4(acc_o[mt][4 * g + 0] * inv, acc_o[mt][4 * g + 1] * inv,
-                                       acc_o[mt][4 * g + 2] * inv, acc_o[mt][4 * g + 3] * inv);
-          *reinterpret_cast<float4*>(prow + 32 * mt + 8 * g + 4 * h) = w;
+        for (int gg = 0; gg < 4; ++gg) {
+          const float4 w = make_float4(acc_o[mt][4 * gg + 0] * inv, acc_o[mt][4 * gg + 1] * inv,
+                                       acc_o[mt][4 * gg + 2] * inv, acc_o[mt][4 * gg + 3] * inv);
+          *reinterpret_cast<float4*>(prow + 32 * mt + 8 * gg + 4 * h) = w;
         }
       }
     if (h == 0 && dh == 0)
@@ -498,7 +522,8 @@ __global__ __launch_bounds__(DQK) void combine_kernel(const float* __restrict__ 
 
 int choose_splits(int T, int num_heads, int max_cols, int dqk, int rowb) {
   const int units = T * ((num_heads + 63) / 64);  // workgroups without splitting
-  if (units <= 0 || units >= kNumCUs) return 1;
+  const int min_splits = ((max_cols + kTile - 1) / kTile * kTile + kMaxSiCols - 1) / kMaxSiCols;
+  if (units <= 0 || units >= kNumCUs) return std::max(1, min_splits);
   const int tiles = (max_cols + kTile - 1) / kTile;
   int s = (kNumCUs + units - 1) / units;
   s = std::min(s, std::max(1, tiles / 4));
@@ -506,7 +531,9 @@ int choose_splits(int T, int num_heads, int max_cols, int dqk, int rowb) {
   const int64_t row_bytes = (int64_t)max_cols * rowb;
   const int64_t part_bytes = 2LL * 128 * dqk * 4;
   s = (int)std::min<int64_t>(s, std::max<int64_t>(1, row_bytes / part_bytes));
-  return std::max(1, s);
+  // a workgroup stages at most kMaxSiCols index columns in LDS
+  const int need = (tiles * kTile + kMaxSiCols - 1) / kMaxSiCols;
+  return std::max(std::max(1, s), need);
 }
 
 template <int DN, int DR>
@@ -528,8 +555,13 @@ int launch(const uint16_t* q, int T, int H, const KvDesc& s, const KvDesc& c, co
   const int head_groups = (H + 63) / 64;
   const int pairs = T * splits;
   const int blocks = (pairs + 7) / 8 * 8 * head_groups;
-  hipLaunchKernelGGL((sparse_mla_kernel<DN, DR>), dim3(blocks), dim3(kThreads), 0, st, q, T, H, s, c,
-                     si, lens, W, P, scale * kLog2e, sink, out, lse, part_o, part_lse, splits,
+  // the index columns of one split are staged in LDS
+  const int max_tiles = (W + P + kTile - 1) / kTile;
+  const int si_cols = (max_tiles + splits - 1) / splits * kTile;
+  SAD_CHECK(si_cols <= kMaxSiCols, SAD_EUNSUPPORTED,
+            "sparse_mla_decode: %d index columns per workgroup exceed %d", si_cols, kMaxSiCols);
+  hipLaunchKernelGGL((sparse_mla_kernel<DN, DR>), dim3(blocks), dim3(kThreads), 0, st, q, T, H,
+                     s, c, si, lens, W, P, scale * kLog2e, sink, out, lse, part_o, part_lse, splits,
                      head_groups);
   int rc = check_launch("sparse_mla_decode(attention)");
   if (rc != SAD_OK || splits == 1) return rc;
@@ -579,8 +611,10 @@ extern "C" int sparse_mla_decode(const uint16_t* q_bf16, int32_t num_tokens, int
             "sparse_mla_decode: q and out must be 16-byte aligned");
   SAD_CHECK(((uintptr_t)workspace & 15) == 0, SAD_EINVAL,
             "sparse_mla_decode: workspace must be 16-byte aligned");
-  KvDesc s{(const uint8_t*)swa->pool, swa->page_stride, swa->num_pages, swa->block_size};
-  KvDesc c{(const uint8_t*)comp->pool, comp->page_stride, comp->num_pages, comp->block_size};
+  KvDesc s{(const uint8_t*)swa->pool, swa->page_stride, swa->num_pages, swa->block_size,
+           __builtin_ctz(swa->block_size)};
+  KvDesc c{(const uint8_t*)comp->pool, comp->page_stride, comp->num_pages, comp->block_size,
+           __builtin_ctz(comp->block_size)};
   hipStream_t st = (hipStream_t)stream;
   if (swa->d_nope == 512)
     return launch<512, 64>(q_bf16, num_tokens, num_heads, s, c, sparse_indices, sparse_topk_lens,
