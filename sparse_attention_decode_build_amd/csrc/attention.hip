@@ -18,7 +18,7 @@
 //     direct global-to-LDS loads (no VGPRs) while tile i is computed; each lane carries
 //     one row of every tile, so it computes one row address per tile;
 //   * tile i is dequantized from LDS (fp32 multiply by the row's block scale, bf16
-//     rounding) into one key-major, XOR-swizzled bf16 tile K[32][D].  S^T = K Q^T reads
+//     rounding) into one key-major bf16 tile K[32][D] (rows padded by one 16-byte chunk).  S^T = K Q^T reads
 //     it with 16-byte fragment loads; O^T += V^T P^T reads the same tile transposed
 //     (ds_read_b64_tr_b16), so no second copy is written;
 //   * S^T puts one head per lane, so the online softmax needs only a swap with lane^32,
@@ -31,6 +31,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "sad_internal.h"
 
@@ -67,6 +68,13 @@ __device__ inline void dma_x4(const void* src, uint32_t lds_wave_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(lds_wave_base), "v"(src) : "memory", "m0");
 }
+// Same with an immediate byte offset on the global address.  The instruction adds its
+// offset to the LDS address as well, so M0 is lowered by the same amount.
+template <int OFF>
+__device__ inline void dma_x4_off(const void* src, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%2"
+               :: "s"(lds_wave_base - OFF), "v"(src), "n"(OFF) : "memory", "m0");
+}
 __device__ inline void dma_x1(const void* src, uint32_t lds_wave_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                :: "s"(lds_wave_base), "v"(src) : "memory", "m0");
@@ -75,6 +83,32 @@ template <int N>
 __device__ inline void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
+// Scheduling hint for a chain of N MFMAs that each consume R LDS reads: keep
+// kLdsAhead reads in flight ahead of the chain, then one MFMA per R reads.
+constexpr int kLdsAhead = 8;
+template <int N, int R>
+__device__ inline void sched_reads_ahead() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, kLdsAhead, 0);
+  constexpr int body = N - kLdsAhead / R;
+#pragma unroll
+  for (int i = 0; i < body; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, kLdsAhead / R, 0);
+}
+
+// Compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>).
+template <typename F, int... J>
+__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <typename T>
 __device__ inline uint32_t lds_addr(const T* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T*)p;
@@ -111,7 +145,7 @@ struct Shape {
   static constexpr int VAL_LOADS = (CPR + 7) / 8;     // value DMAs per wave per tile
   static constexpr int DMA_PER_TILE = VAL_LOADS + 1;  // + one scale DMA
   static constexpr int RAW_V = VAL_LOADS * kWaves * 64 * 16;  // [chunk][row][16 B], padded
-  static constexpr int RAW_S = kThreads;                      // fp32 [row][NSC], padded
+  static constexpr int RAW_S = kThreads;                      // fp32 [block][row], padded
   static constexpr int NOPE_U = DN / 16 / kWaves;  // 16-byte fp8 chunks per wave (2 rows each)
   static constexpr int ROPE_CH = DR / 8;           // 16-byte bf16 chunks of the rope part
   static_assert(ROWB % 16 == 0 && DN % 64 == 0, "rows are whole chunks, 64-element scale blocks");
@@ -132,7 +166,9 @@ __device__ inline int kt_off(int key, int dim) {
 }
 
 // Row values / scales of one attended column, or the zero row when the column is not
-// attended (past ncols, slot -1, page outside the pool).
+// attended (past ncols, slot -1, page outside the pool).  ONE: the window and the
+// compressed columns read the same cache (wave-uniform descriptor).
+template <bool ONE>
 __device__ inline void col_row(int col, int ncols, int window, const int32_t* si_lds, int col_base,
                                const KvDesc& swa, const KvDesc& comp, int rowb, int nsc,
                                const uint8_t** vals, const uint8_t** scales) {
@@ -140,51 +176,53 @@ __device__ inline void col_row(int col, int ncols, int window, const int32_t* si
   *scales = kZeroRow;
   if (col >= ncols) return;
   const int slot = si_lds[col - col_base];
-  const KvDesc& kv = col < window ? swa : comp;
+  const KvDesc& kv = (ONE || col < window) ? swa : comp;
   if (slot < 0) return;
   const int page = slot >> kv.block_shift;
-  if ((int64_t)page >= kv.num_pages) return;
+  if (page >= (int)kv.num_pages) return;  // num_pages * block fits in int32
   const int ro = slot & (kv.block - 1);
   const uint8_t* pg = kv.pool + (int64_t)page * kv.stride;
   *vals = pg + ro * rowb;
   *scales = pg + (kv.block * rowb + ro * 4 * nsc);
 }
 
-// Copy one tile's raw rows HBM -> LDS.  Values go chunk-major ([chunk][row][16 B]), so
-// lane l of every value DMA carries row l%32 and only one row address is needed per
-// lane; scales go row-major ([row][NSC] fp32).  Every wave issues exactly DMA_PER_TILE
-// loads with all lanes active (padding lanes read the zero row into padding LDS), so
-// a wave's vmcnt advances by a known amount per tile.
-template <int DN, int DR>
-__device__ inline void dma_tile(int lane, int wave, uint8_t (&raw_v)[Shape<DN, DR>::RAW_V],
-                                float (&raw_s)[Shape<DN, DR>::RAW_S], int tile0, int ncols,
-                                int window, const int32_t* si_lds, int col_base, const KvDesc& swa,
-                                const KvDesc& comp) {
+// Copy one tile's raw rows HBM -> LDS.  Lane l of every wave carries row l%32 and
+// computes that row's address once.  Values go chunk-major ([chunk][row][16 B]): load j
+// of wave w brings chunks 8j + 2w + {0, 1} (lane halves) of all 32 rows.  Scales go
+// block-major ([block][row] fp32): lane l of wave w brings block 2w + l/32 of its row.
+// Every wave issues exactly DMA_PER_TILE loads with all lanes active (padding lanes
+// read the zero row into padding LDS), so a wave's vmcnt advances by a known amount
+// per tile.  Returns the tile's validity mask (bit j: column tile0 + j is attended).
+template <int DN, int DR, bool ONE>
+__device__ inline uint32_t dma_tile(int lane, int wave, uint8_t (&raw_v)[Shape<DN, DR>::RAW_V],
+                                    float (&raw_s)[Shape<DN, DR>::RAW_S], int tile0, int ncols,
+                                    int window, const int32_t* si_lds, int col_base, const KvDesc& swa,
+                                    const KvDesc& comp) {
   using S = Shape<DN, DR>;
+  __builtin_assume(wave >= 0 && wave < kWaves);
+  const int h = lane >> 5;
   const uint8_t* vrow;
   const uint8_t* srow;
-  col_row(tile0 + (lane & 31), ncols, window, si_lds, col_base, swa, comp, S::ROWB, S::NSC, &vrow, &srow);
-  const uint32_t vbase = lds_addr(raw_v);
-#pragma unroll
-  for (int j = 0; j < S::VAL_LOADS; ++j) {
-    const int jj = j * kWaves + wave;         // wave-uniform
-    const int c16 = 2 * jj + (lane >> 5);     // chunk carried by this lane
-    const uint8_t* src = c16 < S::CPR ? vrow + 16 * c16 : kZeroRow;
-    dma_x4(src, __builtin_amdgcn_readfirstlane(vbase + jj * 1024));
-  }
-  const int q = wave * 64 + lane;
-  const int srow_i = q / S::NSC;
-  const uint8_t* vr2;
-  const uint8_t* sr2;
-  col_row(tile0 + srow_i, srow_i < kTile ? ncols : 0, window, si_lds, col_base, swa, comp, S::ROWB, S::NSC,
-          &vr2, &sr2);
-  const uint8_t* ssrc = srow_i < kTile ? sr2 + 4 * (q - srow_i * S::NSC) : kZeroRow;
-  dma_x1(ssrc, __builtin_amdgcn_readfirstlane(lds_addr(raw_s) + wave * 256));
+  col_row<ONE>(tile0 + (lane & 31), ncols, window, si_lds, col_base, swa, comp, S::ROWB, S::NSC, &vrow, &srow);
+  const uint32_t vbase = lds_addr(raw_v) + wave * 1024;
+  const int c0 = 2 * wave + h;  // chunk of load 0
+  const uint8_t* vsrc = vrow + 16 * c0;
+  static_for<S::VAL_LOADS>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(vbase + j * kWaves * 1024);
+    if constexpr (8 * j + 2 * kWaves <= S::CPR)
+      dma_x4_off<128 * j>(vsrc, dst);  // every chunk of this load exists
+    else
+      dma_x4_off<0>(8 * j + c0 < S::CPR ? vsrc + 128 * j : kZeroRow, dst);
+  });
+  dma_x1(c0 < S::NSC ? srow + 4 * c0 : kZeroRow, __builtin_amdgcn_readfirstlane(lds_addr(raw_s) + wave * 256));
+  return (uint32_t)__ballot(vrow != kZeroRow);  // lanes 0..31 carry rows 0..31
 }
 
-// Dequantize the raw tile into the swizzled bf16 K tile: fp8 elements become
+// Dequantize the raw tile into the padded bf16 K tile: fp8 elements become
 // bf16_rne(float(e4m3) * scale), rope elements are copied.  Lane (key = lane%32,
-// h = lane/32) of wave w converts 8-element halves of the wave's fp8 chunks.
+// h = lane/32) of wave w converts 8-element halves of the wave's fp8 chunks.  All LDS
+// reads are issued before the arithmetic so their latencies overlap.
 template <int DN, int DR>
 __device__ inline void dequant_tile(int lane, int wave, const uint8_t (&raw_v)[Shape<DN, DR>::RAW_V],
                                     const float (&raw_s)[Shape<DN, DR>::RAW_S],
@@ -192,16 +230,25 @@ __device__ inline void dequant_tile(int lane, int wave, const uint8_t (&raw_v)[S
   using S = Shape<DN, DR>;
   const int key = lane & 31;
   const int h = lane >> 5;
+  uint2 raw[S::NOPE_U];
+  float sc[S::NOPE_U];
 #pragma unroll
   for (int u = 0; u < S::NOPE_U; ++u) {
     const int c16 = wave * S::NOPE_U + u;
-    const int d0 = 16 * c16 + 8 * h;
-    const uint2 raw = *reinterpret_cast<const uint2*>(raw_v + (c16 * 32 + key) * 16 + 8 * h);
-    const float sc = raw_s[key * S::NSC + (16 * c16) / 64];
-    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.x, false) * sc;
-    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.x, true) * sc;
-    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.y, false) * sc;
-    const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.y, true) * sc;
+    raw[u] = *reinterpret_cast<const uint2*>(raw_v + (c16 * 32 + key) * 16 + 8 * h);
+    if (u == 0 || (16 * c16) % 64 == 0) sc[u] = raw_s[((16 * c16) / 64) * 32 + key];
+    else sc[u] = sc[u - 1];
+  }
+  const int rc = 2 * wave + h;  // rope chunk of this lane
+  uint4 rope = make_uint4(0u, 0u, 0u, 0u);
+  if (rc < S::ROPE_CH) rope = *reinterpret_cast<const uint4*>(raw_v + ((DN / 16 + rc) * 32 + key) * 16);
+#pragma unroll
+  for (int u = 0; u < S::NOPE_U; ++u) {
+    const int d0 = 16 * (wave * S::NOPE_U + u) + 8 * h;
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[u].x, false) * sc[u];
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[u].x, true) * sc[u];
+    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[u].y, false) * sc[u];
+    const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[u].y, true) * sc[u];
     uint4 w;
     w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2_t));
     w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2_t));
@@ -209,15 +256,10 @@ __device__ inline void dequant_tile(int lane, int wave, const uint8_t (&raw_v)[S
     w.w = __builtin_bit_cast(uint32_t, __builtin_convertvector(d, bf16x2_t));
     *reinterpret_cast<uint4*>(kt + kt_off<S::KCH>(key, d0)) = w;
   }
-  const int rc = 2 * wave + h;  // rope chunk of this lane
-  if (rc < S::ROPE_CH) {
-    const int c16 = DN / 16 + rc;
-    const uint4 w = *reinterpret_cast<const uint4*>(raw_v + (c16 * 32 + key) * 16);
-    *reinterpret_cast<uint4*>(kt + kt_off<S::KCH>(key, DN + 8 * rc)) = w;
-  }
+  if (rc < S::ROPE_CH) *reinterpret_cast<uint4*>(kt + kt_off<S::KCH>(key, DN + 8 * rc)) = rope;
 }
 
-template <int DN, int DR>
+template <int DN, int DR, bool ONE>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(1, 1)))
 sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads, KvDesc swa,
@@ -231,14 +273,8 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   constexpr int KSMAX = S::KS0;
   constexpr int MTMAX = S::MT0;
   constexpr int NV = S::DMA_PER_TILE;
-  __shared__ __align__(16) uint8_t raw_v0[S::RAW_V];
-  __shared__ __align__(16) uint8_t raw_v1[S::RAW_V];
-  __shared__ __align__(16) uint8_t raw_v2[S::RAW_V];
-  __shared__ __align__(16) uint8_t raw_v3[S::RAW_V];
-  __shared__ __align__(16) float raw_s0[S::RAW_S];
-  __shared__ __align__(16) float raw_s1[S::RAW_S];
-  __shared__ __align__(16) float raw_s2[S::RAW_S];
-  __shared__ __align__(16) float raw_s3[S::RAW_S];
+  __shared__ __align__(16) uint8_t raw_v[kStages][S::RAW_V];
+  __shared__ __align__(16) float raw_s[kStages][S::RAW_S];
   __shared__ __align__(16) uint16_t kt[kTile * S::KCH * 8];
   __shared__ __align__(16) float xbuf[kWaves * 16 * 64];
   __shared__ __align__(16) int32_t si_lds[kMaxSiCols];  // this split's sparse_indices columns
@@ -266,6 +302,8 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   const int ks_n = dh == 0 ? S::KS0 : S::KS1;  // k-steps of this wave's dims
   const int mt_n = dh == 0 ? S::MT0 : S::MT1;  // m-tiles of this wave's dims
   const int dim0 = dh == 0 ? 0 : 32 * S::MT0;  // first dim of this wave's half
+  // the fp32 sum of the weights is only needed for the log-sum-exp outputs
+  const bool want_lse = lse_out != nullptr || num_splits > 1;
 
   const int width = window + padded;
   const int32_t* si_row = si + (int64_t)t * width;
@@ -290,6 +328,9 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     if (kk < ks_n && head < num_heads)
       qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + dim0 + 16 * kk + 8 * h);
   }
+  // Q^T lives in AGPRs (an MFMA operand only), leaving the VGPRs for fragments in flight
+#pragma unroll
+  for (int kk = 0; kk < KSMAX; ++kk) asm volatile("" : "+a"(qf[kk]));
   f32x16_t acc_o[MTMAX];
 #pragma unroll
   for (int mt = 0; mt < MTMAX; ++mt)
@@ -303,32 +344,29 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   // re-check the Q loads inside the tile loop)
   __builtin_amdgcn_s_waitcnt(0x0F70);
   lds_barrier();  // si_lds complete
-  // Prologue: DMA of the first three tiles.
+  // Prologue: DMA of the first three tiles.  Each DMA also yields the tile's validity
+  // mask (bit j: column j is attended); the masks rotate with the ring.
+  uint32_t mask0 = 0, mask1 = 0, mask2 = 0;
   if (tile_begin < tile_end)
-    dma_tile<DN, DR>(lane, wave, raw_v0, raw_s0, tile_begin * kTile, ncols, window, si_lds, col_base, swa, comp);
+    mask0 = dma_tile<DN, DR, ONE>(lane, wave, raw_v[0], raw_s[0], tile_begin * kTile, ncols, window, si_lds,
+                             col_base, swa, comp);
   if (tile_begin + 1 < tile_end)
-    dma_tile<DN, DR>(lane, wave, raw_v1, raw_s1, (tile_begin + 1) * kTile, ncols, window, si_lds, col_base, swa,
-                     comp);
+    mask1 = dma_tile<DN, DR, ONE>(lane, wave, raw_v[1], raw_s[1], (tile_begin + 1) * kTile, ncols, window, si_lds,
+                             col_base, swa, comp);
   if (tile_begin + 2 < tile_end)
-    dma_tile<DN, DR>(lane, wave, raw_v2, raw_s2, (tile_begin + 2) * kTile, ncols, window, si_lds, col_base, swa,
-                     comp);
+    mask2 = dma_tile<DN, DR, ONE>(lane, wave, raw_v[2], raw_s[2], (tile_begin + 2) * kTile, ncols, window, si_lds,
+                             col_base, swa, comp);
 
-  // One tile step; the tag selects the ring slot holding this tile.
-  auto step = [&](int tile, auto slot_tag) __attribute__((always_inline)) {
-    constexpr int SL = decltype(slot_tag)::value;
-    auto& raw_v = SL == 0 ? raw_v0 : (SL == 1 ? raw_v1 : (SL == 2 ? raw_v2 : raw_v3));
-    auto& raw_s = SL == 0 ? raw_s0 : (SL == 1 ? raw_s1 : (SL == 2 ? raw_s2 : raw_s3));
-    // tile + 3 goes to the slot tile - 1 used
-    auto& nraw_v = SL == 0 ? raw_v3 : (SL == 1 ? raw_v0 : (SL == 2 ? raw_v1 : raw_v2));
-    auto& nraw_s = SL == 0 ? raw_s3 : (SL == 1 ? raw_s0 : (SL == 2 ? raw_s1 : raw_s2));
-    const int tile0 = tile * kTile;
+  // First half of a tile step: wait for the tile, start the DMA three tiles ahead,
+  // dequantize, S^T = K Q^T (both dim halves summed), masking.  Returns the tile's
+  // scaled row maximum per head (log2 domain).
+  auto front = [&](int tile, int slot, f32x16_t& s) __attribute__((always_inline)) -> float {
     // Per-lane indices are recomputed in every step from an opaque copy of the lane id:
     // hoisting them out of the tile loop would keep dozens of registers live.
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
     const int n_s = lane_s & 31;
     const int h_s = lane_s >> 5;
-
     // This wave's DMA of this tile landed; the DMAs of the next tiles may be in flight.
     const int ahead = min(tile_end - 1 - tile, kStages - 2);
     if (ahead >= 2)
@@ -337,48 +375,42 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
       wait_vmem<NV>();
     else
       wait_vmem<0>();
-    lds_barrier();  // every wave's DMA of this tile landed; the previous tile's compute is done
+    lds_barrier();  // every wave's DMA of this tile landed; the previous tile's PV is done
+    const uint32_t valid_mask = mask0;
+    uint32_t mask3 = 0;
     if (tile + 3 < tile_end)
-      dma_tile<DN, DR>(lane_s, wave, nraw_v, nraw_s, tile0 + 3 * kTile, ncols, window, si_lds, col_base, swa,
-                       comp);
-    // validity of this tile's 32 columns, one bit per key
-    uint32_t valid_mask;
-    {
-      const uint8_t* vr;
-      const uint8_t* sr;
-      col_row(tile0 + n_s, ncols, window, si_lds, col_base, swa, comp, S::ROWB, S::NSC, &vr, &sr);
-      valid_mask = (uint32_t)__ballot(vr != kZeroRow);
-    }
-    dequant_tile<DN, DR>(lane_s, wave, raw_v, raw_s, kt);
+      mask3 = dma_tile<DN, DR, ONE>(lane_s, wave, raw_v[(slot + 3) & 3], raw_s[(slot + 3) & 3],
+                               (tile + 3) * kTile, ncols, window, si_lds, col_base, swa, comp);
+    mask0 = mask1;
+    mask1 = mask2;
+    mask2 = mask3;
+    dequant_tile<DN, DR>(lane_s, wave, raw_v[slot], raw_s[slot], kt);
     lds_barrier();  // K tile complete
 
     // ---- partial S^T = K Q^T over this wave's dims: lane (head n, half h) gets
-    //      keys 8*(r/4) + 4h + r%4, r = 0..15
-    f32x16_t s;
+    //      keys 8*(r/4) + 4h + r%4, r = 0..15.  All fragment reads are issued first.
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.0f;
     if (block_active) {
+      const uint16_t* kbase = kt + kt_off<S::KCH>(n_s, dim0 + 8 * h_s);
+      bf16x8_t af[KSMAX];
 #pragma unroll
-      for (int kk = 0; kk < KSMAX; ++kk) {
-        if (kk < ks_n) {
-          const bf16x8_t a =
-              *reinterpret_cast<const bf16x8_t*>(kt + kt_off<S::KCH>(n_s, dim0 + 16 * kk + 8 * h_s));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
-        }
-      }
+      for (int kk = 0; kk < KSMAX; ++kk)
+        if (kk < ks_n) af[kk] = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * kk);
+#pragma unroll
+      for (int kk = 0; kk < KSMAX; ++kk)
+        if (kk < ks_n) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], qf[kk], s, 0, 0, 0);
+      // schedule: kLdsAhead fragment reads in flight ahead of the MFMA chain
+      sched_reads_ahead<KSMAX, 1>();
     }
-    // ---- add the partner wave's half: S = S(dims half 0) + S(dims half 1)
+    // ---- add the partner wave's half (addition commutes: both waves get the same sum)
 #pragma unroll
     for (int r = 0; r < 16; ++r) xbuf[(wave * 16 + r) * 64 + lane_s] = s[r];
     lds_barrier();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float other = xbuf[((wave ^ 1) * 16 + r) * 64 + lane_s];
-      s[r] = dh == 0 ? s[r] + other : other + s[r];
-    }
-    if (!block_active) return;
-    // ---- online softmax (log2 domain, lazy rescaling); identical in both dim halves.
-    //      Masking is skipped for fully attended tiles (the common case).
+    for (int r = 0; r < 16; ++r) s[r] += xbuf[((wave ^ 1) * 16 + r) * 64 + lane_s];
+    if (!block_active) return -INFINITY;
+    // ---- masking (skipped for fully attended tiles, the common case) and row maximum
     if (valid_mask != 0xFFFFFFFFu) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -389,28 +421,30 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
-    const bool upd = tmax > m_run + kRescaleSlack;  // also true when m_run is -inf
-    if (__ballot(upd) != 0ull) {
-      const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;  // exp2(-inf) = 0
-      if (upd) m_run = tmax;
-      l_run *= alpha;
-      l_lse *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < MTMAX; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
-    }
+    return fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
+  };
+
+  // Second half: weights relative to the running maximum, O^T += V^T P^T.
+  auto back = [&](const f32x16_t& s) __attribute__((always_inline)) {
+    if (!block_active) return;
+    int lane_s = lane;
+    asm volatile("" : "+v"(lane_s));
     const float m_use = m_run == -INFINITY ? 0.0f : m_run;
     bf16x8_t pb[2];
+    float pf[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      // normalize by the same rounded weights the PV MFMA multiplies with
-      const float pf = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -m_use));
-      const __bf16 p = (__bf16)pf;
-      l_run += (float)p;
-      l_lse += pf;
-      pb[r >> 3][r & 7] = p;
+    for (int r = 0; r < 16; r += 2) {
+      pf[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -m_use));
+      pf[r + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], scale_log2, -m_use));
+      const bf16x2_t w = __builtin_convertvector(f32x2_t{pf[r], pf[r + 1]}, bf16x2_t);
+      pb[r >> 3][r & 7] = w[0];
+      pb[r >> 3][(r & 7) + 1] = w[1];
+      // O is normalized by the sum of the same rounded weights the PV MFMA multiplies with
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(w, bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
+    }
+    if (want_lse) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) l_lse += pf[r];
     }
     // ---- O^T += V^T P^T over this wave's output dims.  The V^T fragment (lane: dim
     //      32mt + lane%32, 8 keys) comes from the key-major tile through two transposing
@@ -419,30 +453,59 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     const int g = lane_s >> 4;
     const int ia = (lane_s & 15) >> 2;
     const int ib = lane_s & 3;
+    const uint16_t* vbase = kt + kt_off<S::KCH>(4 * (g >> 1) + ia, dim0 + 16 * (g & 1) + 4 * ib);
+    s16x4_t vf[MTMAX][4];
+#pragma unroll
+    for (int mt = 0; mt < MTMAX; ++mt)
+      if (mt < mt_n)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)  // keys 8*q4 + 4*(g/2) + ia
+          vf[mt][q4] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(vbase + kt_off<S::KCH>(8 * q4, 32 * mt)));
 #pragma unroll
     for (int mt = 0; mt < MTMAX; ++mt) {
       if (mt < mt_n) {
-        const int dim = dim0 + 32 * mt + 16 * (g & 1) + 4 * ib;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int key0 = 16 * ks + 4 * (g >> 1) + ia;
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4_t*)(kt + kt_off<S::KCH>(key0, dim)));
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4_t*)(kt + kt_off<S::KCH>(key0 + 8, dim)));
           const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+              bf16x8_t, __builtin_shufflevector(vf[mt][2 * ks], vf[mt][2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7));
           acc_o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], acc_o[mt], 0, 0, 0);
         }
       }
     }
+    sched_reads_ahead<2 * MTMAX, 2>();
   };
 
-  for (int tile = tile_begin; tile < tile_end; tile += kStages) {
-    step(tile, std::integral_constant<int, 0>{});
-    if (tile + 1 < tile_end) step(tile + 1, std::integral_constant<int, 1>{});
-    if (tile + 2 < tile_end) step(tile + 2, std::integral_constant<int, 2>{});
-    if (tile + 3 < tile_end) step(tile + 3, std::integral_constant<int, 3>{});
+  // Tile loop.  The running maximum is kept until a tile exceeds it by 2^slack; the
+  // (rare) rescale of O then runs outside the inner loop, so the O accumulators stay
+  // in place across the steps of the inner loop.
+  int tile = tile_begin;
+  int slot = 0;
+  for (;;) {
+    f32x16_t s;
+    float tmax = -INFINITY;
+    bool rescale = false;
+    for (; tile < tile_end; ++tile) {
+      tmax = front(tile, slot, s);
+      slot = (slot + 1) & (kStages - 1);
+      if (__ballot(tmax > m_run + kRescaleSlack) != 0ull) {  // also true when m_run is -inf
+        rescale = true;
+        break;
+      }
+      back(s);
+    }
+    if (!rescale) break;
+    const bool upd = tmax > m_run + kRescaleSlack;
+    const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;  // exp2(-inf) = 0
+    if (upd) m_run = tmax;
+    l_run *= alpha;
+    l_lse *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < MTMAX; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
+    back(s);
+    ++tile;
   }
 
   if (!block_active || head >= num_heads) return;
@@ -560,9 +623,16 @@ int launch(const uint16_t* q, int T, int H, const KvDesc& s, const KvDesc& c, co
   const int si_cols = (max_tiles + splits - 1) / splits * kTile;
   SAD_CHECK(si_cols <= kMaxSiCols, SAD_EUNSUPPORTED,
             "sparse_mla_decode: %d index columns per workgroup exceed %d", si_cols, kMaxSiCols);
-  hipLaunchKernelGGL((sparse_mla_kernel<DN, DR>), dim3(blocks), dim3(kThreads), 0, st, q, T, H,
-                     s, c, si, lens, W, P, scale * kLog2e, sink, out, lse, part_o, part_lse, splits,
-                     head_groups);
+  // one cache for both segments (the usual case): wave-uniform row descriptors
+  const bool one = s.pool == c.pool && s.stride == c.stride && s.num_pages == c.num_pages && s.block == c.block;
+  if (one)
+    hipLaunchKernelGGL((sparse_mla_kernel<DN, DR, true>), dim3(blocks), dim3(kThreads), 0, st, q, T, H,
+                       s, c, si, lens, W, P, scale * kLog2e, sink, out, lse, part_o, part_lse, splits,
+                       head_groups);
+  else
+    hipLaunchKernelGGL((sparse_mla_kernel<DN, DR, false>), dim3(blocks), dim3(kThreads), 0, st, q, T, H,
+                       s, c, si, lens, W, P, scale * kLog2e, sink, out, lse, part_o, part_lse, splits,
+                       head_groups);
   int rc = check_launch("sparse_mla_decode(attention)");
   if (rc != SAD_OK || splits == 1) return rc;
   hipLaunchKernelGGL((combine_kernel<Sh::DQK>), dim3(H, T), dim3(Sh::DQK), 0, st, part_o, part_lse,
