@@ -168,6 +168,89 @@ def cpu_baseline(wl: WL.Workload, budget_s: float) -> dict:
                       f"of layer 0 of the same {WORKLOAD} workload, float64 numpy oracle, {dt:.1f} s"}
 
 
+def copy_calibration(gib: float) -> int:
+    """A plain device copy of known size (fp32 multiply by one: reads N bytes, writes N
+    bytes), run three times.  Under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE per
+    dispatch scale the counters of the other kernels to bytes."""
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {n * 4} bytes read and written per dispatch")
+    return 0
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(directory: str, suffix: str) -> str:
+    for root, _, files in os.walk(directory):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {directory}")
+
+
+def summarize_stats(directory: str) -> int:
+    """Markdown table of a rocprofv3 --kernel-trace --stats --output-format csv run."""
+    rows = _read_csv(_find(directory, "kernel_stats.csv"))
+    print("| kernel | calls | average (us) | min (us) | max (us) |")
+    print("|---|---|---|---|---|")
+    other_calls, other_ns = 0, 0.0
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "")
+        if not name.startswith("sad::"):  # torch kernels of the workload generator
+            other_calls += int(r["Calls"])
+            other_ns += float(r["TotalDurationNs"])
+            continue
+        print(f"| `{name.split('(')[0]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    print(f"| other (workload generation, torch) | {other_calls} | total {other_ns / 1e3:.0f} us | | |")
+    return 0
+
+
+def _pmc_mean(directory: str, counter: str, pattern: str, largest: bool = False) -> tuple:
+    """Mean counter value per dispatch of the kernels whose name contains `pattern`
+    (largest: only dispatches within 2x of the largest value, e.g. the 1 GiB copy among
+    smaller kernels of the same name)."""
+    rows = [r for r in _read_csv(_find(directory, "counter_collection.csv"))
+            if r["Counter_Name"] == counter and pattern in r["Kernel_Name"]]
+    if not rows:
+        raise RuntimeError(f"no {counter} rows for kernels matching {pattern!r} under {directory}")
+    vals = [float(r["Counter_Value"]) for r in rows]
+    if largest:
+        top = max(vals)
+        vals = [v for v in vals if v >= 0.5 * top]
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str) -> int:
+    """Attention kernel HBM traffic per launch from two rocprofv3 --pmc runs of
+    `bench.py --copy-calibration-gib 1 ...` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+    each scaled by the same counter on the 1 GiB copy kernel."""
+    copy_pat, attn_pat = "MulFunctor", "sparse_mla_kernel"
+    cal = float(1 << 30)
+    cf, _ = _pmc_mean(fetch_dir, "FETCH_SIZE", copy_pat, largest=True)
+    cw, _ = _pmc_mean(write_dir, "WRITE_SIZE", copy_pat, largest=True)
+    af, nf = _pmc_mean(fetch_dir, "FETCH_SIZE", attn_pat)
+    aw, nw = _pmc_mean(write_dir, "WRITE_SIZE", attn_pat)
+    kf, kw = cal / (cf * 1024.0), cal / (cw * 1024.0)
+    fetch_b, write_b = af * 1024.0 * kf, aw * 1024.0 * kw
+    src = open(os.path.join(ROOT, "sparse_attention_decode_build_amd", "csrc", "attention.hip"), "rb").read()
+    print(f"- attention.hip sha256: `{hashlib.sha256(src).hexdigest()}`")
+    print(f"- copy kernel (1 GiB read + 1 GiB written): FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB "
+          f"-> scale factors {kf:.4f} (fetch), {kw:.4f} (write)")
+    print(f"- sparse_mla_kernel FETCH_SIZE mean {af:.0f} KiB over {nf} dispatches -> {fetch_b / 1e6:.2f} MB")
+    print(f"- sparse_mla_kernel WRITE_SIZE mean {aw:.0f} KiB over {nw} dispatches -> {write_b / 1e6:.2f} MB")
+    print(f"- bytes per launch: {fetch_b + write_b:.0f}")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,7 +259,16 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=4, help="independent layers rotated per step")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                    help="first run a plain copy of this many GiB (rocprofv3 counter calibration)")
+    ap.add_argument("--summarize-stats", metavar="DIR", help="print a rocprofv3 kernel-stats CSV as markdown")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print attention traffic per launch from two rocprofv3 --pmc CSV runs")
     args = ap.parse_args()
+    if args.summarize_stats:
+        return summarize_stats(args.summarize_stats)
+    if args.summarize_traffic:
+        return summarize_traffic(*args.summarize_traffic)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the step is data-parallel "
               "over requests and needs no collectives; run with --gpus 1", file=sys.stderr)
@@ -186,6 +278,8 @@ def main() -> int:
         return 2
     torch.cuda.set_device(0)
     sad.load()
+    if args.copy_calibration_gib > 0:
+        copy_calibration(args.copy_calibration_gib)
     t0 = time.perf_counter()
     wl = WL.make_workload(WORKLOAD, "cuda", num_layers=args.layers)
     torch.cuda.synchronize()
