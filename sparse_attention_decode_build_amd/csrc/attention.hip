@@ -41,7 +41,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;              // attended columns per tile
-constexpr int kStages = 4;             // raw tiles in the LDS ring (DMA runs 3 tiles ahead)
+constexpr int kStages = 4;             // raw tiles in the LDS ring (DMA runs kStages-1 tiles ahead)
 constexpr int kMaxSiCols = 4352;       // index columns one workgroup stages in LDS (17 KB)
 constexpr float kRescaleSlack = 8.0f;  // keep the running max until exceeded by 2^8
 constexpr float kLog2e = 1.4426950408889634f;
@@ -141,17 +141,16 @@ struct Shape {
   static constexpr int KS0 = 2 * MT0;       // QK k-steps (16 dims) of dim half 0
   static constexpr int KS1 = 2 * MT1;
   static constexpr int KCH = DQK / 8 + 1;  // 16-byte chunks per K row in LDS (odd: one pad chunk)
-  static constexpr int CPR = ROWB / 16;               // 16-byte chunks of a cached row
-  static constexpr int VAL_LOADS = (CPR + 7) / 8;     // value DMAs per wave per tile
-  static constexpr int DMA_PER_TILE = VAL_LOADS + 1;  // + one scale DMA
-  static constexpr int RAW_V = VAL_LOADS * kWaves * 64 * 16;  // [chunk][row][16 B], padded
-  static constexpr int RAW_S = kThreads;                      // fp32 [block][row], padded
-  static constexpr int NOPE_U = DN / 16 / kWaves;  // 16-byte fp8 chunks per wave (2 rows each)
-  static constexpr int ROPE_CH = DR / 8;           // 16-byte bf16 chunks of the rope part
-  static_assert(ROWB % 16 == 0 && DN % 64 == 0, "rows are whole chunks, 64-element scale blocks");
-  static_assert((DN / 16) % kWaves == 0, "fp8 chunks split evenly over the waves");
-  static_assert(kTile * NSC <= kThreads, "one scale dword per thread");
-  static_assert(ROPE_CH <= 2 * kWaves, "at most one rope chunk per thread");
+  static constexpr int CPR = ROWB / 16;          // 16-byte chunks of a cached row
+  static constexpr int LINES = (CPR + 7) / 8;    // 128-byte lines of a cached row
+  static constexpr int FP8_LINES = DN / 128;     // lines holding fp8 values (the rest: rope)
+  static constexpr int ROPE_CH = DR / 8;         // 16-byte bf16 chunks of the rope part
+  static constexpr int DMA_PER_TILE = LINES + 1;  // value loads + one scale load per wave
+  static constexpr int RAW_V = kWaves * LINES * 1024;  // [wave][line][row%8][chunk%8][16 B]
+  static constexpr int RAW_S = kThreads;               // fp32 [row][8], padded
+  static_assert(ROWB % 16 == 0 && DN % 128 == 0, "rows are whole chunks; fp8 part is whole lines");
+  static_assert(ROPE_CH <= 8 && NSC <= 8, "rope part within one line, at most 8 scales per row");
+  static_assert(kTile == 8 * kWaves, "each wave carries 8 rows of a tile");
   static_assert(DQK % 32 == 0, "output dims in 32-row MFMA tiles");
 };
 
@@ -186,77 +185,81 @@ __device__ inline void col_row(int col, int ncols, int window, const int32_t* si
   *scales = pg + (kv.block * rowb + ro * 4 * nsc);
 }
 
-// Copy one tile's raw rows HBM -> LDS.  Lane l of every wave carries row l%32 and
-// computes that row's address once.  Values go chunk-major ([chunk][row][16 B]): load j
-// of wave w brings chunks 8j + 2w + {0, 1} (lane halves) of all 32 rows.  Scales go
-// block-major ([block][row] fp32): lane l of wave w brings block 2w + l/32 of its row.
-// Every wave issues exactly DMA_PER_TILE loads with all lanes active (padding lanes
-// read the zero row into padding LDS), so a wave's vmcnt advances by a known amount
-// per tile.  Returns the tile's validity mask (bit j: column tile0 + j is attended).
+// Copy one tile's raw rows HBM -> LDS.  Wave w carries rows 8w..8w+7 of the tile:
+// lane l handles row 8w + l/8 and 16-byte chunk l%8 of each 128-byte line, so every
+// load reads whole lines (8 rows x 128 contiguous bytes) and each lane computes one row
+// address.  Values land as [wave][line][row%8][chunk%8] (16 B each), scales as
+// [row][8] fp32.  Every wave issues exactly DMA_PER_TILE loads with all lanes active
+// (lanes past the row read the zero row into padding LDS), so a wave's vmcnt advances
+// by a known amount per tile.  The wave's 8-bit validity (bit r: row 8w + r attended)
+// is stored in byte w of *mask_word.
 template <int DN, int DR, bool ONE>
-__device__ inline uint32_t dma_tile(int lane, int wave, uint8_t (&raw_v)[Shape<DN, DR>::RAW_V],
-                                    float (&raw_s)[Shape<DN, DR>::RAW_S], int tile0, int ncols,
-                                    int window, const int32_t* si_lds, int col_base, const KvDesc& swa,
-                                    const KvDesc& comp) {
+__device__ inline void dma_tile(int lane, int wave, uint8_t (&raw_v)[Shape<DN, DR>::RAW_V],
+                                float (&raw_s)[Shape<DN, DR>::RAW_S], uint32_t* mask_word, int tile0,
+                                int ncols, int window, const int32_t* si_lds, int col_base, const KvDesc& swa,
+                                const KvDesc& comp) {
   using S = Shape<DN, DR>;
   __builtin_assume(wave >= 0 && wave < kWaves);
-  const int h = lane >> 5;
+  const int c = lane & 7;
   const uint8_t* vrow;
   const uint8_t* srow;
-  col_row<ONE>(tile0 + (lane & 31), ncols, window, si_lds, col_base, swa, comp, S::ROWB, S::NSC, &vrow, &srow);
-  const uint32_t vbase = lds_addr(raw_v) + wave * 1024;
-  const int c0 = 2 * wave + h;  // chunk of load 0
-  const uint8_t* vsrc = vrow + 16 * c0;
-  static_for<S::VAL_LOADS>([&](auto jc) {
+  col_row<ONE>(tile0 + 8 * wave + (lane >> 3), ncols, window, si_lds, col_base, swa, comp, S::ROWB, S::NSC,
+               &vrow, &srow);
+  const uint32_t vbase = lds_addr(raw_v) + wave * S::LINES * 1024;
+  const uint8_t* vsrc = vrow + 16 * c;
+  static_for<S::LINES>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(vbase + j * kWaves * 1024);
-    if constexpr (8 * j + 2 * kWaves <= S::CPR)
-      dma_x4_off<128 * j>(vsrc, dst);  // every chunk of this load exists
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(vbase + j * 1024);
+    if constexpr (8 * j + 8 <= S::CPR)
+      dma_x4_off<128 * j>(vsrc, dst);  // every chunk of this line exists
     else
-      dma_x4_off<0>(8 * j + c0 < S::CPR ? vsrc + 128 * j : kZeroRow, dst);
+      dma_x4_off<0>(8 * j + c < S::CPR ? vsrc + 128 * j : kZeroRow, dst);
   });
-  dma_x1(c0 < S::NSC ? srow + 4 * c0 : kZeroRow, __builtin_amdgcn_readfirstlane(lds_addr(raw_s) + wave * 256));
-  return (uint32_t)__ballot(vrow != kZeroRow);  // lanes 0..31 carry rows 0..31
+  dma_x1(c < S::NSC ? srow + 4 * c : kZeroRow, __builtin_amdgcn_readfirstlane(lds_addr(raw_s) + wave * 256));
+  // lane 8r carries row 8w + r: gather ballot bits 0, 8, .., 56 into one byte
+  const uint64_t b = __ballot(vrow != kZeroRow) & 0x0101010101010101ull;
+  const uint32_t m8 = (uint32_t)((b * 0x0102040810204080ull) >> 56);
+  if (lane == 0) reinterpret_cast<uint8_t*>(mask_word)[wave] = (uint8_t)m8;
 }
 
-// Dequantize the raw tile into the padded bf16 K tile: fp8 elements become
-// bf16_rne(float(e4m3) * scale), rope elements are copied.  Lane (key = lane%32,
-// h = lane/32) of wave w converts 8-element halves of the wave's fp8 chunks.  All LDS
-// reads are issued before the arithmetic so their latencies overlap.
+// Dequantize this wave's 8 rows of the raw tile into the padded bf16 K tile: fp8
+// elements become bf16_rne(float(e4m3) * scale), rope elements are copied.  Lane
+// (row 8w + l/8, chunk l%8) converts 16 elements of each fp8 line and copies one rope
+// chunk.  It reads only the wave's own DMA, so only this wave's vmcnt guards it.  All
+// LDS reads are issued before the arithmetic so their latencies overlap.
 template <int DN, int DR>
 __device__ inline void dequant_tile(int lane, int wave, const uint8_t (&raw_v)[Shape<DN, DR>::RAW_V],
                                     const float (&raw_s)[Shape<DN, DR>::RAW_S],
                                     uint16_t (&kt)[kTile * Shape<DN, DR>::KCH * 8]) {
   using S = Shape<DN, DR>;
-  const int key = lane & 31;
-  const int h = lane >> 5;
-  uint2 raw[S::NOPE_U];
-  float sc[S::NOPE_U];
+  const int c = lane & 7;
+  const int key = 8 * wave + (lane >> 3);
+  const uint8_t* src = raw_v + wave * S::LINES * 1024 + (lane >> 3) * 128 + 16 * c;
+  uint4 raw[S::FP8_LINES];
+  float sc[S::FP8_LINES];
 #pragma unroll
-  for (int u = 0; u < S::NOPE_U; ++u) {
-    const int c16 = wave * S::NOPE_U + u;
-    raw[u] = *reinterpret_cast<const uint2*>(raw_v + (c16 * 32 + key) * 16 + 8 * h);
-    if (u == 0 || (16 * c16) % 64 == 0) sc[u] = raw_s[((16 * c16) / 64) * 32 + key];
-    else sc[u] = sc[u - 1];
+  for (int j = 0; j < S::FP8_LINES; ++j) {
+    raw[j] = *reinterpret_cast<const uint4*>(src + j * 1024);
+    sc[j] = raw_s[key * 8 + 2 * j + (c >> 2)];  // dims 128j + 16c .. +16: scale block 2j + c/4
   }
-  const int rc = 2 * wave + h;  // rope chunk of this lane
   uint4 rope = make_uint4(0u, 0u, 0u, 0u);
-  if (rc < S::ROPE_CH) rope = *reinterpret_cast<const uint4*>(raw_v + ((DN / 16 + rc) * 32 + key) * 16);
+  if (c < S::ROPE_CH) rope = *reinterpret_cast<const uint4*>(src + S::FP8_LINES * 1024);
+  uint16_t* dst = kt + kt_off<S::KCH>(key, 16 * c);
 #pragma unroll
-  for (int u = 0; u < S::NOPE_U; ++u) {
-    const int d0 = 16 * (wave * S::NOPE_U + u) + 8 * h;
-    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[u].x, false) * sc[u];
-    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[u].x, true) * sc[u];
-    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[u].y, false) * sc[u];
-    const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[u].y, true) * sc[u];
-    uint4 w;
-    w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2_t));
-    w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2_t));
-    w.z = __builtin_bit_cast(uint32_t, __builtin_convertvector(c, bf16x2_t));
-    w.w = __builtin_bit_cast(uint32_t, __builtin_convertvector(d, bf16x2_t));
-    *reinterpret_cast<uint4*>(kt + kt_off<S::KCH>(key, d0)) = w;
+  for (int j = 0; j < S::FP8_LINES; ++j) {
+    const uint32_t wv[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+    uint32_t o[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[q], false) * sc[j];
+      const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[q], true) * sc[j];
+      o[2 * q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
+      o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
+    }
+    *reinterpret_cast<uint4*>(dst + 128 * j) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(dst + 128 * j + 8) = make_uint4(o[4], o[5], o[6], o[7]);
   }
-  if (rc < S::ROPE_CH) *reinterpret_cast<uint4*>(kt + kt_off<S::KCH>(key, DN + 8 * rc)) = rope;
+  if (c < S::ROPE_CH) *reinterpret_cast<uint4*>(kt + kt_off<S::KCH>(key, DN + 8 * c)) = rope;
 }
 
 template <int DN, int DR, bool ONE>
@@ -275,6 +278,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   constexpr int NV = S::DMA_PER_TILE;
   __shared__ __align__(16) uint8_t raw_v[kStages][S::RAW_V];
   __shared__ __align__(16) float raw_s[kStages][S::RAW_S];
+  __shared__ uint32_t tile_mask[kStages];  // validity of the tile in each ring slot (bit j: column j)
   __shared__ __align__(16) uint16_t kt[kTile * S::KCH * 8];
   __shared__ __align__(16) float xbuf[kWaves * 16 * 64];
   __shared__ __align__(16) int32_t si_lds[kMaxSiCols];  // this split's sparse_indices columns
@@ -344,20 +348,16 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   // re-check the Q loads inside the tile loop)
   __builtin_amdgcn_s_waitcnt(0x0F70);
   lds_barrier();  // si_lds complete
-  // Prologue: DMA of the first three tiles.  Each DMA also yields the tile's validity
-  // mask (bit j: column j is attended); the masks rotate with the ring.
-  uint32_t mask0 = 0, mask1 = 0, mask2 = 0;
-  if (tile_begin < tile_end)
-    mask0 = dma_tile<DN, DR, ONE>(lane, wave, raw_v[0], raw_s[0], tile_begin * kTile, ncols, window, si_lds,
-                             col_base, swa, comp);
-  if (tile_begin + 1 < tile_end)
-    mask1 = dma_tile<DN, DR, ONE>(lane, wave, raw_v[1], raw_s[1], (tile_begin + 1) * kTile, ncols, window, si_lds,
-                             col_base, swa, comp);
-  if (tile_begin + 2 < tile_end)
-    mask2 = dma_tile<DN, DR, ONE>(lane, wave, raw_v[2], raw_s[2], (tile_begin + 2) * kTile, ncols, window, si_lds,
-                             col_base, swa, comp);
+  // Prologue: DMA of the first kStages-1 tiles (each also records its validity mask).
+  constexpr int kAhead = kStages - 1;
+  static_for<kAhead>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if (tile_begin + j < tile_end)
+      dma_tile<DN, DR, ONE>(lane, wave, raw_v[j], raw_s[j], &tile_mask[j], (tile_begin + j) * kTile, ncols,
+                            window, si_lds, col_base, swa, comp);
+  });
 
-  // First half of a tile step: wait for the tile, start the DMA three tiles ahead,
+  // First half of a tile step: wait for the tile, start the DMA kStages-1 tiles ahead,
   // dequantize, S^T = K Q^T (both dim halves summed), masking.  Returns the tile's
   // scaled row maximum per head (log2 domain).
   auto front = [&](int tile, int slot, f32x16_t& s) __attribute__((always_inline)) -> float {
@@ -369,21 +369,16 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     const int h_s = lane_s >> 5;
     // This wave's DMA of this tile landed; the DMAs of the next tiles may be in flight.
     const int ahead = min(tile_end - 1 - tile, kStages - 2);
-    if (ahead >= 2)
-      wait_vmem<2 * NV>();
-    else if (ahead == 1)
-      wait_vmem<NV>();
-    else
-      wait_vmem<0>();
+    static_for<kStages - 1>([&](auto ac) {
+      constexpr int a = kStages - 2 - decltype(ac)::value;
+      if (ahead == a) wait_vmem<a * NV>();
+    });
     lds_barrier();  // every wave's DMA of this tile landed; the previous tile's PV is done
-    const uint32_t valid_mask = mask0;
-    uint32_t mask3 = 0;
-    if (tile + 3 < tile_end)
-      mask3 = dma_tile<DN, DR, ONE>(lane_s, wave, raw_v[(slot + 3) & 3], raw_s[(slot + 3) & 3],
-                               (tile + 3) * kTile, ncols, window, si_lds, col_base, swa, comp);
-    mask0 = mask1;
-    mask1 = mask2;
-    mask2 = mask3;
+    const uint32_t valid_mask = tile_mask[slot];  // written with this tile's DMA, before the barrier
+    const int nslot = slot == 0 ? kStages - 1 : slot - 1;  // the slot the previous tile used
+    if (tile + kAhead < tile_end)
+      dma_tile<DN, DR, ONE>(lane_s, wave, raw_v[nslot], raw_s[nslot], &tile_mask[nslot], (tile + kAhead) * kTile,
+                            ncols, window, si_lds, col_base, swa, comp);
     dequant_tile<DN, DR>(lane_s, wave, raw_v[slot], raw_s[slot], kt);
     lds_barrier();  // K tile complete
 
@@ -487,7 +482,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     bool rescale = false;
     for (; tile < tile_end; ++tile) {
       tmax = front(tile, slot, s);
-      slot = (slot + 1) & (kStages - 1);
+      slot = slot + 1 == kStages ? 0 : slot + 1;
       if (__ballot(tmax > m_run + kRescaleSlack) != 0ull) {  // also true when m_run is -inf
         rescale = true;
         break;

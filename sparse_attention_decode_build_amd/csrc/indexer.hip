@@ -25,7 +25,14 @@ namespace {
 // ------------------------------------------------------------------ scoring
 
 constexpr int kScoreThreads = 256;
-constexpr int kScoreChunk = 1024;  // compressed rows per workgroup
+constexpr int kRowsPerWave = 256;                                  // 16 groups of 16 rows
+constexpr int kScoreChunk = kRowsPerWave * (kScoreThreads / 64);  // compressed rows per workgroup
+constexpr int kGroupBatch = 8;  // 16-row groups whose key loads are in flight together
+
+typedef int gi32x4_t __attribute__((__vector_size__(4 * sizeof(int))));
+
+// Source of the loads of absent or unbacked key groups (their scores become -inf).
+__device__ __align__(16) uint8_t kZeroKey[64];
 
 struct IdxDesc {
   const uint8_t* pool;
@@ -34,6 +41,9 @@ struct IdxDesc {
   int block;
 };
 
+// One wave scores 256 consecutive compressed rows of one token.  The page ids of those
+// rows are loaded once up front (one per lane), so the key loads of 8 row groups are
+// independent and go out together.
 template <int DIM>
 __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
     sad_batch b, const uint8_t* __restrict__ qv, const uint8_t* __restrict__ qs,
@@ -48,9 +58,16 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
   TokenGeom g;
   if (!token_geometry(b, t, ratio, g)) return;
   const int n_rows = min(g.n_comp, bt_cols * kc.block);
-  const int s_begin = blockIdx.x * kScoreChunk;
-  if (s_begin >= n_rows) return;
-  const int s_end = min(s_begin + kScoreChunk, n_rows);
+  const int w_begin = blockIdx.x * kScoreChunk + wave * kRowsPerWave;
+  if (w_begin >= n_rows) return;  // no barriers in this kernel: waves may leave early
+  const int w_rows = min(kRowsPerWave, n_rows - w_begin);
+
+  // Page ids of this wave's rows: lane i holds table column col0 + i (a 16-row group
+  // never straddles a page, since 16 divides the page size).
+  const int32_t* bt_row = bt + (int64_t)g.req * bt_stride;
+  const int col0 = w_begin / kc.block;
+  const int ncol = (w_begin + w_rows - 1) / kc.block - col0 + 1;  // <= 16
+  const int pid = lane < ncol ? bt_row[col0 + lane] : -1;
 
   // A operands: 16 heads x 128 dims per tile; lane (m = lane%16, grp = lane/16)
   // holds dims [32*grp, 32*grp+32) of head 16*ht + m and that block's exponent.
@@ -79,41 +96,42 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
       wl[ht][j] = ho < num_heads ? wts[(int64_t)t * num_heads + ho] : 0.0f;
     }
   }
-  const int32_t* bt_row = bt + (int64_t)g.req * bt_stride;
   float* lrow = logits + (int64_t)t * logits_stride;
   float* drow = dbg != nullptr ? dbg + (int64_t)t * dbg_stride : nullptr;
 
-  // Each wave takes 16-row groups; two groups in flight per iteration.
-  for (int s0 = s_begin + wave * 16; s0 < s_end; s0 += 2 * 4 * 16) {
-    i32x8_t kb[2];
-    int ksc[2];
-    bool kval[2];
+#pragma unroll 1
+  for (int gb = 0; gb < kRowsPerWave / 16; gb += kGroupBatch) {
+    // Wave-uniform page bases and 32-bit lane offsets first; invalid or absent groups
+    // read the zero key, so the loads below go out unconditionally and together.
+    const uint8_t* pbase[kGroupBatch];
+    uint32_t voff[kGroupBatch];
+    uint32_t soff[kGroupBatch];
+    bool kval[kGroupBatch];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int sg = s0 + u * 4 * 16;
-      kb[u] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-      ksc[u] = 127;
-      kval[u] = false;
-      if (sg < s_end) {
-        const int col = sg / kc.block;  // 16 | block, so the group sits in one page
-        const int page = bt_row[col];
-        kval[u] = page >= 0 && (int64_t)page < kc.num_pages;
-        if (kval[u] && grp < SB) {
-          const int ro = sg - col * kc.block + m;
-          const uint8_t* pg = kc.pool + (int64_t)page * kc.stride;
-          const int4 v = *reinterpret_cast<const int4*>(pg + (int64_t)ro * VB + 16 * grp);
-          kb[u][0] = v.x;
-          kb[u][1] = v.y;
-          kb[u][2] = v.z;
-          kb[u][3] = v.w;
-          ksc[u] = pg[(int64_t)kc.block * VB + (int64_t)ro * SB + grp];
-        }
-      }
+    for (int u = 0; u < kGroupBatch; ++u) {
+      const int r0 = 16 * (gb + u);
+      const int sg = w_begin + r0;
+      const int cl = min(sg / kc.block - col0, 15);
+      const int page = __builtin_amdgcn_readlane(pid, cl);  // wave-uniform
+      kval[u] = r0 < w_rows && page >= 0 && (int64_t)page < kc.num_pages;
+      const int ro = sg - (sg / kc.block) * kc.block + m;
+      pbase[u] = kval[u] ? kc.pool + (int64_t)page * kc.stride : kZeroKey;
+      voff[u] = kval[u] ? (uint32_t)(ro * VB + 16 * grp) : (uint32_t)(16 * grp);
+      soff[u] = kval[u] ? (uint32_t)(kc.block * VB + ro * SB + grp) : 0u;
+    }
+    i32x8_t kb[kGroupBatch];
+    int ksc[kGroupBatch];
+#pragma unroll
+    for (int u = 0; u < kGroupBatch; ++u) {
+      const gi32x4_t v = *(const __attribute__((address_space(1))) gi32x4_t*)(pbase[u] + voff[u]);
+      kb[u] = i32x8_t{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+      ksc[u] = *(const __attribute__((address_space(1))) uint8_t*)(pbase[u] + soff[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int sg = s0 + u * 4 * 16;
-      if (sg >= s_end) break;
+    for (int u = 0; u < kGroupBatch; ++u) {
+      const int r0 = 16 * (gb + u);
+      if (r0 >= w_rows) break;
+      const int sg = w_begin + r0;
       float part = 0.0f;
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
@@ -128,7 +146,7 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
       // lanes m, m+16, m+32, m+48 hold the 4 head groups of row sg + m
       part += __shfl_xor(part, 16, 64);
       part += __shfl_xor(part, 32, 64);
-      if (lane < 16 && sg + lane < s_end) {
+      if (lane < 16 && r0 + lane < w_rows) {
         const float v = kval[u] ? part : -INFINITY;
         lrow[sg + lane] = v;
         if (drow != nullptr) drow[sg + lane] = v;
