@@ -41,9 +41,9 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;              // attended columns per tile
-constexpr int kStages = 4;             // raw tiles in the LDS ring (DMA runs kStages-1 tiles ahead)
 constexpr int kMaxSiCols = 4352;       // index columns one workgroup stages in LDS (17 KB)
-constexpr float kRescaleSlack = 8.0f;  // keep the running max until exceeded by 2^8
+constexpr float kRescaleSlack = 8.0f;
+constexpr int kXRow = 20;  // floats per lane in the S exchange buffer (16 + pad: conflict-free 16-byte access)  // keep the running max until exceeded by 2^8
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -167,14 +167,16 @@ __device__ inline int kt_off(int key, int dim) {
 // Row values / scales of one attended column, or the zero row when the column is not
 // attended (past ncols, slot -1, page outside the pool).  ONE: the window and the
 // compressed columns read the same cache (wave-uniform descriptor).
+// The slot id is read from LDS one step before the addresses are formed
+// (col_slot), so the read's latency is off the critical path.
+__device__ inline int col_slot(int col, int col_end, const int32_t* si_lds, int col_base) {
+  return col < col_end ? si_lds[col - col_base] : -1;  // col_end: end of the staged columns
+}
 template <bool ONE>
-__device__ inline void col_row(int col, int ncols, int window, const int32_t* si_lds, int col_base,
-                               const KvDesc& swa, const KvDesc& comp, int rowb, int nsc,
-                               const uint8_t** vals, const uint8_t** scales) {
-  *vals = kZeroRow;
-  *scales = kZeroRow;
-  if (col >= ncols) return;
-  const int slot = si_lds[col - col_base];
+__device__ inline void slot_row(int slot, int col, int window, const KvDesc& swa, const KvDesc& comp, int rowb,
+                                int nsc, const uint8_t* zrow, const uint8_t** vals, const uint8_t** scales) {
+  *vals = zrow;
+  *scales = zrow;
   const KvDesc& kv = (ONE || col < window) ? swa : comp;
   if (slot < 0) return;
   const int page = slot >> kv.block_shift;
@@ -186,25 +188,18 @@ __device__ inline void col_row(int col, int ncols, int window, const int32_t* si
 }
 
 // Copy one tile's raw rows HBM -> LDS.  Wave w carries rows 8w..8w+7 of the tile:
-// lane l handles row 8w + l/8 and 16-byte chunk l%8 of each 128-byte line, so every
-// load reads whole lines (8 rows x 128 contiguous bytes) and each lane computes one row
-// address.  Values land as [wave][line][row%8][chunk%8] (16 B each), scales as
-// [row][8] fp32.  Every wave issues exactly DMA_PER_TILE loads with all lanes active
-// (lanes past the row read the zero row into padding LDS), so a wave's vmcnt advances
-// by a known amount per tile.  The wave's 8-bit validity (bit r: row 8w + r attended)
-// is stored in byte w of *mask_word.
-template <int DN, int DR, bool ONE>
-__device__ inline void dma_tile(int lane, int wave, uint8_t (&raw_v)[Shape<DN, DR>::RAW_V],
-                                float (&raw_s)[Shape<DN, DR>::RAW_S], uint32_t* mask_word, int tile0,
-                                int ncols, int window, const int32_t* si_lds, int col_base, const KvDesc& swa,
-                                const KvDesc& comp) {
+// lane l handles row 8w + l/8 (address vrow/srow, from slot_row) and 16-byte chunk l%8 of
+// each 128-byte line, so every load reads whole lines (8 rows x 128 contiguous bytes).
+// Values land as [wave][line][row%8][chunk%8] (16 B each), scales as [row][8] fp32.
+// Every wave issues exactly DMA_PER_TILE loads with all lanes active (lanes past the
+// row read the zero row into padding LDS), so a wave's vmcnt advances by a known
+// amount per tile.  Returns the wave's 8-bit validity (bit r: row 8w + r attended).
+template <int DN, int DR>
+__device__ inline uint32_t dma_issue(int lane, int wave, uint8_t (&raw_v)[Shape<DN, DR>::RAW_V],
+                                     float (&raw_s)[Shape<DN, DR>::RAW_S], const uint8_t* vrow,
+                                     const uint8_t* srow, const uint8_t* zrow) {
   using S = Shape<DN, DR>;
-  __builtin_assume(wave >= 0 && wave < kWaves);
   const int c = lane & 7;
-  const uint8_t* vrow;
-  const uint8_t* srow;
-  col_row<ONE>(tile0 + 8 * wave + (lane >> 3), ncols, window, si_lds, col_base, swa, comp, S::ROWB, S::NSC,
-               &vrow, &srow);
   const uint32_t vbase = lds_addr(raw_v) + wave * S::LINES * 1024;
   const uint8_t* vsrc = vrow + 16 * c;
   static_for<S::LINES>([&](auto jc) {
@@ -213,40 +208,40 @@ __device__ inline void dma_tile(int lane, int wave, uint8_t (&raw_v)[Shape<DN, D
     if constexpr (8 * j + 8 <= S::CPR)
       dma_x4_off<128 * j>(vsrc, dst);  // every chunk of this line exists
     else
-      dma_x4_off<0>(8 * j + c < S::CPR ? vsrc + 128 * j : kZeroRow, dst);
+      dma_x4_off<0>(8 * j + c < S::CPR ? vsrc + 128 * j : zrow, dst);
   });
-  dma_x1(c < S::NSC ? srow + 4 * c : kZeroRow, __builtin_amdgcn_readfirstlane(lds_addr(raw_s) + wave * 256));
+  dma_x1(c < S::NSC ? srow + 4 * c : zrow, __builtin_amdgcn_readfirstlane(lds_addr(raw_s) + wave * 256));
   // lane 8r carries row 8w + r: gather ballot bits 0, 8, .., 56 into one byte
-  const uint64_t b = __ballot(vrow != kZeroRow) & 0x0101010101010101ull;
-  const uint32_t m8 = (uint32_t)((b * 0x0102040810204080ull) >> 56);
-  if (lane == 0) reinterpret_cast<uint8_t*>(mask_word)[wave] = (uint8_t)m8;
+  const uint64_t b = __ballot(vrow != zrow) & 0x0101010101010101ull;
+  return (uint32_t)((b * 0x0102040810204080ull) >> 56);
 }
 
-// Dequantize this wave's 8 rows of the raw tile into the padded bf16 K tile: fp8
-// elements become bf16_rne(float(e4m3) * scale), rope elements are copied.  Lane
-// (row 8w + l/8, chunk l%8) converts 16 elements of each fp8 line and copies one rope
-// chunk.  It reads only the wave's own DMA, so only this wave's vmcnt guards it.  All
-// LDS reads are issued before the arithmetic so their latencies overlap.
-template <int DN, int DR>
-__device__ inline void dequant_tile(int lane, int wave, const uint8_t (&raw_v)[Shape<DN, DR>::RAW_V],
-                                    const float (&raw_s)[Shape<DN, DR>::RAW_S],
-                                    uint16_t (&kt)[kTile * Shape<DN, DR>::KCH * 8]) {
+// Dequantize fp8 lines [J0, J1) (and the rope line when ROPE) of this wave's 8 rows of
+// the raw tile into the padded bf16 K tile: fp8 elements become
+// bf16_rne(float(e4m3) * scale), rope elements are copied.  Lane (row 8w + l/8, chunk
+// l%8) converts 16 elements per line.  It reads only the wave's own DMA, so only this
+// wave's vmcnt guards it.  All LDS reads are issued before the arithmetic.
+template <int DN, int DR, int J0, int J1, bool ROPE>
+__device__ inline void dequant_lines(int lane, int wave, const uint8_t (&raw_v)[Shape<DN, DR>::RAW_V],
+                                     const float (&raw_s)[Shape<DN, DR>::RAW_S],
+                                     uint16_t (&kt)[kTile * Shape<DN, DR>::KCH * 8]) {
   using S = Shape<DN, DR>;
+  constexpr int NJ = J1 - J0;
   const int c = lane & 7;
   const int key = 8 * wave + (lane >> 3);
   const uint8_t* src = raw_v + wave * S::LINES * 1024 + (lane >> 3) * 128 + 16 * c;
-  uint4 raw[S::FP8_LINES];
-  float sc[S::FP8_LINES];
+  uint4 raw[NJ > 0 ? NJ : 1];
+  float sc[NJ > 0 ? NJ : 1];
 #pragma unroll
-  for (int j = 0; j < S::FP8_LINES; ++j) {
-    raw[j] = *reinterpret_cast<const uint4*>(src + j * 1024);
-    sc[j] = raw_s[key * 8 + 2 * j + (c >> 2)];  // dims 128j + 16c .. +16: scale block 2j + c/4
+  for (int j = 0; j < NJ; ++j) {
+    raw[j] = *reinterpret_cast<const uint4*>(src + (J0 + j) * 1024);
+    sc[j] = raw_s[key * 8 + 2 * (J0 + j) + (c >> 2)];  // dims 128j + 16c .. +16: scale block 2j + c/4
   }
   uint4 rope = make_uint4(0u, 0u, 0u, 0u);
-  if (c < S::ROPE_CH) rope = *reinterpret_cast<const uint4*>(src + S::FP8_LINES * 1024);
+  if (ROPE && c < S::ROPE_CH) rope = *reinterpret_cast<const uint4*>(src + S::FP8_LINES * 1024);
   uint16_t* dst = kt + kt_off<S::KCH>(key, 16 * c);
 #pragma unroll
-  for (int j = 0; j < S::FP8_LINES; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const uint32_t wv[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
     uint32_t o[8];
 #pragma unroll
@@ -256,10 +251,10 @@ __device__ inline void dequant_tile(int lane, int wave, const uint8_t (&raw_v)[S
       o[2 * q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
       o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
     }
-    *reinterpret_cast<uint4*>(dst + 128 * j) = make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4*>(dst + 128 * j + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+    *reinterpret_cast<uint4*>(dst + 128 * (J0 + j)) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(dst + 128 * (J0 + j) + 8) = make_uint4(o[4], o[5], o[6], o[7]);
   }
-  if (c < S::ROPE_CH) *reinterpret_cast<uint4*>(kt + kt_off<S::KCH>(key, DN + 8 * c)) = rope;
+  if (ROPE && c < S::ROPE_CH) *reinterpret_cast<uint4*>(kt + kt_off<S::KCH>(key, DN + 8 * c)) = rope;
 }
 
 template <int DN, int DR, bool ONE>
@@ -276,11 +271,14 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   constexpr int KSMAX = S::KS0;
   constexpr int MTMAX = S::MT0;
   constexpr int NV = S::DMA_PER_TILE;
-  __shared__ __align__(16) uint8_t raw_v[kStages][S::RAW_V];
-  __shared__ __align__(16) float raw_s[kStages][S::RAW_S];
-  __shared__ uint32_t tile_mask[kStages];  // validity of the tile in each ring slot (bit j: column j)
-  __shared__ __align__(16) uint16_t kt[kTile * S::KCH * 8];
-  __shared__ __align__(16) float xbuf[kWaves * 16 * 64];
+  constexpr int JH = S::FP8_LINES / 2;  // fp8 lines dequantized alongside QK; the rest alongside PV
+  // Two raw slots (this wave's rows of tiles i+1 and i+2 arrive there) and two K tiles
+  // (tile i is computed on while tile i+1 is dequantized into the other).
+  __shared__ __align__(16) uint8_t raw_v[2][S::RAW_V];
+  __shared__ __align__(16) float raw_s[2][S::RAW_S];
+  __shared__ __align__(16) uint16_t kt[2][kTile * S::KCH * 8];
+  __shared__ uint32_t kt_mask[2];  // validity of the tile in each K buffer (bit j: column j)
+  __shared__ __align__(16) float xbuf[kWaves * 64 * kXRow];  // [wave][lane][kXRow]: partial S
   __shared__ __align__(16) int32_t si_lds[kMaxSiCols];  // this split's sparse_indices columns
 
   // Block -> (token, split, head group): the head groups of one (token, split) are
@@ -297,6 +295,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;  // wave-uniform
+  __builtin_assume(wave >= 0 && wave < kWaves);
   const int n = lane & 31;    // head within the wave's block / key row within a fragment
   const int h = lane >> 5;    // lane half
   const int hb = wave >> 1;   // head block of this wave
@@ -308,6 +307,9 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   const int dim0 = dh == 0 ? 0 : 32 * S::MT0;  // first dim of this wave's half
   // the fp32 sum of the weights is only needed for the log-sum-exp outputs
   const bool want_lse = lse_out != nullptr || num_splits > 1;
+  // the zero row's address, kept opaque so it is not reloaded in the loop
+  const uint8_t* zrow = kZeroRow;
+  asm volatile("" : "+s"(zrow));
 
   const int width = window + padded;
   const int32_t* si_row = si + (int64_t)t * width;
@@ -348,62 +350,102 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   // re-check the Q loads inside the tile loop)
   __builtin_amdgcn_s_waitcnt(0x0F70);
   lds_barrier();  // si_lds complete
-  // Prologue: DMA of the first kStages-1 tiles (each also records its validity mask).
-  constexpr int kAhead = kStages - 1;
-  static_for<kAhead>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    if (tile_begin + j < tile_end)
-      dma_tile<DN, DR, ONE>(lane, wave, raw_v[j], raw_s[j], &tile_mask[j], (tile_begin + j) * kTile, ncols,
-                            window, si_lds, col_base, swa, comp);
-  });
 
-  // First half of a tile step: wait for the tile, start the DMA kStages-1 tiles ahead,
-  // dequantize, S^T = K Q^T (both dim halves summed), masking.  Returns the tile's
-  // scaled row maximum per head (log2 domain).
-  auto front = [&](int tile, int slot, f32x16_t& s) __attribute__((always_inline)) -> float {
-    // Per-lane indices are recomputed in every step from an opaque copy of the lane id:
-    // hoisting them out of the tile loop would keep dozens of registers live.
+  // Row addresses of this lane's row (8*wave + lane/8) of a tile.
+  auto row_slot = [&](int tile) __attribute__((always_inline)) -> int {
+    return col_slot(tile * kTile + 8 * wave + (lane >> 3), col_end, si_lds, col_base);
+  };
+  auto row_addr_of = [&](int tile, int slot, const uint8_t** vrow, const uint8_t** srow)
+      __attribute__((always_inline)) {
+    slot_row<ONE>(slot, tile * kTile + 8 * wave + (lane >> 3), window, swa, comp, S::ROWB, S::NSC, zrow, vrow,
+                  srow);
+  };
+  auto row_addr = [&](int tile, const uint8_t** vrow, const uint8_t** srow) __attribute__((always_inline)) {
+    row_addr_of(tile, row_slot(tile), vrow, srow);
+  };
+  // Prologue: DMA of tiles 0 and 1, dequant of tile 0, DMA of tile 2.  A wave's mask
+  // byte of a tile is kept from its DMA until it writes it beside that tile's K buffer.
+  uint32_t mask_a = 0, mask_b = 0;  // this wave's bytes for the tiles in raw slots 1 and 0
+  {
+    const uint8_t* vr;
+    const uint8_t* sr;
+    uint32_t m0 = 0;
+    if (tile_begin < tile_end) {
+      row_addr(tile_begin, &vr, &sr);
+      m0 = dma_issue<DN, DR>(lane, wave, raw_v[0], raw_s[0], vr, sr, zrow);
+    }
+    if (tile_begin + 1 < tile_end) {
+      row_addr(tile_begin + 1, &vr, &sr);
+      mask_a = dma_issue<DN, DR>(lane, wave, raw_v[1], raw_s[1], vr, sr, zrow);
+    }
+    if (tile_begin < tile_end) {
+      if (tile_begin + 1 < tile_end)
+        wait_vmem<NV>();
+      else
+        wait_vmem<0>();
+      dequant_lines<DN, DR, 0, S::FP8_LINES, true>(lane, wave, raw_v[0], raw_s[0], kt[0]);
+      if (lane == 0) reinterpret_cast<uint8_t*>(&kt_mask[0])[wave] = (uint8_t)m0;
+    }
+    if (tile_begin + 2 < tile_end) {
+      row_addr(tile_begin + 2, &vr, &sr);
+      mask_b = dma_issue<DN, DR>(lane, wave, raw_v[0], raw_s[0], vr, sr, zrow);
+    }
+  }
+  int pre_slot = row_slot(tile_begin + 3);  // slot id of this lane's row of the next DMA
+
+  // First half of step i (tile i in K buffer b = i%2, tile i+1 in raw slot 1-b... see
+  // below): barrier, S^T = K Q^T over this wave's dims interleaved with the dequant of
+  // the first fp8 lines of tile i+1, both dim halves summed, masking.  Returns the
+  // tile's scaled row maximum per head (log2 domain).
+  // Raw slots: tile i+1 sits in slot (i+1)%2, tile i+2 in slot i%2.
+  auto front = [&](int tile, int b, f32x16_t& s) __attribute__((always_inline)) -> float {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
     const int n_s = lane_s & 31;
     const int h_s = lane_s >> 5;
-    // This wave's DMA of this tile landed; the DMAs of the next tiles may be in flight.
-    const int ahead = min(tile_end - 1 - tile, kStages - 2);
-    static_for<kStages - 1>([&](auto ac) {
-      constexpr int a = kStages - 2 - decltype(ac)::value;
-      if (ahead == a) wait_vmem<a * NV>();
-    });
-    lds_barrier();  // every wave's DMA of this tile landed; the previous tile's PV is done
-    const uint32_t valid_mask = tile_mask[slot];  // written with this tile's DMA, before the barrier
-    const int nslot = slot == 0 ? kStages - 1 : slot - 1;  // the slot the previous tile used
-    if (tile + kAhead < tile_end)
-      dma_tile<DN, DR, ONE>(lane_s, wave, raw_v[nslot], raw_s[nslot], &tile_mask[nslot], (tile + kAhead) * kTile,
-                            ncols, window, si_lds, col_base, swa, comp);
-    dequant_tile<DN, DR>(lane_s, wave, raw_v[slot], raw_s[slot], kt);
-    lds_barrier();  // K tile complete
-
+    const int nb = b ^ 1;
+    lds_barrier();  // tile i's K buffer complete; tile i-1's PV is done with the other buffer
+    const uint32_t valid_mask = kt_mask[b];
+    // this wave's DMA of tile i+1 landed (tile i+2's may still be in flight)
+    if (tile + 2 < tile_end)
+      wait_vmem<NV>();
+    else
+      wait_vmem<0>();
     // ---- partial S^T = K Q^T over this wave's dims: lane (head n, half h) gets
-    //      keys 8*(r/4) + 4h + r%4, r = 0..15.  All fragment reads are issued first.
+    //      keys 8*(r/4) + 4h + r%4, r = 0..15 ...
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-    if (block_active) {
-      const uint16_t* kbase = kt + kt_off<S::KCH>(n_s, dim0 + 8 * h_s);
-      bf16x8_t af[KSMAX];
+    const uint16_t* kbase = kt[b] + kt_off<S::KCH>(n_s, dim0 + 8 * h_s);
+    bf16x8_t af[KSMAX];
 #pragma unroll
-      for (int kk = 0; kk < KSMAX; ++kk)
-        if (kk < ks_n) af[kk] = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * kk);
+    for (int kk = 0; kk < KSMAX; ++kk)
+      if (kk < ks_n) af[kk] = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * kk);
+    // ... while the first fp8 lines of tile i+1 are dequantized into the other buffer
+    // (a stale slot past the last tile only writes the unused buffer)
+    dequant_lines<DN, DR, 0, JH, true>(lane_s, wave, raw_v[nb], raw_s[nb], kt[nb]);
 #pragma unroll
-      for (int kk = 0; kk < KSMAX; ++kk)
-        if (kk < ks_n) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], qf[kk], s, 0, 0, 0);
-      // schedule: kLdsAhead fragment reads in flight ahead of the MFMA chain
-      sched_reads_ahead<KSMAX, 1>();
-    }
+    for (int kk = 0; kk < KSMAX; ++kk)
+      if (kk < ks_n) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], qf[kk], s, 0, 0, 0);
     // ---- add the partner wave's half (addition commutes: both waves get the same sum)
+    {
+      float4* xw = reinterpret_cast<float4*>(xbuf + (wave * 64 + lane_s) * kXRow);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) xbuf[(wave * 16 + r) * 64 + lane_s] = s[r];
+      for (int q4 = 0; q4 < 4; ++q4) xw[q4] = make_float4(s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]);
+    }
     lds_barrier();
+    {
+      const float4* xr = reinterpret_cast<const float4*>(xbuf + ((wave ^ 1) * 64 + lane_s) * kXRow);
+      float4 o[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] += xbuf[((wave ^ 1) * 16 + r) * 64 + lane_s];
+      for (int q4 = 0; q4 < 4; ++q4) o[q4] = xr[q4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        s[4 * q4] += o[q4].x;
+        s[4 * q4 + 1] += o[q4].y;
+        s[4 * q4 + 2] += o[q4].z;
+        s[4 * q4 + 3] += o[q4].w;
+      }
+    }
     if (!block_active) return -INFINITY;
     // ---- masking (skipped for fully attended tiles, the common case) and row maximum
     if (valid_mask != 0xFFFFFFFFu) {
@@ -419,75 +461,91 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     return fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
   };
 
-  // Second half: weights relative to the running maximum, O^T += V^T P^T.
-  auto back = [&](const f32x16_t& s) __attribute__((always_inline)) {
-    if (!block_active) return;
+  // Second half: weights relative to the running maximum, O^T += V^T P^T interleaved
+  // with the dequant of the remaining lines of tile i+1, then this wave's DMA of
+  // tile i+3 into the raw slot tile i+1 came from.
+  auto back = [&](int tile, int b, const f32x16_t& s) __attribute__((always_inline)) {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
-    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-    bf16x8_t pb[2];
-    float pf[16];
+    const int nb = b ^ 1;
+    if (block_active) {
+      const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+      bf16x8_t pb[2];
+      float pf[16];
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      pf[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -m_use));
-      pf[r + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], scale_log2, -m_use));
-      const bf16x2_t w = __builtin_convertvector(f32x2_t{pf[r], pf[r + 1]}, bf16x2_t);
-      pb[r >> 3][r & 7] = w[0];
-      pb[r >> 3][(r & 7) + 1] = w[1];
-      // O is normalized by the sum of the same rounded weights the PV MFMA multiplies with
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(w, bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
-    }
-    if (want_lse) {
+      for (int r = 0; r < 16; r += 2) {
+        pf[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -m_use));
+        pf[r + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], scale_log2, -m_use));
+        const bf16x2_t w = __builtin_convertvector(f32x2_t{pf[r], pf[r + 1]}, bf16x2_t);
+        pb[r >> 3][r & 7] = w[0];
+        pb[r >> 3][(r & 7) + 1] = w[1];
+        // O is normalized by the sum of the same rounded weights the PV MFMA multiplies with
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(w, bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
+      }
+      if (want_lse) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) l_lse += pf[r];
-    }
-    // ---- O^T += V^T P^T over this wave's output dims.  The V^T fragment (lane: dim
-    //      32mt + lane%32, 8 keys) comes from the key-major tile through two transposing
-    //      reads: in each 16-lane group, lane (a = i/4, b = i%4) points at key a of the
-    //      4-key set and dims 4b..4b+3, and lane j receives dim j of all 4 keys.
-    const int g = lane_s >> 4;
-    const int ia = (lane_s & 15) >> 2;
-    const int ib = lane_s & 3;
-    const uint16_t* vbase = kt + kt_off<S::KCH>(4 * (g >> 1) + ia, dim0 + 16 * (g & 1) + 4 * ib);
-    s16x4_t vf[MTMAX][4];
+        for (int r = 0; r < 16; ++r) l_lse += pf[r];
+      }
+      // ---- O^T += V^T P^T over this wave's output dims.  The V^T fragment (lane: dim
+      //      32mt + lane%32, 8 keys) comes from the key-major tile through two transposing
+      //      reads: in each 16-lane group, lane (a = i/4, b = i%4) points at key a of the
+      //      4-key set and dims 4b..4b+3, and lane j receives dim j of all 4 keys.
+      const int g = lane_s >> 4;
+      const int ia = (lane_s & 15) >> 2;
+      const int ib = lane_s & 3;
+      const uint16_t* vbase = kt[b] + kt_off<S::KCH>(4 * (g >> 1) + ia, dim0 + 16 * (g & 1) + 4 * ib);
+      s16x4_t vf[MTMAX][4];
 #pragma unroll
-    for (int mt = 0; mt < MTMAX; ++mt)
-      if (mt < mt_n)
+      for (int mt = 0; mt < MTMAX; ++mt)
+        if (mt < mt_n)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)  // keys 8*q4 + 4*(g/2) + ia
-          vf[mt][q4] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4_t*)(vbase + kt_off<S::KCH>(8 * q4, 32 * mt)));
+          for (int q4 = 0; q4 < 4; ++q4)  // keys 8*q4 + 4*(g/2) + ia
+            vf[mt][q4] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(vbase + kt_off<S::KCH>(8 * q4, 32 * mt)));
+      dequant_lines<DN, DR, JH, S::FP8_LINES, false>(lane_s, wave, raw_v[nb], raw_s[nb], kt[nb]);
 #pragma unroll
-    for (int mt = 0; mt < MTMAX; ++mt) {
-      if (mt < mt_n) {
+      for (int mt = 0; mt < MTMAX; ++mt) {
+        if (mt < mt_n) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8_t a = __builtin_bit_cast(
-              bf16x8_t, __builtin_shufflevector(vf[mt][2 * ks], vf[mt][2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-          acc_o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], acc_o[mt], 0, 0, 0);
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8_t a = __builtin_bit_cast(
+                bf16x8_t, __builtin_shufflevector(vf[mt][2 * ks], vf[mt][2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+            acc_o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], acc_o[mt], 0, 0, 0);
+          }
         }
       }
+    } else {
+      dequant_lines<DN, DR, JH, S::FP8_LINES, false>(lane_s, wave, raw_v[nb], raw_s[nb], kt[nb]);
     }
-    sched_reads_ahead<2 * MTMAX, 2>();
+    // tile i+1 is fully dequantized: publish its mask byte, then reuse its raw slot
+    if (lane_s == 0) reinterpret_cast<uint8_t*>(&kt_mask[nb])[wave] = (uint8_t)mask_a;
+    mask_a = mask_b;
+    mask_b = 0;
+    if (tile + 3 < tile_end) {
+      const uint8_t* vr;
+      const uint8_t* sr;
+      row_addr_of(tile + 3, pre_slot, &vr, &sr);
+      mask_b = dma_issue<DN, DR>(lane_s, wave, raw_v[nb], raw_s[nb], vr, sr, zrow);
+    }
+    pre_slot = row_slot(tile + 4);
   };
 
   // Tile loop.  The running maximum is kept until a tile exceeds it by 2^slack; the
   // (rare) rescale of O then runs outside the inner loop, so the O accumulators stay
   // in place across the steps of the inner loop.
   int tile = tile_begin;
-  int slot = 0;
   for (;;) {
     f32x16_t s;
     float tmax = -INFINITY;
     bool rescale = false;
     for (; tile < tile_end; ++tile) {
-      tmax = front(tile, slot, s);
-      slot = slot + 1 == kStages ? 0 : slot + 1;
+      const int b = (tile - tile_begin) & 1;
+      tmax = front(tile, b, s);
       if (__ballot(tmax > m_run + kRescaleSlack) != 0ull) {  // also true when m_run is -inf
         rescale = true;
         break;
       }
-      back(s);
+      back(tile, b, s);
     }
     if (!rescale) break;
     const bool upd = tmax > m_run + kRescaleSlack;
@@ -499,7 +557,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     for (int mt = 0; mt < MTMAX; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
-    back(s);
+    back(tile, (tile - tile_begin) & 1, s);
     ++tile;
   }
 
