@@ -17,15 +17,28 @@
 // 8-bit radix passes over per-wave LDS histograms, then compacts the winners in
 // row order (ties at the threshold go to the lower row id), so the output is
 // ascending.
+#include <type_traits>
+#include <utility>
+
 #include "sad_internal.h"
 
 namespace sad {
 namespace {
 
+// Compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>).
+template <typename F, int... J>
+__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // ------------------------------------------------------------------ scoring
 
 constexpr int kScoreThreads = 256;
-constexpr int kRowsPerWave = 256;                                  // 16 groups of 16 rows
+constexpr int kRowsPerWave = 1024;                                 // 64 groups of 16 rows
 constexpr int kScoreChunk = kRowsPerWave * (kScoreThreads / 64);  // compressed rows per workgroup
 constexpr int kGroupBatch = 8;  // 16-row groups whose key loads are in flight together
 
@@ -41,9 +54,16 @@ struct IdxDesc {
   int block;
 };
 
-// One wave scores 256 consecutive compressed rows of one token.  The page ids of those
-// rows are loaded once up front (one per lane), so the key loads of 8 row groups are
-// independent and go out together.
+// Keys of one batch of 8 row groups: lane (m = lane%16, grp = lane/16) holds 16 packed
+// bytes (dims 32*grp .. +32) and the e8m0 exponent of row 16*u + m.
+struct KeyBatch {
+  gi32x4_t v[kGroupBatch];
+  int e[kGroupBatch];
+};
+
+// One wave scores 1024 consecutive compressed rows of one token, 8 groups of 16 rows at
+// a time; the loads of the next batch are issued before the current one is scored.  The
+// page ids of the wave's rows are loaded once up front (one per lane, at most 64 pages).
 template <int DIM>
 __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
     sad_batch b, const uint8_t* __restrict__ qv, const uint8_t* __restrict__ qs,
@@ -61,32 +81,46 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
   const int w_begin = blockIdx.x * kScoreChunk + wave * kRowsPerWave;
   if (w_begin >= n_rows) return;  // no barriers in this kernel: waves may leave early
   const int w_rows = min(kRowsPerWave, n_rows - w_begin);
+  const int n_groups = (w_rows + 15) / 16;
 
   // Page ids of this wave's rows: lane i holds table column col0 + i (a 16-row group
   // never straddles a page, since 16 divides the page size).
   const int32_t* bt_row = bt + (int64_t)g.req * bt_stride;
   const int col0 = w_begin / kc.block;
-  const int ncol = (w_begin + w_rows - 1) / kc.block - col0 + 1;  // <= 16
+  const int ncol = (w_begin + w_rows - 1) / kc.block - col0 + 1;  // <= 64
   const int pid = lane < ncol ? bt_row[col0 + lane] : -1;
 
-  // A operands: 16 heads x 128 dims per tile; lane (m = lane%16, grp = lane/16)
-  // holds dims [32*grp, 32*grp+32) of head 16*ht + m and that block's exponent.
   const int m = lane & 15;
   const int grp = lane >> 4;
-  i32x8_t qa[4];
+  // Issue the loads of groups gb .. gb+7 (absent or unbacked groups read the zero key,
+  // so every load goes out unconditionally).
+  auto load = [&](int gb, KeyBatch& kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kGroupBatch; ++u) {
+      const int sg = w_begin + 16 * (gb + u);
+      const int page = __builtin_amdgcn_readlane(pid, min(sg / kc.block - col0, 63));  // wave-uniform
+      const bool ok = gb + u < n_groups && page >= 0 && (int64_t)page < kc.num_pages;
+      const int ro = sg - (sg / kc.block) * kc.block + m;
+      const uint8_t* base = ok ? kc.pool + (int64_t)page * kc.stride : kZeroKey;
+      const uint32_t voff = ok ? (uint32_t)(ro * VB + 16 * grp) : (uint32_t)(16 * grp);
+      const uint32_t soff = ok ? (uint32_t)(kc.block * VB + ro * SB + grp) : 0u;
+      kb.v[u] = *(const __attribute__((address_space(1))) gi32x4_t*)(base + voff);
+      kb.e[u] = *(const __attribute__((address_space(1))) uint8_t*)(base + soff);
+    }
+  };
+
+  // A operands: 16 heads x 128 dims per tile; lane (m, grp) holds dims [32*grp, 32*grp+32)
+  // of head 16*ht + m and that block's exponent.
+  gi32x4_t qa[4];
   int qsc[4];
   float wl[4][4];
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
     const int h = ht * 16 + m;
-    qa[ht] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    qa[ht] = gi32x4_t{0, 0, 0, 0};
     qsc[ht] = 127;
     if (h < num_heads && grp < SB) {
-      const int4 v = *reinterpret_cast<const int4*>(qv + ((int64_t)t * num_heads + h) * VB + 16 * grp);
-      qa[ht][0] = v.x;
-      qa[ht][1] = v.y;
-      qa[ht][2] = v.z;
-      qa[ht][3] = v.w;
+      qa[ht] = *reinterpret_cast<const gi32x4_t*>(qv + ((int64_t)t * num_heads + h) * VB + 16 * grp);
       qsc[ht] = qs[((int64_t)t * num_heads + h) * SB + grp];
     }
     // this lane's outputs are heads 16*ht + 4*grp + j
@@ -99,66 +133,53 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
   float* lrow = logits + (int64_t)t * logits_stride;
   float* drow = dbg != nullptr ? dbg + (int64_t)t * dbg_stride : nullptr;
 
-#pragma unroll 1
-  for (int gb = 0; gb < kRowsPerWave / 16; gb += kGroupBatch) {
-    // Wave-uniform page bases and 32-bit lane offsets first; invalid or absent groups
-    // read the zero key, so the loads below go out unconditionally and together.
-    const uint8_t* pbase[kGroupBatch];
-    uint32_t voff[kGroupBatch];
-    uint32_t soff[kGroupBatch];
-    bool kval[kGroupBatch];
+  // Score groups gb .. gb+7 from kb (absent groups are scored too, on the zero key;
+  // only rows before the end are stored).
+  auto score = [&](int gb, const KeyBatch& kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kGroupBatch; ++u) {
-      const int r0 = 16 * (gb + u);
-      const int sg = w_begin + r0;
-      const int cl = min(sg / kc.block - col0, 15);
-      const int page = __builtin_amdgcn_readlane(pid, cl);  // wave-uniform
-      kval[u] = r0 < w_rows && page >= 0 && (int64_t)page < kc.num_pages;
-      const int ro = sg - (sg / kc.block) * kc.block + m;
-      pbase[u] = kval[u] ? kc.pool + (int64_t)page * kc.stride : kZeroKey;
-      voff[u] = kval[u] ? (uint32_t)(ro * VB + 16 * grp) : (uint32_t)(16 * grp);
-      soff[u] = kval[u] ? (uint32_t)(kc.block * VB + ro * SB + grp) : 0u;
-    }
-    i32x8_t kb[kGroupBatch];
-    int ksc[kGroupBatch];
-#pragma unroll
-    for (int u = 0; u < kGroupBatch; ++u) {
-      const gi32x4_t v = *(const __attribute__((address_space(1))) gi32x4_t*)(pbase[u] + voff[u]);
-      kb[u] = i32x8_t{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-      ksc[u] = *(const __attribute__((address_space(1))) uint8_t*)(pbase[u] + soff[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kGroupBatch; ++u) {
-      const int r0 = 16 * (gb + u);
-      if (r0 >= w_rows) break;
-      const int sg = w_begin + r0;
+      const int sg = w_begin + 16 * (gb + u);
+      const int page = __builtin_amdgcn_readlane(pid, min(sg / kc.block - col0, 63));
+      const bool ok = page >= 0 && (int64_t)page < kc.num_pages;
+      const i32x8_t kv = {kb.v[u][0], kb.v[u][1], kb.v[u][2], kb.v[u][3], 0, 0, 0, 0};
       float part = 0.0f;
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
-        if (ht * 16 >= num_heads) break;
+        const i32x8_t qv8 = {qa[ht][0], qa[ht][1], qa[ht][2], qa[ht][3], 0, 0, 0, 0};
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
         // format 4 = E2M1 for both operands; scales are e8m0 in byte 0
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kb[u], acc, 4, 4, 0, qsc[ht],
-                                                              0, ksc[u]);
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qv8, kv, acc, 4, 4, 0, qsc[ht], 0, kb.e[u]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) part += wl[ht][j] * fmaxf(acc[j], 0.0f);
       }
       // lanes m, m+16, m+32, m+48 hold the 4 head groups of row sg + m
       part += __shfl_xor(part, 16, 64);
       part += __shfl_xor(part, 32, 64);
-      if (lane < 16 && r0 + lane < w_rows) {
-        const float v = kval[u] ? part : -INFINITY;
+      if (lane < 16 && sg + lane < w_begin + w_rows) {
+        const float v = ok ? part : -INFINITY;
         lrow[sg + lane] = v;
         if (drow != nullptr) drow[sg + lane] = v;
       }
     }
-  }
+  };
+
+  // Straight-line schedule (so the memory waits are exact): the loads of batch b+1 are
+  // in flight while batch b is scored.
+  constexpr int kBatches = kRowsPerWave / 16 / kGroupBatch;
+  KeyBatch kbuf[2];
+  load(0, kbuf[0]);
+  static_for<kBatches>([&](auto bc) {
+    constexpr int bi = decltype(bc)::value;
+    if constexpr (bi + 1 < kBatches) load((bi + 1) * kGroupBatch, kbuf[(bi + 1) & 1]);
+    score(bi * kGroupBatch, kbuf[bi & 1]);
+  });
 }
 
 // ------------------------------------------------------------------ top-k
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kDigitBins = 4096;  // radix digits of 12 bits (then 12, then 8)
 
 __device__ inline uint32_t order_key(float f) {
   // -inf and NaN mark rows that are not candidates
@@ -188,17 +209,40 @@ __device__ inline int block_excl_scan(int v, int* sh, int* total) {
   return off + incl - v;
 }
 
+// The digit bin holding the kk-th largest counted key (1-based), scanning the bins
+// from the top: returns it and the number of keys in higher bins (*above), and the
+// number of counted keys (*total).  Thread t owns bins 4095-4t .. 4092-4t.
+__device__ inline int select_bin(const int* hist, int kk, int* sh, int* pick, int* above, int* total) {
+  const int tid = threadIdx.x;
+  int c[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) c[q] = hist[kDigitBins - 1 - (4 * tid + q)];
+  int a = block_excl_scan(c[0] + c[1] + c[2] + c[3], sh, total);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (a < kk && kk <= a + c[q]) {
+      pick[0] = kDigitBins - 1 - (4 * tid + q);
+      pick[1] = a;
+    }
+    a += c[q];
+  }
+  __syncthreads();
+  *above = pick[1];
+  return pick[0];
+}
+
 template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     sad_batch b, int ratio, int max_rows, const float* __restrict__ logits, int64_t logits_stride,
     int k, int32_t* __restrict__ out) {
-  __shared__ int hist[kTopkWaves][256];
+  // logits staged in row order (coalesced global loads), then read back thread-contiguous
+  constexpr int kStride = KPT <= 16 ? KPT + 4 : KPT;  // padded rows: conflict-free 16-byte reads
+  __shared__ __align__(16) float stage[kTopkThreads * kStride];
+  __shared__ int hist[kDigitBins];
   __shared__ int scan_sh[kTopkWaves];
   __shared__ int pick[2];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   int32_t* orow = out + (int64_t)t * k;
   TokenGeom g;
   const bool ok = token_geometry(b, t, ratio, g);
@@ -208,77 +252,57 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     return;
   }
   const float* lrow = logits + (int64_t)t * logits_stride;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int r = i * kTopkThreads + tid;  // row; thread r / KPT holds it
+    stage[(r / KPT) * kStride + r % KPT] = r < n ? lrow[r] : -INFINITY;
+  }
+  for (int j = tid; j < kDigitBins; j += kTopkThreads) hist[j] = 0;
+  __syncthreads();
   const int base = tid * KPT;
   uint32_t key[KPT];
-  int nvalid_local = 0;
 #pragma unroll
   for (int i = 0; i < KPT; i += 4) {
-    float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-    if (base + i + 3 < n) {
-      v = *reinterpret_cast<const float4*>(lrow + base + i);
-    } else {
-      if (base + i + 0 < n) v.x = lrow[base + i + 0];
-      if (base + i + 1 < n) v.y = lrow[base + i + 1];
-      if (base + i + 2 < n) v.z = lrow[base + i + 2];
-    }
+    const float4 v = *reinterpret_cast<const float4*>(&stage[tid * kStride + i]);
     key[i + 0] = order_key(v.x);
     key[i + 1] = order_key(v.y);
     key[i + 2] = order_key(v.z);
     key[i + 3] = order_key(v.w);
   }
+
+  // Pass 1: top 12 bits of every candidate key (this also counts the candidates).
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) nvalid_local += key[i] != 0u;
-  int nvalid;
-  (void)block_excl_scan(nvalid_local, scan_sh, &nvalid);
+  for (int i = 0; i < KPT; ++i)
+    if (key[i] != 0u) atomicAdd(&hist[key[i] >> 20], 1);
+  __syncthreads();
+  int above, nvalid;
+  const int d1 = select_bin(hist, k, scan_sh, pick, &above, &nvalid);
 
   uint32_t thr = 0u;  // keys > thr are taken, plus `need` keys == thr in row order
   int need = 0;
   if (nvalid > k) {
-    uint32_t prefix = 0u, pmask = 0u;
-    int kk = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int j = tid; j < kTopkWaves * 256; j += kTopkThreads) (&hist[0][0])[j] = 0;
-      __syncthreads();
+    int kk = k - above;
+    // Pass 2: next 12 bits of the keys in digit d1.
+    for (int j = tid; j < kDigitBins; j += kTopkThreads) hist[j] = 0;
+    __syncthreads();
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        if ((key[i] & pmask) == prefix) atomicAdd(&hist[wave][(key[i] >> shift) & 255u], 1);
-      }
-      __syncthreads();
-      if (wave == 0) {
-        // lane owns bins 4*lane .. 4*lane+3; suffix sums from the top bin down
-        int c[4];
+    for (int i = 0; i < KPT; ++i)
+      if ((int)(key[i] >> 20) == d1) atomicAdd(&hist[(key[i] >> 8) & 4095u], 1);
+    __syncthreads();
+    int dummy;
+    const int d2 = select_bin(hist, kk, scan_sh, pick, &above, &dummy);
+    kk -= above;
+    const uint32_t prefix = ((uint32_t)d1 << 20) | ((uint32_t)d2 << 8);
+    // Pass 3: last 8 bits of the keys in digits (d1, d2).
+    for (int j = tid; j < kDigitBins; j += kTopkThreads) hist[j] = 0;
+    __syncthreads();
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          int s = 0;
-          for (int w = 0; w < kTopkWaves; ++w) s += hist[w][4 * lane + q];
-          c[q] = s;
-        }
-        const int lane_sum = c[0] + c[1] + c[2] + c[3];
-        // inclusive suffix over lanes: sum of lane_sum for lanes >= this lane
-        int suf = lane_sum;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int o = __shfl_down(suf, off, 64);
-          if (lane + off < 64) suf += o;
-        }
-        int above = suf - lane_sum;  // keys in bins of higher lanes
-#pragma unroll
-        for (int q = 3; q >= 0; --q) {
-          if (above < kk && kk <= above + c[q]) {
-            pick[0] = 4 * lane + q;
-            pick[1] = above;
-          }
-          above += c[q];
-        }
-      }
-      __syncthreads();
-      const int d = pick[0];
-      kk -= pick[1];
-      prefix |= (uint32_t)d << shift;
-      pmask |= 255u << shift;
-      __syncthreads();
-    }
-    thr = prefix;
+    for (int i = 0; i < KPT; ++i)
+      if ((key[i] >> 8) == (prefix >> 8)) atomicAdd(&hist[key[i] & 255u], 1);
+    __syncthreads();
+    const int d3 = select_bin(hist, kk, scan_sh, pick, &above, &dummy);
+    kk -= above;
+    thr = prefix | (uint32_t)d3;
     need = kk;
   }
 
