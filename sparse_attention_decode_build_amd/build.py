@@ -28,6 +28,9 @@ FLAGS = [
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]
+# Per-file extra flags.  The indexer's MFMA results feed VALU work right away, so its
+# MFMAs write VGPRs (the attention kernel keeps its long-lived accumulators in AGPRs).
+EXTRA_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc() -> str:
@@ -45,7 +48,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
-        cmd = [hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")

@@ -10,6 +10,7 @@ namespace sad {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPerThread = 8;  // consecutive compressed candidates per thread and chunk
 
 __global__ __launch_bounds__(kThreads) void build_sparse_indices_kernel(
     sad_batch b, const int32_t* __restrict__ replay, const int32_t* __restrict__ swa_bt,
@@ -42,23 +43,33 @@ __global__ __launch_bounds__(kThreads) void build_sparse_indices_kernel(
     row[j] = s;
   }
 
-  // Compressed columns: kept candidates packed left in candidate order.
+  // Compressed columns: kept candidates packed left in candidate order.  Each thread
+  // takes kPerThread consecutive candidates of a chunk: their id and table loads go out
+  // together, and one workgroup scan places the kept ones.
   const int ncand = !ok ? 0 : (topk_local != nullptr ? topk : min(g.n_comp, padded));
   const int32_t* comp_row = ok ? comp_bt + (int64_t)g.req * comp_stride : nullptr;
   const int32_t* cand_row = topk_local != nullptr ? topk_local + (int64_t)t * topk_stride : nullptr;
   int base = 0;
-  for (int c0 = 0; c0 < ncand; c0 += kThreads) {
-    const int c = c0 + tid;
-    int s = -1;
-    if (c < ncand) {
-      const int l = cand_row != nullptr ? cand_row[c] : c;
-      if (l >= 0 && l < g.n_comp) s = page_slot(comp_row, comp_cols, comp_block, comp_pages, l);
+  for (int c0 = 0; c0 < ncand; c0 += kThreads * kPerThread) {
+    const int cb = c0 + tid * kPerThread;
+    int l[kPerThread];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int c = cb + i;
+      l[i] = c < ncand ? (cand_row != nullptr ? cand_row[c] : c) : -1;
     }
-    const uint64_t m = __ballot(s >= 0);
-    const int below = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_count[wave] = __popcll(m);
+    int sl[kPerThread];
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      sl[i] = (l[i] >= 0 && l[i] < g.n_comp) ? page_slot(comp_row, comp_cols, comp_block, comp_pages, l[i]) : -1;
+      cnt += sl[i] >= 0;
+    }
+    // exclusive scan of the per-thread counts
+    const int incl = wave_incl_scan(cnt);
+    if (lane == 63) wave_count[wave] = incl;
     __syncthreads();
-    int off = base;
+    int off = base + incl - cnt;
     int total = base;
 #pragma unroll
     for (int w = 0; w < kThreads / 64; ++w) {
@@ -66,7 +77,9 @@ __global__ __launch_bounds__(kThreads) void build_sparse_indices_kernel(
       if (w < wave) off += cw;
       total += cw;
     }
-    if (s >= 0) row[window + off + below] = s;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i)
+      if (sl[i] >= 0) row[window + off++] = sl[i];
     base = total;
     __syncthreads();
   }

@@ -44,8 +44,8 @@ constexpr int kGroupBatch = 8;  // 16-row groups whose key loads are in flight t
 
 typedef int gi32x4_t __attribute__((__vector_size__(4 * sizeof(int))));
 
-// Source of the loads of absent or unbacked key groups (their scores become -inf).
-__device__ __align__(16) uint8_t kZeroKey[64];
+// Buffer-resource flags word for raw (unformatted, unswizzled) loads on gfx9-family GPUs.
+constexpr int kRawBufferFlags = 0x00020000;
 
 struct IdxDesc {
   const uint8_t* pool;
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
   constexpr int SB = DIM / 32;   // exponent bytes per row
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   TokenGeom g;
   if (!token_geometry(b, t, ratio, g)) return;
   const int n_rows = min(g.n_comp, bt_cols * kc.block);
@@ -92,23 +92,27 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
 
   const int m = lane & 15;
   const int grp = lane >> 4;
-  // Issue the loads of groups gb .. gb+7 (absent or unbacked groups read the zero key,
-  // so every load goes out unconditionally).
+  // Issue the loads of groups gb .. gb+7 as buffer loads: a wave-uniform resource per
+  // page (zero records for an absent or unbacked group, so its loads return zeros and
+  // touch no memory), the group's first row as the scalar offset and a per-lane
+  // constant offset.  Every load goes out unconditionally.
+  // (lanes past the key's dims, grp >= SB, read out of range: zeros)
+  const uint32_t lane_voff = grp < SB ? (uint32_t)(m * VB + 16 * grp) : (1u << 30);
+  const uint32_t lane_soff = grp < SB ? (uint32_t)(m * SB + grp) : (1u << 30);
   auto load = [&](int gb, KeyBatch& kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kGroupBatch; ++u) {
       const int sg = w_begin + 16 * (gb + u);
       const int page = __builtin_amdgcn_readlane(pid, min(sg / kc.block - col0, 63));  // wave-uniform
       const bool ok = gb + u < n_groups && page >= 0 && (int64_t)page < kc.num_pages;
-      const int ro = sg - (sg / kc.block) * kc.block + m;
-      const uint8_t* base = ok ? kc.pool + (int64_t)page * kc.stride : kZeroKey;
-      const uint32_t voff = ok ? (uint32_t)(ro * VB + 16 * grp) : (uint32_t)(16 * grp);
-      const uint32_t soff = ok ? (uint32_t)(kc.block * VB + ro * SB + grp) : 0u;
-      kb.v[u] = *(const __attribute__((address_space(1))) gi32x4_t*)(base + voff);
-      kb.e[u] = *(const __attribute__((address_space(1))) uint8_t*)(base + soff);
+      const int r0 = sg & (kc.block - 1);  // first row of the group in its page
+      const uint8_t* pg = kc.pool + (int64_t)(ok ? page : 0) * kc.stride;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)pg, (short)0, ok ? (int)kc.stride : 0, kRawBufferFlags);
+      kb.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_voff, r0 * VB, 0);
+      kb.e[u] = __builtin_amdgcn_raw_buffer_load_b8(rs, lane_soff, kc.block * VB + r0 * SB, 0);
     }
   };
-
   // A operands: 16 heads x 128 dims per tile; lane (m, grp) holds dims [32*grp, 32*grp+32)
   // of head 16*ht + m and that block's exponent.
   gi32x4_t qa[4];
@@ -132,35 +136,51 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
   }
   float* lrow = logits + (int64_t)t * logits_stride;
   float* drow = dbg != nullptr ? dbg + (int64_t)t * dbg_stride : nullptr;
+  // the ReLU's upper clamp, kept opaque so the clamp stays one med3 instruction
+  float fmax_big = 3.402823466e+38f;
+  asm volatile("" : "+s"(fmax_big));
 
   // Score groups gb .. gb+7 from kb (absent groups are scored too, on the zero key;
-  // only rows before the end are stored).
-  auto score = [&](int gb, const KeyBatch& kb) __attribute__((always_inline)) {
+  // only rows before the end are stored).  The MFMAs of group u+1 are issued before the
+  // results of group u are combined.
+  auto mma = [&](const KeyBatch& kb, int u, f32x4_t (&acc)[4]) __attribute__((always_inline)) {
+    const i32x8_t kv = {kb.v[u][0], kb.v[u][1], kb.v[u][2], kb.v[u][3], 0, 0, 0, 0};
 #pragma unroll
-    for (int u = 0; u < kGroupBatch; ++u) {
-      const int sg = w_begin + 16 * (gb + u);
-      const int page = __builtin_amdgcn_readlane(pid, min(sg / kc.block - col0, 63));
-      const bool ok = page >= 0 && (int64_t)page < kc.num_pages;
-      const i32x8_t kv = {kb.v[u][0], kb.v[u][1], kb.v[u][2], kb.v[u][3], 0, 0, 0, 0};
-      float part = 0.0f;
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
-        const i32x8_t qv8 = {qa[ht][0], qa[ht][1], qa[ht][2], qa[ht][3], 0, 0, 0, 0};
-        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        // format 4 = E2M1 for both operands; scales are e8m0 in byte 0
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qv8, kv, acc, 4, 4, 0, qsc[ht], 0, kb.e[u]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) part += wl[ht][j] * fmaxf(acc[j], 0.0f);
-      }
-      // lanes m, m+16, m+32, m+48 hold the 4 head groups of row sg + m
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
-      if (lane < 16 && sg + lane < w_begin + w_rows) {
-        const float v = ok ? part : -INFINITY;
-        lrow[sg + lane] = v;
-        if (drow != nullptr) drow[sg + lane] = v;
-      }
+    for (int ht = 0; ht < 4; ++ht) {
+      const i32x8_t qv8 = {qa[ht][0], qa[ht][1], qa[ht][2], qa[ht][3], 0, 0, 0, 0};
+      // format 4 = E2M1 for both operands; scales are e8m0 in byte 0
+      acc[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qv8, kv, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4,
+                                                                 0, qsc[ht], 0, kb.e[u]);
+      asm volatile("" : "+v"(acc[ht]));  // results in VGPRs: the combine reads them directly
     }
+  };
+  auto combine = [&](int gb, int u, const f32x4_t (&acc)[4]) __attribute__((always_inline)) {
+    const int sg = w_begin + 16 * (gb + u);
+    const int page = __builtin_amdgcn_readlane(pid, min(sg / kc.block - col0, 63));
+    const bool ok = page >= 0 && (int64_t)page < kc.num_pages;
+    float part = 0.0f;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)  // ReLU as one med3 (clamp to [0, FLT_MAX])
+        part = __builtin_fmaf(wl[ht][j], __builtin_amdgcn_fmed3f(acc[ht][j], 0.0f, fmax_big), part);
+    // lanes m, m+16, m+32, m+48 hold the 4 head groups of row sg + m
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    if (lane < 16 && sg + lane < w_begin + w_rows) {
+      const float v = ok ? part : -INFINITY;
+      lrow[sg + lane] = v;
+      if (drow != nullptr) drow[sg + lane] = v;
+    }
+  };
+  auto score = [&](int gb, const KeyBatch& kb) __attribute__((always_inline)) {
+    f32x4_t acc[2][4];
+    mma(kb, 0, acc[0]);
+    static_for<kGroupBatch>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u + 1 < kGroupBatch) mma(kb, u + 1, acc[(u + 1) & 1]);
+      combine(gb, u, acc[u & 1]);
+    });
   };
 
   // Straight-line schedule (so the memory waits are exact): the loads of batch b+1 are
