@@ -229,8 +229,8 @@ int gather_dequant_kv(const sad_kv_cache* swa, const sad_kv_cache* comp,
  *                window_size + padded_topk, d_nope + d_rope)
  * num_heads in {8, 16, ..., 128} (a multiple of 8, <= 128); (d_nope, d_rope)
  * = (512, 64) or (128, 32); page sizes (block_size) of both caches are powers of two.
- * A token's columns may be split over several workgroups (few tokens, or more than
- * 4352 columns); the partial results are merged through the workspace.
+ * With few tokens a token's columns are split over several workgroups; the partial
+ * results are merged through the workspace.
  */
 int sparse_mla_decode(const uint16_t* q_bf16, int32_t num_tokens, int32_t num_heads,
                       const sad_kv_cache* swa, const sad_kv_cache* comp,

@@ -9,24 +9,25 @@
 //   * one workgroup = one token x one group of 64 heads x one split of the token's
 //     attended columns, 4 waves (one per SIMD).  Wave w owns heads 32*(w/2) .. +32 of
 //     the group and half of the latent dims (w%2): its Q^T fragments for those dims stay
-//     in VGPRs, and its O^T accumulator for those output dims in AGPRs, for the whole
+//     in AGPRs, and its O^T accumulator for those output dims in AGPRs, for the whole
 //     split.  The two waves of a head block add their partial S^T through LDS;
 //   * the workgroups of one token's head groups are numbered 8 apart so they run on the
 //     same XCD at the same time and the second read of each row hits that XCD's L2;
-//   * the workgroup's index columns are staged in LDS once; columns are then taken 32
-//     at a time.  The raw cache bytes of tiles i+1..i+3 are in flight HBM -> LDS as
-//     direct global-to-LDS loads (no VGPRs) while tile i is computed; each lane carries
-//     one row of every tile, so it computes one row address per tile;
-//   * tile i is dequantized from LDS (fp32 multiply by the row's block scale, bf16
-//     rounding) into one key-major bf16 tile K[32][D] (rows padded by one 16-byte chunk).  S^T = K Q^T reads
-//     it with 16-byte fragment loads; O^T += V^T P^T reads the same tile transposed
-//     (ds_read_b64_tr_b16), so no second copy is written;
+//   * columns are taken 32 at a time (a tile); wave w carries rows 8w..8w+7 of every
+//     tile.  Its raw cache bytes of tiles i+1..i+3 are in flight HBM -> LDS as direct
+//     global-to-LDS loads of whole 128-byte lines (no VGPRs) while tile i is computed;
+//     the slot ids of a tile are one scalar load per wave, a step ahead;
+//   * two-stage pipeline: while S^T = K Q^T and O^T += V^T P^T run on tile i's K tile,
+//     each wave dequantizes its own rows of tile i+1 (fp32 multiply by the row's block
+//     scale, bf16 rounding) into the other K buffer, key-major with rows padded by one
+//     16-byte chunk; QK reads it with 16-byte fragment loads and PV reads the same tile
+//     transposed (ds_read_b64_tr_b16), so no second copy is written;
 //   * S^T puts one head per lane, so the online softmax needs only a swap with lane^32,
 //     and the probabilities already sit in the B-operand layout of the PV MFMA;
 //   * splits of one token write (o / l, log2-sum-exp) partials that a second kernel
 //     merges, with the sink, when more than one split is used.
 // Barriers are raw s_barrier with explicit LDS waits so that the in-flight LDS DMA of
-// the next tile is only waited for when that tile is consumed.
+// the next tiles is only waited for when a tile is consumed.
 #include <math.h>
 
 #include <algorithm>
@@ -41,7 +42,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;              // attended columns per tile
-constexpr int kMaxSiCols = 4352;       // index columns one workgroup stages in LDS (17 KB)
+constexpr int kRawSlots = 3;           // raw tiles in LDS: the next one (being dequantized) + 2 in flight
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kXRow = 20;  // floats per lane in the S exchange buffer (16 + pad: conflict-free 16-byte access)  // keep the running max until exceeded by 2^8
 constexpr float kLog2e = 1.4426950408889634f;
@@ -167,11 +168,6 @@ __device__ inline int kt_off(int key, int dim) {
 // Row values / scales of one attended column, or the zero row when the column is not
 // attended (past ncols, slot -1, page outside the pool).  ONE: the window and the
 // compressed columns read the same cache (wave-uniform descriptor).
-// The slot id is read from LDS one step before the addresses are formed
-// (col_slot), so the read's latency is off the critical path.
-__device__ inline int col_slot(int col, int col_end, const int32_t* si_lds, int col_base) {
-  return col < col_end ? si_lds[col - col_base] : -1;  // col_end: end of the staged columns
-}
 template <bool ONE>
 __device__ inline void slot_row(int slot, int col, int window, const KvDesc& swa, const KvDesc& comp, int rowb,
                                 int nsc, const uint8_t* zrow, const uint8_t** vals, const uint8_t** scales) {
@@ -272,14 +268,13 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   constexpr int MTMAX = S::MT0;
   constexpr int NV = S::DMA_PER_TILE;
   constexpr int JH = S::FP8_LINES / 2;  // fp8 lines dequantized alongside QK; the rest alongside PV
-  // Two raw slots (this wave's rows of tiles i+1 and i+2 arrive there) and two K tiles
-  // (tile i is computed on while tile i+1 is dequantized into the other).
-  __shared__ __align__(16) uint8_t raw_v[2][S::RAW_V];
-  __shared__ __align__(16) float raw_s[2][S::RAW_S];
+  // Three raw slots (this wave's rows of tiles i+1, i+2 and i+3 arrive there) and two K
+  // tiles (tile i is computed on while tile i+1 is dequantized into the other).
+  __shared__ __align__(16) uint8_t raw_v[kRawSlots][S::RAW_V];
+  __shared__ __align__(16) float raw_s[kRawSlots][S::RAW_S];
   __shared__ __align__(16) uint16_t kt[2][kTile * S::KCH * 8];
   __shared__ uint32_t kt_mask[2];  // validity of the tile in each K buffer (bit j: column j)
   __shared__ __align__(16) float xbuf[kWaves * 64 * kXRow];  // [wave][lane][kXRow]: partial S
-  __shared__ __align__(16) int32_t si_lds[kMaxSiCols];  // this split's sparse_indices columns
 
   // Block -> (token, split, head group): the head groups of one (token, split) are
   // 8 blocks apart, i.e. on the same XCD and dispatched together.
@@ -294,7 +289,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;  // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   __builtin_assume(wave >= 0 && wave < kWaves);
   const int n = lane & 31;    // head within the wave's block / key row within a fragment
   const int h = lane >> 5;    // lane half
@@ -318,13 +313,8 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   const int per = (ntiles + num_splits - 1) / num_splits;
   const int tile_begin = split * per;
   const int tile_end = min(ntiles, tile_begin + per);
-  const int col_base = tile_begin * kTile;
   const int col_end = min(ncols, tile_end * kTile);
   const uint16_t* qrow = q + ((int64_t)t * num_heads + min(head, num_heads - 1)) * DQK;
-
-  // Stage this split's index columns in LDS (the tile loop then issues no global
-  // loads besides the row DMA).
-  for (int c = col_base + tid; c < col_end; c += kThreads) si_lds[c - col_base] = si_row[c];
 
   // Q^T fragments: lane (head n, half h) holds dims dim0 + [16kk + 8h, 16kk + 8h + 8).
   bf16x8_t qf[KSMAX];
@@ -346,15 +336,47 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   float l_run = 0.0f;  // sum of the bf16-rounded weights (normalizes O)
   float l_lse = 0.0f;  // sum of the fp32 weights (log-sum-exp)
 
-  // Q fragments and index columns landed (a wait the compiler sees, so it does not
-  // re-check the Q loads inside the tile loop)
+  // Q fragments landed (a wait the compiler sees, so it does not re-check the Q loads
+  // inside the tile loop)
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  lds_barrier();  // si_lds complete
 
-  // Row addresses of this lane's row (8*wave + lane/8) of a tile.
-  auto row_slot = [&](int tile) __attribute__((always_inline)) -> int {
-    return col_slot(tile * kTile + 8 * wave + (lane >> 3), col_end, si_lds, col_base);
+  // Slot id of this lane's row (8*wave + lane/8) of a tile: the wave's 8 ids are one
+  // scalar load (counted by lgkmcnt, so the row DMA's vmcnt accounting is untouched);
+  // it is issued one step before the DMA that uses it.  A window past the end of the
+  // sparse_indices row is moved back inside it (the ids of such columns are unused).
+  struct SlotIds {
+    int v[8];  // sparse_indices[c .. c+8) of the wave's rows (c = lc, wave-uniform)
+    int c0;    // first column of the wave's rows
+    int lc;    // first column loaded
   };
+  auto load_slots = [&](int tile) __attribute__((always_inline)) -> SlotIds {
+    SlotIds ids;
+    ids.c0 = tile * kTile + 8 * wave;  // wave-uniform
+    ids.lc = max(0, min(ids.c0, width - 8));
+    const int32_t* p = si_row + ids.lc;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ids.v[j] = p[j];  // always inside the row; unused past col_end
+    return ids;
+  };
+  auto pick_slot = [&](const SlotIds& ids) __attribute__((always_inline)) -> int {
+    // lanes 0..7 take the 8 ids, then every lane fetches its row's id with one shuffle
+    int w8 = 0;
+#define SAD_WRITELANE(j) asm("v_writelane_b32 %0, %1, " #j : "+v"(w8) : "s"(ids.v[j]))
+    SAD_WRITELANE(0);
+    SAD_WRITELANE(1);
+    SAD_WRITELANE(2);
+    SAD_WRITELANE(3);
+    SAD_WRITELANE(4);
+    SAD_WRITELANE(5);
+    SAD_WRITELANE(6);
+    SAD_WRITELANE(7);
+#undef SAD_WRITELANE
+    const int r = lane >> 3;
+    const int idx = min(ids.c0 + r - ids.lc, 7);
+    const int x = __builtin_amdgcn_ds_bpermute(idx << 2, w8);
+    return ids.c0 + r < col_end ? x : -1;
+  };
+  auto row_slot = [&](int tile) __attribute__((always_inline)) -> int { return pick_slot(load_slots(tile)); };
   auto row_addr_of = [&](int tile, int slot, const uint8_t** vrow, const uint8_t** srow)
       __attribute__((always_inline)) {
     slot_row<ONE>(slot, tile * kTile + 8 * wave + (lane >> 3), window, swa, comp, S::ROWB, S::NSC, zrow, vrow,
@@ -363,9 +385,19 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   auto row_addr = [&](int tile, const uint8_t** vrow, const uint8_t** srow) __attribute__((always_inline)) {
     row_addr_of(tile, row_slot(tile), vrow, srow);
   };
-  // Prologue: DMA of tiles 0 and 1, dequant of tile 0, DMA of tile 2.  A wave's mask
-  // byte of a tile is kept from its DMA until it writes it beside that tile's K buffer.
-  uint32_t mask_a = 0, mask_b = 0;  // this wave's bytes for the tiles in raw slots 1 and 0
+  // Wait until at most `after` tiles' DMAs issued after the awaited one are in flight.
+  auto wait_tiles = [&](int after) __attribute__((always_inline)) {
+    if (after >= 2)
+      wait_vmem<2 * NV>();
+    else if (after == 1)
+      wait_vmem<NV>();
+    else
+      wait_vmem<0>();
+  };
+  // Prologue: DMA of tiles 0, 1, 2 (raw slots 0, 1, 2), dequant of tile 0, DMA of tile 3
+  // into slot 0.  Tile j uses raw slot j % 3.  A wave's mask byte of a tile is kept from
+  // its DMA until it writes it beside that tile's K buffer.
+  uint32_t mask_a = 0, mask_b = 0, mask_c = 0;  // this wave's bytes for tiles i+1, i+2, i+3
   {
     const uint8_t* vr;
     const uint8_t* sr;
@@ -378,27 +410,27 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
       row_addr(tile_begin + 1, &vr, &sr);
       mask_a = dma_issue<DN, DR>(lane, wave, raw_v[1], raw_s[1], vr, sr, zrow);
     }
+    if (tile_begin + 2 < tile_end) {
+      row_addr(tile_begin + 2, &vr, &sr);
+      mask_b = dma_issue<DN, DR>(lane, wave, raw_v[2], raw_s[2], vr, sr, zrow);
+    }
     if (tile_begin < tile_end) {
-      if (tile_begin + 1 < tile_end)
-        wait_vmem<NV>();
-      else
-        wait_vmem<0>();
+      wait_tiles(min(2, tile_end - 1 - tile_begin));
       dequant_lines<DN, DR, 0, S::FP8_LINES, true>(lane, wave, raw_v[0], raw_s[0], kt[0]);
       if (lane == 0) reinterpret_cast<uint8_t*>(&kt_mask[0])[wave] = (uint8_t)m0;
     }
-    if (tile_begin + 2 < tile_end) {
-      row_addr(tile_begin + 2, &vr, &sr);
-      mask_b = dma_issue<DN, DR>(lane, wave, raw_v[0], raw_s[0], vr, sr, zrow);
+    if (tile_begin + 3 < tile_end) {
+      row_addr(tile_begin + 3, &vr, &sr);
+      mask_c = dma_issue<DN, DR>(lane, wave, raw_v[0], raw_s[0], vr, sr, zrow);
     }
   }
-  int pre_slot = row_slot(tile_begin + 3);  // slot id of this lane's row of the next DMA
+  SlotIds pre_ids = load_slots(tile_begin + 4);  // slot ids of the wave's rows of the next DMA
 
-  // First half of step i (tile i in K buffer b = i%2, tile i+1 in raw slot 1-b... see
-  // below): barrier, S^T = K Q^T over this wave's dims interleaved with the dequant of
-  // the first fp8 lines of tile i+1, both dim halves summed, masking.  Returns the
-  // tile's scaled row maximum per head (log2 domain).
-  // Raw slots: tile i+1 sits in slot (i+1)%2, tile i+2 in slot i%2.
-  auto front = [&](int tile, int b, f32x16_t& s) __attribute__((always_inline)) -> float {
+  // First half of step i (tile i in K buffer b = i%2, tile i+1 in raw slot rs): barrier,
+  // S^T = K Q^T over this wave's dims interleaved with the dequant of the first fp8 lines
+  // of tile i+1, both dim halves summed, masking.  Returns the tile's scaled row maximum
+  // per head (log2 domain).
+  auto front = [&](int tile, int b, int rs, f32x16_t& s) __attribute__((always_inline)) -> float {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
     const int n_s = lane_s & 31;
@@ -406,11 +438,8 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     const int nb = b ^ 1;
     lds_barrier();  // tile i's K buffer complete; tile i-1's PV is done with the other buffer
     const uint32_t valid_mask = kt_mask[b];
-    // this wave's DMA of tile i+1 landed (tile i+2's may still be in flight)
-    if (tile + 2 < tile_end)
-      wait_vmem<NV>();
-    else
-      wait_vmem<0>();
+    // this wave's DMA of tile i+1 landed (tiles i+2 and i+3 may still be in flight)
+    wait_tiles(min(2, tile_end - 2 - tile));
     // ---- partial S^T = K Q^T over this wave's dims: lane (head n, half h) gets
     //      keys 8*(r/4) + 4h + r%4, r = 0..15 ...
 #pragma unroll
@@ -422,7 +451,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
       if (kk < ks_n) af[kk] = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * kk);
     // ... while the first fp8 lines of tile i+1 are dequantized into the other buffer
     // (a stale slot past the last tile only writes the unused buffer)
-    dequant_lines<DN, DR, 0, JH, true>(lane_s, wave, raw_v[nb], raw_s[nb], kt[nb]);
+    dequant_lines<DN, DR, 0, JH, true>(lane_s, wave, raw_v[rs], raw_s[rs], kt[nb]);
 #pragma unroll
     for (int kk = 0; kk < KSMAX; ++kk)
       if (kk < ks_n) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], qf[kk], s, 0, 0, 0);
@@ -463,8 +492,8 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
 
   // Second half: weights relative to the running maximum, O^T += V^T P^T interleaved
   // with the dequant of the remaining lines of tile i+1, then this wave's DMA of
-  // tile i+3 into the raw slot tile i+1 came from.
-  auto back = [&](int tile, int b, const f32x16_t& s) __attribute__((always_inline)) {
+  // tile i+4 into the raw slot tile i+1 came from.
+  auto back = [&](int tile, int b, int rs, const f32x16_t& s) __attribute__((always_inline)) {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
     const int nb = b ^ 1;
@@ -502,7 +531,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
           for (int q4 = 0; q4 < 4; ++q4)  // keys 8*q4 + 4*(g/2) + ia
             vf[mt][q4] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4_t*)(vbase + kt_off<S::KCH>(8 * q4, 32 * mt)));
-      dequant_lines<DN, DR, JH, S::FP8_LINES, false>(lane_s, wave, raw_v[nb], raw_s[nb], kt[nb]);
+      dequant_lines<DN, DR, JH, S::FP8_LINES, false>(lane_s, wave, raw_v[rs], raw_s[rs], kt[nb]);
 #pragma unroll
       for (int mt = 0; mt < MTMAX; ++mt) {
         if (mt < mt_n) {
@@ -515,37 +544,39 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
         }
       }
     } else {
-      dequant_lines<DN, DR, JH, S::FP8_LINES, false>(lane_s, wave, raw_v[nb], raw_s[nb], kt[nb]);
+      dequant_lines<DN, DR, JH, S::FP8_LINES, false>(lane_s, wave, raw_v[rs], raw_s[rs], kt[nb]);
     }
     // tile i+1 is fully dequantized: publish its mask byte, then reuse its raw slot
     if (lane_s == 0) reinterpret_cast<uint8_t*>(&kt_mask[nb])[wave] = (uint8_t)mask_a;
     mask_a = mask_b;
-    mask_b = 0;
-    if (tile + 3 < tile_end) {
+    mask_b = mask_c;
+    mask_c = 0;
+    if (tile + 4 < tile_end) {
       const uint8_t* vr;
       const uint8_t* sr;
-      row_addr_of(tile + 3, pre_slot, &vr, &sr);
-      mask_b = dma_issue<DN, DR>(lane_s, wave, raw_v[nb], raw_s[nb], vr, sr, zrow);
+      row_addr_of(tile + 4, pick_slot(pre_ids), &vr, &sr);
+      mask_c = dma_issue<DN, DR>(lane_s, wave, raw_v[rs], raw_s[rs], vr, sr, zrow);
     }
-    pre_slot = row_slot(tile + 4);
+    pre_ids = load_slots(tile + 5);
   };
 
   // Tile loop.  The running maximum is kept until a tile exceeds it by 2^slack; the
   // (rare) rescale of O then runs outside the inner loop, so the O accumulators stay
   // in place across the steps of the inner loop.
   int tile = tile_begin;
+  int rs = 1;  // raw slot of tile i+1
   for (;;) {
     f32x16_t s;
     float tmax = -INFINITY;
     bool rescale = false;
-    for (; tile < tile_end; ++tile) {
+    for (; tile < tile_end; ++tile, rs = rs == kRawSlots - 1 ? 0 : rs + 1) {
       const int b = (tile - tile_begin) & 1;
-      tmax = front(tile, b, s);
+      tmax = front(tile, b, rs, s);
       if (__ballot(tmax > m_run + kRescaleSlack) != 0ull) {  // also true when m_run is -inf
         rescale = true;
         break;
       }
-      back(tile, b, s);
+      back(tile, b, rs, s);
     }
     if (!rescale) break;
     const bool upd = tmax > m_run + kRescaleSlack;
@@ -557,8 +588,9 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     for (int mt = 0; mt < MTMAX; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
-    back(tile, (tile - tile_begin) & 1, s);
+    back(tile, (tile - tile_begin) & 1, rs, s);
     ++tile;
+    rs = rs == kRawSlots - 1 ? 0 : rs + 1;
   }
 
   if (!block_active || head >= num_heads) return;
@@ -638,8 +670,7 @@ __global__ __launch_bounds__(DQK) void combine_kernel(const float* __restrict__ 
 
 int choose_splits(int T, int num_heads, int max_cols, int dqk, int rowb) {
   const int units = T * ((num_heads + 63) / 64);  // workgroups without splitting
-  const int min_splits = ((max_cols + kTile - 1) / kTile * kTile + kMaxSiCols - 1) / kMaxSiCols;
-  if (units <= 0 || units >= kNumCUs) return std::max(1, min_splits);
+  if (units <= 0 || units >= kNumCUs) return 1;
   const int tiles = (max_cols + kTile - 1) / kTile;
   int s = (kNumCUs + units - 1) / units;
   s = std::min(s, std::max(1, tiles / 4));
@@ -647,9 +678,7 @@ int choose_splits(int T, int num_heads, int max_cols, int dqk, int rowb) {
   const int64_t row_bytes = (int64_t)max_cols * rowb;
   const int64_t part_bytes = 2LL * 128 * dqk * 4;
   s = (int)std::min<int64_t>(s, std::max<int64_t>(1, row_bytes / part_bytes));
-  // a workgroup stages at most kMaxSiCols index columns in LDS
-  const int need = (tiles * kTile + kMaxSiCols - 1) / kMaxSiCols;
-  return std::max(std::max(1, s), need);
+  return std::max(1, s);
 }
 
 template <int DN, int DR>
@@ -671,11 +700,6 @@ int launch(const uint16_t* q, int T, int H, const KvDesc& s, const KvDesc& c, co
   const int head_groups = (H + 63) / 64;
   const int pairs = T * splits;
   const int blocks = (pairs + 7) / 8 * 8 * head_groups;
-  // the index columns of one split are staged in LDS
-  const int max_tiles = (W + P + kTile - 1) / kTile;
-  const int si_cols = (max_tiles + splits - 1) / splits * kTile;
-  SAD_CHECK(si_cols <= kMaxSiCols, SAD_EUNSUPPORTED,
-            "sparse_mla_decode: %d index columns per workgroup exceed %d", si_cols, kMaxSiCols);
   // one cache for both segments (the usual case): wave-uniform row descriptors
   const bool one = s.pool == c.pool && s.stride == c.stride && s.num_pages == c.num_pages && s.block == c.block;
   if (one)
