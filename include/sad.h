@@ -225,6 +225,8 @@ int gather_dequant_kv(const sad_kv_cache* swa, const sad_kv_cache* comp,
  *   q_bf16  [num_tokens, num_heads, d_nope + d_rope] bf16
  *   out_bf16 [num_tokens, num_heads, d_nope + d_rope] bf16
  *   lse      NULL or fp32 [num_tokens, num_heads]
+ *   sparse_indices [num_tokens, window_size + padded_topk] int32 (may be NULL
+ *            when window_size + padded_topk = 0); sparse_topk_lens [num_tokens]
  *   workspace >= sparse_mla_decode_workspace_size(num_tokens, num_heads,
  *                window_size + padded_topk, d_nope + d_rope)
  * num_heads in {8, 16, ..., 128} (a multiple of 8, <= 128); (d_nope, d_rope)

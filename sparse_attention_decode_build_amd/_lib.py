@@ -240,6 +240,9 @@ def sparse_mla_decode(q, swa: KvCache, comp: KvCache, sparse_indices, sparse_top
     _need(sparse_indices, torch.int32, "sparse_indices", dim=2)
     _need(sparse_topk_lens, torch.int32, "sparse_topk_lens", dim=1)
     T, H, D = q.shape
+    if tuple(sparse_indices.shape) != (T, window_size + padded_topk) or tuple(sparse_topk_lens.shape) != (T,):
+        raise ValueError("sparse_mla_decode: sparse_indices must be [T, window_size + padded_topk] and "
+                         "sparse_topk_lens [T]")
     if attn_sink is not None:
         _need(attn_sink, torch.float32, "attn_sink", dim=1)
     if out is None:

@@ -253,7 +253,57 @@ __device__ inline void dequant_lines(int lane, int wave, const uint8_t (&raw_v)[
   if (ROPE && c < S::ROPE_CH) *reinterpret_cast<uint4*>(kt + kt_off<S::KCH>(key, DN + 8 * c)) = rope;
 }
 
-template <int DN, int DR, bool ONE>
+// This wave's 8 rows of one raw tile held in registers between their LDS reads and the
+// store into a K tile: lane (row 8w + l/8, chunk l%8) keeps 16 fp8 values and their
+// block scale per fp8 line, and one 16-byte chunk of the rope line (zero-row padding
+// for chunks past the rope part).
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+template <int DN, int DR>
+struct RawRows {
+  u32x4_t v[Shape<DN, DR>::FP8_LINES];
+  float sc[Shape<DN, DR>::FP8_LINES];
+  u32x4_t rope;
+};
+
+template <int DN, int DR>
+__device__ inline void raw_load(int lane, int wave, const uint8_t (&raw_v)[Shape<DN, DR>::RAW_V],
+                                const float (&raw_s)[Shape<DN, DR>::RAW_S], RawRows<DN, DR>& r) {
+  using S = Shape<DN, DR>;
+  const int c = lane & 7;
+  const int key = 8 * wave + (lane >> 3);
+  const uint8_t* src = raw_v + wave * S::LINES * 1024 + (lane >> 3) * 128 + 16 * c;
+#pragma unroll
+  for (int j = 0; j < S::FP8_LINES; ++j) {
+    r.v[j] = *reinterpret_cast<const u32x4_t*>(src + j * 1024);
+    r.sc[j] = raw_s[key * 8 + 2 * j + (c >> 2)];  // dims 128j + 16c .. +16: scale block 2j + c/4
+  }
+  r.rope = *reinterpret_cast<const u32x4_t*>(src + S::FP8_LINES * 1024);
+}
+
+template <int DN, int DR>
+__device__ inline void rows_store(int lane, int wave, const u32x4_t (&o)[2 * Shape<DN, DR>::FP8_LINES],
+                                  const u32x4_t& rope, uint16_t (&kt)[kTile * Shape<DN, DR>::KCH * 8]) {
+  using S = Shape<DN, DR>;
+  const int c = lane & 7;
+  const int key = 8 * wave + (lane >> 3);
+  uint16_t* dst = kt + kt_off<S::KCH>(key, 16 * c);
+#pragma unroll
+  for (int j = 0; j < S::FP8_LINES; ++j) {
+    *reinterpret_cast<u32x4_t*>(dst + 128 * j) = o[2 * j];
+    *reinterpret_cast<u32x4_t*>(dst + 128 * j + 8) = o[2 * j + 1];
+  }
+  if (c < S::ROPE_CH) *reinterpret_cast<u32x4_t*>(kt + kt_off<S::KCH>(key, DN + 8 * c)) = rope;
+}
+
+// max(x of this lane, x of lane ^ 32): the two lane halves swapped in one VALU op.
+__device__ inline float max_xor32(float x) {
+  float a = x, b = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
+template <int DN, int DR, bool ONE, bool LSE>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                                amdgpu_waves_per_eu(1, 1)))
 sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads, KvDesc swa,
@@ -267,9 +317,9 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   constexpr int KSMAX = S::KS0;
   constexpr int MTMAX = S::MT0;
   constexpr int NV = S::DMA_PER_TILE;
-  constexpr int JH = S::FP8_LINES / 2;  // fp8 lines dequantized alongside QK; the rest alongside PV
-  // Three raw slots (this wave's rows of tiles i+1, i+2 and i+3 arrive there) and two K
-  // tiles (tile i is computed on while tile i+1 is dequantized into the other).
+  // Three raw slots (this wave's rows of tiles i+2, i+3 and i+4 arrive there) and two K
+  // tiles (tile i, read by PV, and tile i+1, read by QK; tile i+2 is written into the
+  // first one once every wave's PV is done with it).
   __shared__ __align__(16) uint8_t raw_v[kRawSlots][S::RAW_V];
   __shared__ __align__(16) float raw_s[kRawSlots][S::RAW_S];
   __shared__ __align__(16) uint16_t kt[2][kTile * S::KCH * 8];
@@ -300,8 +350,6 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   const int ks_n = dh == 0 ? S::KS0 : S::KS1;  // k-steps of this wave's dims
   const int mt_n = dh == 0 ? S::MT0 : S::MT1;  // m-tiles of this wave's dims
   const int dim0 = dh == 0 ? 0 : 32 * S::MT0;  // first dim of this wave's half
-  // the fp32 sum of the weights is only needed for the log-sum-exp outputs
-  const bool want_lse = lse_out != nullptr || num_splits > 1;
   // the zero row's address, kept opaque so it is not reloaded in the loop
   const uint8_t* zrow = kZeroRow;
   asm volatile("" : "+s"(zrow));
@@ -352,10 +400,16 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   auto load_slots = [&](int tile) __attribute__((always_inline)) -> SlotIds {
     SlotIds ids;
     ids.c0 = tile * kTile + 8 * wave;  // wave-uniform
-    ids.lc = max(0, min(ids.c0, width - 8));
-    const int32_t* p = si_row + ids.lc;
+    if (width >= 8) {
+      ids.lc = max(0, min(ids.c0, width - 8));
+      const int32_t* p = si_row + ids.lc;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ids.v[j] = p[j];  // always inside the row; unused past col_end
+      for (int j = 0; j < 8; ++j) ids.v[j] = p[j];  // always inside the row; unused past col_end
+    } else {  // a row of fewer than 8 ids: only the ids that exist are read
+      ids.lc = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ids.v[j] = j < width ? si_row[j] : -1;
+    }
     return ids;
   };
   auto pick_slot = [&](const SlotIds& ids) __attribute__((always_inline)) -> int {
@@ -376,14 +430,16 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     const int x = __builtin_amdgcn_ds_bpermute(idx << 2, w8);
     return ids.c0 + r < col_end ? x : -1;
   };
-  auto row_slot = [&](int tile) __attribute__((always_inline)) -> int { return pick_slot(load_slots(tile)); };
   auto row_addr_of = [&](int tile, int slot, const uint8_t** vrow, const uint8_t** srow)
       __attribute__((always_inline)) {
     slot_row<ONE>(slot, tile * kTile + 8 * wave + (lane >> 3), window, swa, comp, S::ROWB, S::NSC, zrow, vrow,
                   srow);
   };
-  auto row_addr = [&](int tile, const uint8_t** vrow, const uint8_t** srow) __attribute__((always_inline)) {
-    row_addr_of(tile, row_slot(tile), vrow, srow);
+  auto dma_tile = [&](int tile, int slot_index) __attribute__((always_inline)) -> uint32_t {
+    const uint8_t* vr;
+    const uint8_t* sr;
+    row_addr_of(tile, pick_slot(load_slots(tile)), &vr, &sr);
+    return dma_issue<DN, DR>(lane, wave, raw_v[slot_index], raw_s[slot_index], vr, sr, zrow);
   };
   // Wait until at most `after` tiles' DMAs issued after the awaited one are in flight.
   auto wait_tiles = [&](int after) __attribute__((always_inline)) {
@@ -394,208 +450,271 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     else
       wait_vmem<0>();
   };
-  // Prologue: DMA of tiles 0, 1, 2 (raw slots 0, 1, 2), dequant of tile 0, DMA of tile 3
-  // into slot 0.  Tile j uses raw slot j % 3.  A wave's mask byte of a tile is kept from
-  // its DMA until it writes it beside that tile's K buffer.
-  uint32_t mask_a = 0, mask_b = 0, mask_c = 0;  // this wave's bytes for tiles i+1, i+2, i+3
+  // This wave's partial S^T of one tile (its dims, its head block) from a K buffer.
+  auto qk_partial = [&](int b, f32x16_t& s) __attribute__((always_inline)) {
+    int lane_s = lane;
+    asm volatile("" : "+v"(lane_s));
+    const uint16_t* kbase = kt[b] + kt_off<S::KCH>(lane_s & 31, dim0 + 8 * (lane_s >> 5));
+    bf16x8_t af[KSMAX];
+#pragma unroll
+    for (int kk = 0; kk < KSMAX; ++kk)
+      if (kk < ks_n) af[kk] = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * kk);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KSMAX; ++kk)
+      if (kk < ks_n) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], qf[kk], s, 0, 0, 0);
+  };
+  // Publish a partial S^T for the partner wave (same head block, other dim half), then
+  // set this wave's own copy to -inf at the tile's unattended columns: the partner adds
+  // the raw partial to its own masked copy, so both sums are -inf there.
+  auto publish_partial = [&](f32x16_t& s, int b) __attribute__((always_inline)) {
+    float4* xw = reinterpret_cast<float4*>(xbuf + (wave * 64 + lane) * kXRow);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) xw[q4] = make_float4(s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]);
+    const uint32_t vm = __builtin_amdgcn_readfirstlane(kt_mask[b]);
+    if (vm != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * h + (r & 3);
+        s[r] = ((vm >> key) & 1u) ? s[r] : -INFINITY;
+      }
+    }
+  };
+
+  // Prologue: DMA of tiles 0, 1, 2 (raw slots 0, 1, 2); tiles 0 and 1 dequantized into K
+  // buffers 0 and 1; DMA of tiles 3 and 4 into slots 0 and 1; S^T partial of tile 0.
+  // Tile j uses raw slot j % 3 and K buffer j % 2.  A wave's mask byte of a tile is kept
+  // from its DMA until it writes it beside that tile's K buffer.
+  uint32_t mask_a = 0, mask_b = 0, mask_c = 0;  // this wave's bytes for tiles i+2, i+3, i+4
+  f32x16_t s_nxt;                               // own partial S^T of the next tile (masked)
+  SlotIds pre_ids;                              // slot ids of the wave's rows of the next DMA
   {
-    const uint8_t* vr;
-    const uint8_t* sr;
-    uint32_t m0 = 0;
-    if (tile_begin < tile_end) {
-      row_addr(tile_begin, &vr, &sr);
-      m0 = dma_issue<DN, DR>(lane, wave, raw_v[0], raw_s[0], vr, sr, zrow);
-    }
-    if (tile_begin + 1 < tile_end) {
-      row_addr(tile_begin + 1, &vr, &sr);
-      mask_a = dma_issue<DN, DR>(lane, wave, raw_v[1], raw_s[1], vr, sr, zrow);
-    }
-    if (tile_begin + 2 < tile_end) {
-      row_addr(tile_begin + 2, &vr, &sr);
-      mask_b = dma_issue<DN, DR>(lane, wave, raw_v[2], raw_s[2], vr, sr, zrow);
-    }
+    uint32_t m0 = 0, m1 = 0;
+    if (tile_begin < tile_end) m0 = dma_tile(tile_begin, 0);
+    if (tile_begin + 1 < tile_end) m1 = dma_tile(tile_begin + 1, 1);
+    if (tile_begin + 2 < tile_end) mask_a = dma_tile(tile_begin + 2, 2);
     if (tile_begin < tile_end) {
       wait_tiles(min(2, tile_end - 1 - tile_begin));
       dequant_lines<DN, DR, 0, S::FP8_LINES, true>(lane, wave, raw_v[0], raw_s[0], kt[0]);
       if (lane == 0) reinterpret_cast<uint8_t*>(&kt_mask[0])[wave] = (uint8_t)m0;
     }
-    if (tile_begin + 3 < tile_end) {
-      row_addr(tile_begin + 3, &vr, &sr);
-      mask_c = dma_issue<DN, DR>(lane, wave, raw_v[0], raw_s[0], vr, sr, zrow);
+    if (tile_begin + 1 < tile_end) {
+      wait_tiles(min(1, tile_end - 2 - tile_begin));
+      dequant_lines<DN, DR, 0, S::FP8_LINES, true>(lane, wave, raw_v[1], raw_s[1], kt[1]);
+      if (lane == 0) reinterpret_cast<uint8_t*>(&kt_mask[1])[wave] = (uint8_t)m1;
     }
-  }
-  SlotIds pre_ids = load_slots(tile_begin + 4);  // slot ids of the wave's rows of the next DMA
-
-  // First half of step i (tile i in K buffer b = i%2, tile i+1 in raw slot rs): barrier,
-  // S^T = K Q^T over this wave's dims interleaved with the dequant of the first fp8 lines
-  // of tile i+1, both dim halves summed, masking.  Returns the tile's scaled row maximum
-  // per head (log2 domain).
-  auto front = [&](int tile, int b, int rs, f32x16_t& s) __attribute__((always_inline)) -> float {
-    int lane_s = lane;
-    asm volatile("" : "+v"(lane_s));
-    const int n_s = lane_s & 31;
-    const int h_s = lane_s >> 5;
-    const int nb = b ^ 1;
-    lds_barrier();  // tile i's K buffer complete; tile i-1's PV is done with the other buffer
-    const uint32_t valid_mask = kt_mask[b];
-    // this wave's DMA of tile i+1 landed (tiles i+2 and i+3 may still be in flight)
-    wait_tiles(min(2, tile_end - 2 - tile));
-    // ---- partial S^T = K Q^T over this wave's dims: lane (head n, half h) gets
-    //      keys 8*(r/4) + 4h + r%4, r = 0..15 ...
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-    const uint16_t* kbase = kt[b] + kt_off<S::KCH>(n_s, dim0 + 8 * h_s);
-    bf16x8_t af[KSMAX];
-#pragma unroll
-    for (int kk = 0; kk < KSMAX; ++kk)
-      if (kk < ks_n) af[kk] = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * kk);
-    // ... while the first fp8 lines of tile i+1 are dequantized into the other buffer
-    // (a stale slot past the last tile only writes the unused buffer)
-    dequant_lines<DN, DR, 0, JH, true>(lane_s, wave, raw_v[rs], raw_s[rs], kt[nb]);
-#pragma unroll
-    for (int kk = 0; kk < KSMAX; ++kk)
-      if (kk < ks_n) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], qf[kk], s, 0, 0, 0);
-    // ---- add the partner wave's half (addition commutes: both waves get the same sum)
-    {
-      float4* xw = reinterpret_cast<float4*>(xbuf + (wave * 64 + lane_s) * kXRow);
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) xw[q4] = make_float4(s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]);
-    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // raw reads of slots 0 and 1 done before their refill
+    if (tile_begin + 3 < tile_end) mask_b = dma_tile(tile_begin + 3, 0);
+    if (tile_begin + 4 < tile_end) mask_c = dma_tile(tile_begin + 4, 1);
+    pre_ids = load_slots(tile_begin + 5);
     lds_barrier();
-    {
-      const float4* xr = reinterpret_cast<const float4*>(xbuf + ((wave ^ 1) * 64 + lane_s) * kXRow);
-      float4 o[4];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) o[q4] = xr[q4];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        s[4 * q4] += o[q4].x;
-        s[4 * q4 + 1] += o[q4].y;
-        s[4 * q4 + 2] += o[q4].z;
-        s[4 * q4 + 3] += o[q4].w;
-      }
-    }
-    if (!block_active) return -INFINITY;
-    // ---- masking (skipped for fully attended tiles, the common case) and row maximum
-    if (valid_mask != 0xFFFFFFFFu) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + 4 * h_s + (r & 3);
-        s[r] = ((valid_mask >> key) & 1u) ? s[r] : -INFINITY;
-      }
-    }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-    return fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
-  };
+    qk_partial(0, s_nxt);
+    publish_partial(s_nxt, 0);
+  }
 
-  // Second half: weights relative to the running maximum, O^T += V^T P^T interleaved
-  // with the dequant of the remaining lines of tile i+1, then this wave's DMA of
-  // tile i+4 into the raw slot tile i+1 came from.
-  auto back = [&](int tile, int b, int rs, const f32x16_t& s) __attribute__((always_inline)) {
+  // Phase 1 of step i (after a barrier: K buffer (i+1)%2 holds tile i+1, and every
+  // wave's partial S^T of tile i is published): S^T of tile i+1 on the MFMAs while the
+  // vector ALUs finish tile i: partner partial added, row maximum, lazy rescale
+  // decision, weights.  Returns whether any head of the wave needs its O rescaled.
+  auto phase1 = [&](int b, const f32x16_t& s_own, bf16x8_t (&pb)[2], float& alpha)
+                    __attribute__((always_inline)) -> bool {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
-    const int nb = b ^ 1;
-    if (block_active) {
-      const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-      bf16x8_t pb[2];
-      float pf[16];
+    lds_barrier();
+    const float4* xr = reinterpret_cast<const float4*>(xbuf + ((wave ^ 1) * 64 + lane_s) * kXRow);
+    float4 o[4];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        pf[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -m_use));
-        pf[r + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], scale_log2, -m_use));
-        const bf16x2_t w = __builtin_convertvector(f32x2_t{pf[r], pf[r + 1]}, bf16x2_t);
+    for (int q4 = 0; q4 < 4; ++q4) o[q4] = xr[q4];
+    // ---- S^T of tile i+1 (K buffer b ^ 1); past the last tile it reads a stale buffer
+    //      and the result is unused.  Fragments are read kLdsAhead MFMAs ahead.
+    const uint16_t* kbase = kt[b ^ 1] + kt_off<S::KCH>(lane_s & 31, dim0 + 8 * (lane_s >> 5));
+    bf16x8_t af[KSMAX];
+    static_for<(kLdsAhead < KSMAX ? kLdsAhead : KSMAX)>([&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
+      if (kk < ks_n) af[kk] = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * kk);
+    });
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s_nxt[r] = 0.0f;
+    // ---- tile i, in 12 pieces placed between the MFMAs: both dim halves summed (-inf
+    //      at unattended columns), row maximum, lazy rescale decision, 8 weight pairs
+    float sv[16];
+    float tmax = -INFINITY;
+    float m_use = 0.0f;
+    bool upd = false;
+    auto piece = [&](auto pc) __attribute__((always_inline)) {
+      constexpr int c = decltype(pc)::value;
+      if constexpr (c < 2) {
+#pragma unroll
+        for (int q4 = 2 * c; q4 < 2 * c + 2; ++q4) {
+          sv[4 * q4] = s_own[4 * q4] + o[q4].x;
+          sv[4 * q4 + 1] = s_own[4 * q4 + 1] + o[q4].y;
+          sv[4 * q4 + 2] = s_own[4 * q4 + 2] + o[q4].z;
+          sv[4 * q4 + 3] = s_own[4 * q4 + 3] + o[q4].w;
+        }
+      } else if constexpr (c == 2) {
+        tmax = sv[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sv[r]);
+      } else if constexpr (c == 3) {
+        tmax = max_xor32(tmax) * scale_log2;
+        // the running maximum is kept until a tile exceeds it by 2^slack (also true
+        // when it is still -inf)
+        upd = tmax > m_run + kRescaleSlack;
+        const float m_new = upd ? tmax : m_run;
+        alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // exp2(-inf) = 0
+        m_use = m_new == -INFINITY ? 0.0f : m_new;
+        m_run = m_new;
+        l_run *= alpha;
+        if (LSE) l_lse *= alpha;
+      } else {
+        constexpr int r = 2 * (c - 4);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], scale_log2, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + 1], scale_log2, -m_use));
+        const bf16x2_t w = __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_t);
         pb[r >> 3][r & 7] = w[0];
         pb[r >> 3][(r & 7) + 1] = w[1];
         // O is normalized by the sum of the same rounded weights the PV MFMA multiplies with
         l_run = __builtin_amdgcn_fdot2_f32_bf16(w, bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
+        if (LSE) l_lse += p0 + p1;
       }
-      if (want_lse) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) l_lse += pf[r];
+    };
+    constexpr int kPieces = 12;
+    // MFMA slot of each piece: the first two slots cover the partner partial's read
+    constexpr int kFirst = KSMAX >= kPieces + 2 ? 2 : 0;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<KSMAX>([&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
+      if (kk < ks_n) s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], qf[kk], s_nxt, 0, 0, 0);
+      if constexpr (kk + kLdsAhead < KSMAX) {
+        if (kk + kLdsAhead < ks_n) af[kk + kLdsAhead] = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * (kk + kLdsAhead));
       }
-      // ---- O^T += V^T P^T over this wave's output dims.  The V^T fragment (lane: dim
-      //      32mt + lane%32, 8 keys) comes from the key-major tile through two transposing
-      //      reads: in each 16-lane group, lane (a = i/4, b = i%4) points at key a of the
-      //      4-key set and dims 4b..4b+3, and lane j receives dim j of all 4 keys.
-      const int g = lane_s >> 4;
-      const int ia = (lane_s & 15) >> 2;
-      const int ib = lane_s & 3;
-      const uint16_t* vbase = kt[b] + kt_off<S::KCH>(4 * (g >> 1) + ia, dim0 + 16 * (g & 1) + 4 * ib);
-      s16x4_t vf[MTMAX][4];
-#pragma unroll
-      for (int mt = 0; mt < MTMAX; ++mt)
-        if (mt < mt_n)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)  // keys 8*q4 + 4*(g/2) + ia
-            vf[mt][q4] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)(vbase + kt_off<S::KCH>(8 * q4, 32 * mt)));
-      dequant_lines<DN, DR, JH, S::FP8_LINES, false>(lane_s, wave, raw_v[rs], raw_s[rs], kt[nb]);
-#pragma unroll
-      for (int mt = 0; mt < MTMAX; ++mt) {
-        if (mt < mt_n) {
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8_t a = __builtin_bit_cast(
-                bf16x8_t, __builtin_shufflevector(vf[mt][2 * ks], vf[mt][2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-            acc_o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], acc_o[mt], 0, 0, 0);
-          }
-        }
-      }
-    } else {
-      dequant_lines<DN, DR, JH, S::FP8_LINES, false>(lane_s, wave, raw_v[rs], raw_s[rs], kt[nb]);
-    }
-    // tile i+1 is fully dequantized: publish its mask byte, then reuse its raw slot
-    if (lane_s == 0) reinterpret_cast<uint8_t*>(&kt_mask[nb])[wave] = (uint8_t)mask_a;
-    mask_a = mask_b;
-    mask_b = mask_c;
-    mask_c = 0;
-    if (tile + 4 < tile_end) {
-      const uint8_t* vr;
-      const uint8_t* sr;
-      row_addr_of(tile + 4, pick_slot(pre_ids), &vr, &sr);
-      mask_c = dma_issue<DN, DR>(lane_s, wave, raw_v[rs], raw_s[rs], vr, sr, zrow);
-    }
-    pre_ids = load_slots(tile + 5);
+      static_for<kPieces>([&](auto pc) {
+        constexpr int c = decltype(pc)::value;
+        constexpr int slot = c + kFirst < KSMAX ? c + kFirst : KSMAX - 1;
+        if constexpr (slot == kk) piece(pc);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    return __ballot(upd) != 0ull;
   };
 
-  // Tile loop.  The running maximum is kept until a tile exceeds it by 2^slack; the
-  // (rare) rescale of O then runs outside the inner loop, so the O accumulators stay
-  // in place across the steps of the inner loop.
+  // Phases 2 and 3 of step i: O^T += V^T P^T on tile i while this wave's rows of tile
+  // i+2 are read from their raw slot and dequantized into registers; a barrier (every
+  // wave's PV is done with K buffer b, every partner partial is read); then DMA of tile
+  // i+5 into the raw slot just read, tile i+2 stored into K buffer b, and the partial
+  // S^T of tile i+1 published.
+  auto back = [&](int tile, int b, int rs2, const bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
+    int lane_s = lane;
+    asm volatile("" : "+v"(lane_s));
+    const int slot5 = pick_slot(pre_ids);
+    wait_tiles(min(2, tile_end - 3 - tile));  // this wave's DMA of tile i+2 landed
+    RawRows<DN, DR> rr;
+    raw_load<DN, DR>(lane_s, wave, raw_v[rs2], raw_s[rs2], rr);
+    // ---- O^T += V^T P^T over this wave's output dims.  The V^T fragment (lane: dim
+    //      32mt + lane%32, 8 keys) comes from the key-major tile through two transposing
+    //      reads: in each 16-lane group, lane (a = i/4, b = i%4) points at key a of the
+    //      4-key set and dims 4b..4b+3, and lane j receives dim j of all 4 keys.  Read
+    //      j = 4mt + q4 covers keys 8*q4 + 4*(g/2) + ia of m-tile mt; MFMA i = 2mt + ks
+    //      takes reads 2i and 2i+1, issued kLdsAhead reads earlier.  Between the MFMAs,
+    //      one 4-byte word of the raw rows at a time is dequantized.
+    const int g = lane_s >> 4;
+    const int ia = (lane_s & 15) >> 2;
+    const int ib = lane_s & 3;
+    const uint16_t* vbase = kt[b] + kt_off<S::KCH>(4 * (g >> 1) + ia, dim0 + 16 * (g & 1) + 4 * ib);
+    constexpr int NREAD = 4 * MTMAX;
+    const int nread = 4 * mt_n;
+    s16x4_t vf[NREAD];
+    auto vread = [&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      if (j < nread)
+        vf[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(vbase + kt_off<S::KCH>(8 * (j & 3), 32 * (j >> 2))));
+    };
+    static_for<(kLdsAhead < NREAD ? kLdsAhead : NREAD)>(vread);
+    u32x4_t dq[2 * S::FP8_LINES];
+    constexpr int NWORD = 4 * S::FP8_LINES;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<2 * MTMAX>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int mt = i >> 1;
+      if (mt < mt_n) {
+        const bf16x8_t a = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(vf[2 * i], vf[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc_o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[i & 1], acc_o[mt], 0, 0, 0);
+      }
+      if constexpr (2 * i + kLdsAhead < NREAD) {
+        vread(std::integral_constant<int, 2 * i + kLdsAhead>{});
+        vread(std::integral_constant<int, 2 * i + kLdsAhead + 1>{});
+      }
+      // dequantize words i (and, when there are more words than MFMAs, the rest at the end)
+      static_for<NWORD>([&](auto wc) {
+        constexpr int w = decltype(wc)::value;
+        constexpr int slot = w < 2 * MTMAX ? w : 2 * MTMAX - 1;
+        if constexpr (slot == i) {
+          constexpr int j = w >> 2;
+          constexpr int qw = w & 3;
+          const uint32_t word = rr.v[j][qw];
+          const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false) * rr.sc[j];
+          const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true) * rr.sc[j];
+          dq[2 * j + (qw >> 1)][2 * (qw & 1)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
+          dq[2 * j + (qw >> 1)][2 * (qw & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // the conversion stays beside the MFMAs (not sunk past the barrier)
+#pragma unroll
+    for (int j = 0; j < 2 * S::FP8_LINES; ++j) asm volatile("" :: "v"(dq[j]));
+    lds_barrier();
+    // ---- phase 3
+    uint32_t mask_new = 0;
+    if (tile + 5 < tile_end) {
+      const uint8_t* vr;
+      const uint8_t* sr;
+      row_addr_of(tile + 5, slot5, &vr, &sr);
+      mask_new = dma_issue<DN, DR>(lane_s, wave, raw_v[rs2], raw_s[rs2], vr, sr, zrow);
+    }
+    pre_ids = load_slots(tile + 6);
+    rows_store<DN, DR>(lane_s, wave, dq, rr.rope, kt[b]);  // tile i+2 (stale rows past the last tile)
+    if (lane_s == 0) reinterpret_cast<uint8_t*>(&kt_mask[b])[wave] = (uint8_t)mask_a;
+    mask_a = mask_b;
+    mask_b = mask_c;
+    mask_c = mask_new;
+    publish_partial(s_nxt, b ^ 1);  // tile i+1
+  };
+
+  // Tile loop.  A step whose tile raises some head's running maximum leaves the inner
+  // loop so that the (rare) rescale of O runs outside it and the O accumulators stay in
+  // place across the steps of the inner loop.
   int tile = tile_begin;
-  int rs = 1;  // raw slot of tile i+1
+  int rs2 = 2;  // raw slot of tile i+2
   for (;;) {
-    f32x16_t s;
-    float tmax = -INFINITY;
+    bf16x8_t pb[2];
+    float alpha = 1.0f;
     bool rescale = false;
-    for (; tile < tile_end; ++tile, rs = rs == kRawSlots - 1 ? 0 : rs + 1) {
+    for (; tile < tile_end; ++tile, rs2 = rs2 == kRawSlots - 1 ? 0 : rs2 + 1) {
       const int b = (tile - tile_begin) & 1;
-      tmax = front(tile, b, rs, s);
-      if (__ballot(tmax > m_run + kRescaleSlack) != 0ull) {  // also true when m_run is -inf
+      f32x16_t s_own = s_nxt;
+      if (phase1(b, s_own, pb, alpha)) {
         rescale = true;
         break;
       }
-      back(tile, b, rs, s);
+      back(tile, b, rs2, pb);
     }
     if (!rescale) break;
-    const bool upd = tmax > m_run + kRescaleSlack;
-    const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.0f;  // exp2(-inf) = 0
-    if (upd) m_run = tmax;
-    l_run *= alpha;
-    l_lse *= alpha;
 #pragma unroll
     for (int mt = 0; mt < MTMAX; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
-    back(tile, (tile - tile_begin) & 1, rs, s);
+    back(tile, (tile - tile_begin) & 1, rs2, pb);
     ++tile;
-    rs = rs == kRawSlots - 1 ? 0 : rs + 1;
+    rs2 = rs2 == kRawSlots - 1 ? 0 : rs2 + 1;
   }
 
   if (!block_active || head >= num_heads) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float l_exp = l_lse + __shfl_xor(l_lse, 32, 64);
+  const float l_exp = LSE ? l_lse + __shfl_xor(l_lse, 32, 64) : l_tot;
   // lane (n, h) holds O^T rows (dims) dim0 + 32mt + 8(r/4) + 4h + r%4 for head n
   if (num_splits == 1) {
     const float s2 = sink != nullptr ? sink[head] * kLog2e : -INFINITY;
@@ -702,14 +821,16 @@ int launch(const uint16_t* q, int T, int H, const KvDesc& s, const KvDesc& c, co
   const int blocks = (pairs + 7) / 8 * 8 * head_groups;
   // one cache for both segments (the usual case): wave-uniform row descriptors
   const bool one = s.pool == c.pool && s.stride == c.stride && s.num_pages == c.num_pages && s.block == c.block;
+  // the fp32 sum of the weights is only kept for the log-sum-exp outputs
+  const bool want_lse = lse != nullptr || splits > 1;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kThreads), 0, st, q, T, H, s, c, si, lens, W, P,
+                       scale * kLog2e, sink, out, lse, part_o, part_lse, splits, head_groups);
+  };
   if (one)
-    hipLaunchKernelGGL((sparse_mla_kernel<DN, DR, true>), dim3(blocks), dim3(kThreads), 0, st, q, T, H,
-                       s, c, si, lens, W, P, scale * kLog2e, sink, out, lse, part_o, part_lse, splits,
-                       head_groups);
+    want_lse ? go(sparse_mla_kernel<DN, DR, true, true>) : go(sparse_mla_kernel<DN, DR, true, false>);
   else
-    hipLaunchKernelGGL((sparse_mla_kernel<DN, DR, false>), dim3(blocks), dim3(kThreads), 0, st, q, T, H,
-                       s, c, si, lens, W, P, scale * kLog2e, sink, out, lse, part_o, part_lse, splits,
-                       head_groups);
+    want_lse ? go(sparse_mla_kernel<DN, DR, false, true>) : go(sparse_mla_kernel<DN, DR, false, false>);
   int rc = check_launch("sparse_mla_decode(attention)");
   if (rc != SAD_OK || splits == 1) return rc;
   hipLaunchKernelGGL((combine_kernel<Sh::DQK>), dim3(H, T), dim3(Sh::DQK), 0, st, part_o, part_lse,
@@ -752,8 +873,8 @@ extern "C" int sparse_mla_decode(const uint16_t* q_bf16, int32_t num_tokens, int
             "sparse_mla_decode: num_heads %d unsupported (multiple of 8, <= 128)", num_heads);
   SAD_CHECK(num_tokens < 65536, SAD_EINVAL, "sparse_mla_decode: num_tokens must be < 65536");
   if (num_tokens == 0) return SAD_OK;
-  SAD_CHECK(q_bf16 && sparse_indices && sparse_topk_lens && out_bf16, SAD_EINVAL,
-            "sparse_mla_decode: NULL pointer argument");
+  SAD_CHECK(q_bf16 && (sparse_indices || window_size + padded_topk == 0) && sparse_topk_lens && out_bf16,
+            SAD_EINVAL, "sparse_mla_decode: NULL pointer argument");
   SAD_CHECK(((uintptr_t)q_bf16 & 15) == 0 && ((uintptr_t)out_bf16 & 15) == 0, SAD_EINVAL,
             "sparse_mla_decode: q and out must be 16-byte aligned");
   SAD_CHECK(((uintptr_t)workspace & 15) == 0, SAD_EINVAL,

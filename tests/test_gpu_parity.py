@@ -228,6 +228,36 @@ def test_nothing_attended_gives_zero_and_neg_inf_lse():
     assert torch.all(torch.isneginf(lse)).item()
 
 
+@pytest.mark.parametrize("window,padded", [(3, 2), (0, 5), (7, 0), (0, 0), (5, 64)])
+def test_narrow_index_rows(window, padded):
+    """Index rows narrower than one wave's 8 slot ids (and an empty row)."""
+    wl = _wl("tiny")
+    cfg = wl.cfg
+    view = WL.host_view(wl)
+    T = wl.num_tokens
+    rng = np.random.default_rng(window * 100 + padded)
+    pages = np.array(sorted(view.kv_pages.keys()), np.int64)  # pages the host view holds
+    si = (rng.choice(pages, (T, window + padded)) * cfg.block
+          + rng.integers(0, cfg.block, (T, window + padded))).astype(np.int32)
+    si[rng.random(si.shape) < 0.2] = -1
+    lens = rng.integers(0, padded + 1, T).astype(np.int32)
+    kv, _ = _caches(wl)
+    L = wl.layers[0]
+    lse = torch.empty((T, cfg.heads), dtype=torch.float32, device="cuda")
+    out = sad.sparse_mla_decode(L.q, kv, kv, torch.from_numpy(si).cuda(), torch.from_numpy(lens).cuda(),
+                                window, padded, wl.softmax_scale, lse=lse)
+    torch.cuda.synchronize()
+    o_o, lse_o = O.sparse_mla_decode(view.q, view.kv_pages, view.kv_pages, si, lens, window, cfg.block,
+                                     cfg.block, cfg.d_nope, cfg.d_rope, wl.softmax_scale,
+                                     tokens=list(range(T)))
+    err = np.abs(bf16_to_f64(out) - o_o)
+    assert np.all(err <= np.maximum(ATOL_OUT, _bf16_ulp(o_o)))
+    lg = lse.cpu().numpy()
+    fin = np.isfinite(lse_o)
+    assert np.array_equal(np.isfinite(lg), fin)
+    assert np.max(np.abs(lg[fin] - lse_o[fin]), initial=0.0) <= ATOL_LSE
+
+
 def test_empty_batch_is_a_no_op():
     wl = _wl("tiny")
     cfg = wl.cfg
