@@ -43,8 +43,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;              // attended columns per tile
 constexpr int kRawSlots = 3;           // raw tiles in LDS: the next one (being dequantized) + 2 in flight
-constexpr float kRescaleSlack = 8.0f;
-constexpr int kXRow = 20;  // floats per lane in the S exchange buffer (16 + pad: conflict-free 16-byte access)  // keep the running max until exceeded by 2^8
+constexpr float kRescaleSlack = 8.0f;  // keep the running max until exceeded by 2^8
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -281,21 +280,6 @@ __device__ inline void raw_load(int lane, int wave, const uint8_t (&raw_v)[Shape
   r.rope = *reinterpret_cast<const u32x4_t*>(src + S::FP8_LINES * 1024);
 }
 
-template <int DN, int DR>
-__device__ inline void rows_store(int lane, int wave, const u32x4_t (&o)[2 * Shape<DN, DR>::FP8_LINES],
-                                  const u32x4_t& rope, uint16_t (&kt)[kTile * Shape<DN, DR>::KCH * 8]) {
-  using S = Shape<DN, DR>;
-  const int c = lane & 7;
-  const int key = 8 * wave + (lane >> 3);
-  uint16_t* dst = kt + kt_off<S::KCH>(key, 16 * c);
-#pragma unroll
-  for (int j = 0; j < S::FP8_LINES; ++j) {
-    *reinterpret_cast<u32x4_t*>(dst + 128 * j) = o[2 * j];
-    *reinterpret_cast<u32x4_t*>(dst + 128 * j + 8) = o[2 * j + 1];
-  }
-  if (c < S::ROPE_CH) *reinterpret_cast<u32x4_t*>(kt + kt_off<S::KCH>(key, DN + 8 * c)) = rope;
-}
-
 // max(x of this lane, x of lane ^ 32): the two lane halves swapped in one VALU op.
 __device__ inline float max_xor32(float x) {
   float a = x, b = x;
@@ -324,7 +308,8 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   __shared__ __align__(16) float raw_s[kRawSlots][S::RAW_S];
   __shared__ __align__(16) uint16_t kt[2][kTile * S::KCH * 8];
   __shared__ uint32_t kt_mask[2];  // validity of the tile in each K buffer (bit j: column j)
-  __shared__ __align__(16) float xbuf[kWaves * 64 * kXRow];  // [wave][lane][kXRow]: partial S
+  __shared__ int32_t ids_lds[4][kWaves][64];  // slot ids of tiles j+5 .. j+8 (lanes 0..7 of each wave)
+  __shared__ __align__(16) float xbuf[kWaves * 64 * 16];  // [wave][q4][lane] float4: partial S
 
   // Block -> (token, split, head group): the head groups of one (token, split) are
   // 8 blocks apart, i.e. on the same XCD and dispatched together.
@@ -388,10 +373,11 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   // inside the tile loop)
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  // Slot id of this lane's row (8*wave + lane/8) of a tile: the wave's 8 ids are one
-  // scalar load (counted by lgkmcnt, so the row DMA's vmcnt accounting is untouched);
-  // it is issued one step before the DMA that uses it.  A window past the end of the
-  // sparse_indices row is moved back inside it (the ids of such columns are unused).
+  // Slot id of this lane's row (8*wave + lane/8) of a tile.  For the first five tiles the
+  // wave's 8 ids are one scalar load (a window past the end of the sparse_indices row is
+  // moved back inside it; the ids of such columns are unused).  Later tiles' ids arrive
+  // three steps ahead as a direct global -> LDS load in the row DMAs' vmcnt stream, so
+  // no scalar load is outstanding at a barrier's lgkmcnt wait.
   struct SlotIds {
     int v[8];  // sparse_indices[c .. c+8) of the wave's rows (c = lc, wave-uniform)
     int c0;    // first column of the wave's rows
@@ -415,7 +401,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   auto pick_slot = [&](const SlotIds& ids) __attribute__((always_inline)) -> int {
     // lanes 0..7 take the 8 ids, then every lane fetches its row's id with one shuffle
     int w8 = 0;
-#define SAD_WRITELANE(j) asm("v_writelane_b32 %0, %1, " #j : "+v"(w8) : "s"(ids.v[j]))
+#define SAD_WRITELANE(j) asm("v_writelane_b32 %0, %1, " #j : "+v"(w8) : "s"(__builtin_amdgcn_readfirstlane(ids.v[j])))
     SAD_WRITELANE(0);
     SAD_WRITELANE(1);
     SAD_WRITELANE(2);
@@ -441,6 +427,18 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     row_addr_of(tile, pick_slot(load_slots(tile)), &vr, &sr);
     return dma_issue<DN, DR>(lane, wave, raw_v[slot_index], raw_s[slot_index], vr, sr, zrow);
   };
+  // ids of the wave's 8 rows of a tile -> the LDS ring (lanes 0..7; the others read the
+  // zero row into the unused part of the wave's 256 bytes)
+  auto id_fetch = [&](int tile) __attribute__((always_inline)) {
+    const int col = tile * kTile + 8 * wave + lane;
+    const void* src = lane < 8 && col < width ? static_cast<const void*>(si_row + col) : static_cast<const void*>(zrow);
+    dma_x1(src, __builtin_amdgcn_readfirstlane(lds_addr(ids_lds[(tile - tile_begin) & 3][wave])));
+  };
+  auto slot_of = [&](int tile) __attribute__((always_inline)) -> int {
+    const int r = lane >> 3;
+    const int x = ids_lds[(tile - tile_begin) & 3][wave][r];
+    return tile * kTile + 8 * wave + r < col_end ? x : -1;
+  };
   // Wait until at most `after` tiles' DMAs issued after the awaited one are in flight.
   auto wait_tiles = [&](int after) __attribute__((always_inline)) {
     if (after >= 2)
@@ -450,174 +448,174 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     else
       wait_vmem<0>();
   };
-  // This wave's partial S^T of one tile (its dims, its head block) from a K buffer.
-  auto qk_partial = [&](int b, f32x16_t& s) __attribute__((always_inline)) {
-    int lane_s = lane;
-    asm volatile("" : "+v"(lane_s));
-    const uint16_t* kbase = kt[b] + kt_off<S::KCH>(lane_s & 31, dim0 + 8 * (lane_s >> 5));
-    bf16x8_t af[KSMAX];
-#pragma unroll
-    for (int kk = 0; kk < KSMAX; ++kk)
-      if (kk < ks_n) af[kk] = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * kk);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < KSMAX; ++kk)
-      if (kk < ks_n) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], qf[kk], s, 0, 0, 0);
+  RawRows<DN, DR> rr;             // this wave's raw rows of the tile being dequantized
+  u32x4_t dq[2 * S::FP8_LINES];  // ... and their fp8 part as bf16 (rope part: rr.rope)
+  // One fp8 word of the raw rows (4 e4m3 values) -> 4 bf16 in dq: word w of line j holds
+  // elements 16c + 4(w%4) .. +4 of that line.
+  auto convert_word = [&](auto wc) __attribute__((always_inline)) {
+    constexpr int w = decltype(wc)::value;
+    constexpr int j = w >> 2;
+    constexpr int qw = w & 3;
+    const uint32_t word = rr.v[j][qw];
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false) * rr.sc[j];
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true) * rr.sc[j];
+    dq[2 * j + (qw >> 1)][2 * (qw & 1)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
+    dq[2 * j + (qw >> 1)][2 * (qw & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
   };
-  // Publish a partial S^T for the partner wave (same head block, other dim half), then
-  // set this wave's own copy to -inf at the tile's unattended columns: the partner adds
-  // the raw partial to its own masked copy, so both sums are -inf there.
-  auto publish_partial = [&](f32x16_t& s, int b) __attribute__((always_inline)) {
-    float4* xw = reinterpret_cast<float4*>(xbuf + (wave * 64 + lane) * kXRow);
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) xw[q4] = make_float4(s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]);
-    const uint32_t vm = __builtin_amdgcn_readfirstlane(kt_mask[b]);
-    if (vm != 0xFFFFFFFFu) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + 4 * h + (r & 3);
-        s[r] = ((vm >> key) & 1u) ? s[r] : -INFINITY;
-      }
-    }
-  };
+  constexpr int NWORD = 4 * S::FP8_LINES;
 
-  // Prologue: DMA of tiles 0, 1, 2 (raw slots 0, 1, 2); tiles 0 and 1 dequantized into K
-  // buffers 0 and 1; DMA of tiles 3 and 4 into slots 0 and 1; S^T partial of tile 0.
-  // Tile j uses raw slot j % 3 and K buffer j % 2.  A wave's mask byte of a tile is kept
-  // from its DMA until it writes it beside that tile's K buffer.
-  uint32_t mask_a = 0, mask_b = 0, mask_c = 0;  // this wave's bytes for tiles i+2, i+3, i+4
-  f32x16_t s_nxt;                               // own partial S^T of the next tile (masked)
-  SlotIds pre_ids;                              // slot ids of the wave's rows of the next DMA
+  // Prologue: DMA of tiles 0, 1, 2 (raw slots 0, 1, 2); tile 0 dequantized into K buffer
+  // 0 and tile 1 into registers; DMA of tiles 3 and 4 into slots 0 and 1.  Tile j uses
+  // raw slot j % 3 and K buffer j % 2.  A wave's mask byte of a tile is kept from its DMA
+  // until it writes it beside that tile's K buffer.
+  uint32_t mask_a = 0, mask_b = 0, mask_c = 0, mask_d = 0;  // this wave's bytes for tiles j+1 .. j+4
   {
-    uint32_t m0 = 0, m1 = 0;
+    id_fetch(tile_begin + 5);
+    id_fetch(tile_begin + 6);
+    id_fetch(tile_begin + 7);
+    uint32_t m0 = 0;
     if (tile_begin < tile_end) m0 = dma_tile(tile_begin, 0);
-    if (tile_begin + 1 < tile_end) m1 = dma_tile(tile_begin + 1, 1);
-    if (tile_begin + 2 < tile_end) mask_a = dma_tile(tile_begin + 2, 2);
+    if (tile_begin + 1 < tile_end) mask_a = dma_tile(tile_begin + 1, 1);
+    if (tile_begin + 2 < tile_end) mask_b = dma_tile(tile_begin + 2, 2);
     if (tile_begin < tile_end) {
       wait_tiles(min(2, tile_end - 1 - tile_begin));
       dequant_lines<DN, DR, 0, S::FP8_LINES, true>(lane, wave, raw_v[0], raw_s[0], kt[0]);
       if (lane == 0) reinterpret_cast<uint8_t*>(&kt_mask[0])[wave] = (uint8_t)m0;
     }
-    if (tile_begin + 1 < tile_end) {
-      wait_tiles(min(1, tile_end - 2 - tile_begin));
-      dequant_lines<DN, DR, 0, S::FP8_LINES, true>(lane, wave, raw_v[1], raw_s[1], kt[1]);
-      if (lane == 0) reinterpret_cast<uint8_t*>(&kt_mask[1])[wave] = (uint8_t)m1;
-    }
+    wait_tiles(min(1, tile_end - 2 - tile_begin));
+    raw_load<DN, DR>(lane, wave, raw_v[1], raw_s[1], rr);  // stale past the last tile (unused)
+    static_for<NWORD>(convert_word);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // raw reads of slots 0 and 1 done before their refill
-    if (tile_begin + 3 < tile_end) mask_b = dma_tile(tile_begin + 3, 0);
-    if (tile_begin + 4 < tile_end) mask_c = dma_tile(tile_begin + 4, 1);
-    pre_ids = load_slots(tile_begin + 5);
-    lds_barrier();
-    qk_partial(0, s_nxt);
-    publish_partial(s_nxt, 0);
+    if (tile_begin + 3 < tile_end) mask_c = dma_tile(tile_begin + 3, 0);
+    if (tile_begin + 4 < tile_end) mask_d = dma_tile(tile_begin + 4, 1);
   }
 
-  // Phase 1 of step i (after a barrier: K buffer (i+1)%2 holds tile i+1, and every
-  // wave's partial S^T of tile i is published): S^T of tile i+1 on the MFMAs while the
-  // vector ALUs finish tile i: partner partial added, row maximum, lazy rescale
-  // decision, weights.  Returns whether any head of the wave needs its O rescaled.
-  auto phase1 = [&](int b, const f32x16_t& s_own, bf16x8_t (&pb)[2], float& alpha)
-                    __attribute__((always_inline)) -> bool {
+  // Phase A of step j (after a barrier: K buffer b holds tile j, the other one is free):
+  // S^T = K Q^T over this wave's dims on the MFMAs while this wave's dequantized rows of
+  // tile j+1 (and its mask byte) are stored into the other buffer; the partial S^T is
+  // published for the partner wave (same head block, other dim half); barrier.
+  auto phase_a = [&](int b, f32x16_t& s) __attribute__((always_inline)) {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
     lds_barrier();
-    const float4* xr = reinterpret_cast<const float4*>(xbuf + ((wave ^ 1) * 64 + lane_s) * kXRow);
-    float4 o[4];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) o[q4] = xr[q4];
-    // ---- S^T of tile i+1 (K buffer b ^ 1); past the last tile it reads a stale buffer
-    //      and the result is unused.  Fragments are read kLdsAhead MFMAs ahead.
-    const uint16_t* kbase = kt[b ^ 1] + kt_off<S::KCH>(lane_s & 31, dim0 + 8 * (lane_s >> 5));
+    const uint16_t* kbase = kt[b] + kt_off<S::KCH>(lane_s & 31, dim0 + 8 * (lane_s >> 5));
+    uint16_t* sdst = kt[b ^ 1] + kt_off<S::KCH>(8 * wave + (lane_s >> 3), 16 * (lane_s & 7));
     bf16x8_t af[KSMAX];
     static_for<(kLdsAhead < KSMAX ? kLdsAhead : KSMAX)>([&](auto kc) {
       constexpr int kk = decltype(kc)::value;
       if (kk < ks_n) af[kk] = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * kk);
     });
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s_nxt[r] = 0.0f;
-    // ---- tile i, in 12 pieces placed between the MFMAs: both dim halves summed (-inf
-    //      at unattended columns), row maximum, lazy rescale decision, 8 weight pairs
-    float sv[16];
-    float tmax = -INFINITY;
-    float m_use = 0.0f;
-    bool upd = false;
-    auto piece = [&](auto pc) __attribute__((always_inline)) {
-      constexpr int c = decltype(pc)::value;
-      if constexpr (c < 2) {
-#pragma unroll
-        for (int q4 = 2 * c; q4 < 2 * c + 2; ++q4) {
-          sv[4 * q4] = s_own[4 * q4] + o[q4].x;
-          sv[4 * q4 + 1] = s_own[4 * q4 + 1] + o[q4].y;
-          sv[4 * q4 + 2] = s_own[4 * q4 + 2] + o[q4].z;
-          sv[4 * q4 + 3] = s_own[4 * q4 + 3] + o[q4].w;
-        }
-      } else if constexpr (c == 2) {
-        tmax = sv[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sv[r]);
-      } else if constexpr (c == 3) {
-        tmax = max_xor32(tmax) * scale_log2;
-        // the running maximum is kept until a tile exceeds it by 2^slack (also true
-        // when it is still -inf)
-        upd = tmax > m_run + kRescaleSlack;
-        const float m_new = upd ? tmax : m_run;
-        alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // exp2(-inf) = 0
-        m_use = m_new == -INFINITY ? 0.0f : m_new;
-        m_run = m_new;
-        l_run *= alpha;
-        if (LSE) l_lse *= alpha;
-      } else {
-        constexpr int r = 2 * (c - 4);
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], scale_log2, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + 1], scale_log2, -m_use));
-        const bf16x2_t w = __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_t);
-        pb[r >> 3][r & 7] = w[0];
-        pb[r >> 3][(r & 7) + 1] = w[1];
-        // O is normalized by the sum of the same rounded weights the PV MFMA multiplies with
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(w, bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
-        if (LSE) l_lse += p0 + p1;
-      }
-    };
-    constexpr int kPieces = 12;
-    // MFMA slot of each piece: the first two slots cover the partner partial's read
-    constexpr int kFirst = KSMAX >= kPieces + 2 ? 2 : 0;
+    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+    constexpr int NSTORE = 2 * S::FP8_LINES + 2;  // fp8 chunks, rope chunk, mask byte
+    static_assert(NSTORE <= KSMAX, "one store per MFMA slot");
     __builtin_amdgcn_sched_barrier(0);
     static_for<KSMAX>([&](auto kc) {
       constexpr int kk = decltype(kc)::value;
-      if (kk < ks_n) s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], qf[kk], s_nxt, 0, 0, 0);
+      if (kk < ks_n) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], qf[kk], s, 0, 0, 0);
       if constexpr (kk + kLdsAhead < KSMAX) {
         if (kk + kLdsAhead < ks_n) af[kk + kLdsAhead] = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * (kk + kLdsAhead));
       }
-      static_for<kPieces>([&](auto pc) {
-        constexpr int c = decltype(pc)::value;
-        constexpr int slot = c + kFirst < KSMAX ? c + kFirst : KSMAX - 1;
-        if constexpr (slot == kk) piece(pc);
-      });
+      if constexpr (kk < 2 * S::FP8_LINES) {
+        *reinterpret_cast<u32x4_t*>(sdst + 128 * (kk >> 1) + 8 * (kk & 1)) = dq[kk];
+      } else if constexpr (kk == 2 * S::FP8_LINES) {
+        if ((lane_s & 7) < S::ROPE_CH)
+          *reinterpret_cast<u32x4_t*>(kt[b ^ 1] + kt_off<S::KCH>(8 * wave + (lane_s >> 3), DN + 8 * (lane_s & 7))) = rr.rope;
+      } else if constexpr (kk == 2 * S::FP8_LINES + 1) {
+        if (lane_s == 0) reinterpret_cast<uint8_t*>(&kt_mask[b ^ 1])[wave] = (uint8_t)mask_a;
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
+    mask_a = mask_b;
+    mask_b = mask_c;
+    mask_c = mask_d;
+    float4* xw = reinterpret_cast<float4*>(xbuf) + wave * 4 * 64 + lane_s;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) xw[64 * q4] = make_float4(s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]);
+    lds_barrier();
+  };
+
+  // Phase B: both dim halves summed, unattended columns -inf, row maximum, lazy rescale
+  // decision, weights.  Returns whether any head of the wave needs its O rescaled.
+  auto phase_b = [&](int b, const f32x16_t& s, bf16x8_t (&pb)[2], float& alpha) __attribute__((always_inline)) -> bool {
+    int lane_s = lane;
+    asm volatile("" : "+v"(lane_s));
+    const float4* xr = reinterpret_cast<const float4*>(xbuf) + (wave ^ 1) * 4 * 64 + lane_s;
+    float sv[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 o = xr[64 * q4];
+      sv[4 * q4] = s[4 * q4] + o.x;
+      sv[4 * q4 + 1] = s[4 * q4 + 1] + o.y;
+      sv[4 * q4 + 2] = s[4 * q4 + 2] + o.z;
+      sv[4 * q4 + 3] = s[4 * q4 + 3] + o.w;
+    }
+    const uint32_t vm = __builtin_amdgcn_readfirstlane(kt_mask[b]);
+    if (vm != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 8 * (r >> 2) + 4 * (lane_s >> 5) + (r & 3);
+        sv[r] = ((vm >> key) & 1u) ? sv[r] : -INFINITY;
+      }
+    }
+    float tmax = sv[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sv[r]);
+    tmax = max_xor32(tmax) * scale_log2;
+    // the running maximum is kept until a tile exceeds it by 2^slack (also true when it
+    // is still -inf)
+    const bool upd = tmax > m_run + kRescaleSlack;
+    const float m_new = upd ? tmax : m_run;
+    alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // exp2(-inf) = 0
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    m_run = m_new;
+    l_run *= alpha;
+    if (LSE) l_lse *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], scale_log2, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + 1], scale_log2, -m_use));
+      const bf16x2_t w = __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_t);
+      pb[r >> 3][r & 7] = w[0];
+      pb[r >> 3][(r & 7) + 1] = w[1];
+      // O is normalized by the sum of the same rounded weights the PV MFMA multiplies with
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(w, bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
+      if (LSE) l_lse += p0 + p1;
+    }
     return __ballot(upd) != 0ull;
   };
 
-  // Phases 2 and 3 of step i: O^T += V^T P^T on tile i while this wave's rows of tile
-  // i+2 are read from their raw slot and dequantized into registers; a barrier (every
-  // wave's PV is done with K buffer b, every partner partial is read); then DMA of tile
-  // i+5 into the raw slot just read, tile i+2 stored into K buffer b, and the partial
-  // S^T of tile i+1 published.
-  auto back = [&](int tile, int b, int rs2, const bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
+  // Phase C: O^T += V^T P^T on tile j while this wave's rows of tile j+2 are read from
+  // their raw slot and dequantized into registers, then this wave's DMA of tile j+5 into
+  // that raw slot.
+  auto phase_c = [&](int tile, int b, int rs2, const bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
-    const int slot5 = pick_slot(pre_ids);
-    wait_tiles(min(2, tile_end - 3 - tile));  // this wave's DMA of tile i+2 landed
-    RawRows<DN, DR> rr;
+    // This wave's DMA of tile j+2 and the ids of tile j+5 landed.  From the second
+    // step on, every step issues the DMA of tile j+5 (zero rows past the last tile)
+    // and the id load of tile j+8, so the loads issued after them are counted exactly.
+    {
+      const int k = tile - tile_begin;
+      if (k >= 2) {
+        wait_vmem<2 * NV + 2>();
+      } else if (k == 1) {
+        if (tile_begin + 4 < tile_end)
+          wait_vmem<2 * NV + 1>();
+        else
+          wait_vmem<NV + 1>();
+      } else {
+        wait_tiles(min(2, tile_end - 3 - tile));
+      }
+    }
+    const int slot5 = slot_of(tile + 5);
     raw_load<DN, DR>(lane_s, wave, raw_v[rs2], raw_s[rs2], rr);
-    // ---- O^T += V^T P^T over this wave's output dims.  The V^T fragment (lane: dim
-    //      32mt + lane%32, 8 keys) comes from the key-major tile through two transposing
-    //      reads: in each 16-lane group, lane (a = i/4, b = i%4) points at key a of the
-    //      4-key set and dims 4b..4b+3, and lane j receives dim j of all 4 keys.  Read
-    //      j = 4mt + q4 covers keys 8*q4 + 4*(g/2) + ia of m-tile mt; MFMA i = 2mt + ks
-    //      takes reads 2i and 2i+1, issued kLdsAhead reads earlier.  Between the MFMAs,
-    //      one 4-byte word of the raw rows at a time is dequantized.
+    // ---- The V^T fragment (lane: dim 32mt + lane%32, 8 keys) comes from the key-major
+    //      tile through two transposing reads: in each 16-lane group, lane (a = i/4,
+    //      b = i%4) points at key a of the 4-key set and dims 4b..4b+3, and lane j
+    //      receives dim j of all 4 keys.  Read r = 4mt + q4 covers keys 8*q4 + 4*(g/2) + ia
+    //      of m-tile mt; MFMA i = 2mt + ks takes reads 2i and 2i+1, issued kLdsAhead
+    //      reads earlier.  Between the MFMAs, one 4-byte word of the raw rows at a time
+    //      is dequantized.
     const int g = lane_s >> 4;
     const int ia = (lane_s & 15) >> 2;
     const int ib = lane_s & 3;
@@ -632,8 +630,6 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
             (__attribute__((address_space(3))) s16x4_t*)(vbase + kt_off<S::KCH>(8 * (j & 3), 32 * (j >> 2))));
     };
     static_for<(kLdsAhead < NREAD ? kLdsAhead : NREAD)>(vread);
-    u32x4_t dq[2 * S::FP8_LINES];
-    constexpr int NWORD = 4 * S::FP8_LINES;
     __builtin_amdgcn_sched_barrier(0);
     static_for<2 * MTMAX>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
@@ -647,70 +643,57 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
         vread(std::integral_constant<int, 2 * i + kLdsAhead>{});
         vread(std::integral_constant<int, 2 * i + kLdsAhead + 1>{});
       }
-      // dequantize words i (and, when there are more words than MFMAs, the rest at the end)
+      // word w in slot min(w, last): more words than MFMAs go to the last slot
       static_for<NWORD>([&](auto wc) {
         constexpr int w = decltype(wc)::value;
         constexpr int slot = w < 2 * MTMAX ? w : 2 * MTMAX - 1;
-        if constexpr (slot == i) {
-          constexpr int j = w >> 2;
-          constexpr int qw = w & 3;
-          const uint32_t word = rr.v[j][qw];
-          const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false) * rr.sc[j];
-          const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true) * rr.sc[j];
-          dq[2 * j + (qw >> 1)][2 * (qw & 1)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
-          dq[2 * j + (qw >> 1)][2 * (qw & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
-        }
+        if constexpr (slot == i) convert_word(wc);
       });
       __builtin_amdgcn_sched_barrier(0);
     });
-    // the conversion stays beside the MFMAs (not sunk past the barrier)
+    // every raw word is converted (so this wave's reads of the raw slot are complete)
+    // before the slot is refilled
 #pragma unroll
     for (int j = 0; j < 2 * S::FP8_LINES; ++j) asm volatile("" :: "v"(dq[j]));
-    lds_barrier();
-    // ---- phase 3
-    uint32_t mask_new = 0;
-    if (tile + 5 < tile_end) {
+    {
       const uint8_t* vr;
       const uint8_t* sr;
       row_addr_of(tile + 5, slot5, &vr, &sr);
-      mask_new = dma_issue<DN, DR>(lane_s, wave, raw_v[rs2], raw_s[rs2], vr, sr, zrow);
+      mask_d = dma_issue<DN, DR>(lane_s, wave, raw_v[rs2], raw_s[rs2], vr, sr, zrow);
     }
-    pre_ids = load_slots(tile + 6);
-    rows_store<DN, DR>(lane_s, wave, dq, rr.rope, kt[b]);  // tile i+2 (stale rows past the last tile)
-    if (lane_s == 0) reinterpret_cast<uint8_t*>(&kt_mask[b])[wave] = (uint8_t)mask_a;
-    mask_a = mask_b;
-    mask_b = mask_c;
-    mask_c = mask_new;
-    publish_partial(s_nxt, b ^ 1);  // tile i+1
+    id_fetch(tile + 8);
   };
 
   // Tile loop.  A step whose tile raises some head's running maximum leaves the inner
   // loop so that the (rare) rescale of O runs outside it and the O accumulators stay in
   // place across the steps of the inner loop.
   int tile = tile_begin;
-  int rs2 = 2;  // raw slot of tile i+2
+  int rs2 = 2;  // raw slot of tile j+2
   for (;;) {
+    f32x16_t s;
     bf16x8_t pb[2];
     float alpha = 1.0f;
     bool rescale = false;
     for (; tile < tile_end; ++tile, rs2 = rs2 == kRawSlots - 1 ? 0 : rs2 + 1) {
       const int b = (tile - tile_begin) & 1;
-      f32x16_t s_own = s_nxt;
-      if (phase1(b, s_own, pb, alpha)) {
+      phase_a(b, s);
+      if (phase_b(b, s, pb, alpha)) {
         rescale = true;
         break;
       }
-      back(tile, b, rs2, pb);
+      phase_c(tile, b, rs2, pb);
     }
     if (!rescale) break;
 #pragma unroll
     for (int mt = 0; mt < MTMAX; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
-    back(tile, (tile - tile_begin) & 1, rs2, pb);
+    phase_c(tile, (tile - tile_begin) & 1, rs2, pb);
     ++tile;
     rs2 = rs2 == kRawSlots - 1 ? 0 : rs2 + 1;
   }
+  // the direct-to-LDS loads issued past the last tile land before the workgroup ends
+  wait_vmem<0>();
 
   if (!block_active || head >= num_heads) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
