@@ -535,13 +535,29 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     lds_barrier();
   };
 
+  // Weights of one pair of this lane's S^T values (r, r+1) relative to the running
+  // maximum, into the PV B operand; O is normalized by the sum of the same rounded
+  // weights the PV MFMA multiplies with.
+  float sv[16];       // this lane's S^T values of the current tile (both dim halves)
+  float m_use = 0.0f;  // the maximum the weights are relative to (log2 domain)
+  auto weight_pair = [&](auto rc, bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
+    constexpr int r = decltype(rc)::value;
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], scale_log2, -m_use));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + 1], scale_log2, -m_use));
+    const bf16x2_t w = __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_t);
+    pb[r >> 3][r & 7] = w[0];
+    pb[r >> 3][(r & 7) + 1] = w[1];
+    l_run = __builtin_amdgcn_fdot2_f32_bf16(w, bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
+    if (LSE) l_lse += p0 + p1;
+  };
+
   // Phase B: both dim halves summed, unattended columns -inf, row maximum, lazy rescale
-  // decision, weights.  Returns whether any head of the wave needs its O rescaled.
+  // decision, and the weights of keys 0..15 (pb[0]; keys 16..31 follow between the first
+  // PV MFMAs).  Returns whether any head of the wave needs its O rescaled.
   auto phase_b = [&](int b, const f32x16_t& s, bf16x8_t (&pb)[2], float& alpha) __attribute__((always_inline)) -> bool {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
     const float4* xr = reinterpret_cast<const float4*>(xbuf) + (wave ^ 1) * 4 * 64 + lane_s;
-    float sv[16];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const float4 o = xr[64 * q4];
@@ -567,28 +583,18 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     const bool upd = tmax > m_run + kRescaleSlack;
     const float m_new = upd ? tmax : m_run;
     alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // exp2(-inf) = 0
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    m_use = m_new == -INFINITY ? 0.0f : m_new;
     m_run = m_new;
     l_run *= alpha;
     if (LSE) l_lse *= alpha;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], scale_log2, -m_use));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r + 1], scale_log2, -m_use));
-      const bf16x2_t w = __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_t);
-      pb[r >> 3][r & 7] = w[0];
-      pb[r >> 3][(r & 7) + 1] = w[1];
-      // O is normalized by the sum of the same rounded weights the PV MFMA multiplies with
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(w, bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
-      if (LSE) l_lse += p0 + p1;
-    }
+    static_for<4>([&](auto pc) { weight_pair(std::integral_constant<int, 2 * decltype(pc)::value>{}, pb); });
     return __ballot(upd) != 0ull;
   };
 
   // Phase C: O^T += V^T P^T on tile j while this wave's rows of tile j+2 are read from
   // their raw slot and dequantized into registers, then this wave's DMA of tile j+5 into
   // that raw slot.
-  auto phase_c = [&](int tile, int b, int rs2, const bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
+  auto phase_c = [&](int tile, int b, int rs2, bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
     // This wave's DMA of tile j+2 and the ids of tile j+5 landed.  From the second
@@ -612,33 +618,43 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     // ---- The V^T fragment (lane: dim 32mt + lane%32, 8 keys) comes from the key-major
     //      tile through two transposing reads: in each 16-lane group, lane (a = i/4,
     //      b = i%4) points at key a of the 4-key set and dims 4b..4b+3, and lane j
-    //      receives dim j of all 4 keys.  Read r = 4mt + q4 covers keys 8*q4 + 4*(g/2) + ia
-    //      of m-tile mt; MFMA i = 2mt + ks takes reads 2i and 2i+1, issued kLdsAhead
-    //      reads earlier.  Between the MFMAs, one 4-byte word of the raw rows at a time
-    //      is dequantized.
+    //      receives dim j of all 4 keys.  Read (mt, q4) covers keys 8*q4 + 4*(g/2) + ia of
+    //      m-tile mt.  The MFMAs run keys 0..15 of every m-tile first (ks = 0), then
+    //      keys 16..31: MFMA i = ks*MT + mt takes reads 2i and 2i+1 = (mt, 2ks) and
+    //      (mt, 2ks+1), issued kLdsAhead reads earlier.  Between the MFMAs go the weights
+    //      of keys 16..31 (before the first ks = 1 MFMA) and, one 4-byte word at a time,
+    //      the dequantization of the raw rows.
     const int g = lane_s >> 4;
     const int ia = (lane_s & 15) >> 2;
     const int ib = lane_s & 3;
     const uint16_t* vbase = kt[b] + kt_off<S::KCH>(4 * (g >> 1) + ia, dim0 + 16 * (g & 1) + 4 * ib);
     constexpr int NREAD = 4 * MTMAX;
-    const int nread = 4 * mt_n;
     s16x4_t vf[NREAD];
     auto vread = [&](auto jc) __attribute__((always_inline)) {
       constexpr int j = decltype(jc)::value;
-      if (j < nread)
+      constexpr int i = j >> 1;              // MFMA
+      constexpr int mt = i % MTMAX;
+      constexpr int q4 = 2 * (i / MTMAX) + (j & 1);
+      if (mt < mt_n)
         vf[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4_t*)(vbase + kt_off<S::KCH>(8 * (j & 3), 32 * (j >> 2))));
+            (__attribute__((address_space(3))) s16x4_t*)(vbase + kt_off<S::KCH>(8 * q4, 32 * mt)));
     };
     static_for<(kLdsAhead < NREAD ? kLdsAhead : NREAD)>(vread);
     __builtin_amdgcn_sched_barrier(0);
     static_for<2 * MTMAX>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      constexpr int mt = i >> 1;
+      constexpr int mt = i % MTMAX;
+      constexpr int ks = i / MTMAX;
       if (mt < mt_n) {
         const bf16x8_t a = __builtin_bit_cast(
             bf16x8_t, __builtin_shufflevector(vf[2 * i], vf[2 * i + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-        acc_o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[i & 1], acc_o[mt], 0, 0, 0);
+        acc_o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], acc_o[mt], 0, 0, 0);
       }
+      // pair p of keys 16..31 in slot min(p, MT-1): all before the first ks = 1 MFMA
+      static_for<4>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        if constexpr ((p < MTMAX - 1 ? p : MTMAX - 1) == i) weight_pair(std::integral_constant<int, 8 + 2 * p>{}, pb);
+      });
       if constexpr (2 * i + kLdsAhead < NREAD) {
         vread(std::integral_constant<int, 2 * i + kLdsAhead>{});
         vread(std::integral_constant<int, 2 * i + kLdsAhead + 1>{});
