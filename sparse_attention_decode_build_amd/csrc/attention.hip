@@ -170,16 +170,18 @@ __device__ inline int kt_off(int key, int dim) {
 template <bool ONE>
 __device__ inline void slot_row(int slot, int col, int window, const KvDesc& swa, const KvDesc& comp, int rowb,
                                 int nsc, const uint8_t* zrow, const uint8_t** vals, const uint8_t** scales) {
-  *vals = zrow;
-  *scales = zrow;
   const KvDesc& kv = (ONE || col < window) ? swa : comp;
-  if (slot < 0) return;
-  const int page = slot >> kv.block_shift;
-  if (page >= (int)kv.num_pages) return;  // num_pages * block fits in int32
-  const int ro = slot & (kv.block - 1);
+  // branch-free, so it can sit between other work without splitting it into blocks
+  const bool ok = slot >= 0 && (slot >> kv.block_shift) < (int)kv.num_pages;  // num_pages * block fits in int32
+  const int s2 = ok ? slot : 0;
+  const int page = s2 >> kv.block_shift;
+  const int ro = s2 & (kv.block - 1);
   const uint8_t* pg = kv.pool + (int64_t)page * kv.stride;
-  *vals = pg + ro * rowb;
-  *scales = pg + (kv.block * rowb + ro * 4 * nsc);
+  const uint8_t* v = pg + ro * rowb;
+  const uint8_t* sc = pg + (kv.block * rowb + ro * 4 * nsc);
+  asm("" : "+v"(v), "+v"(sc));  // computed on every lane (no branch around them)
+  *vals = ok ? v : zrow;
+  *scales = ok ? sc : zrow;
 }
 
 // Copy one tile's raw rows HBM -> LDS.  Wave w carries rows 8w..8w+7 of the tile:
@@ -209,6 +211,33 @@ __device__ inline uint32_t dma_issue(int lane, int wave, uint8_t (&raw_v)[Shape<
   // lane 8r carries row 8w + r: gather ballot bits 0, 8, .., 56 into one byte
   const uint64_t b = __ballot(vrow != zrow) & 0x0101010101010101ull;
   return (uint32_t)((b * 0x0102040810204080ull) >> 56);
+}
+
+// Load J of dma_issue on its own (J < LINES: value line J; J == LINES: the scales), so
+// the loads of one tile can be spread between other work in the same order.
+template <int DN, int DR, int J>
+__device__ inline void dma_one(int lane, int wave, uint8_t (&raw_v)[Shape<DN, DR>::RAW_V],
+                               float (&raw_s)[Shape<DN, DR>::RAW_S], const uint8_t* vrow, const uint8_t* srow,
+                               const uint8_t* zrow) {
+  using S = Shape<DN, DR>;
+  const int c = lane & 7;
+  if constexpr (J < S::LINES) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(raw_v) + wave * S::LINES * 1024 + J * 1024);
+    if constexpr (8 * J + 8 <= S::CPR)
+      dma_x4_off<128 * J>(vrow + 16 * c, dst);
+    else
+      dma_x4_off<0>(8 * J + c < S::CPR ? vrow + 16 * c + 128 * J : zrow, dst);
+  } else {
+    dma_x1(c < S::NSC ? srow + 4 * c : zrow, __builtin_amdgcn_readfirstlane(lds_addr(raw_s) + wave * 256));
+  }
+}
+__device__ inline uint32_t row_mask(const uint8_t* vrow, const uint8_t* zrow) {
+  const uint64_t b = __ballot(vrow != zrow) & 0x0101010101010101ull;
+  return (uint32_t)((b * 0x0102040810204080ull) >> 56);
+}
+template <int N>
+__device__ inline void wait_lgkm() {
+  asm volatile("s_waitcnt lgkmcnt(%0)" :: "n"(N) : "memory");
 }
 
 // Dequantize fp8 lines [J0, J1) (and the rope line when ROPE) of this wave's 8 rows of
@@ -630,6 +659,13 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     const uint16_t* vbase = kt[b] + kt_off<S::KCH>(4 * (g >> 1) + ia, dim0 + 16 * (g & 1) + 4 * ib);
     constexpr int NREAD = 4 * MTMAX;
     s16x4_t vf[NREAD];
+    // slots of the DMA loads (the last NV slots but one), and the V^T reads issued after
+    // the raw reads by then when both dim halves have the same m-tiles (else 0: wait all)
+    constexpr int DSLOT0 = 2 * MTMAX - 1 - NV > 0 ? 2 * MTMAX - 1 - NV : 1;
+    constexpr int V_BEFORE = kLdsAhead + 2 * DSLOT0 < NREAD ? kLdsAhead + 2 * DSLOT0 : NREAD;
+    constexpr int RAW_AFTER = S::MT0 == S::MT1 ? (V_BEFORE < 15 ? V_BEFORE : 15) : 0;
+    const uint8_t* vr5 = zrow;
+    const uint8_t* sr5 = zrow;
     auto vread = [&](auto jc) __attribute__((always_inline)) {
       constexpr int j = decltype(jc)::value;
       constexpr int i = j >> 1;              // MFMA
@@ -665,18 +701,20 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
         constexpr int slot = w < 2 * MTMAX ? w : 2 * MTMAX - 1;
         if constexpr (slot == i) convert_word(wc);
       });
+      // the DMA of tile j+5 into the raw slot just read, one load per slot, so a stall
+      // of the memory pipeline overlaps the MFMAs already issued
+      if constexpr (i == DSLOT0 - 1) {
+        row_addr_of(tile + 5, slot5, &vr5, &sr5);
+        mask_d = row_mask(vr5, zrow);
+      }
+      if constexpr (i >= DSLOT0 && i < DSLOT0 + NV) {
+        // this wave's reads of the raw slot are complete before its refill: at most
+        // RAW_AFTER LDS reads issued after them are still outstanding
+        if constexpr (i == DSLOT0) wait_lgkm<RAW_AFTER>();
+        dma_one<DN, DR, i - DSLOT0>(lane_s, wave, raw_v[rs2], raw_s[rs2], vr5, sr5, zrow);
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
-    // every raw word is converted (so this wave's reads of the raw slot are complete)
-    // before the slot is refilled
-#pragma unroll
-    for (int j = 0; j < 2 * S::FP8_LINES; ++j) asm volatile("" :: "v"(dq[j]));
-    {
-      const uint8_t* vr;
-      const uint8_t* sr;
-      row_addr_of(tile + 5, slot5, &vr, &sr);
-      mask_d = dma_issue<DN, DR>(lane_s, wave, raw_v[rs2], raw_s[rs2], vr, sr, zrow);
-    }
     id_fetch(tile + 8);
   };
 
