@@ -14,7 +14,7 @@
 //   * the workgroups of one token's head groups are numbered 8 apart so they run on the
 //     same XCD at the same time and the second read of each row hits that XCD's L2;
 //   * columns are taken 32 at a time (a tile); wave w carries rows 8w..8w+7 of every
-//     tile.  The raw cache bytes of tiles j+2 and j+3 are in flight HBM -> LDS as direct
+//     tile.  The raw cache bytes of tiles j+2 .. j+4 are in flight HBM -> LDS as direct
 //     global-to-LDS loads of whole 128-byte lines (no VGPRs) while tile j is computed,
 //     and the slot ids of a tile arrive the same way three steps before its rows;
 //   * step j: (A) S^T = K Q^T on tile j's K tile while each wave stores its rows of
@@ -23,8 +23,8 @@
 //     halves of S^T summed, row maximum, weights.  (C) O^T += V^T P^T, with V^T read
 //     from the same K tile through ds_read_b64_tr_b16 (no transposed copy), while the
 //     wave's rows of tile j+2 are read from LDS and dequantized into registers (fp32
-//     multiply by the row's block scale, bf16 rounding) and the loads of tile j+4 are
-//     issued; barrier.  Each MFMA slot's companions are fixed in source order;
+//     multiply by the row's block scale, bf16 rounding) and the loads of tile j+5 are
+//     issued between them; barrier.  Each MFMA slot's companions are fixed in source order;
 //   * S^T puts one head per lane, so the online softmax needs only a swap with lane^32,
 //     and the probabilities already sit in the B-operand layout of the PV MFMA;
 //   * splits of one token write (o / l, log2-sum-exp) partials that a second kernel
@@ -45,7 +45,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;              // attended columns per tile
-constexpr int kRawSlots = 2;           // raw tiles in LDS: the one being dequantized + the next in flight
+constexpr int kRawSlots = 3;           // raw tiles in LDS: the one being dequantized + two in flight
 constexpr float kRescaleSlack = 8.0f;  // keep the running max until exceeded by 2^8
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -340,7 +340,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   __shared__ __align__(16) float raw_s[kRawSlots][S::RAW_S];
   __shared__ __align__(16) uint16_t kt[2][kTile * S::KCH * 8];
   __shared__ uint32_t kt_mask[2];  // validity of the tile in each K buffer (bit j: column j)
-  __shared__ int32_t ids_lds[4][kWaves][64];  // slot ids of tiles j+4 .. j+7 (lanes 0..7 of each wave)
+  __shared__ int32_t ids_lds[4][kWaves][64];  // slot ids of tiles j+5 .. j+8 (lanes 0..7 of each wave)
   __shared__ __align__(16) float xbuf[kWaves * 64 * 16];  // [wave][q4][lane] float4: partial S
 
   // Block -> (token, split, head group): the head groups of one (token, split) are
@@ -496,29 +496,30 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   };
   constexpr int NWORD = 4 * S::FP8_LINES;
 
-  // Prologue: DMA of tiles 0, 1 (raw slots 0, 1); tile 0 dequantized into K buffer 0 and
-  // tile 1 into registers; DMA of tiles 2 and 3 into slots 0 and 1.  Tile j uses
+  // Prologue: DMA of tiles 0, 1, 2 (raw slots 0, 1, 2); tile 0 dequantized into K buffer
+  // 0 and tile 1 into registers; DMA of tiles 3 and 4 into slots 0 and 1.  Tile j uses
   // raw slot j % 3 and K buffer j % 2.  A wave's mask byte of a tile is kept from its DMA
   // until it writes it beside that tile's K buffer.
-  uint32_t mask_a = 0, mask_b = 0, mask_c = 0;  // this wave's bytes for tiles j+1 .. j+3
+  uint32_t mask_a = 0, mask_b = 0, mask_c = 0, mask_d = 0;  // this wave's bytes for tiles j+1 .. j+4
   {
-    id_fetch(tile_begin + 4);
     id_fetch(tile_begin + 5);
     id_fetch(tile_begin + 6);
+    id_fetch(tile_begin + 7);
     uint32_t m0 = 0;
     if (tile_begin < tile_end) m0 = dma_tile(tile_begin, 0);
     if (tile_begin + 1 < tile_end) mask_a = dma_tile(tile_begin + 1, 1);
+    if (tile_begin + 2 < tile_end) mask_b = dma_tile(tile_begin + 2, 2);
     if (tile_begin < tile_end) {
-      wait_tiles(min(1, tile_end - 1 - tile_begin));
+      wait_tiles(min(2, tile_end - 1 - tile_begin));
       dequant_lines<DN, DR, 0, S::FP8_LINES, true>(lane, wave, raw_v[0], raw_s[0], kt[0]);
       if (lane == 0) reinterpret_cast<uint8_t*>(&kt_mask[0])[wave] = (uint8_t)m0;
     }
-    wait_tiles(0);
+    wait_tiles(min(1, tile_end - 2 - tile_begin));
     raw_load<DN, DR>(lane, wave, raw_v[1], raw_s[1], rr);  // stale past the last tile (unused)
     static_for<NWORD>(convert_word);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // raw reads of slots 0 and 1 done before their refill
-    if (tile_begin + 2 < tile_end) mask_b = dma_tile(tile_begin + 2, 0);
-    if (tile_begin + 3 < tile_end) mask_c = dma_tile(tile_begin + 3, 1);
+    if (tile_begin + 3 < tile_end) mask_c = dma_tile(tile_begin + 3, 0);
+    if (tile_begin + 4 < tile_end) mask_d = dma_tile(tile_begin + 4, 1);
   }
 
   // Phase A of step j (after a barrier: K buffer b holds tile j, the other one is free):
@@ -559,6 +560,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     });
     mask_a = mask_b;
     mask_b = mask_c;
+    mask_c = mask_d;
     float4* xw = reinterpret_cast<float4*>(xbuf) + wave * 4 * 64 + lane_s;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) xw[64 * q4] = make_float4(s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]);
@@ -622,27 +624,28 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   };
 
   // Phase C: O^T += V^T P^T on tile j while this wave's rows of tile j+2 are read from
-  // their raw slot and dequantized into registers, then this wave's DMA of tile j+4 into
+  // their raw slot and dequantized into registers, then this wave's DMA of tile j+5 into
   // that raw slot.
   auto phase_c = [&](int tile, int b, int rs2, bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
-    // This wave's DMA of tile j+2 and the ids of tile j+4 landed.  From the second
-    // step on, every step issues the DMA of tile j+4 (zero rows past the last tile)
-    // and the id load of tile j+7, so the loads issued after them are counted exactly.
-    // (Two tiles of rows in flight: a third one left the memory pipeline so full that
-    // issuing the loads stalled the wave for longer than the deeper lookahead saved.)
+    // This wave's DMA of tile j+2 and the ids of tile j+5 landed.  From the second
+    // step on, every step issues the DMA of tile j+5 (zero rows past the last tile)
+    // and the id load of tile j+8, so the loads issued after them are counted exactly.
     {
       const int k = tile - tile_begin;
       if (k >= 2) {
-        wait_vmem<NV + 2>();
+        wait_vmem<2 * NV + 2>();
       } else if (k == 1) {
-        wait_vmem<NV + 1>();
+        if (tile_begin + 4 < tile_end)
+          wait_vmem<2 * NV + 1>();
+        else
+          wait_vmem<NV + 1>();
       } else {
-        wait_tiles(min(1, tile_end - 3 - tile));
+        wait_tiles(min(2, tile_end - 3 - tile));
       }
     }
-    const int slot4 = slot_of(tile + 4);
+    const int slot5 = slot_of(tile + 5);
     raw_load<DN, DR>(lane_s, wave, raw_v[rs2], raw_s[rs2], rr);
     // ---- The V^T fragment (lane: dim 32mt + lane%32, 8 keys) comes from the key-major
     //      tile through two transposing reads: in each 16-lane group, lane (a = i/4,
@@ -659,13 +662,17 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     const uint16_t* vbase = kt[b] + kt_off<S::KCH>(4 * (g >> 1) + ia, dim0 + 16 * (g & 1) + 4 * ib);
     constexpr int NREAD = 4 * MTMAX;
     s16x4_t vf[NREAD];
-    // slots of the DMA loads (the last NV slots but one), and the V^T reads issued after
-    // the raw reads by then when both dim halves have the same m-tiles (else 0: wait all)
-    constexpr int DSLOT0 = 2 * MTMAX - 1 - NV > 0 ? 2 * MTMAX - 1 - NV : 1;
+    // slots of the DMA loads: every second slot, ending with the last one (a burst of
+    // loads in consecutive slots stalled on a full memory pipeline), and the V^T reads
+    // issued after the raw reads by then when both dim halves have the same m-tiles
+    // (else 0: wait for all)
+    constexpr int DSTEP = 2 * MTMAX - 1 - 2 * (NV - 1) >= 1 ? 2 : 1;
+    constexpr int DSLOT0 = 2 * MTMAX - 1 - DSTEP * (NV - 1) >= 1 ? 2 * MTMAX - 1 - DSTEP * (NV - 1) : 1;
+    static_assert(DSLOT0 + DSTEP * (NV - 1) < 2 * MTMAX, "every DMA load has a slot");
     constexpr int V_BEFORE = kLdsAhead + 2 * DSLOT0 < NREAD ? kLdsAhead + 2 * DSLOT0 : NREAD;
     constexpr int RAW_AFTER = S::MT0 == S::MT1 ? (V_BEFORE < 15 ? V_BEFORE : 15) : 0;
-    const uint8_t* vr4 = zrow;
-    const uint8_t* sr4 = zrow;
+    const uint8_t* vr5 = zrow;
+    const uint8_t* sr5 = zrow;
     auto vread = [&](auto jc) __attribute__((always_inline)) {
       constexpr int j = decltype(jc)::value;
       constexpr int i = j >> 1;              // MFMA
@@ -701,28 +708,28 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
         constexpr int slot = w < 2 * MTMAX ? w : 2 * MTMAX - 1;
         if constexpr (slot == i) convert_word(wc);
       });
-      // the DMA of tile j+4 into the raw slot just read, one load per slot, so a stall
+      // the DMA of tile j+5 into the raw slot just read, one load per second slot, so a stall
       // of the memory pipeline overlaps the MFMAs already issued
       if constexpr (i == DSLOT0 - 1) {
-        row_addr_of(tile + 4, slot4, &vr4, &sr4);
-        mask_c = row_mask(vr4, zrow);
+        row_addr_of(tile + 5, slot5, &vr5, &sr5);
+        mask_d = row_mask(vr5, zrow);
       }
-      if constexpr (i >= DSLOT0 && i < DSLOT0 + NV) {
+      if constexpr (i >= DSLOT0 && (i - DSLOT0) % DSTEP == 0 && (i - DSLOT0) / DSTEP < NV) {
         // this wave's reads of the raw slot are complete before its refill: at most
         // RAW_AFTER LDS reads issued after them are still outstanding
         if constexpr (i == DSLOT0) wait_lgkm<RAW_AFTER>();
-        dma_one<DN, DR, i - DSLOT0>(lane_s, wave, raw_v[rs2], raw_s[rs2], vr4, sr4, zrow);
+        dma_one<DN, DR, (i - DSLOT0) / DSTEP>(lane_s, wave, raw_v[rs2], raw_s[rs2], vr5, sr5, zrow);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
-    id_fetch(tile + 7);
+    id_fetch(tile + 8);
   };
 
   // Tile loop.  A step whose tile raises some head's running maximum leaves the inner
   // loop so that the (rare) rescale of O runs outside it and the O accumulators stay in
   // place across the steps of the inner loop.
   int tile = tile_begin;
-  int rs2 = 0;  // raw slot of tile j+2
+  int rs2 = 2;  // raw slot of tile j+2
   for (;;) {
     f32x16_t s;
     bf16x8_t pb[2];
