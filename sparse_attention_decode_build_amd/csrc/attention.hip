@@ -583,10 +583,61 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     if (LSE) l_lse += p0 + p1;
   };
 
+  // ---- Phase C's LDS reads, issued during phase B (which leaves LDS idle otherwise).
+  //      The V^T fragment (lane: dim 32mt + lane%32, 8 keys) comes from the key-major
+  //      tile through two transposing reads: in each 16-lane group, lane (a = i/4,
+  //      b = i%4) points at key a of the 4-key set and dims 4b..4b+3, and lane j
+  //      receives dim j of all 4 keys.  Read (mt, q4) covers keys 8*q4 + 4*(g/2) + ia of
+  //      m-tile mt.  The PV MFMAs run keys 0..15 of every m-tile first (ks = 0), then
+  //      keys 16..31: MFMA i = ks*MT + mt takes reads 2i and 2i+1 = (mt, 2ks) and
+  //      (mt, 2ks+1), issued kLdsAhead reads earlier.
+  constexpr int NREAD = 4 * MTMAX;
+  s16x4_t vf[NREAD];
+  int slot5 = -1;  // slot id of this lane's row of tile j+5
+  auto v_base = [&](int b, int lane_s) __attribute__((always_inline)) -> const uint16_t* {
+    const int g = lane_s >> 4;
+    const int ia = (lane_s & 15) >> 2;
+    const int ib = lane_s & 3;
+    return kt[b] + kt_off<S::KCH>(4 * (g >> 1) + ia, dim0 + 16 * (g & 1) + 4 * ib);
+  };
+  auto vread = [&](auto jc, const uint16_t* vbase) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int i = j >> 1;  // MFMA
+    constexpr int mt = i % MTMAX;
+    constexpr int q4 = 2 * (i / MTMAX) + (j & 1);
+    if (mt < mt_n)
+      vf[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(vbase + kt_off<S::KCH>(8 * q4, 32 * mt)));
+  };
+  // this wave's DMA of tile j+2 and the ids of tile j+5 landed, then the raw rows of
+  // tile j+2, the slot ids of tile j+5 and the first V^T fragments of tile j
+  auto c_reads = [&](int tile, int b, int rs2, int lane_s) __attribute__((always_inline)) {
+    // From the second step on, every step issues the DMA of tile j+5 (zero rows past the
+    // last tile) and the id load of tile j+8, so the loads issued after them are
+    // counted exactly.
+    const int k = tile - tile_begin;
+    if (k >= 2) {
+      wait_vmem<2 * NV + 2>();
+    } else if (k == 1) {
+      if (tile_begin + 4 < tile_end)
+        wait_vmem<2 * NV + 1>();
+      else
+        wait_vmem<NV + 1>();
+    } else {
+      wait_tiles(min(2, tile_end - 3 - tile));
+    }
+    slot5 = slot_of(tile + 5);
+    raw_load<DN, DR>(lane_s, wave, raw_v[rs2], raw_s[rs2], rr);
+    const uint16_t* vbase = v_base(b, lane_s);
+    static_for<(kLdsAhead < NREAD ? kLdsAhead : NREAD)>([&](auto jc) { vread(jc, vbase); });
+  };
+
   // Phase B: both dim halves summed, unattended columns -inf, row maximum, lazy rescale
-  // decision, and the weights of keys 0..15 (pb[0]; keys 16..31 follow between the first
-  // PV MFMAs).  Returns whether any head of the wave needs its O rescaled.
-  auto phase_b = [&](int b, const f32x16_t& s, bf16x8_t (&pb)[2], float& alpha) __attribute__((always_inline)) -> bool {
+  // decision, phase C's first LDS reads, and the weights of keys 0..15 (pb[0]; keys
+  // 16..31 follow between the first PV MFMAs).  Returns whether any head of the wave
+  // needs its O rescaled.
+  auto phase_b = [&](int tile, int b, int rs2, const f32x16_t& s, bf16x8_t (&pb)[2], float& alpha)
+                     __attribute__((always_inline)) -> bool {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
     const float4* xr = reinterpret_cast<const float4*>(xbuf) + (wave ^ 1) * 4 * 64 + lane_s;
@@ -619,49 +670,21 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     m_run = m_new;
     l_run *= alpha;
     if (LSE) l_lse *= alpha;
+    c_reads(tile, b, rs2, lane_s);
     static_for<4>([&](auto pc) { weight_pair(std::integral_constant<int, 2 * decltype(pc)::value>{}, pb); });
     return __ballot(upd) != 0ull;
   };
 
-  // Phase C: O^T += V^T P^T on tile j while this wave's rows of tile j+2 are read from
-  // their raw slot and dequantized into registers, then this wave's DMA of tile j+5 into
-  // that raw slot.
+  // Phase C: O^T += V^T P^T on tile j while this wave's rows of tile j+2 (read from their
+  // raw slot in phase B) are dequantized into registers and this wave's DMA of tile j+5
+  // into that raw slot is issued.
   auto phase_c = [&](int tile, int b, int rs2, bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
-    // This wave's DMA of tile j+2 and the ids of tile j+5 landed.  From the second
-    // step on, every step issues the DMA of tile j+5 (zero rows past the last tile)
-    // and the id load of tile j+8, so the loads issued after them are counted exactly.
-    {
-      const int k = tile - tile_begin;
-      if (k >= 2) {
-        wait_vmem<2 * NV + 2>();
-      } else if (k == 1) {
-        if (tile_begin + 4 < tile_end)
-          wait_vmem<2 * NV + 1>();
-        else
-          wait_vmem<NV + 1>();
-      } else {
-        wait_tiles(min(2, tile_end - 3 - tile));
-      }
-    }
-    const int slot5 = slot_of(tile + 5);
-    raw_load<DN, DR>(lane_s, wave, raw_v[rs2], raw_s[rs2], rr);
-    // ---- The V^T fragment (lane: dim 32mt + lane%32, 8 keys) comes from the key-major
-    //      tile through two transposing reads: in each 16-lane group, lane (a = i/4,
-    //      b = i%4) points at key a of the 4-key set and dims 4b..4b+3, and lane j
-    //      receives dim j of all 4 keys.  Read (mt, q4) covers keys 8*q4 + 4*(g/2) + ia of
-    //      m-tile mt.  The MFMAs run keys 0..15 of every m-tile first (ks = 0), then
-    //      keys 16..31: MFMA i = ks*MT + mt takes reads 2i and 2i+1 = (mt, 2ks) and
-    //      (mt, 2ks+1), issued kLdsAhead reads earlier.  Between the MFMAs go the weights
-    //      of keys 16..31 (before the first ks = 1 MFMA) and, one 4-byte word at a time,
-    //      the dequantization of the raw rows.
-    const int g = lane_s >> 4;
-    const int ia = (lane_s & 15) >> 2;
-    const int ib = lane_s & 3;
-    const uint16_t* vbase = kt[b] + kt_off<S::KCH>(4 * (g >> 1) + ia, dim0 + 16 * (g & 1) + 4 * ib);
-    constexpr int NREAD = 4 * MTMAX;
-    s16x4_t vf[NREAD];
+    // Between the PV MFMAs go the weights of keys 16..31 (before the first ks = 1
+    // MFMA), the V^T reads kLdsAhead ahead, one 4-byte word of the raw rows at a time
+    // dequantized, and the DMA loads of tile j+5.
+    const uint16_t* vbase = v_base(b, lane_s);
     // slots of the DMA loads: every second slot, ending with the last one (a burst of
     // loads in consecutive slots stalled on a full memory pipeline), and the V^T reads
     // issued after the raw reads by then when both dim halves have the same m-tiles
@@ -673,16 +696,6 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     constexpr int RAW_AFTER = S::MT0 == S::MT1 ? (V_BEFORE < 15 ? V_BEFORE : 15) : 0;
     const uint8_t* vr5 = zrow;
     const uint8_t* sr5 = zrow;
-    auto vread = [&](auto jc) __attribute__((always_inline)) {
-      constexpr int j = decltype(jc)::value;
-      constexpr int i = j >> 1;              // MFMA
-      constexpr int mt = i % MTMAX;
-      constexpr int q4 = 2 * (i / MTMAX) + (j & 1);
-      if (mt < mt_n)
-        vf[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4_t*)(vbase + kt_off<S::KCH>(8 * q4, 32 * mt)));
-    };
-    static_for<(kLdsAhead < NREAD ? kLdsAhead : NREAD)>(vread);
     __builtin_amdgcn_sched_barrier(0);
     static_for<2 * MTMAX>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
@@ -699,8 +712,8 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
         if constexpr ((p < MTMAX - 1 ? p : MTMAX - 1) == i) weight_pair(std::integral_constant<int, 8 + 2 * p>{}, pb);
       });
       if constexpr (2 * i + kLdsAhead < NREAD) {
-        vread(std::integral_constant<int, 2 * i + kLdsAhead>{});
-        vread(std::integral_constant<int, 2 * i + kLdsAhead + 1>{});
+        vread(std::integral_constant<int, 2 * i + kLdsAhead>{}, vbase);
+        vread(std::integral_constant<int, 2 * i + kLdsAhead + 1>{}, vbase);
       }
       // word w in slot min(w, last): more words than MFMAs go to the last slot
       static_for<NWORD>([&](auto wc) {
@@ -738,7 +751,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     for (; tile < tile_end; ++tile, rs2 = rs2 == kRawSlots - 1 ? 0 : rs2 + 1) {
       const int b = (tile - tile_begin) & 1;
       phase_a(b, s);
-      if (phase_b(b, s, pb, alpha)) {
+      if (phase_b(tile, b, rs2, s, pb, alpha)) {
         rescale = true;
         break;
       }
