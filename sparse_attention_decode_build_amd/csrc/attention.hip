@@ -17,14 +17,15 @@
 //     tile.  The raw cache bytes of tiles j+2 .. j+4 are in flight HBM -> LDS as direct
 //     global-to-LDS loads of whole 128-byte lines (no VGPRs) while tile j is computed,
 //     and the slot ids of a tile arrive the same way three steps before its rows;
-//   * step j: (A) S^T = K Q^T on tile j's K tile while each wave stores its rows of
-//     tile j+1, dequantized in registers during the previous step, into the other K
-//     buffer (key-major, rows padded by one 16-byte chunk); barrier.  (B) both dim
-//     halves of S^T summed, row maximum, weights.  (C) O^T += V^T P^T, with V^T read
-//     from the same K tile through ds_read_b64_tr_b16 (no transposed copy), while the
-//     wave's rows of tile j+2 are read from LDS and dequantized into registers (fp32
-//     multiply by the row's block scale, bf16 rounding) and the loads of tile j+5 are
-//     issued between them; barrier.  Each MFMA slot's companions are fixed in source order;
+//   * step j: (A) S^T = K Q^T on tile j's K tile; barrier.  (B) each wave stores its
+//     rows of tile j+1, dequantized in registers during the previous step, into the
+//     other K buffer (key-major, rows padded by one 16-byte chunk); both dim halves of
+//     S^T summed, row maximum, weights; phase C's first LDS reads issued.  (C) O^T +=
+//     V^T P^T, with V^T read from the same K tile through ds_read_b64_tr_b16 (no
+//     transposed copy), while the wave's rows of tile j+2 (read from LDS in B) are
+//     dequantized into registers (fp32 multiply by the row's block scale, bf16
+//     rounding) and the loads of tile j+5 are issued between the MFMAs; barrier.  Each
+//     MFMA slot's companions are fixed in source order;
 //   * S^T puts one head per lane, so the online softmax needs only a swap with lane^32,
 //     and the probabilities already sit in the B-operand layout of the PV MFMA;
 //   * splits of one token write (o / l, log2-sum-exp) partials that a second kernel
@@ -523,15 +524,13 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   }
 
   // Phase A of step j (after a barrier: K buffer b holds tile j, the other one is free):
-  // S^T = K Q^T over this wave's dims on the MFMAs while this wave's dequantized rows of
-  // tile j+1 (and its mask byte) are stored into the other buffer; the partial S^T is
-  // published for the partner wave (same head block, other dim half); barrier.
+  // S^T = K Q^T over this wave's dims on the MFMAs; the partial S^T is published for the
+  // partner wave (same head block, other dim half); barrier.
   auto phase_a = [&](int b, f32x16_t& s) __attribute__((always_inline)) {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
     lds_barrier();
     const uint16_t* kbase = kt[b] + kt_off<S::KCH>(lane_s & 31, dim0 + 8 * (lane_s >> 5));
-    uint16_t* sdst = kt[b ^ 1] + kt_off<S::KCH>(8 * wave + (lane_s >> 3), 16 * (lane_s & 7));
     bf16x8_t af[KSMAX];
     static_for<(kLdsAhead < KSMAX ? kLdsAhead : KSMAX)>([&](auto kc) {
       constexpr int kk = decltype(kc)::value;
@@ -539,8 +538,6 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     });
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-    constexpr int NSTORE = 2 * S::FP8_LINES + 2;  // fp8 chunks, rope chunk, mask byte
-    static_assert(NSTORE <= KSMAX, "one store per MFMA slot");
     __builtin_amdgcn_sched_barrier(0);
     static_for<KSMAX>([&](auto kc) {
       constexpr int kk = decltype(kc)::value;
@@ -548,19 +545,8 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
       if constexpr (kk + kLdsAhead < KSMAX) {
         if (kk + kLdsAhead < ks_n) af[kk + kLdsAhead] = *reinterpret_cast<const bf16x8_t*>(kbase + 16 * (kk + kLdsAhead));
       }
-      if constexpr (kk < 2 * S::FP8_LINES) {
-        *reinterpret_cast<u32x4_t*>(sdst + 128 * (kk >> 1) + 8 * (kk & 1)) = dq[kk];
-      } else if constexpr (kk == 2 * S::FP8_LINES) {
-        if ((lane_s & 7) < S::ROPE_CH)
-          *reinterpret_cast<u32x4_t*>(kt[b ^ 1] + kt_off<S::KCH>(8 * wave + (lane_s >> 3), DN + 8 * (lane_s & 7))) = rr.rope;
-      } else if constexpr (kk == 2 * S::FP8_LINES + 1) {
-        if (lane_s == 0) reinterpret_cast<uint8_t*>(&kt_mask[b ^ 1])[wave] = (uint8_t)mask_a;
-      }
       __builtin_amdgcn_sched_barrier(0);
     });
-    mask_a = mask_b;
-    mask_b = mask_c;
-    mask_c = mask_d;
     float4* xw = reinterpret_cast<float4*>(xbuf) + wave * 4 * 64 + lane_s;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) xw[64 * q4] = make_float4(s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]);
@@ -632,18 +618,38 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     static_for<(kLdsAhead < NREAD ? kLdsAhead : NREAD)>([&](auto jc) { vread(jc, vbase); });
   };
 
-  // Phase B: both dim halves summed, unattended columns -inf, row maximum, lazy rescale
-  // decision, phase C's first LDS reads, and the weights of keys 0..15 (pb[0]; keys
-  // 16..31 follow between the first PV MFMAs).  Returns whether any head of the wave
-  // needs its O rescaled.
+  // Phase B: this wave's rows of tile j+1 stored into the free K buffer; both dim halves
+  // of S^T summed, unattended columns -inf, row maximum, lazy rescale decision, phase
+  // C's first LDS reads, and the weights of keys 0..15 (pb[0]; keys 16..31 follow
+  // between the first PV MFMAs).  Returns whether any head of the wave needs its O
+  // rescaled.
   auto phase_b = [&](int tile, int b, int rs2, const f32x16_t& s, bf16x8_t (&pb)[2], float& alpha)
                      __attribute__((always_inline)) -> bool {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
     const float4* xr = reinterpret_cast<const float4*>(xbuf) + (wave ^ 1) * 4 * 64 + lane_s;
+    float4 ox[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) ox[q4] = xr[64 * q4];
+    // this wave's rows of tile j+1 (dequantized in registers during the previous step)
+    // and its mask byte into the other K buffer, free since the step began; LDS is
+    // otherwise idle here, while phase A's fragment reads kept it busy
+    {
+      const int key = 8 * wave + (lane_s >> 3);
+      const int c = lane_s & 7;
+      uint16_t* sdst = kt[b ^ 1] + kt_off<S::KCH>(key, 16 * c);
+#pragma unroll
+      for (int kk = 0; kk < 2 * S::FP8_LINES; ++kk)
+        *reinterpret_cast<u32x4_t*>(sdst + 128 * (kk >> 1) + 8 * (kk & 1)) = dq[kk];
+      if (c < S::ROPE_CH) *reinterpret_cast<u32x4_t*>(kt[b ^ 1] + kt_off<S::KCH>(key, DN + 8 * c)) = rr.rope;
+      if (lane_s == 0) reinterpret_cast<uint8_t*>(&kt_mask[b ^ 1])[wave] = (uint8_t)mask_a;
+      mask_a = mask_b;
+      mask_b = mask_c;
+      mask_c = mask_d;
+    }
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 o = xr[64 * q4];
+      const float4 o = ox[q4];
       sv[4 * q4] = s[4 * q4] + o.x;
       sv[4 * q4 + 1] = s[4 * q4 + 1] + o.y;
       sv[4 * q4 + 2] = s[4 * q4 + 2] + o.z;
