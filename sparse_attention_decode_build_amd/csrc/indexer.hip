@@ -272,10 +272,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     return;
   }
   const float* lrow = logits + (int64_t)t * logits_stride;
+  // all loads first (at an index clamped into the row, so none is conditional and they
+  // are in flight together), then the rows past n become -inf
+  float lv[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) lv[i] = lrow[min(i * kTopkThreads + tid, n - 1)];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int r = i * kTopkThreads + tid;  // row; thread r / KPT holds it
-    stage[(r / KPT) * kStride + r % KPT] = r < n ? lrow[r] : -INFINITY;
+    stage[(r / KPT) * kStride + r % KPT] = r < n ? lv[i] : -INFINITY;
   }
   for (int j = tid; j < kDigitBins; j += kTopkThreads) hist[j] = 0;
   __syncthreads();
