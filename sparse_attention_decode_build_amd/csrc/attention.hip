@@ -454,12 +454,6 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     slot_row<ONE>(slot, tile * kTile + 8 * wave + (lane >> 3), window, swa, comp, S::ROWB, S::NSC, zrow, vrow,
                   srow);
   };
-  auto dma_tile = [&](int tile, int slot_index) __attribute__((always_inline)) -> uint32_t {
-    const uint8_t* vr;
-    const uint8_t* sr;
-    row_addr_of(tile, pick_slot(load_slots(tile)), &vr, &sr);
-    return dma_issue<DN, DR>(lane, wave, raw_v[slot_index], raw_s[slot_index], vr, sr, zrow);
-  };
   // ids of the wave's 8 rows of a tile -> the LDS ring (lanes 0..7; the others read the
   // zero row into the unused part of the wave's 256 bytes)
   auto id_fetch = [&](int tile) __attribute__((always_inline)) {
@@ -503,13 +497,37 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   // until it writes it beside that tile's K buffer.
   uint32_t mask_a = 0, mask_b = 0, mask_c = 0, mask_d = 0;  // this wave's bytes for tiles j+1 .. j+4
   {
+    // The slot ids of tiles 0..4 are all loaded and picked before the first row DMA, so
+    // no id load waits behind a row DMA in the vmcnt stream.
+    int sl[5];
+    if (width >= 8) {
+      SlotIds ids[5];
+#pragma unroll
+      for (int k = 0; k < 5; ++k) {
+        ids[k].c0 = (tile_begin + k) * kTile + 8 * wave;
+        ids[k].lc = max(0, min(ids[k].c0, width - 8));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ids[k].v[j] = si_row[ids[k].lc + j];
+      }
+#pragma unroll
+      for (int k = 0; k < 5; ++k) sl[k] = pick_slot(ids[k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 5; ++k) sl[k] = pick_slot(load_slots(tile_begin + k));
+    }
+    auto dma_at = [&](int tile, int slot, int slot_index) __attribute__((always_inline)) -> uint32_t {
+      const uint8_t* vr;
+      const uint8_t* sr;
+      row_addr_of(tile, slot, &vr, &sr);
+      return dma_issue<DN, DR>(lane, wave, raw_v[slot_index], raw_s[slot_index], vr, sr, zrow);
+    };
     id_fetch(tile_begin + 5);
     id_fetch(tile_begin + 6);
     id_fetch(tile_begin + 7);
     uint32_t m0 = 0;
-    if (tile_begin < tile_end) m0 = dma_tile(tile_begin, 0);
-    if (tile_begin + 1 < tile_end) mask_a = dma_tile(tile_begin + 1, 1);
-    if (tile_begin + 2 < tile_end) mask_b = dma_tile(tile_begin + 2, 2);
+    if (tile_begin < tile_end) m0 = dma_at(tile_begin, sl[0], 0);
+    if (tile_begin + 1 < tile_end) mask_a = dma_at(tile_begin + 1, sl[1], 1);
+    if (tile_begin + 2 < tile_end) mask_b = dma_at(tile_begin + 2, sl[2], 2);
     if (tile_begin < tile_end) {
       wait_tiles(min(2, tile_end - 1 - tile_begin));
       dequant_lines<DN, DR, 0, S::FP8_LINES, true>(lane, wave, raw_v[0], raw_s[0], kt[0]);
@@ -519,8 +537,8 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     raw_load<DN, DR>(lane, wave, raw_v[1], raw_s[1], rr);  // stale past the last tile (unused)
     static_for<NWORD>(convert_word);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // raw reads of slots 0 and 1 done before their refill
-    if (tile_begin + 3 < tile_end) mask_c = dma_tile(tile_begin + 3, 0);
-    if (tile_begin + 4 < tile_end) mask_d = dma_tile(tile_begin + 4, 1);
+    if (tile_begin + 3 < tile_end) mask_c = dma_at(tile_begin + 3, sl[3], 0);
+    if (tile_begin + 4 < tile_end) mask_d = dma_at(tile_begin + 4, sl[4], 1);
   }
 
   // Phase A of step j (after a barrier: K buffer b holds tile j, the other one is free):
