@@ -390,9 +390,6 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     if (kk < ks_n && head < num_heads)
       qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + dim0 + 16 * kk + 8 * h);
   }
-  // Q^T lives in AGPRs (an MFMA operand only), leaving the VGPRs for fragments in flight
-#pragma unroll
-  for (int kk = 0; kk < KSMAX; ++kk) asm volatile("" : "+a"(qf[kk]));
   f32x16_t acc_o[MTMAX];
 #pragma unroll
   for (int mt = 0; mt < MTMAX; ++mt)
@@ -402,9 +399,6 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   float l_run = 0.0f;  // sum of the bf16-rounded weights (normalizes O)
   float l_lse = 0.0f;  // sum of the fp32 weights (log-sum-exp)
 
-  // Q fragments landed (a wait the compiler sees, so it does not re-check the Q loads
-  // inside the tile loop)
-  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // Slot id of this lane's row (8*wave + lane/8) of a tile.  For the first five tiles the
   // wave's 8 ids are one scalar load (a window past the end of the sparse_indices row is
@@ -515,6 +509,12 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
 #pragma unroll
       for (int k = 0; k < 5; ++k) sl[k] = pick_slot(load_slots(tile_begin + k));
     }
+    // Q fragments landed together with the ids (a wait the compiler sees, so it does not
+    // re-check the Q loads inside the tile loop); Q^T lives in AGPRs from here on (an
+    // MFMA operand only), leaving the VGPRs for fragments in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+#pragma unroll
+    for (int kk = 0; kk < KSMAX; ++kk) asm volatile("" : "+a"(qf[kk]));
     auto dma_at = [&](int tile, int slot, int slot_index) __attribute__((always_inline)) -> uint32_t {
       const uint8_t* vr;
       const uint8_t* sr;
