@@ -387,8 +387,9 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
 #pragma unroll
   for (int kk = 0; kk < KSMAX; ++kk) {
     qf[kk] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    if (kk < ks_n && head < num_heads)
-      qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + dim0 + 16 * kk + 8 * h);
+    // qrow is clamped to an existing head: the lanes of heads past num_heads load a copy
+    // (their outputs are never written), so no load is conditional
+    if (kk < ks_n) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + dim0 + 16 * kk + 8 * h);
   }
   f32x16_t acc_o[MTMAX];
 #pragma unroll
