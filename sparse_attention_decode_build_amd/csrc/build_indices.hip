@@ -52,18 +52,34 @@ __global__ __launch_bounds__(kThreads) void build_sparse_indices_kernel(
   int base = 0;
   for (int c0 = 0; c0 < ncand; c0 += kThreads * kPerThread) {
     const int cb = c0 + tid * kPerThread;
+    // Loads take clamped in-range addresses and are masked afterwards, so all of a
+    // thread's loads of one kind are in flight together.
     int l[kPerThread];
+    if (cand_row != nullptr) {
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = cb + i;
-      l[i] = c < ncand ? (cand_row != nullptr ? cand_row[c] : c) : -1;
+      for (int i = 0; i < kPerThread; ++i) l[i] = cand_row[min(cb + i, ncand - 1)];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) l[i] = cb + i;
+    }
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i)
+      if (cb + i >= ncand || l[i] < 0 || l[i] >= g.n_comp || l[i] / comp_block >= comp_cols) l[i] = -1;
+    int pg[kPerThread];
+    if (comp_cols > 0) {
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) pg[i] = comp_row[l[i] < 0 ? 0 : l[i] / comp_block];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPerThread; ++i) pg[i] = -1;
     }
     int sl[kPerThread];
     int cnt = 0;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      sl[i] = (l[i] >= 0 && l[i] < g.n_comp) ? page_slot(comp_row, comp_cols, comp_block, comp_pages, l[i]) : -1;
-      cnt += sl[i] >= 0;
+      const bool keep = l[i] >= 0 && pg[i] >= 0 && (int64_t)pg[i] < comp_pages;
+      sl[i] = keep ? pg[i] * comp_block + l[i] % comp_block : -1;
+      cnt += keep;
     }
     // exclusive scan of the per-thread counts
     const int incl = wave_incl_scan(cnt);
