@@ -26,6 +26,12 @@ Readings taken where the pages are silent (each is listed in the design doc):
   (fail closed) and is dropped
 * attention values are the whole dequantized row (Dv = Dn + Dr); the sink is
   one extra logit with a zero value vector
+* indexer query preparation: the RoPE output is rounded to bf16 before the
+  Hadamard rotation; the rotation's sum is exact, then float32, times
+  float32(D^-1/2), then bf16; the MXFP4 exponent is the smallest e with
+  6 * 2^e >= amax (-127 for a zero block), codes round to nearest, ties even;
+  weights * softmax_scale * head_scale in float32, left to right; a position
+  outside the cos/sin table gives zero codes, scale byte 0 and weight 0
 """
 
 from __future__ import annotations
@@ -428,6 +434,146 @@ def sparse_mla_decode(q_bits, kv_swa, kv_comp, sparse_indices, sparse_topk_lens,
         else:
             o[i], lse[i] = attend(q_bits[t], rows, softmax_scale, attn_sink)
     return (o, lse, mass) if return_mass else (o, lse)
+
+
+# ---------------------------------------------------------------------------
+# Indexer query preparation: RoPE tail -> Hadamard -> MXFP4, weight fold
+# ---------------------------------------------------------------------------
+
+
+def rope_gptj_tail(x: np.ndarray, cos: np.ndarray, sin: np.ndarray, rope_dim: int) -> np.ndarray:
+    """GPT-J (interleaved) rotary embedding of the last ``rope_dim`` elements, float32.
+
+    [ops] ``_apply_gptj_rope_tail_rows``: the row is taken to float32; each pair
+    (e, o) = (x[n + 2i], x[n + 2i + 1]) of the tail (n = D - rope_dim) becomes
+    (e*cos_i - o*sin_i, e*sin_i + o*cos_i), every product and sum a separate
+    float32 operation.  ``x`` [..., D]; ``cos``/``sin`` [..., rope_dim/2]
+    broadcast over the middle axes.  The leading part is returned unchanged.
+    """
+    out = np.array(x, dtype=np.float32, copy=True)
+    n = out.shape[-1] - rope_dim
+    e = out[..., n::2].copy()
+    o = out[..., n + 1::2].copy()
+    c = np.asarray(cos, dtype=np.float32)
+    s = np.asarray(sin, dtype=np.float32)
+    while c.ndim < e.ndim:
+        c = c[..., None, :]
+        s = s[..., None, :]
+    out[..., n::2] = (e * c).astype(np.float32) - (o * s).astype(np.float32)
+    out[..., n + 1::2] = (e * s).astype(np.float32) + (o * c).astype(np.float32)
+    return out
+
+
+def hadamard_matrix(n: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order n (a power of two): H[i, j] = (-1)^popcount(i & j)."""
+    i = np.arange(n)
+    bits = np.bitwise_and.outer(i, i)
+    parity = np.zeros_like(bits)
+    while bits.any():
+        parity ^= bits & 1
+        bits >>= 1
+    return np.where(parity == 1, -1.0, 1.0)
+
+
+def hadamard_rotate(x_bf16_bits: np.ndarray) -> np.ndarray:
+    """Scaled Hadamard rotation of bf16 rows; returns bf16 bits.
+
+    [ops] ``_deepseek_v4_hadamard_rotate``: the rows are bf16, the transform is
+    the Sylvester Hadamard matrix with scale D^-1/2, and the result is bf16.
+    Reading of the arithmetic: the sum H x is exact (float64; exact for bf16
+    inputs whose magnitudes span less than 2^38), rounded once to float32,
+    multiplied by float32(D^-1/2) in float32, and rounded to bf16 (nearest even).
+    """
+    x = bf16_bits_to_float(x_bf16_bits)
+    d = x.shape[-1]
+    exact = x @ hadamard_matrix(d).T
+    scale = np.float32(d ** -0.5)
+    y = (exact.astype(np.float32) * scale).astype(np.float32)
+    return float32_to_bf16_bits(y)
+
+
+def mxfp4_encode(x: np.ndarray):
+    """Values [..., D] -> (packed E2M1 nibbles [..., D/2] u8, e8m0 bytes [..., D/32] u8).
+
+    Per 32 consecutive elements with largest magnitude a: the shared exponent e
+    is the smallest integer with 6 * 2^e >= a (6 is the largest E2M1 magnitude;
+    the analogue of the pages' FP8 rule scale = amax / max), e = -127 when a is
+    zero, clamped to [-127, 127]; its byte is e + 127 ([ops]
+    ``read_deepseek_v4_indexer_mxfp4_cache``: scale 2^(b-127)).  Each element
+    becomes the E2M1 code whose magnitude ([ops] ``_e2m1_values``) is nearest
+    to |x| / 2^e, a tie going to the even code, with the sign bit (0x8) set
+    when x < 0.  The even element is the low nibble.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    lead, d = x.shape[:-1], x.shape[-1]
+    blocks = x.reshape(-1, d // 32, 32)
+    exps = np.empty(blocks.shape[:2], dtype=np.int64)
+    codes = np.empty(blocks.shape, dtype=np.uint8)
+    mags = np.array(E2M1_MAGNITUDES)
+    for r in range(blocks.shape[0]):
+        for b in range(blocks.shape[1]):
+            blk = blocks[r, b]
+            a = float(np.max(np.abs(blk)))
+            if a == 0.0:
+                e = -127
+            else:
+                e = math.ceil(math.log2(a / 6.0))
+                while 6.0 * 2.0 ** (e - 1) >= a:
+                    e -= 1
+                while 6.0 * 2.0 ** e < a:
+                    e += 1
+                e = min(max(e, -127), 127)
+            exps[r, b] = e
+            for j in range(32):
+                v = abs(blk[j]) / 2.0 ** e
+                dist = np.abs(mags - v)
+                best = int(np.flatnonzero(dist == dist.min())[0])
+                if best + 1 < 8 and dist[best + 1] == dist[best] and best % 2 == 1:
+                    best += 1
+                codes[r, b, j] = best | (0x8 if blk[j] < 0 else 0)
+    codes = codes.reshape(-1, d)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return (packed.reshape(*lead, d // 2),
+            (exps + 127).astype(np.uint8).reshape(*lead, d // 32))
+
+
+def fold_index_weights(weights: np.ndarray, softmax_scale: float, head_scale: float) -> np.ndarray:
+    """[vllm] ``fused_indexer_q_rope_quant``, MXFP4 path: weights * softmax_scale * head_scale.
+
+    Float32, left to right (the block scales stay with the MXFP4 query).
+    """
+    w = np.asarray(weights, dtype=np.float32)
+    return ((w * np.float32(softmax_scale)).astype(np.float32) * np.float32(head_scale)).astype(np.float32)
+
+
+def prepare_indexer_q_mxfp4(index_q_bits, positions, cos_sin_cache, weights, softmax_scale, head_scale):
+    """Indexer query -> the scorer's MXFP4 inputs.
+
+    [ops] ``deepseek_v4_prepare_indexer_q_mxfp4`` (RoPE, then the Hadamard
+    rotation, then MXFP4) and [vllm] ``fused_indexer_q_rope_quant`` (MXFP4
+    outputs and the weight fold).  ``index_q_bits`` [T, Hi, Di] bf16 bits;
+    ``positions`` [T]; ``cos_sin_cache`` [P, R] float32 (cos in the first R/2
+    columns, sin in the rest); ``weights`` [T, Hi] float32.  The RoPE output is
+    rounded to bf16 before the rotation, as the rotation takes bf16 rows.  A
+    token whose position is outside [0, P) is failed closed: zero codes, scale
+    byte 0, folded weight 0.
+    Returns (q_values [T, Hi, Di/2] u8, q_scales [T, Hi, Di/32] u8, weights_out [T, Hi] f32).
+    """
+    q = bf16_bits_to_float(index_q_bits)
+    T, H, D = q.shape
+    cs = np.asarray(cos_sin_cache, dtype=np.float32)
+    P, R = cs.shape
+    pos = np.asarray(positions, dtype=np.int64)
+    ok = (pos >= 0) & (pos < P)
+    pc = np.where(ok, pos, 0)
+    roped = rope_gptj_tail(q.astype(np.float32), cs[pc, : R // 2], cs[pc, R // 2:], R)
+    rotated = hadamard_rotate(float32_to_bf16_bits(roped))
+    values, scales = mxfp4_encode(bf16_bits_to_float(rotated))
+    w_out = fold_index_weights(weights, softmax_scale, head_scale)
+    values[~ok] = 0
+    scales[~ok] = 0
+    w_out[~ok] = 0.0
+    return values, scales, w_out
 
 
 # ---------------------------------------------------------------------------

@@ -381,3 +381,124 @@ def test_sparse_attention_ignores_padding_and_invalid_columns():
     o2, _ = O.sparse_mla_decode(v.q, v.kv_pages, v.kv_pages, si2, lens, W, cfg.block, cfg.block,
                                 cfg.d_nope, cfg.d_rope, wl.softmax_scale)
     assert np.array_equal(o2, res["out"])
+
+
+# --------------------------------------------------------------------------- indexer query preparation
+
+
+def test_mxfp4_encode_hand_worked_cases():
+    for line in _golden("mxfp4_encode_cases.txt"):
+        text = " ".join(line)
+        sbyte, vals, codes = (part.strip() for part in text.split("|"))
+        vals = [float(v) for v in vals.split()]
+        codes = [int(c, 16) for c in codes.split()]
+        x = np.zeros(32)
+        x[: len(vals)] = vals
+        packed, exps = O.mxfp4_encode(x[None, :])
+        assert int(exps[0, 0]) == int(sbyte), text
+        got = np.empty(32, dtype=np.int64)
+        got[0::2] = packed[0] & 0xF
+        got[1::2] = packed[0] >> 4
+        assert list(got[: len(codes)]) == codes, text
+        assert not got[len(codes):].any(), text
+
+
+def test_mxfp4_encode_matches_threshold_encoder_and_error_bound():
+    # The harness's write-side encoder is a separate implementation (rounding by
+    # threshold counting, exponent from a float log2); on nonzero bf16 blocks the
+    # two must give the same bytes.  The decode of the encoding is within half a
+    # grid step: 2^e for |x| / 2^e in [4, 6], 2^(e-2) below 2.
+    g = torch.Generator().manual_seed(7)
+    x = (torch.randn(64, 128, generator=g) * torch.exp2(torch.randint(-8, 8, (64, 1), generator=g).float()))
+    x = x.bfloat16().float()
+    mine_v, mine_s = O.mxfp4_encode(x.numpy().astype(np.float64))
+    ref_v, ref_s = WL.encode_mxfp4(x)
+    assert np.array_equal(mine_v, ref_v.numpy()) and np.array_equal(mine_s, ref_s.numpy())
+    dec = O.mxfp4_decode(mine_v, mine_s)
+    scale = np.repeat(np.ldexp(1.0, mine_s.astype(np.int64) - 127), 32, axis=1)
+    xv = x.numpy().astype(np.float64)
+    err = np.abs(dec - xv)
+    assert (err <= scale * 1.0).all()
+    small = np.abs(xv) <= 2.0 * scale
+    assert (err[small] <= 0.25 * scale[small]).all()
+    amax = np.abs(xv).reshape(64, 4, 32).max(-1)
+    e = mine_s.astype(np.float64) - 127
+    assert (6.0 * np.exp2(e - 1) < amax).all() and (amax <= 6.0 * np.exp2(e)).all()
+
+
+def test_hadamard_matrix_is_sylvester_and_rotation_is_an_involution():
+    import scipy.linalg
+    for n in (2, 8, 32, 64, 128):
+        assert np.array_equal(O.hadamard_matrix(n), scipy.linalg.hadamard(n))
+    # H / sqrt(n) is orthonormal and symmetric, so rotating twice returns the row
+    # (up to two bf16 roundings), and the norm is kept.
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(40, 128, generator=g).bfloat16()
+    bits = x.view(torch.int16).numpy().view(np.uint16)
+    once = O.hadamard_rotate(bits)
+    twice = O.bf16_bits_to_float(O.hadamard_rotate(once))
+    xf = x.float().numpy().astype(np.float64)
+    assert np.allclose(twice, xf, rtol=0, atol=4 * 2.0 ** -8 * np.abs(xf).max())
+    n0 = np.linalg.norm(xf, axis=1)
+    n1 = np.linalg.norm(O.bf16_bits_to_float(once), axis=1)
+    assert np.allclose(n0, n1, rtol=2.0 ** -7)
+    # A basis vector e_j maps to column j of H, scaled: the sign pattern pins the order.
+    for j in (0, 1, 5, 64, 127):
+        e = np.zeros((1, 128), np.float32)
+        e[0, j] = 1.0
+        out = O.bf16_bits_to_float(O.hadamard_rotate(O.float32_to_bf16_bits(e)))[0]
+        assert np.array_equal(np.sign(out), scipy.linalg.hadamard(128)[:, j])
+        assert np.allclose(np.abs(out), 128 ** -0.5, rtol=2.0 ** -8)
+
+
+def test_rope_tail_is_a_complex_rotation_of_interleaved_pairs():
+    g = np.random.default_rng(11)
+    D, R = 128, 64
+    x = g.standard_normal((5, 3, D)).astype(np.float32)
+    theta = g.uniform(-math.pi, math.pi, (5, R // 2))
+    cos, sin = np.cos(theta).astype(np.float32), np.sin(theta).astype(np.float32)
+    out = O.rope_gptj_tail(x, cos, sin, R)
+    assert np.array_equal(out[..., : D - R], x[..., : D - R])
+    z = (x[..., D - R::2].astype(np.float64) + 1j * x[..., D - R + 1::2].astype(np.float64))
+    w = z * (cos.astype(np.float64) + 1j * sin.astype(np.float64))[:, None, :]
+    assert np.allclose(out[..., D - R::2], w.real, rtol=0, atol=4e-6 * np.abs(z).max())
+    assert np.allclose(out[..., D - R + 1::2], w.imag, rtol=0, atol=4e-6 * np.abs(z).max())
+    # angle 0 is the identity, a quarter turn maps (e, o) to (-o, e): both exact
+    ident = O.rope_gptj_tail(x, np.ones((5, R // 2), np.float32), np.zeros((5, R // 2), np.float32), R)
+    assert np.array_equal(ident, x)
+    quarter = O.rope_gptj_tail(x, np.zeros((5, R // 2), np.float32), np.ones((5, R // 2), np.float32), R)
+    assert np.array_equal(quarter[..., D - R::2], -x[..., D - R + 1::2])
+    assert np.array_equal(quarter[..., D - R + 1::2], x[..., D - R::2])
+
+
+def test_prepare_indexer_q_end_to_end_properties():
+    # The prepared query decodes to the rotated query within the MXFP4 step, the
+    # rotation keeps q . k (both sides rotated alike), the weights are folded, and
+    # a position outside the table fails closed.
+    g = np.random.default_rng(5)
+    T, H, D, R, P = 4, 3, 128, 64, 50
+    q = torch.from_numpy(g.standard_normal((T, H, D)).astype(np.float32)).bfloat16()
+    qb = q.view(torch.int16).numpy().view(np.uint16)
+    pos = np.array([0, 7, 49, 50])
+    ang = np.outer(np.arange(P), 10000.0 ** (-np.arange(R // 2) * 2.0 / R))
+    cs = np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+    w = g.standard_normal((T, H)).astype(np.float32)
+    vals, scales, w_out = O.prepare_indexer_q_mxfp4(qb, pos, cs, w, D ** -0.5, H ** -0.5)
+    assert vals.shape == (T, H, D // 2) and scales.shape == (T, H, D // 32)
+    assert not vals[3].any() and not scales[3].any() and not w_out[3].any()
+    assert np.allclose(w_out[:3], w[:3].astype(np.float64) * D ** -0.5 * H ** -0.5, rtol=2.0 ** -22)
+    dec = O.mxfp4_decode(vals.reshape(-1, D // 2), scales.reshape(-1, D // 32)).reshape(T, H, D)
+    qf = q.float().numpy().astype(np.float64)
+    for t in range(3):
+        th = ang[pos[t]]
+        z = (qf[t, :, D - R::2] + 1j * qf[t, :, D - R + 1::2]) * np.exp(1j * th)
+        ideal = qf[t].copy()
+        ideal[:, D - R::2], ideal[:, D - R + 1::2] = z.real, z.imag
+        ideal = ideal @ O.hadamard_matrix(D) * D ** -0.5
+        step = np.repeat(np.ldexp(1.0, scales[t].astype(np.int64) - 127), 32, axis=1)
+        assert (np.abs(dec[t] - ideal) <= step + 2.0 ** -7 * np.abs(ideal)).all()
+        k = g.standard_normal(D)
+        krot = O.hadamard_matrix(D) @ k * D ** -0.5
+        roped = qf[t].copy()
+        roped[:, D - R::2], roped[:, D - R + 1::2] = z.real, z.imag
+        assert np.allclose(dec[t] @ krot, roped @ k, rtol=0, atol=0.15 * np.linalg.norm(k) * np.abs(roped).max())
