@@ -188,6 +188,46 @@ int indexer_score_topk(const sad_batch* batch, const uint8_t* q_values, const ui
 size_t indexer_score_topk_workspace_size(int32_t num_tokens, int32_t max_ctx_rows, int32_t topk);
 
 /*
+ * prepare_indexer_q_mxfp4 - the indexer query in the form indexer_score_topk takes.
+ *
+ * Defined by [ops] deepseek_v4_prepare_indexer_q_mxfp4 with
+ * _apply_gptj_rope_tail_rows and _deepseek_v4_hadamard_rotate, and by [vllm]
+ * fused_indexer_q_rope_quant (MXFP4 path).  Per (token t, head h) row x of
+ * idx_dim bf16 values:
+ *   1. RoPE, GPT-J style, on the last rope_dim elements: with n = idx_dim - rope_dim,
+ *      c_i = cos_sin_cache[p][i], s_i = cos_sin_cache[p][rope_dim/2 + i] and
+ *      p = positions[t], the pair (e, o) = (x[n+2i], x[n+2i+1]) becomes
+ *      (e*c_i - o*s_i, e*s_i + o*c_i), each product and sum one fp32 operation;
+ *      the row is then rounded to bf16 (nearest even);
+ *   2. y = bf16(fp32(H x) * fp32(idx_dim^-1/2)) with H the Sylvester Hadamard
+ *      matrix (H[i][j] = (-1)^popcount(i & j)); the sum H x is exact (double
+ *      precision) and rounded once to fp32;
+ *   3. MXFP4 per 32 elements: e = the smallest integer with 6 * 2^e >= max|y|
+ *      (-127 for a block below 2^-126), clamped to [-127, 127]; scale byte e + 127;
+ *      each element's E2M1 code is the grid value nearest |y| / 2^e (a tie goes to
+ *      the even code) with bit 3 set when y < 0; the even element is the low nibble;
+ *   4. weights_out = fp32(fp32(weights * softmax_scale) * head_scale).
+ * A token whose position is outside [0, max_pos) is failed closed: its codes and
+ * scale bytes are 0 and its folded weights 0.  Inputs are finite.
+ *
+ *   index_q        [num_tokens, num_idx_heads, idx_dim] bf16, 16-byte aligned
+ *   positions      [num_tokens] int32
+ *   cos_sin_cache  [max_pos, rope_dim] fp32 (cos columns, then sin), 16-byte aligned
+ *   weights        [num_tokens, num_idx_heads] fp32
+ *   q_values       out [num_tokens, num_idx_heads, idx_dim/2] u8, 4-byte aligned
+ *   q_scales       out [num_tokens, num_idx_heads, idx_dim/32] u8 (e8m0)
+ *   weights_out    out [num_tokens, num_idx_heads] fp32
+ * idx_dim in {64, 128} (else SAD_EUNSUPPORTED); rope_dim a multiple of 8 in
+ * (0, idx_dim) and max_pos >= 1 (else SAD_EINVAL).  num_tokens == 0 is a no-op.
+ */
+int prepare_indexer_q_mxfp4(const uint16_t* index_q, const int32_t* positions,
+                            const float* cos_sin_cache, int32_t max_pos, int32_t rope_dim,
+                            const float* weights, float softmax_scale, float head_scale,
+                            int32_t num_tokens, int32_t num_idx_heads, int32_t idx_dim,
+                            uint8_t* q_values, uint8_t* q_scales, float* weights_out,
+                            void* stream);
+
+/*
  * gather_dequant_kv - dequantized rows of every attended column.
  *
  * Defined by [ops] dequantize_deepseek_v4_fp8_ds_mla_cache (slot -> page row,

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     build_sparse_indices,
     gather_dequant_kv,
     indexer_score_topk,
+    prepare_indexer_q_mxfp4,
     indexer_score_topk_workspace_size,
     last_error,
     load,

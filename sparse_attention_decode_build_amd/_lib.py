@@ -47,6 +47,8 @@ _SIGNATURES = {
                                    ctypes.POINTER(SadMxfp4Cache), c_ptr, c_i64, c_i32, c_i32, c_i32,
                                    c_ptr, c_ptr, c_i64, c_ptr, c_size, c_ptr]),
     "indexer_score_topk_workspace_size": (c_size, [c_i32, c_i32, c_i32]),
+    "prepare_indexer_q_mxfp4": (c_i32, [c_ptr, c_ptr, c_ptr, c_i32, c_i32, c_ptr, c_f32, c_f32, c_i32,
+                                        c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr]),
     "gather_dequant_kv": (c_i32, [ctypes.POINTER(SadKvCache), ctypes.POINTER(SadKvCache), c_ptr, c_ptr,
                                   c_i32, c_i32, c_i32, c_ptr, c_ptr]),
     "sparse_mla_decode": (c_i32, [c_ptr, c_i32, c_i32, ctypes.POINTER(SadKvCache),
@@ -171,6 +173,39 @@ def build_sparse_indices(query_start_loc, seq_lens, token_to_req, replay_start, 
         padded_topk, _p(out), _p(lens), _stream(stream))
     _check("build_sparse_indices", rc)
     return out, lens
+
+
+def prepare_indexer_q_mxfp4(index_q, positions, cos_sin_cache, weights, softmax_scale, head_scale,
+                            q_values=None, q_scales=None, weights_out=None, stream=None):
+    """bf16 indexer query [T, Hi, Di] -> (q_values [T, Hi, Di/2] u8, q_scales [T, Hi, Di/32] u8,
+    weights_out [T, Hi] f32): RoPE tail, Hadamard rotation, MXFP4, weight fold."""
+    lib = load()
+    _need(index_q, torch.bfloat16, "index_q", dim=3)
+    _need(positions, torch.int32, "positions", dim=1)
+    _need(cos_sin_cache, torch.float32, "cos_sin_cache", dim=2)
+    _need(weights, torch.float32, "weights", dim=2)
+    T, H, D = index_q.shape
+    if positions.shape[0] != T or tuple(weights.shape) != (T, H):
+        raise ValueError("positions must be [T] and weights [T, Hi]")
+    dev = index_q.device
+    if q_values is None:
+        q_values = torch.empty((T, H, D // 2), dtype=torch.uint8, device=dev)
+    if q_scales is None:
+        q_scales = torch.empty((T, H, D // 32), dtype=torch.uint8, device=dev)
+    if weights_out is None:
+        weights_out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _need(q_values, torch.uint8, "q_values", dim=3)
+    _need(q_scales, torch.uint8, "q_scales", dim=3)
+    _need(weights_out, torch.float32, "weights_out", dim=2)
+    if (tuple(q_values.shape) != (T, H, D // 2) or tuple(q_scales.shape) != (T, H, D // 32)
+            or tuple(weights_out.shape) != (T, H)):
+        raise ValueError("output shapes must be [T, Hi, Di/2], [T, Hi, Di/32] and [T, Hi]")
+    rc = lib.prepare_indexer_q_mxfp4(
+        _p(index_q), _p(positions), _p(cos_sin_cache), cos_sin_cache.shape[0], cos_sin_cache.shape[1],
+        _p(weights), softmax_scale, head_scale, T, H, D, _p(q_values), _p(q_scales), _p(weights_out),
+        _stream(stream))
+    _check("prepare_indexer_q_mxfp4", rc)
+    return q_values, q_scales, weights_out
 
 
 def indexer_score_topk_workspace_size(num_tokens, max_ctx_rows, topk) -> int:

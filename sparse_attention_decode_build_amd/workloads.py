@@ -500,3 +500,38 @@ def host_view(wl: Workload, layer: int = 0, reqs=None) -> HostView:
 def with_overrides(cfg: Config, **kw) -> Config:
     """A variant of a config (e.g. the sparse-equals-dense self-check)."""
     return replace(cfg, **kw)
+
+
+# --------------------------------------------------------------------------
+# Inputs of the indexer query preparation (RoPE, Hadamard, MXFP4, weight fold)
+# --------------------------------------------------------------------------
+
+
+@dataclass
+class IndexerQInputs:
+    index_q: torch.Tensor  # [T, Hi, Di] bf16, N(0, 1)
+    positions: torch.Tensor  # [T] int32
+    cos_sin: torch.Tensor  # [max_pos, rope_dim] fp32: cos columns, then sin
+    weights: torch.Tensor  # [T, Hi] fp32, N(0, 1), before the fold
+    softmax_scale: float  # Di^-1/2
+    head_scale: float  # Hi^-1/2
+
+
+def rope_table(max_pos: int, rope_dim: int, base: float = 10000.0) -> torch.Tensor:
+    """Rotary cos/sin table [max_pos, rope_dim] fp32: angle(p, i) = p * base^(-2i/rope_dim)."""
+    inv = base ** (-torch.arange(rope_dim // 2, dtype=torch.float64) * 2.0 / rope_dim)
+    ang = torch.arange(max_pos, dtype=torch.float64)[:, None] * inv[None, :]
+    return torch.cat([torch.cos(ang), torch.sin(ang)], dim=1).float().contiguous()
+
+
+def make_indexer_q_inputs(num_tokens: int, idx_heads: int, idx_dim: int, rope_dim: int, max_pos: int,
+                          seed: int, device="cpu", positions=None) -> IndexerQInputs:
+    """Seeded inputs; positions are uniform in [0, max_pos) unless given."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(num_tokens, idx_heads, idx_dim, generator=g).bfloat16()
+    w = torch.randn(num_tokens, idx_heads, generator=g)
+    if positions is None:
+        positions = torch.randint(0, max_pos, (num_tokens,), generator=g)
+    positions = torch.as_tensor(positions, dtype=torch.int32)
+    return IndexerQInputs(q.to(device), positions.to(device), rope_table(max_pos, rope_dim).to(device),
+                          w.to(device), idx_dim ** -0.5, idx_heads ** -0.5)

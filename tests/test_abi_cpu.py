@@ -118,3 +118,20 @@ def test_attention_errors(lib):
     assert _call_attn(lib, T=8, P=8192) == L.SAD_EWORKSPACE
     assert "workspace" in L.last_error()
     assert lib.sparse_mla_decode_workspace_size(16448, 128, 2176, 576) == 0
+
+
+def _call_qprep(lib, T=4, H=64, D=128, R=64, P=100, align=FAKE):
+    return lib.prepare_indexer_q_mxfp4(align, FAKE, FAKE, P, R, FAKE, 0.088, 0.125, T, H, D,
+                                       FAKE, FAKE, FAKE, None)
+
+
+def test_prepare_indexer_q_errors(lib):
+    assert _call_qprep(lib, T=0) == L.SAD_OK
+    assert _call_qprep(lib, D=96) == L.SAD_EUNSUPPORTED
+    assert _call_qprep(lib, R=0) == L.SAD_EINVAL
+    assert _call_qprep(lib, R=128) == L.SAD_EINVAL  # not below idx_dim
+    assert _call_qprep(lib, R=36) == L.SAD_EINVAL  # not a multiple of 8
+    assert _call_qprep(lib, P=0) == L.SAD_EINVAL
+    assert _call_qprep(lib, T=-1) == L.SAD_EINVAL
+    assert _call_qprep(lib, align=FAKE + 4) == L.SAD_EINVAL
+    assert "aligned" in L.last_error()
