@@ -205,7 +205,8 @@ size_t indexer_score_topk_workspace_size(int32_t num_tokens, int32_t max_ctx_row
  *   3. MXFP4 per 32 elements: e = the smallest integer with 6 * 2^e >= max|y|
  *      (-127 for a block below 2^-126), clamped to [-127, 127]; scale byte e + 127;
  *      each element's E2M1 code is the grid value nearest |y| / 2^e (a tie goes to
- *      the even code) with bit 3 set when y < 0; the even element is the low nibble;
+ *      the even code) with bit 3 = the sign bit of y (-0.0 gives 0x8); the even
+ *      element is the low nibble;
  *   4. weights_out = fp32(fp32(weights * softmax_scale) * head_scale).
  * A token whose position is outside [0, max_pos) is failed closed: its codes and
  * scale bytes are 0 and its folded weights 0.  Inputs are finite.

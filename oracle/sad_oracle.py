@@ -29,7 +29,8 @@ Readings taken where the pages are silent (each is listed in the design doc):
 * indexer query preparation: the RoPE output is rounded to bf16 before the
   Hadamard rotation; the rotation's sum is exact, then float32, times
   float32(D^-1/2), then bf16; the MXFP4 exponent is the smallest e with
-  6 * 2^e >= amax (-127 for a zero block), codes round to nearest, ties even;
+  6 * 2^e >= amax (-127 for a zero block), codes round to nearest, ties even,
+  the code's sign bit is the value's sign bit (-0.0 -> 0x8);
   weights * softmax_scale * head_scale in float32, left to right; a position
   outside the cos/sin table gives zero codes, scale byte 0 and weight 0
 """
@@ -501,8 +502,9 @@ def mxfp4_encode(x: np.ndarray):
     zero, clamped to [-127, 127]; its byte is e + 127 ([ops]
     ``read_deepseek_v4_indexer_mxfp4_cache``: scale 2^(b-127)).  Each element
     becomes the E2M1 code whose magnitude ([ops] ``_e2m1_values``) is nearest
-    to |x| / 2^e, a tie going to the even code, with the sign bit (0x8) set
-    when x < 0.  The even element is the low nibble.
+    to |x| / 2^e, a tie going to the even code; its sign bit (0x8) is the
+    sign bit of x, so -0.0 encodes as 0x8 (the IEEE reading of a sign).  The
+    even element is the low nibble.
     """
     x = np.asarray(x, dtype=np.float64)
     lead, d = x.shape[:-1], x.shape[-1]
@@ -530,7 +532,7 @@ def mxfp4_encode(x: np.ndarray):
                 best = int(np.flatnonzero(dist == dist.min())[0])
                 if best + 1 < 8 and dist[best + 1] == dist[best] and best % 2 == 1:
                     best += 1
-                codes[r, b, j] = best | (0x8 if blk[j] < 0 else 0)
+                codes[r, b, j] = best | (0x8 if np.signbit(blk[j]) else 0)
     codes = codes.reshape(-1, d)
     packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
     return (packed.reshape(*lead, d // 2),
