@@ -200,8 +200,9 @@ size_t indexer_score_topk_workspace_size(int32_t num_tokens, int32_t max_ctx_row
  *      (e*c_i - o*s_i, e*s_i + o*c_i), each product and sum one fp32 operation;
  *      the row is then rounded to bf16 (nearest even);
  *   2. y = bf16(fp32(H x) * fp32(idx_dim^-1/2)) with H the Sylvester Hadamard
- *      matrix (H[i][j] = (-1)^popcount(i & j)); the sum H x is exact (double
- *      precision) and rounded once to fp32;
+ *      matrix (H[i][j] = (-1)^popcount(i & j)); H x is the fp32 radix-2 fast
+ *      transform: stages over the element-index bits, bit 0 first, each pair
+ *      (i, i + s) becoming (x_i + x_{i+s}, x_i - x_{i+s}) in fp32;
  *   3. MXFP4 per 32 elements: e = the smallest integer with 6 * 2^e >= max|y|
  *      (-127 for a block below 2^-126), clamped to [-127, 127]; scale byte e + 127;
  *      each element's E2M1 code is the grid value nearest |y| / 2^e (a tie goes to
@@ -215,7 +216,7 @@ size_t indexer_score_topk_workspace_size(int32_t num_tokens, int32_t max_ctx_row
  *   positions      [num_tokens] int32
  *   cos_sin_cache  [max_pos, rope_dim] fp32 (cos columns, then sin), 16-byte aligned
  *   weights        [num_tokens, num_idx_heads] fp32
- *   q_values       out [num_tokens, num_idx_heads, idx_dim/2] u8, 4-byte aligned
+ *   q_values       out [num_tokens, num_idx_heads, idx_dim/2] u8, 16-byte aligned
  *   q_scales       out [num_tokens, num_idx_heads, idx_dim/32] u8 (e8m0)
  *   weights_out    out [num_tokens, num_idx_heads] fp32
  * idx_dim in {64, 128} (else SAD_EUNSUPPORTED); rope_dim a multiple of 8 in

@@ -27,8 +27,8 @@ Readings taken where the pages are silent (each is listed in the design doc):
 * attention values are the whole dequantized row (Dv = Dn + Dr); the sink is
   one extra logit with a zero value vector
 * indexer query preparation: the RoPE output is rounded to bf16 before the
-  Hadamard rotation; the rotation's sum is exact, then float32, times
-  float32(D^-1/2), then bf16; the MXFP4 exponent is the smallest e with
+  Hadamard rotation; the rotation is a float32 radix-2 fast transform (index
+  bit 0 first), times float32(D^-1/2), then bf16; the MXFP4 exponent is the smallest e with
   6 * 2^e >= amax (-127 for a zero block), codes round to nearest, ties even,
   the code's sign bit is the value's sign bit (-0.0 -> 0x8);
   weights * softmax_scale * head_scale in float32, left to right; a position
@@ -476,20 +476,40 @@ def hadamard_matrix(n: int) -> np.ndarray:
     return np.where(parity == 1, -1.0, 1.0)
 
 
+def fwht_f32(x: np.ndarray) -> np.ndarray:
+    """Fast Walsh-Hadamard transform of rows [..., D] in float32 (unscaled).
+
+    Radix-2 stages over the element-index bits, bit 0 first: at stage s (s =
+    1, 2, 4, ...) each pair (i, i + s) with bit s of i clear becomes
+    (x_i + x_{i+s}, x_i - x_{i+s}), each a float32 sum.  With exact arithmetic
+    this is H x for the Sylvester matrix H of ``hadamard_matrix``.
+    """
+    y = np.array(x, dtype=np.float32, copy=True)
+    lead, d = y.shape[:-1], y.shape[-1]
+    y = y.reshape(-1, d)
+    s = 1
+    while s < d:
+        v = y.reshape(-1, d // (2 * s), 2, s)
+        a = v[:, :, 0, :].copy()
+        b = v[:, :, 1, :].copy()
+        v[:, :, 0, :] = a + b
+        v[:, :, 1, :] = a - b
+        s *= 2
+    return y.reshape(*lead, d)
+
+
 def hadamard_rotate(x_bf16_bits: np.ndarray) -> np.ndarray:
     """Scaled Hadamard rotation of bf16 rows; returns bf16 bits.
 
     [ops] ``_deepseek_v4_hadamard_rotate``: the rows are bf16, the transform is
-    the Sylvester Hadamard matrix with scale D^-1/2, and the result is bf16.
-    Reading of the arithmetic: the sum H x is exact (float64; exact for bf16
-    inputs whose magnitudes span less than 2^38), rounded once to float32,
-    multiplied by float32(D^-1/2) in float32, and rounded to bf16 (nearest even).
+    the Sylvester Hadamard matrix with scale D^-1/2, computed in float32, and
+    the result is bf16.  Reading of the float32 arithmetic: the radix-2 fast
+    transform of ``fwht_f32`` (index bit 0 first), then one float32 multiply by
+    float32(D^-1/2), then bf16 rounding (nearest even).
     """
-    x = bf16_bits_to_float(x_bf16_bits)
+    x = bf16_bits_to_float(x_bf16_bits).astype(np.float32)
     d = x.shape[-1]
-    exact = x @ hadamard_matrix(d).T
-    scale = np.float32(d ** -0.5)
-    y = (exact.astype(np.float32) * scale).astype(np.float32)
+    y = (fwht_f32(x) * np.float32(d ** -0.5)).astype(np.float32)
     return float32_to_bf16_bits(y)
 
 

@@ -430,6 +430,17 @@ def test_hadamard_matrix_is_sylvester_and_rotation_is_an_involution():
     import scipy.linalg
     for n in (2, 8, 32, 64, 128):
         assert np.array_equal(O.hadamard_matrix(n), scipy.linalg.hadamard(n))
+    # The float32 fast transform is H x: exactly on small integers (every partial sum
+    # is exact in float32), and within its rounding bound (one float32 rounding per
+    # stage) on random bf16 rows.
+    g = np.random.default_rng(8)
+    for n in (2, 16, 64, 128):
+        xi = g.integers(-256, 257, (9, n)).astype(np.float32)
+        assert np.array_equal(O.fwht_f32(xi).astype(np.float64), xi.astype(np.float64) @ scipy.linalg.hadamard(n).T)
+    xb = torch.randn(50, 128, generator=torch.Generator().manual_seed(4)).bfloat16().float().numpy()
+    ex = xb.astype(np.float64) @ scipy.linalg.hadamard(128).T
+    bound = 7 * 2.0 ** -24 * np.abs(xb).sum(axis=1, keepdims=True) * 2
+    assert (np.abs(O.fwht_f32(xb).astype(np.float64) - ex) <= bound).all()
     # H / sqrt(n) is orthonormal and symmetric, so rotating twice returns the row
     # (up to two bf16 roundings), and the norm is kept.
     g = torch.Generator().manual_seed(3)
