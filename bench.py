@@ -251,6 +251,43 @@ def summarize_traffic(fetch_dir: str, write_dir: str) -> int:
     return 0
 
 
+def bench_prepare_indexer_q(num_tokens: int, positions, iters: int = 30, warmup: int = 5) -> dict:
+    """Event-timed prepare_indexer_q_mxfp4 on 64 heads x 128 dims, rope 64 (two input
+    sets alternated).  Algorithmic bytes: per row 2*D in, D/2 + D/32 out, 4 + 4 for the
+    weight in and out; per token its position and its cos/sin row (4 + 4*rope)."""
+    H, D, R, P = 64, 128, 64, 65536
+    sets = [WL.make_indexer_q_inputs(num_tokens, H, D, R, P, seed=31 + i, device="cuda", positions=positions)
+            for i in range(2)]
+    outs = [(torch.empty((num_tokens, H, D // 2), dtype=torch.uint8, device="cuda"),
+             torch.empty((num_tokens, H, D // 32), dtype=torch.uint8, device="cuda"),
+             torch.empty((num_tokens, H), dtype=torch.float32, device="cuda")) for _ in range(2)]
+
+    def call(i):
+        a, o = sets[i % 2], outs[i % 2]
+        sad.prepare_indexer_q_mxfp4(a.index_q, a.positions, a.cos_sin, a.weights, a.softmax_scale,
+                                    a.head_scale, q_values=o[0], q_scales=o[1], weights_out=o[2])
+
+    for i in range(warmup):
+        call(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    # A spin kernel holds the stream while the launches are queued, so the events
+    # time the kernels back to back rather than the host's submission rate.
+    torch.cuda._sleep(4_000_000)
+    e0.record()
+    for i in range(iters):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    rows = num_tokens * H
+    nbytes = rows * (2 * D + D // 2 + D // 32 + 8) + num_tokens * (4 + 4 * R)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del sets, outs
+    return {"tokens": num_tokens, "us_per_launch": us, "algorithmic_bytes": nbytes, "achieved_gbs": gbs,
+            "hbm_frac": gbs / PEAK_HBM_GBS}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -339,6 +376,12 @@ def main() -> int:
         "indexer_hbm_gbs": idx_gbs,
         "step_hbm_frac": (ab["attention"] + ab["indexer"] + ab["build"]) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
+    log("[bench] indexer query preparation (outside the step)")
+    del steps
+    result["next_rows"] = {"prepare_indexer_q_mxfp4": {
+        "bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "decode_128_tokens": bench_prepare_indexer_q(T, [65535] * T),
+        "prefill_16448_tokens": bench_prepare_indexer_q(16448, None)}}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)

@@ -6,13 +6,17 @@
 // fused_indexer_q_rope_quant (MXFP4 path: two E2M1 nibbles per byte, the even element in
 // the low nibble; weights_out = weights * softmax_scale * head_scale).
 //
-// One row (token, head) of D elements is held by D/8 lanes, 8 consecutive elements each:
-//   * one 16-byte load per lane; a RoPE pair of the tail never straddles two lanes;
-//   * the Hadamard butterflies over element-index bits 0..2 run inside the lane, the
-//     higher bits across lanes (xor shuffles), in double precision, where every partial
-//     sum of bf16 values is exact; the sum is then rounded once to float;
-//   * a 32-element scale block is 4 lanes, so its largest magnitude takes two shuffles;
-//   * each lane writes its 8 codes as one 4-byte word, every 4th lane its block's scale.
+// One row (token, head) of D elements is held by the 4 lanes of a quad, D/4 consecutive
+// elements each (16 rows per wave):
+//   * 16-byte loads; a RoPE pair of the tail never straddles two lanes;
+//   * the Hadamard transform is the fp32 radix-2 fast transform, index bit 0 first: the
+//     bits inside a lane's slice in registers, the two top bits across the quad (DPP
+//     quad permutes, no LDS);
+//   * a 32-element scale block lies in one lane (D = 128) or a lane pair (D = 64);
+//   * codes come from the gfx950 FP4 conversion of bf16 pairs with the block scale (it
+//     divides by the scale's power of two, rounds to nearest even, saturates and copies
+//     the sign bit), two elements per instruction; each lane stores its codes as one 16-
+//     or 8-byte word.
 // The kernel streams: 2*D bytes in, D/2 + D/32 bytes out per row, plus the weights.
 #include <cmath>
 
@@ -22,10 +26,23 @@ namespace sad {
 namespace {
 
 constexpr int kQThreads = 256;
+constexpr int kRowsPerBlock = kQThreads / 4;
 
 typedef __attribute__((__vector_size__(16))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
-__device__ inline float bf16_round(float x) { return bf16_bits_to_f32(f32_to_bf16_bits(x)); }
+// Two floats rounded to bf16 (nearest even), packed (a in the low half).
+__device__ inline uint32_t bf16_pack(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// Both floats rounded to bf16 (nearest even) and widened back.
+__device__ inline void bf16_round2(float& a, float& b) {
+  const uint32_t u = bf16_pack(a, b);
+  a = __uint_as_float(u << 16);
+  b = __uint_as_float(u & 0xFFFF0000u);
+}
 
 // Shared exponent of a block whose largest magnitude is `a` (a bf16 value held in a
 // float): the smallest e with 6 * 2^e >= a, -127 for a zero (or subnormal) block.
@@ -39,13 +56,16 @@ __device__ inline int block_exponent(float a) {
   return min(max(e, -127), 127);
 }
 
-// E2M1 code of a magnitude already divided by the block scale: the count of grid
-// midpoints it passes; at a midpoint the even code wins (">" above an even code,
-// ">=" above an odd one).
-__device__ inline uint32_t e2m1_code(float m) {
-  return (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
-         (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
-         (uint32_t)(m > 5.0f);
+// Lane l of a quad reads lane l ^ M (M = 1 or 2) with a DPP quad permute.
+template <int M>
+__device__ inline uint32_t quad_xor(uint32_t v) {
+  constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, false);
+}
+
+template <int M>
+__device__ inline float quad_xor(float v) {
+  return __uint_as_float(quad_xor<M>(__float_as_uint(v)));
 }
 
 template <int D>
@@ -56,90 +76,120 @@ __global__ __launch_bounds__(kQThreads) void prepare_indexer_q_kernel(
     int rows, int heads, uint8_t* __restrict__ q_values, uint8_t* __restrict__ q_scales,
     float* __restrict__ weights_out) {
 #pragma clang fp contract(off)
-  constexpr int LPR = D / 8;                 // lanes per row
-  constexpr int RPB = kQThreads / LPR;       // rows per workgroup
-  static_assert(LPR % 4 == 0 && 64 % LPR == 0, "a row is 4..64 lanes of one wave");
-  const int sub = threadIdx.x % LPR;
-  const int row = (int)blockIdx.x * RPB + (int)threadIdx.x / LPR;
+  constexpr int EPL = D / 4;   // elements per lane
+  constexpr int NG = EPL / 8;  // 8-element (16-byte) groups per lane
+  static_assert(EPL == 16 || EPL == 32, "a lane holds 16 or 32 elements");
+  const int sub = threadIdx.x & 3;
+  const int row = (int)blockIdx.x * kRowsPerBlock + ((int)threadIdx.x >> 2);
   const bool live = row < rows;
-  const int r = live ? row : rows - 1;  // dead lanes still join the shuffles
+  const int r = live ? row : rows - 1;  // dead lanes still join the quad permutes
   const int t = r / heads;
+  const int d_lane = sub * EPL;
 
-  const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(q + (int64_t)r * D + sub * 8);
+  // Every load of the lane is issued before the first use.
+  u32x4_t raw[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+    raw[g] = *reinterpret_cast<const u32x4_t*>(q + (int64_t)r * D + d_lane + 8 * g);
   const int pos = positions[t];
   const float w = weights[r];
   const bool ok = pos >= 0 && pos < max_pos;
-
-  float x[8];
+  const int nope = D - rope_dim;
+  const float* cs = cos_sin + (int64_t)(ok ? pos : 0) * rope_dim;
+  float4 cg[NG], sg[NG];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    x[2 * k] = bf16_bits_to_f32(raw[k] & 0xFFFFu);
-    x[2 * k + 1] = bf16_bits_to_f32(raw[k] >> 16);
+  for (int g = 0; g < NG; ++g) {
+    const int i0 = max(d_lane + 8 * g - nope, 0) >> 1;  // clamped: groups of the head read pair 0
+    cg[g] = *reinterpret_cast<const float4*>(cs + i0);
+    sg[g] = *reinterpret_cast<const float4*>(cs + (rope_dim >> 1) + i0);
   }
 
-  // RoPE on the tail, each product and sum a separately rounded float operation (the
-  // kernel body is compiled without multiply-add contraction).
-  const int nope = D - rope_dim;
-  const int d0 = sub * 8;
-  if (d0 >= nope) {
-    const int i0 = (d0 - nope) >> 1;
-    const float* cs = cos_sin + (int64_t)(ok ? pos : 0) * rope_dim;
-    const float4 c = *reinterpret_cast<const float4*>(cs + i0);
-    const float4 s = *reinterpret_cast<const float4*>(cs + (rope_dim >> 1) + i0);
-    const float cv[4] = {c.x, c.y, c.z, c.w};
-    const float sv[4] = {s.x, s.y, s.z, s.w};
+  float x[EPL];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float e = x[2 * k], o = x[2 * k + 1];
-      x[2 * k] = e * cv[k] - o * sv[k];
-      x[2 * k + 1] = e * sv[k] + o * cv[k];
+      x[8 * g + 2 * k] = __uint_as_float(raw[g][k] << 16);
+      x[8 * g + 2 * k + 1] = __uint_as_float(raw[g][k] & 0xFFFF0000u);
+    }
+
+  // RoPE on the tail (a group of 8 elements is all head or all tail), each product and
+  // sum a separately rounded float operation; then the row is rounded to bf16.
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const bool tail = d_lane + 8 * g >= nope;
+    const float cv[4] = {cg[g].x, cg[g].y, cg[g].z, cg[g].w};
+    const float sv[4] = {sg[g].x, sg[g].y, sg[g].z, sg[g].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float e = x[8 * g + 2 * k], o = x[8 * g + 2 * k + 1];
+      const float re = e * cv[k] - o * sv[k];
+      const float ro = e * sv[k] + o * cv[k];
+      x[8 * g + 2 * k] = tail ? re : e;
+      x[8 * g + 2 * k + 1] = tail ? ro : o;
     }
   }
+#pragma unroll
+  for (int j = 0; j < EPL; j += 2) bf16_round2(x[j], x[j + 1]);
 
-  // Hadamard (Sylvester order): at each index bit, low' = low + high, high' = low - high.
-  double h[8];
+  // Hadamard (Sylvester order), fp32: at each index bit, low' = low + high and
+  // high' = low - high.  Across the quad a lane gets its partner's value p and forms
+  // p + h (low lane) or p - h (high lane) as one exactly rounded fma with +-1.
+  float* h = x;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) h[j] = (double)bf16_round(x[j]);
+  for (int s = 1; s < EPL; s <<= 1) {
 #pragma unroll
-  for (int s = 1; s < 8; s <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < EPL; ++j) {
       if (j & s) continue;
-      const double a = h[j], b = h[j + s];
+      const float a = h[j], b = h[j + s];
       h[j] = a + b;
       h[j + s] = a - b;
     }
   }
+  {
+    const float s1 = (sub & 1) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) {
-    const bool high = (sub & m) != 0;
+    for (int j = 0; j < EPL; ++j) h[j] = __builtin_fmaf(h[j], s1, quad_xor<1>(h[j]));
+    const float s2 = (sub & 2) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const double p = __shfl_xor(h[j], m, 64);
-      h[j] = high ? p - h[j] : h[j] + p;
-    }
+    for (int j = 0; j < EPL; ++j) h[j] = __builtin_fmaf(h[j], s2, quad_xor<2>(h[j]));
   }
-  float y[8];
-  float amax = 0.0f;
+  // Scale, round to bf16 (packed pairs), and the block's largest magnitude from the
+  // bf16 bits (magnitudes order like unsigned integers).
+  uint32_t yb[EPL / 2];
+  uint32_t mx = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    y[j] = bf16_round((float)h[j] * rot_scale);
-    amax = fmaxf(amax, fabsf(y[j]));
+  for (int j = 0; j < EPL; j += 2) {
+    yb[j / 2] = bf16_pack(h[j] * rot_scale, h[j + 1] * rot_scale);
+    const uint32_t m = yb[j / 2] & 0x7FFF7FFFu;
+    mx = max(mx, max(m & 0xFFFFu, m >> 16));
   }
+  if (EPL == 16) mx = max(mx, quad_xor<1>(mx));  // D = 64: a block is a lane pair
+  const float amax = __uint_as_float(mx << 16);
 
-  // MXFP4: a 32-element block is lanes 4b .. 4b+3 of the row.
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  // MXFP4 codes: the conversion divides by the scale's power of two (exponent field
+  // e + 127; 0 means 2^-127), rounds to nearest even, saturates, copies the sign bit.
   const int e = block_exponent(amax);
-  uint32_t word = 0;
+  const float scale = __uint_as_float((uint32_t)(e + 127) << 23);
+  uint32_t word[EPL / 8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t code = e2m1_code(ldexpf(fabsf(y[j]), -e)) | (y[j] < 0.0f ? 8u : 0u);
-    word |= code << (4 * j);
+  for (int wd = 0; wd < EPL / 8; ++wd) {
+    const uint32_t* p = yb + 4 * wd;
+    uint32_t v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2_t, p[0]), scale, 0);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf16x2_t, p[1]), scale, 1);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf16x2_t, p[2]), scale, 2);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf16x2_t, p[3]), scale, 3);
+    word[wd] = ok ? v : 0u;
   }
   if (!live) return;
-  *reinterpret_cast<uint32_t*>(q_values + (int64_t)r * (D / 2) + sub * 4) = ok ? word : 0u;
-  if ((sub & 3) == 0) q_scales[(int64_t)r * (D / 32) + (sub >> 2)] = ok ? (uint8_t)(e + 127) : 0;
+  uint8_t* vout = q_values + (int64_t)r * (D / 2) + sub * (EPL / 2);
+  if constexpr (EPL == 32) {
+    *reinterpret_cast<u32x4_t*>(vout) = u32x4_t{word[0], word[1], word[2], word[3]};
+    q_scales[(int64_t)r * (D / 32) + sub] = ok ? (uint8_t)(e + 127) : 0;
+  } else {
+    *reinterpret_cast<uint2*>(vout) = make_uint2(word[0], word[1]);
+    if ((sub & 1) == 0) q_scales[(int64_t)r * (D / 32) + (sub >> 1)] = ok ? (uint8_t)(e + 127) : 0;
+  }
   if (sub == 0) weights_out[r] = ok ? (w * softmax_scale) * head_scale : 0.0f;
 }
 
@@ -169,12 +219,12 @@ extern "C" int prepare_indexer_q_mxfp4(const uint16_t* index_q, const int32_t* p
                 weights_out,
             SAD_EINVAL, "prepare_indexer_q_mxfp4: NULL pointer argument");
   SAD_CHECK(((uintptr_t)index_q & 15) == 0 && ((uintptr_t)cos_sin_cache & 15) == 0 &&
-                ((uintptr_t)q_values & 3) == 0,
+                ((uintptr_t)q_values & 15) == 0,
             SAD_EINVAL,
             "prepare_indexer_q_mxfp4: index_q and cos_sin_cache must be 16-byte aligned, "
-            "q_values 4-byte aligned");
+            "q_values 16-byte aligned");
   const int64_t rows = (int64_t)num_tokens * num_idx_heads;
-  const int rpb = kQThreads / (idx_dim / 8);
+  const int rpb = kRowsPerBlock;
   const int64_t blocks = (rows + rpb - 1) / rpb;
   SAD_CHECK(rows + rpb < ((int64_t)1 << 31), SAD_EINVAL,
             "prepare_indexer_q_mxfp4: num_tokens * num_idx_heads must be below 2^31");
