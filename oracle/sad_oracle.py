@@ -33,6 +33,11 @@ Readings taken where the pages are silent (each is listed in the design doc):
   the code's sign bit is the value's sign bit (-0.0 -> 0x8);
   weights * softmax_scale * head_scale in float32, left to right; a position
   outside the cos/sin table gives zero codes, scale byte 0 and weight 0
+* output inverse RoPE + FP8: the rotated values are quantized in float32
+  (no bf16 step); power-of-two scales 2^e with e the smallest integer with
+  448 * 2^e >= amax, at least -33; blocks of 128 run along each group's row
+  and may span two heads; output group major [G, T, D]; a position outside
+  the table gives zero codes and zero scales
 """
 
 from __future__ import annotations
@@ -596,6 +601,110 @@ def prepare_indexer_q_mxfp4(index_q_bits, positions, cos_sin_cache, weights, sof
     scales[~ok] = 0
     w_out[~ok] = 0.0
     return values, scales, w_out
+
+
+# ---------------------------------------------------------------------------
+# After attention: inverse RoPE on each head's tail + grouped FP8 quantization
+# ---------------------------------------------------------------------------
+
+
+def inv_rope_gptj_tail(x: np.ndarray, cos: np.ndarray, sin: np.ndarray, rope_dim: int) -> np.ndarray:
+    """Inverse of ``rope_gptj_tail``: each tail pair (e, o) rotated by -angle, float32.
+
+    [ops] model page: the attention RoPE is GPT-J style (``is_neox_style=False``,
+    cos/sin table with the cos half first); [vllm] ``fused_inv_rope_fp8_quant``
+    undoes it on the attention output.  (e, o) -> (e*cos + o*sin, o*cos - e*sin),
+    every product and sum a separate float32 operation.
+    """
+    out = np.array(x, dtype=np.float32, copy=True)
+    n = out.shape[-1] - rope_dim
+    e = out[..., n::2].copy()
+    o = out[..., n + 1::2].copy()
+    c = np.asarray(cos, dtype=np.float32)
+    s = np.asarray(sin, dtype=np.float32)
+    while c.ndim < e.ndim:
+        c = c[..., None, :]
+        s = s[..., None, :]
+    out[..., n::2] = (e * c).astype(np.float32) + (o * s).astype(np.float32)
+    out[..., n + 1::2] = (o * c).astype(np.float32) - (e * s).astype(np.float32)
+    return out
+
+
+_E4M3_POS = E4M3_VALUES[:127]  # codes 0x00..0x7E: 0 .. 448, ascending
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float values with |x| <= 448 -> OCP e4m3fn bytes, nearest value, ties to the even code.
+
+    The sign bit is copied from x (so -0.0 -> 0x80), as a float conversion does.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x).reshape(-1, 1)
+    dist = np.abs(a - _E4M3_POS[None, :])
+    best = np.argmin(dist, axis=1)
+    nxt = np.minimum(best + 1, 126)
+    tie = (dist[np.arange(len(best)), nxt] == dist[np.arange(len(best)), best]) & (nxt != best)
+    best = np.where(tie & (best % 2 == 1), nxt, best)
+    codes = best.astype(np.uint8) | np.where(np.signbit(x.reshape(-1)), 0x80, 0).astype(np.uint8)
+    return codes.reshape(x.shape)
+
+
+def fp8_pow2_quant(blocks: np.ndarray):
+    """Blocks [..., B] -> (e4m3fn bytes [..., B], float32 scales [...]), power-of-two scales.
+
+    [ops] ``_fp8_e4m3_pow2_bytes``: scale = 2^ceil(log2(max(amax / 448, 1e-10))),
+    values = e4m3(clamp(x / scale, +-448)).  Written exactly: e is the smallest
+    integer with 448 * 2^e >= amax, and at least -33 (2^-34 < 1e-10 <= 2^-33).
+    """
+    blocks = np.asarray(blocks, dtype=np.float64)
+    amax = np.abs(blocks).max(axis=-1)
+    e = np.empty(amax.shape, dtype=np.int64)
+    for idx, a in np.ndenumerate(amax):
+        k = -33
+        if a > 0.0:
+            k = math.ceil(math.log2(a / 448.0))
+            while 448.0 * 2.0 ** (k - 1) >= a:
+                k -= 1
+            while 448.0 * 2.0 ** k < a:
+                k += 1
+        e[idx] = max(k, -33)
+    scale = np.ldexp(1.0, e)
+    y = np.clip(blocks / scale[..., None], -448.0, 448.0)
+    return e4m3_encode(y), scale.astype(np.float32)
+
+
+def inv_rope_fp8_quant(o_bits, positions, cos_sin_cache, n_groups: int, rope_dim: int, block: int = 128):
+    """Attention output -> the output projection's grouped FP8 input.
+
+    [vllm] ``fused_inv_rope_fp8_quant`` and [model] ``_project_attention_output``:
+    ``o_bits`` [T, H, Dh] bf16 bits; each head's last ``rope_dim`` elements get
+    the inverse GPT-J RoPE at ``positions[t]`` (float32); the heads are taken
+    in groups of H / n_groups, and each group's row of D = (H / n_groups) * Dh
+    values (heads in order, then dims) is quantized in blocks of ``block``
+    consecutive values with ``fp8_pow2_quant``.  Readings: the rotated values
+    go to the quantizer in float32 (no bf16 step between), blocks may span two
+    heads (only D needs to be a multiple of the block), the output is group
+    major as the pages' buffer is, and a token whose position is outside the
+    table is failed closed (zero codes, zero scales).
+    Returns (codes [G, T, D] u8, scales [G, T, D / block] float32).
+    """
+    x = bf16_bits_to_float(o_bits).astype(np.float32)
+    T, H, Dh = x.shape
+    cs = np.asarray(cos_sin_cache, dtype=np.float32)
+    P, R = cs.shape
+    assert R == rope_dim
+    pos = np.asarray(positions, dtype=np.int64)
+    ok = (pos >= 0) & (pos < P)
+    pc = np.where(ok, pos, 0)
+    rot = inv_rope_gptj_tail(x, cs[pc, : R // 2], cs[pc, R // 2:], R)
+    hpg = H // n_groups
+    D = hpg * Dh
+    rows = rot.reshape(T, n_groups, D).transpose(1, 0, 2)  # [G, T, D]
+    codes, scales = fp8_pow2_quant(rows.reshape(n_groups, T, D // block, block))
+    codes = codes.reshape(n_groups, T, D)
+    codes[:, ~ok] = 0
+    scales[:, ~ok] = 0.0
+    return codes, scales
 
 
 # ---------------------------------------------------------------------------

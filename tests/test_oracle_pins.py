@@ -513,3 +513,76 @@ def test_prepare_indexer_q_end_to_end_properties():
         roped = qf[t].copy()
         roped[:, D - R::2], roped[:, D - R + 1::2] = z.real, z.imag
         assert np.allclose(dec[t] @ krot, roped @ k, rtol=0, atol=0.15 * np.linalg.norm(k) * np.abs(roped).max())
+
+
+# --------------------------------------------------------------------------- output inverse RoPE + FP8
+
+
+def test_fp8_pow2_scale_hand_worked_cases():
+    for amax, e in _golden("fp8_pow2_scale_cases.txt"):
+        b = np.zeros((1, 128))
+        b[0, 5] = -float(amax)
+        _, s = O.fp8_pow2_quant(b)
+        assert s[0] == 2.0 ** int(e), (amax, e, s[0])
+
+
+def test_e4m3_encode_matches_torch_cast():
+    # torch's float8_e4m3fn cast rounds to nearest even; on values within +-448
+    # (midpoints of every binade included) it must give the same bytes.
+    vals = torch.from_numpy(O.E4M3_VALUES[:127].copy())
+    mids = (vals[:-1] + vals[1:]) / 2
+    g = torch.Generator().manual_seed(2)
+    x = torch.cat([vals, -vals, mids, -mids, (torch.rand(20000, generator=g, dtype=torch.float64) - 0.5) * 896,
+                   torch.randn(20000, generator=g, dtype=torch.float64) * 1e-2, torch.tensor([0.0, -0.0])])
+    x = x.float()  # the quantizer's inputs are float32
+    ref = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    mine = O.e4m3_encode(x.numpy().astype(np.float64))
+    assert np.array_equal(mine, ref)
+
+
+def test_inv_rope_undoes_rope_and_is_a_conjugate_rotation():
+    g = np.random.default_rng(12)
+    D, R = 576, 64
+    x = g.standard_normal((3, 4, D)).astype(np.float32)
+    th = g.uniform(-math.pi, math.pi, (3, R // 2))
+    c, s = np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
+    inv = O.inv_rope_gptj_tail(x, c, s, R)
+    assert np.array_equal(inv[..., : D - R], x[..., : D - R])
+    z = x[..., D - R::2].astype(np.float64) + 1j * x[..., D - R + 1::2].astype(np.float64)
+    w = z * (c.astype(np.float64) - 1j * s.astype(np.float64))[:, None, :]
+    assert np.allclose(inv[..., D - R::2], w.real, atol=4e-6 * np.abs(z).max())
+    assert np.allclose(inv[..., D - R + 1::2], w.imag, atol=4e-6 * np.abs(z).max())
+    back = O.rope_gptj_tail(inv, c, s, R)
+    assert np.allclose(back, x, rtol=0, atol=8e-6 * np.abs(x).max())
+    quarter = O.inv_rope_gptj_tail(x, np.zeros_like(c), np.ones_like(s), R)
+    assert np.array_equal(quarter[..., D - R::2], x[..., D - R + 1::2])
+    assert np.array_equal(quarter[..., D - R + 1::2], -x[..., D - R::2])
+
+
+def test_inv_rope_fp8_quant_layout_and_error_bound():
+    # Group-major layout, blocks of 128 along the group's row (heads, then dims),
+    # dequantized values within half an e4m3 step of the rotated values, and a
+    # position outside the table failed closed.
+    g = np.random.default_rng(13)
+    T, H, Dh, R, G, P = 3, 8, 576, 64, 2, 40
+    o = torch.from_numpy(g.standard_normal((T, H, Dh)).astype(np.float32) * 0.05).bfloat16()
+    bits = o.view(torch.int16).numpy().view(np.uint16)
+    cs = WL.rope_table(P, R).numpy()
+    pos = np.array([3, 39, 40])
+    codes, scales = O.inv_rope_fp8_quant(bits, pos, cs, G, R)
+    hpg, D = H // G, H // G * Dh
+    assert codes.shape == (G, T, D) and scales.shape == (G, T, D // 128)
+    assert not codes[:, 2].any() and not scales[:, 2].any()
+    of = o.float().numpy().astype(np.float64)
+    for t in (0, 1):
+        for gi in range(G):
+            for h in range(hpg):
+                head = of[t, gi * hpg + h].copy()
+                th = pos[t] * 10000.0 ** (-np.arange(R // 2) * 2.0 / R)
+                z = (head[Dh - R::2] + 1j * head[Dh - R + 1::2]) * np.exp(-1j * th)
+                head[Dh - R::2], head[Dh - R + 1::2] = z.real, z.imag
+                seg = slice(h * Dh, (h + 1) * Dh)
+                dec = O.E4M3_VALUES[codes[gi, t, seg]] * np.repeat(scales[gi, t], 128)[seg]
+                step = np.repeat(scales[gi, t], 128)[seg]
+                err = np.abs(dec - head)
+                assert (err <= np.maximum(np.abs(head) * 2.0 ** -4, step * 2.0 ** -10) + 1e-6 * np.abs(head)).all()
