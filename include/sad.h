@@ -286,6 +286,41 @@ size_t sparse_mla_decode_workspace_size(int32_t num_tokens, int32_t num_heads,
                                         int32_t max_row_width, int32_t dv);
 
 /* Description of the last non-OK return on the calling thread ("" if none). */
+/*
+ * inv_rope_fp8_quant - the attention output in the form the output projection takes.
+ *
+ * Defined by [vllm] fused_inv_rope_fp8_quant and [model] _project_attention_output
+ * (attention RoPE: GPT-J style, is_neox_style=False; cos/sin table with the cos half
+ * first) and by [ops] _fp8_e4m3_pow2_bytes (power-of-two FP8 block scales).  With
+ * G = n_groups, hpg = num_heads / G and D = hpg * head_dim:
+ *   1. in every head, with n = head_dim - rope_dim, c_i = cos_sin_cache[p][i],
+ *      s_i = cos_sin_cache[p][rope_dim/2 + i] and p = positions[t], the pair
+ *      (e, o) = (x[n+2i], x[n+2i+1]) becomes (e*c_i + o*s_i, o*c_i - e*s_i), each
+ *      product and sum one fp32 operation (the inverse of the forward rotation);
+ *   2. row (g, t) is heads g*hpg .. g*hpg + hpg - 1 of token t, heads then dims (D
+ *      values); it is cut into blocks of 128 consecutive values (a block may span two
+ *      heads);
+ *   3. per block: e = the smallest integer with 448 * 2^e >= max|x|, at least -33
+ *      (= ceil(log2(max(amax / 448, 1e-10)))); out_scales = 2^e (fp32); each code is
+ *      the e4m3fn value nearest x / 2^e (a tie goes to the even code, the sign bit is
+ *      copied) - the rotated fp32 values are quantized directly.
+ * A token whose position is outside [0, max_pos) is failed closed: zero codes and
+ * zero scales.  Inputs are finite.
+ *
+ *   attn_out      [num_tokens, num_heads, head_dim] bf16, 16-byte aligned
+ *   positions     [num_tokens] int32
+ *   cos_sin_cache [max_pos, rope_dim] fp32, 16-byte aligned
+ *   out_fp8       out [n_groups, num_tokens, D] u8 (e4m3fn), 8-byte aligned
+ *   out_scales    out [n_groups, num_tokens, D/128] fp32
+ * num_heads a multiple of n_groups; head_dim and rope_dim multiples of 8 with
+ * 0 < rope_dim <= head_dim; D a multiple of 128; max_pos >= 1 (else SAD_EINVAL).
+ * num_tokens == 0 is a no-op.
+ */
+int inv_rope_fp8_quant(const uint16_t* attn_out, const int32_t* positions,
+                       const float* cos_sin_cache, int32_t max_pos, int32_t rope_dim,
+                       int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                       int32_t n_groups, uint8_t* out_fp8, float* out_scales, void* stream);
+
 const char* sad_last_error(void);
 
 #ifdef __cplusplus

@@ -639,13 +639,17 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     The sign bit is copied from x (so -0.0 -> 0x80), as a float conversion does.
     """
     x = np.asarray(x, dtype=np.float64)
-    a = np.abs(x).reshape(-1, 1)
-    dist = np.abs(a - _E4M3_POS[None, :])
-    best = np.argmin(dist, axis=1)
-    nxt = np.minimum(best + 1, 126)
-    tie = (dist[np.arange(len(best)), nxt] == dist[np.arange(len(best)), best]) & (nxt != best)
-    best = np.where(tie & (best % 2 == 1), nxt, best)
-    codes = best.astype(np.uint8) | np.where(np.signbit(x.reshape(-1)), 0x80, 0).astype(np.uint8)
+    flat = x.reshape(-1)
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    for lo in range(0, len(flat), 1 << 16):  # in chunks, to bound the distance table
+        xs = flat[lo: lo + (1 << 16)]
+        dist = np.abs(np.abs(xs)[:, None] - _E4M3_POS[None, :])
+        best = np.argmin(dist, axis=1)
+        nxt = np.minimum(best + 1, 126)
+        r = np.arange(len(best))
+        tie = (dist[r, nxt] == dist[r, best]) & (nxt != best)
+        best = np.where(tie & (best % 2 == 1), nxt, best)
+        codes[lo: lo + len(xs)] = best.astype(np.uint8) | np.where(np.signbit(xs), 0x80, 0).astype(np.uint8)
     return codes.reshape(x.shape)
 
 

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     indexer_score_topk,
     prepare_indexer_q_mxfp4,
     indexer_score_topk_workspace_size,
+    inv_rope_fp8_quant,
     last_error,
     load,
     sparse_mla_decode,

@@ -55,6 +55,8 @@ _SIGNATURES = {
                                   ctypes.POINTER(SadKvCache), c_ptr, c_ptr, c_i32, c_i32, c_f32, c_ptr,
                                   c_ptr, c_ptr, c_ptr, c_size, c_ptr]),
     "sparse_mla_decode_workspace_size": (c_size, [c_i32, c_i32, c_i32, c_i32]),
+    "inv_rope_fp8_quant": (c_i32, [c_ptr, c_ptr, c_ptr, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_ptr,
+                                   c_ptr, c_ptr]),
     "sad_last_error": (ctypes.c_char_p, []),
 }
 
@@ -294,3 +296,33 @@ def sparse_mla_decode(q, swa: KvCache, comp: KvCache, sparse_indices, sparse_top
                                workspace.numel() if workspace is not None else 0, _stream(stream))
     _check("sparse_mla_decode", rc)
     return out
+
+
+def inv_rope_fp8_quant(attn_out, positions, cos_sin_cache, n_groups, out_fp8=None, out_scales=None,
+                       stream=None):
+    """bf16 attention output [T, H, Dh] -> (fp8 codes [G, T, D] u8, scales [G, T, D/128] f32):
+    inverse RoPE of each head's tail, heads grouped, power-of-two FP8 blocks of 128."""
+    lib = load()
+    _need(attn_out, torch.bfloat16, "attn_out", dim=3)
+    _need(positions, torch.int32, "positions", dim=1)
+    _need(cos_sin_cache, torch.float32, "cos_sin_cache", dim=2)
+    T, H, Dh = attn_out.shape
+    if positions.shape[0] != T:
+        raise ValueError("positions must be [T]")
+    if n_groups < 1 or H % n_groups:
+        raise ValueError("num_heads must be a multiple of n_groups")
+    D = H // n_groups * Dh
+    dev = attn_out.device
+    if out_fp8 is None:
+        out_fp8 = torch.empty((n_groups, T, D), dtype=torch.uint8, device=dev)
+    if out_scales is None:
+        out_scales = torch.empty((n_groups, T, max(D // 128, 1)), dtype=torch.float32, device=dev)
+    _need(out_fp8, torch.uint8, "out_fp8", dim=3)
+    _need(out_scales, torch.float32, "out_scales", dim=3)
+    if tuple(out_fp8.shape) != (n_groups, T, D) or tuple(out_scales.shape) != (n_groups, T, D // 128):
+        raise ValueError("outputs must be [G, T, D] and [G, T, D/128]")
+    rc = lib.inv_rope_fp8_quant(_p(attn_out), _p(positions), _p(cos_sin_cache), cos_sin_cache.shape[0],
+                                cos_sin_cache.shape[1], T, H, Dh, n_groups, _p(out_fp8), _p(out_scales),
+                                _stream(stream))
+    _check("inv_rope_fp8_quant", rc)
+    return out_fp8, out_scales

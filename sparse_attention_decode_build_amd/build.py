@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsad.so")
-SOURCES = ("abi.hip", "build_indices.hip", "indexer.hip", "indexer_q.hip", "gather.hip", "attention.hip")
+SOURCES = ("abi.hip", "build_indices.hip", "indexer.hip", "indexer_q.hip", "gather.hip", "attention.hip",
+           "out_quant.hip")
 ARCH = "gfx950"
 
 # hipcc flags: gfx950 only; packed-FP32 VALU ops disabled (hipcc's host pass warns

@@ -135,3 +135,19 @@ def test_prepare_indexer_q_errors(lib):
     assert _call_qprep(lib, T=-1) == L.SAD_EINVAL
     assert _call_qprep(lib, align=FAKE + 4) == L.SAD_EINVAL
     assert "aligned" in L.last_error()
+
+
+def _call_outq(lib, T=4, H=128, Dh=576, R=64, G=16, P=100, align=FAKE):
+    return lib.inv_rope_fp8_quant(align, FAKE, FAKE, P, R, T, H, Dh, G, FAKE, FAKE, None)
+
+
+def test_inv_rope_fp8_quant_errors(lib):
+    assert _call_outq(lib, T=0) == L.SAD_OK
+    assert _call_outq(lib, G=3) == L.SAD_EINVAL  # 128 heads not a multiple of 3
+    assert _call_outq(lib, R=0) == L.SAD_EINVAL
+    assert _call_outq(lib, R=36) == L.SAD_EINVAL
+    assert _call_outq(lib, R=640) == L.SAD_EINVAL  # rope longer than the head
+    assert _call_outq(lib, H=2, G=2, Dh=72, R=8) == L.SAD_EINVAL  # D = 72 not a multiple of 128
+    assert _call_outq(lib, P=0) == L.SAD_EINVAL
+    assert _call_outq(lib, align=FAKE + 8) == L.SAD_EINVAL
+    assert "aligned" in L.last_error()
