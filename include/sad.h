@@ -310,10 +310,10 @@ size_t sparse_mla_decode_workspace_size(int32_t num_tokens, int32_t num_heads,
  *   attn_out      [num_tokens, num_heads, head_dim] bf16, 16-byte aligned
  *   positions     [num_tokens] int32
  *   cos_sin_cache [max_pos, rope_dim] fp32, 16-byte aligned
- *   out_fp8       out [n_groups, num_tokens, D] u8 (e4m3fn), 8-byte aligned
+ *   out_fp8       out [n_groups, num_tokens, D] u8 (e4m3fn), 16-byte aligned
  *   out_scales    out [n_groups, num_tokens, D/128] fp32
- * num_heads a multiple of n_groups; head_dim and rope_dim multiples of 8 with
- * 0 < rope_dim <= head_dim; D a multiple of 128; max_pos >= 1 (else SAD_EINVAL).
+ * num_heads a multiple of n_groups; head_dim (>= 32) and rope_dim multiples of 8
+ * with 0 < rope_dim <= head_dim; D a multiple of 128; max_pos >= 1 (else SAD_EINVAL).
  * num_tokens == 0 is a no-op.
  */
 int inv_rope_fp8_quant(const uint16_t* attn_out, const int32_t* positions,

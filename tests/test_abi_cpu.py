@@ -148,6 +148,7 @@ def test_inv_rope_fp8_quant_errors(lib):
     assert _call_outq(lib, R=36) == L.SAD_EINVAL
     assert _call_outq(lib, R=640) == L.SAD_EINVAL  # rope longer than the head
     assert _call_outq(lib, H=2, G=2, Dh=72, R=8) == L.SAD_EINVAL  # D = 72 not a multiple of 128
+    assert _call_outq(lib, H=16, G=1, Dh=24, R=8) == L.SAD_EINVAL  # head_dim below 32
     assert _call_outq(lib, P=0) == L.SAD_EINVAL
     assert _call_outq(lib, align=FAKE + 8) == L.SAD_EINVAL
     assert "aligned" in L.last_error()
