@@ -38,6 +38,11 @@ Readings taken where the pages are silent (each is listed in the design doc):
   448 * 2^e >= amax, at least -33; blocks of 128 run along each group's row
   and may span two heads; output group major [G, T, D]; a position outside
   the table gives zero codes and zero scales
+* cache write side: RoPE at the compressed position floor(p / ratio) * ratio;
+  KV nope scales in the fp32 form, float32(max(amax, 1e-4)) / 448, codes
+  e4m3(clamp(x / scale)) with float32 division; indexer keys take the query's
+  RoPE -> bf16 -> rotation -> MXFP4 steps; a negative slot, a page past the pool
+  or a position outside the cos/sin table is skipped
 """
 
 from __future__ import annotations
@@ -709,6 +714,95 @@ def inv_rope_fp8_quant(o_bits, positions, cos_sin_cache, n_groups: int, rope_dim
     codes[:, ~ok] = 0
     scales[:, ~ok] = 0.0
     return codes, scales
+
+
+# ---------------------------------------------------------------------------
+# Cache write side: compressed KV rows and indexer keys into their paged caches
+# ---------------------------------------------------------------------------
+
+
+def compressed_position(positions, ratio: int) -> np.ndarray:
+    """[ops] ``_fp8_ds_mla_cache_rows``: the RoPE position of a compressed row is its
+    token position rounded down to a multiple of the compress ratio."""
+    return (np.asarray(positions, dtype=np.int64) // ratio) * ratio
+
+
+def encode_kv_nope(x: np.ndarray):
+    """bf16-valued nope rows [n, Dn] -> (e4m3fn bytes [n, Dn], fp32 scales [n, Dn/64]).
+
+    Per 64 elements ([ops] ``_fp8_ds_mla_cache_rows``: blocks of 64, amax clamped
+    below at 1e-4), with the fp32 scale form of these caches: scale =
+    float32(max(amax, 1e-4)) / 448 and code = e4m3(clamp(x / scale, +-448)), both
+    divisions single float32 operations.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    n, dn = x.shape
+    blocks = x.reshape(n, dn // 64, 64)
+    amax = np.maximum(np.abs(blocks).max(axis=-1), np.float32(1.0e-4)).astype(np.float32)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    y = np.clip((blocks / scale[..., None]).astype(np.float32), -448.0, 448.0)
+    return e4m3_encode(y.astype(np.float64)).reshape(n, dn), scale
+
+
+def insert_kv_rows(kv_pages: dict, rows_bits, positions, cos_sin_cache, ratio: int, slots,
+                   block_size: int, d_nope: int, d_rope: int, num_pages: int, page_bytes: int) -> dict:
+    """Write compressed KV rows into the paged latent cache; returns the updated pages.
+
+    [ops] ``_write_fp8_ds_mla_cache_rows_capturable`` / ``_fp8_ds_mla_cache_rows``:
+    the rope tail is rotated (GPT-J) at the compressed position and stored bf16;
+    the nope part is stored FP8 with one scale per 64 (``encode_kv_nope``); row
+    ``o`` of page ``g`` holds its values at ``g*stride + o*(Dn + 2*Dr)`` and its
+    scales at ``g*stride + B*(Dn + 2*Dr) + o*4*Dn/64``.  A slot that is negative
+    or whose page is past the pool is skipped.  Pages not yet in ``kv_pages`` start
+    as zero bytes.
+    """
+    x = bf16_bits_to_float(rows_bits).astype(np.float32)
+    cs = np.asarray(cos_sin_cache, dtype=np.float32)
+    cp = compressed_position(positions, ratio)
+    out = {k: v.copy() for k, v in kv_pages.items()}
+    row_b, nsc = d_nope + 2 * d_rope, d_nope // 64
+    for i, s in enumerate(np.asarray(slots, dtype=np.int64)):
+        if s < 0 or s // block_size >= num_pages or not (0 <= cp[i] < cs.shape[0]):
+            continue
+        roped = rope_gptj_tail(x[i], cs[cp[i], : d_rope // 2], cs[cp[i], d_rope // 2:], d_rope)
+        codes, scale = encode_kv_nope(x[i: i + 1, :d_nope])
+        g, o = int(s) // block_size, int(s) % block_size
+        page = out.setdefault(g, np.zeros(page_bytes, dtype=np.uint8))
+        page[o * row_b: o * row_b + d_nope] = codes[0]
+        page[o * row_b + d_nope: (o + 1) * row_b] = float32_to_bf16_bits(roped[d_nope:]).view(np.uint8)
+        sb = block_size * row_b + o * 4 * nsc
+        page[sb: sb + 4 * nsc] = scale[0].astype(np.float32).view(np.uint8)
+    return out
+
+
+def insert_index_keys(idx_pages: dict, keys_bits, positions, cos_sin_cache, ratio: int, slots,
+                      block_size: int, dim: int, num_pages: int, page_bytes: int) -> dict:
+    """Write compressed indexer keys into the paged MXFP4 cache; returns the updated pages.
+
+    [ops] compressor path (``_apply_gptj_rope_tail_rows`` at the compressed
+    position, then ``_deepseek_v4_hadamard_rotate``, then the quantizer) and
+    ``write_deepseek_v4_indexer_mxfp4_cache`` (page = ``[B x dim/2 values]`` then
+    ``[B x dim/32 e8m0]``).  The key takes the same RoPE -> bf16 -> rotation ->
+    MXFP4 steps as the query in ``prepare_indexer_q_mxfp4``.  A slot that is
+    negative or whose page is past the pool is skipped.
+    """
+    cs = np.asarray(cos_sin_cache, dtype=np.float32)
+    R = cs.shape[1]
+    cp = compressed_position(positions, ratio)
+    out = {k: v.copy() for k, v in idx_pages.items()}
+    vb, sb = dim // 2, dim // 32
+    x = bf16_bits_to_float(keys_bits).astype(np.float32)
+    for i, s in enumerate(np.asarray(slots, dtype=np.int64)):
+        if s < 0 or s // block_size >= num_pages or not (0 <= cp[i] < cs.shape[0]):
+            continue
+        roped = rope_gptj_tail(x[i], cs[cp[i], : R // 2], cs[cp[i], R // 2:], R)
+        rotated = hadamard_rotate(float32_to_bf16_bits(roped))
+        vals, exps = mxfp4_encode(bf16_bits_to_float(rotated)[None, :])
+        g, o = int(s) // block_size, int(s) % block_size
+        page = out.setdefault(g, np.zeros(page_bytes, dtype=np.uint8))
+        page[o * vb: (o + 1) * vb] = vals[0]
+        page[block_size * vb + o * sb: block_size * vb + (o + 1) * sb] = exps[0]
+    return out
 
 
 # ---------------------------------------------------------------------------

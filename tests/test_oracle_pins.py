@@ -586,3 +586,99 @@ def test_inv_rope_fp8_quant_layout_and_error_bound():
                 step = np.repeat(scales[gi, t], 128)[seg]
                 err = np.abs(dec - head)
                 assert (err <= np.maximum(np.abs(head) * 2.0 ** -4, step * 2.0 ** -10) + 1e-6 * np.abs(head)).all()
+
+
+# --------------------------------------------------------------------------- cache write side
+
+
+def test_kv_nope_encoder_matches_harness_encoder_and_floor():
+    g = torch.Generator().manual_seed(17)
+    x = (torch.randn(30, 512, generator=g) * torch.exp2(torch.randint(-12, 12, (30, 1), generator=g).float()))
+    x[3] = 0.0
+    x[4] *= 1e-9  # amax below 1e-4: the scale floors at 1e-4 / 448
+    x = x.bfloat16().float()
+    codes, scales = O.encode_kv_nope(x.numpy())
+    hc, hs = WL.encode_fp8_rows(x)
+    assert np.array_equal(codes, hc.numpy()) and np.array_equal(scales.view(np.uint32), hs.numpy().view(np.uint32))
+    assert np.all(scales[3] == np.float32(np.float32(1e-4) / np.float32(448.0)))
+
+
+def _kv_geom(d_nope=512, d_rope=64, block=16):
+    row_b = d_nope + 2 * d_rope
+    return row_b, block * (row_b + 4 * (d_nope // 64))
+
+
+def test_insert_kv_rows_round_trip_and_skips():
+    g = np.random.default_rng(19)
+    Dn, Dr, B, npages = 512, 64, 16, 6
+    row_b, page_bytes = _kv_geom(Dn, Dr, B)
+    rows = torch.from_numpy(g.standard_normal((5, Dn + Dr)).astype(np.float32)).bfloat16()
+    bits = rows.view(torch.int16).numpy().view(np.uint16)
+    cs = WL.rope_table(100, Dr).numpy()
+    pos = np.array([3, 7, 8, 50, 60])
+    slots = np.array([5, -1, 17, 6 * B, 40])  # one skipped by -1, one past the pool
+    before = {p: g.integers(0, 256, page_bytes).astype(np.uint8) for p in range(npages)}
+    after = O.insert_kv_rows(before, bits, pos, cs, 4, slots, B, Dn, Dr, npages, page_bytes)
+    back = O.dequant_rows(after, [5, 17, 40], B, Dn, Dr)
+    xf = rows.float().numpy().astype(np.float64)
+    for r, i in enumerate([0, 2, 4]):
+        nope = O.bf16_bits_to_float(back[r, :Dn])
+        assert (np.abs(nope - xf[i, :Dn]) <= np.abs(xf[i, :Dn]) * 2.0 ** -4 + 2.0 ** -9 * np.repeat(
+            np.abs(xf[i, :Dn]).reshape(-1, 64).max(1), 64) / 448 * 2).all()
+        cp = (pos[i] // 4) * 4
+        th = cp * 10000.0 ** (-np.arange(Dr // 2) * 2.0 / Dr)
+        z = (xf[i, Dn::2] + 1j * xf[i, Dn + 1::2]) * np.exp(1j * th)
+        rope = O.bf16_bits_to_float(back[r, Dn:])
+        assert np.allclose(rope[0::2], z.real, atol=2.0 ** -7 * np.abs(z).max())
+        assert np.allclose(rope[1::2], z.imag, atol=2.0 ** -7 * np.abs(z).max())
+    # only the written rows' value bytes and scale bytes changed
+    for p in range(npages):
+        diff = np.flatnonzero(after[p] != before[p])
+        allowed = set()
+        for s in (5, 17, 40):
+            if s // B == p:
+                o = s % B
+                allowed |= set(range(o * row_b, (o + 1) * row_b))
+                allowed |= set(range(B * row_b + o * 32, B * row_b + o * 32 + 32))
+        assert set(diff.tolist()) <= allowed
+
+
+def test_compressed_position_groups_tokens():
+    assert list(O.compressed_position([0, 3, 4, 7, 8, 127, 128], 4)) == [0, 0, 4, 4, 8, 124, 128]
+    assert list(O.compressed_position([5, 130], 128)) == [0, 128]
+    Dn, Dr, B = 128, 32, 16
+    row_b, page_bytes = _kv_geom(Dn, Dr, B)
+    row = torch.randn(1, Dn + Dr, generator=torch.Generator().manual_seed(1)).bfloat16()
+    bits = np.repeat(row.view(torch.int16).numpy().view(np.uint16), 3, axis=0)
+    cs = WL.rope_table(64, Dr).numpy()
+    out = O.insert_kv_rows({}, bits, [8, 11, 12], cs, 4, [0, 1, 2], B, Dn, Dr, 1, page_bytes)[0]
+    r0, r1, r2 = (out[i * row_b: (i + 1) * row_b] for i in range(3))
+    assert np.array_equal(r0, r1) and not np.array_equal(r0[Dn:], r2[Dn:])
+
+
+def test_insert_index_keys_matches_the_rotated_key():
+    # The written key decodes to the RoPE'd (at the compressed position), rotated key
+    # within the MXFP4 step, in the right page row, with its exponents after the values.
+    g = np.random.default_rng(23)
+    D, R, B, npages = 128, 64, 16, 3
+    page_bytes = B * (D // 2 + D // 32)
+    keys = torch.from_numpy(g.standard_normal((3, D)).astype(np.float32)).bfloat16()
+    bits = keys.view(torch.int16).numpy().view(np.uint16)
+    cs = WL.rope_table(200, R).numpy()
+    pos, slots = np.array([9, 100, 150]), np.array([3, 20, -1])
+    pages = O.insert_index_keys({}, bits, pos, cs, 4, slots, B, D, npages, page_bytes)
+    assert set(pages) == {0, 1}
+    got, valid = O.read_index_keys(pages, np.array([0, 1]), 21, B, D, npages)
+    kf = keys.float().numpy().astype(np.float64)
+    import scipy.linalg
+    H = scipy.linalg.hadamard(D) / np.sqrt(D)
+    for i, s in ((0, 3), (1, 20)):
+        cp = (pos[i] // 4) * 4
+        th = cp * 10000.0 ** (-np.arange(R // 2) * 2.0 / R)
+        k = kf[i].copy()
+        z = (k[D - R::2] + 1j * k[D - R + 1::2]) * np.exp(1j * th)
+        k[D - R::2], k[D - R + 1::2] = z.real, z.imag
+        ideal = H @ k
+        step = np.repeat(np.ldexp(1.0, pages[s // B][B * D // 2 + (s % B) * 4: B * D // 2 + (s % B) * 4 + 4]
+                                  .astype(np.int64) - 127), 32)
+        assert (np.abs(got[s] - ideal) <= step + 2.0 ** -7 * np.abs(ideal)).all()
