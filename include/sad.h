@@ -321,6 +321,58 @@ int inv_rope_fp8_quant(const uint16_t* attn_out, const int32_t* positions,
                        int32_t num_tokens, int32_t num_heads, int32_t head_dim,
                        int32_t n_groups, uint8_t* out_fp8, float* out_scales, void* stream);
 
+/*
+ * insert_kv_rows - compressed KV rows into the paged FP8 latent cache (the write side
+ * of the rows sparse_mla_decode reads).
+ *
+ * Defined by [ops] _write_fp8_ds_mla_cache_rows_capturable and _fp8_ds_mla_cache_rows,
+ * with the fp32 scale form of the cache (sad_kv_cache): for row i with slot
+ * s = slot_mapping[i] and compressed position c = floor(positions[i] / ratio) * ratio:
+ *   - rope part: GPT-J rotation at c ((e, o) -> (e*cos - o*sin, e*sin + o*cos), each
+ *     product and sum one fp32 operation), stored bf16 (nearest even);
+ *   - nope part, per 64 values: scale = fp32(max(amax, 1e-4)) / 448 and code =
+ *     e4m3fn(clamp(x / scale, +-448)) (correctly rounded fp32 divisions, nearest even);
+ *   - row s % B of page s / B: values at page*page_stride + (s % B)*(Dn + 2*Dr), scales
+ *     at page*page_stride + B*(Dn + 2*Dr) + (s % B)*4*Dn/64.
+ * A negative slot, a page past num_pages or c outside [0, max_pos) writes nothing.  The
+ * cache's pool is written in place; two rows with the same slot race.
+ *
+ *   rows           [num_rows, Dn + Dr] bf16 (before RoPE), 16-byte aligned
+ *   positions      [num_rows] int32 token positions
+ *   cos_sin_cache  [max_pos, Dr] fp32 (cos columns, then sin), 16-byte aligned
+ *   slot_mapping   [num_rows] int32
+ * (Dn, Dr) and the page geometry as for sparse_mla_decode; compress_ratio >= 1 and
+ * max_pos >= 1 (else SAD_EINVAL).  num_rows == 0 is a no-op.
+ */
+int insert_kv_rows(const uint16_t* rows, const int32_t* positions, const float* cos_sin_cache,
+                   int32_t max_pos, int32_t compress_ratio, const int32_t* slot_mapping,
+                   int32_t num_rows, const sad_kv_cache* cache, void* stream);
+
+/*
+ * insert_index_keys - compressed indexer keys into the paged MXFP4 cache (the write side
+ * of the keys indexer_score_topk reads).
+ *
+ * Defined by the [ops] compressor path (_apply_gptj_rope_tail_rows at the compressed
+ * position, then _deepseek_v4_hadamard_rotate, then the quantizer) and
+ * write_deepseek_v4_indexer_mxfp4_cache (page = [B x dim/2 values] then
+ * [B x dim/32 e8m0]).  Each key takes exactly the steps 1-3 of prepare_indexer_q_mxfp4
+ * (RoPE on the last rope_dim values at c = floor(positions[i] / ratio) * ratio, bf16,
+ * the fp32 fast Hadamard transform with scale dim^-1/2, bf16, MXFP4) and is stored at
+ * row s % B of page s / B, s = slot_mapping[i].  A negative slot, a page past
+ * num_pages or c outside [0, max_pos) writes nothing; the pool is written in place.
+ *
+ *   keys           [num_rows, dim] bf16 (before RoPE), 16-byte aligned
+ *   positions      [num_rows] int32; cos_sin_cache [max_pos, rope_dim] fp32, 16-byte aligned
+ *   slot_mapping   [num_rows] int32
+ * dim in {64, 128} and block_size in {16, 64} (else SAD_EUNSUPPORTED); rope_dim a
+ * multiple of 8 in (0, dim); page_stride >= block_size*(dim/2 + dim/32), a multiple of
+ * 16; the pool 16-byte aligned (else SAD_EINVAL).  num_rows == 0 is a no-op.
+ */
+int insert_index_keys(const uint16_t* keys, const int32_t* positions, const float* cos_sin_cache,
+                      int32_t max_pos, int32_t rope_dim, int32_t compress_ratio,
+                      const int32_t* slot_mapping, int32_t num_rows, const sad_mxfp4_cache* cache,
+                      void* stream);
+
 const char* sad_last_error(void);
 
 #ifdef __cplusplus

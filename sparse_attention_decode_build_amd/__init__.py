@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     indexer_score_topk,
     prepare_indexer_q_mxfp4,
     indexer_score_topk_workspace_size,
+    insert_index_keys,
+    insert_kv_rows,
     inv_rope_fp8_quant,
     last_error,
     load,

@@ -57,6 +57,10 @@ _SIGNATURES = {
     "sparse_mla_decode_workspace_size": (c_size, [c_i32, c_i32, c_i32, c_i32]),
     "inv_rope_fp8_quant": (c_i32, [c_ptr, c_ptr, c_ptr, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_ptr,
                                    c_ptr, c_ptr]),
+    "insert_kv_rows": (c_i32, [c_ptr, c_ptr, c_ptr, c_i32, c_i32, c_ptr, c_i32, ctypes.POINTER(SadKvCache),
+                               c_ptr]),
+    "insert_index_keys": (c_i32, [c_ptr, c_ptr, c_ptr, c_i32, c_i32, c_i32, c_ptr, c_i32,
+                                  ctypes.POINTER(SadMxfp4Cache), c_ptr]),
     "sad_last_error": (ctypes.c_char_p, []),
 }
 
@@ -326,3 +330,39 @@ def inv_rope_fp8_quant(attn_out, positions, cos_sin_cache, n_groups, out_fp8=Non
                                 _stream(stream))
     _check("inv_rope_fp8_quant", rc)
     return out_fp8, out_scales
+
+
+def insert_kv_rows(rows, positions, cos_sin_cache, compress_ratio, slot_mapping, cache: KvCache, stream=None):
+    """Write bf16 rows [N, Dn+Dr] (before RoPE) into the paged FP8 cache at their slots (in place)."""
+    lib = load()
+    _need(rows, torch.bfloat16, "rows", dim=2)
+    _need(positions, torch.int32, "positions", dim=1)
+    _need(cos_sin_cache, torch.float32, "cos_sin_cache", dim=2)
+    _need(slot_mapping, torch.int32, "slot_mapping", dim=1)
+    N = rows.shape[0]
+    if positions.shape[0] != N or slot_mapping.shape[0] != N or rows.shape[1] != cache.d_nope + cache.d_rope:
+        raise ValueError("rows [N, Dn+Dr], positions [N] and slot_mapping [N] must agree")
+    if cos_sin_cache.shape[1] != cache.d_rope:
+        raise ValueError("cos_sin_cache must be [max_pos, d_rope]")
+    kc = cache.c()
+    rc = lib.insert_kv_rows(_p(rows), _p(positions), _p(cos_sin_cache), cos_sin_cache.shape[0], compress_ratio,
+                            _p(slot_mapping), N, ctypes.byref(kc), _stream(stream))
+    _check("insert_kv_rows", rc)
+
+
+def insert_index_keys(keys, positions, cos_sin_cache, compress_ratio, slot_mapping, cache: IndexerCache,
+                      stream=None):
+    """Write bf16 keys [N, dim] (before RoPE) into the paged MXFP4 cache at their slots (in place)."""
+    lib = load()
+    _need(keys, torch.bfloat16, "keys", dim=2)
+    _need(positions, torch.int32, "positions", dim=1)
+    _need(cos_sin_cache, torch.float32, "cos_sin_cache", dim=2)
+    _need(slot_mapping, torch.int32, "slot_mapping", dim=1)
+    N = keys.shape[0]
+    if positions.shape[0] != N or slot_mapping.shape[0] != N or keys.shape[1] != cache.dim:
+        raise ValueError("keys [N, dim], positions [N] and slot_mapping [N] must agree")
+    kc = cache.c()
+    rc = lib.insert_index_keys(_p(keys), _p(positions), _p(cos_sin_cache), cos_sin_cache.shape[0],
+                               cos_sin_cache.shape[1], compress_ratio, _p(slot_mapping), N, ctypes.byref(kc),
+                               _stream(stream))
+    _check("insert_index_keys", rc)

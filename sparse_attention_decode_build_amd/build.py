@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsad.so")
 SOURCES = ("abi.hip", "build_indices.hip", "indexer.hip", "indexer_q.hip", "gather.hip", "attention.hip",
-           "out_quant.hip")
+           "out_quant.hip", "cache_write.hip")
 ARCH = "gfx950"
 
 # hipcc flags: gfx950 only; packed-FP32 VALU ops disabled (hipcc's host pass warns

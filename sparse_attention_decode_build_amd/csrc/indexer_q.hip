@@ -68,34 +68,25 @@ __device__ inline float quad_xor(float v) {
   return __uint_as_float(quad_xor<M>(__float_as_uint(v)));
 }
 
+// The lane's part of one row's transform: RoPE on the tail at cos/sin row `cs`, bf16,
+// the fp32 fast Hadamard transform (Sylvester order), the scale and bf16, and the
+// MXFP4 codes of the lane's D/4 values (word[D/32], the even value in the low nibble).
+// Returns the exponent of the lane's scale block.  All four lanes of the quad call it
+// (the top transform stages are quad permutes).
 template <int D>
-__global__ __launch_bounds__(kQThreads) void prepare_indexer_q_kernel(
-    const uint16_t* __restrict__ q, const int32_t* __restrict__ positions,
-    const float* __restrict__ cos_sin, int max_pos, int rope_dim,
-    const float* __restrict__ weights, float softmax_scale, float head_scale, float rot_scale,
-    int rows, int heads, uint8_t* __restrict__ q_values, uint8_t* __restrict__ q_scales,
-    float* __restrict__ weights_out) {
+__device__ inline int quad_row_mxfp4(const uint16_t* __restrict__ row, const float* __restrict__ cs,
+                                     int rope_dim, int sub, float rot_scale, uint32_t* word) {
 #pragma clang fp contract(off)
   constexpr int EPL = D / 4;   // elements per lane
   constexpr int NG = EPL / 8;  // 8-element (16-byte) groups per lane
   static_assert(EPL == 16 || EPL == 32, "a lane holds 16 or 32 elements");
-  const int sub = threadIdx.x & 3;
-  const int row = (int)blockIdx.x * kRowsPerBlock + ((int)threadIdx.x >> 2);
-  const bool live = row < rows;
-  const int r = live ? row : rows - 1;  // dead lanes still join the quad permutes
-  const int t = r / heads;
   const int d_lane = sub * EPL;
+  const int nope = D - rope_dim;
 
   // Every load of the lane is issued before the first use.
   u32x4_t raw[NG];
 #pragma unroll
-  for (int g = 0; g < NG; ++g)
-    raw[g] = *reinterpret_cast<const u32x4_t*>(q + (int64_t)r * D + d_lane + 8 * g);
-  const int pos = positions[t];
-  const float w = weights[r];
-  const bool ok = pos >= 0 && pos < max_pos;
-  const int nope = D - rope_dim;
-  const float* cs = cos_sin + (int64_t)(ok ? pos : 0) * rope_dim;
+  for (int g = 0; g < NG; ++g) raw[g] = *reinterpret_cast<const u32x4_t*>(row + d_lane + 8 * g);
   float4 cg[NG], sg[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
@@ -165,13 +156,11 @@ __global__ __launch_bounds__(kQThreads) void prepare_indexer_q_kernel(
     mx = max(mx, max(m & 0xFFFFu, m >> 16));
   }
   if (EPL == 16) mx = max(mx, quad_xor<1>(mx));  // D = 64: a block is a lane pair
-  const float amax = __uint_as_float(mx << 16);
 
   // MXFP4 codes: the conversion divides by the scale's power of two (exponent field
   // e + 127; 0 means 2^-127), rounds to nearest even, saturates, copies the sign bit.
-  const int e = block_exponent(amax);
+  const int e = block_exponent(__uint_as_float(mx << 16));
   const float scale = __uint_as_float((uint32_t)(e + 127) << 23);
-  uint32_t word[EPL / 8];
 #pragma unroll
   for (int wd = 0; wd < EPL / 8; ++wd) {
     const uint32_t* p = yb + 4 * wd;
@@ -179,18 +168,75 @@ __global__ __launch_bounds__(kQThreads) void prepare_indexer_q_kernel(
     v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf16x2_t, p[1]), scale, 1);
     v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf16x2_t, p[2]), scale, 2);
     v = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(v, __builtin_bit_cast(bf16x2_t, p[3]), scale, 3);
-    word[wd] = ok ? v : 0u;
+    word[wd] = v;
   }
-  if (!live) return;
-  uint8_t* vout = q_values + (int64_t)r * (D / 2) + sub * (EPL / 2);
+  return e;
+}
+
+// The lane's codes (D/4 values) and, from one lane per 32-value block, its scale byte.
+template <int D>
+__device__ inline void store_quad_row(uint8_t* vout, uint8_t* sout, int sub, const uint32_t* word,
+                                      int e, bool ok) {
+  constexpr int EPL = D / 4;
+  uint8_t* v = vout + sub * (EPL / 2);
   if constexpr (EPL == 32) {
-    *reinterpret_cast<u32x4_t*>(vout) = u32x4_t{word[0], word[1], word[2], word[3]};
-    q_scales[(int64_t)r * (D / 32) + sub] = ok ? (uint8_t)(e + 127) : 0;
+    *reinterpret_cast<u32x4_t*>(v) = ok ? u32x4_t{word[0], word[1], word[2], word[3]} : u32x4_t{0, 0, 0, 0};
+    sout[sub] = ok ? (uint8_t)(e + 127) : 0;
   } else {
-    *reinterpret_cast<uint2*>(vout) = make_uint2(word[0], word[1]);
-    if ((sub & 1) == 0) q_scales[(int64_t)r * (D / 32) + (sub >> 1)] = ok ? (uint8_t)(e + 127) : 0;
+    *reinterpret_cast<uint2*>(v) = ok ? make_uint2(word[0], word[1]) : make_uint2(0u, 0u);
+    if ((sub & 1) == 0) sout[sub >> 1] = ok ? (uint8_t)(e + 127) : 0;
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(kQThreads) void prepare_indexer_q_kernel(
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ positions,
+    const float* __restrict__ cos_sin, int max_pos, int rope_dim,
+    const float* __restrict__ weights, float softmax_scale, float head_scale, float rot_scale,
+    int rows, int heads, uint8_t* __restrict__ q_values, uint8_t* __restrict__ q_scales,
+    float* __restrict__ weights_out) {
+#pragma clang fp contract(off)
+  const int sub = threadIdx.x & 3;
+  const int row = (int)blockIdx.x * kRowsPerBlock + ((int)threadIdx.x >> 2);
+  const bool live = row < rows;
+  const int r = live ? row : rows - 1;  // dead lanes still join the quad permutes
+  const int t = r / heads;
+  const int pos = positions[t];
+  const float w = weights[r];
+  const bool ok = pos >= 0 && pos < max_pos;
+  uint32_t word[D / 32];
+  const int e = quad_row_mxfp4<D>(q + (int64_t)r * D, cos_sin + (int64_t)(ok ? pos : 0) * rope_dim,
+                                  rope_dim, sub, rot_scale, word);
+  if (!live) return;
+  store_quad_row<D>(q_values + (int64_t)r * (D / 2), q_scales + (int64_t)r * (D / 32), sub, word, e, ok);
   if (sub == 0) weights_out[r] = ok ? (w * softmax_scale) * head_scale : 0.0f;
+}
+
+// Key rows written into the paged MXFP4 cache at their slots (RoPE at the compressed
+// position); a negative slot, a page past the pool or a position outside the table
+// writes nothing.
+template <int D>
+__global__ __launch_bounds__(kQThreads) void insert_index_keys_kernel(
+    const uint16_t* __restrict__ keys, const int32_t* __restrict__ positions,
+    const float* __restrict__ cos_sin, int max_pos, int rope_dim, int ratio, float rot_scale,
+    const int32_t* __restrict__ slots, int rows, uint8_t* __restrict__ pool, int64_t page_stride,
+    int64_t num_pages, int block) {
+  const int sub = threadIdx.x & 3;
+  const int row = (int)blockIdx.x * kRowsPerBlock + ((int)threadIdx.x >> 2);
+  const bool live = row < rows;
+  const int r = live ? row : rows - 1;
+  const int slot = slots[r];
+  const int pos = positions[r];
+  const int cp = pos >= 0 ? (pos / ratio) * ratio : -1;
+  const bool ok = slot >= 0 && (int64_t)(slot / block) < num_pages && cp >= 0 && cp < max_pos;
+  uint32_t word[D / 32];
+  const int e = quad_row_mxfp4<D>(keys + (int64_t)r * D, cos_sin + (int64_t)(cp >= 0 && cp < max_pos ? cp : 0) * rope_dim,
+                                  rope_dim, sub, rot_scale, word);
+  if (!live || !ok) return;
+  uint8_t* page = pool + (int64_t)(slot / block) * page_stride;
+  const int ro = slot % block;
+  store_quad_row<D>(page + (int64_t)ro * (D / 2), page + (int64_t)block * (D / 2) + (int64_t)ro * (D / 32),
+                    sub, word, e, true);
 }
 
 }  // namespace
@@ -241,4 +287,51 @@ extern "C" int prepare_indexer_q_mxfp4(const uint16_t* index_q, const int32_t* p
                        q_values, q_scales, weights_out);
   }
   return check_launch("prepare_indexer_q_mxfp4");
+}
+
+extern "C" int insert_index_keys(const uint16_t* keys, const int32_t* positions,
+                                 const float* cos_sin_cache, int32_t max_pos, int32_t rope_dim,
+                                 int32_t compress_ratio, const int32_t* slot_mapping,
+                                 int32_t num_rows, const sad_mxfp4_cache* cache, void* stream) {
+  clear_error();
+  SAD_CHECK(cache != nullptr, SAD_EINVAL, "insert_index_keys: cache is NULL");
+  const int D = cache->dim;
+  SAD_CHECK(D == 64 || D == 128, SAD_EUNSUPPORTED,
+            "insert_index_keys: dim must be 64 or 128 (got %d)", D);
+  SAD_CHECK(cache->block_size == 16 || cache->block_size == 64, SAD_EUNSUPPORTED,
+            "insert_index_keys: block_size must be 16 or 64 (got %d)", cache->block_size);
+  SAD_CHECK(num_rows >= 0 && max_pos >= 0 && compress_ratio >= 1 && cache->num_pages >= 0,
+            SAD_EINVAL, "insert_index_keys: bad size");
+  SAD_CHECK(rope_dim > 0 && rope_dim < D && rope_dim % 8 == 0, SAD_EINVAL,
+            "insert_index_keys: rope_dim must be a multiple of 8 in (0, dim) (got %d)", rope_dim);
+  SAD_CHECK(cache->page_stride >= (int64_t)cache->block_size * (D / 2 + D / 32), SAD_EINVAL,
+            "insert_index_keys: page_stride below block_size * (dim/2 + dim/32)");
+  if (num_rows == 0) return SAD_OK;
+  SAD_CHECK(max_pos >= 1, SAD_EINVAL, "insert_index_keys: the cos/sin table has no row");
+  SAD_CHECK(keys && positions && cos_sin_cache && slot_mapping && cache->pool, SAD_EINVAL,
+            "insert_index_keys: NULL pointer argument");
+  SAD_CHECK(((uintptr_t)keys & 15) == 0 && ((uintptr_t)cos_sin_cache & 15) == 0 &&
+                ((uintptr_t)cache->pool & 15) == 0 && cache->page_stride % 16 == 0,
+            SAD_EINVAL,
+            "insert_index_keys: keys, cos_sin_cache and the pool must be 16-byte aligned, "
+            "page_stride a multiple of 16");
+  SAD_CHECK(cache->num_pages * (int64_t)cache->block_size <= INT32_MAX, SAD_EINVAL,
+            "insert_index_keys: pool too large for int32 slots");
+  SAD_CHECK((int64_t)num_rows + kRowsPerBlock < ((int64_t)1 << 31), SAD_EINVAL,
+            "insert_index_keys: too many rows");
+  const unsigned grid = (unsigned)(((int64_t)num_rows + kRowsPerBlock - 1) / kRowsPerBlock);
+  const float rot_scale = (float)(1.0 / std::sqrt((double)D));
+  uint8_t* pool = (uint8_t*)const_cast<void*>(cache->pool);
+  if (D == 128) {
+    hipLaunchKernelGGL((insert_index_keys_kernel<128>), dim3(grid), dim3(kQThreads), 0,
+                       (hipStream_t)stream, keys, positions, cos_sin_cache, max_pos, rope_dim,
+                       compress_ratio, rot_scale, slot_mapping, num_rows, pool, cache->page_stride,
+                       cache->num_pages, cache->block_size);
+  } else {
+    hipLaunchKernelGGL((insert_index_keys_kernel<64>), dim3(grid), dim3(kQThreads), 0,
+                       (hipStream_t)stream, keys, positions, cos_sin_cache, max_pos, rope_dim,
+                       compress_ratio, rot_scale, slot_mapping, num_rows, pool, cache->page_stride,
+                       cache->num_pages, cache->block_size);
+  }
+  return check_launch("insert_index_keys");
 }

@@ -152,3 +152,30 @@ def test_inv_rope_fp8_quant_errors(lib):
     assert _call_outq(lib, P=0) == L.SAD_EINVAL
     assert _call_outq(lib, align=FAKE + 8) == L.SAD_EINVAL
     assert "aligned" in L.last_error()
+
+
+def test_insert_kv_rows_errors(lib):
+    c = _kv()
+    ok = lambda **k: lib.insert_kv_rows(k.get("rows", FAKE), FAKE, FAKE, k.get("P", 100), k.get("ratio", 4), FAKE,
+                                        k.get("N", 3), ctypes.byref(k.get("cache", c)), None)
+    assert ok(N=0) == L.SAD_OK
+    assert ok(ratio=0) == L.SAD_EINVAL
+    assert ok(P=0) == L.SAD_EINVAL
+    assert ok(rows=FAKE + 2) == L.SAD_EINVAL
+    assert ok(cache=_kv(d_nope=256)) == L.SAD_EUNSUPPORTED
+    assert ok(cache=_kv(stride=1024)) == L.SAD_EINVAL
+    assert lib.insert_kv_rows(FAKE, FAKE, FAKE, 100, 4, FAKE, 3, None, None) == L.SAD_EINVAL
+
+
+def test_insert_index_keys_errors(lib):
+    def call(dim=128, block=64, R=64, N=3, P=100, ratio=4, stride=None):
+        stride = stride if stride is not None else block * (dim // 2 + dim // 32)
+        keys = L.SadMxfp4Cache(FAKE, stride, 10, block, dim)
+        return lib.insert_index_keys(FAKE, FAKE, FAKE, P, R, ratio, FAKE, N, ctypes.byref(keys), None)
+    assert call(N=0) == L.SAD_OK
+    assert call(dim=96) == L.SAD_EUNSUPPORTED
+    assert call(block=32) == L.SAD_EUNSUPPORTED
+    assert call(R=128) == L.SAD_EINVAL
+    assert call(ratio=0) == L.SAD_EINVAL
+    assert call(stride=64) == L.SAD_EINVAL
+    assert call(P=0) == L.SAD_EINVAL
