@@ -251,6 +251,78 @@ def summarize_traffic(fetch_dir: str, write_dir: str) -> int:
     return 0
 
 
+def _time_launches(call, iters: int, warmup: int) -> float:
+    """Average microseconds per launch of ``call(i)``, queued behind a spin kernel so
+    the events time the kernels back to back rather than the host's submission rate."""
+    for i in range(warmup):
+        call(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(4_000_000)
+    e0.record()
+    for i in range(iters):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / iters
+
+
+def bench_inv_rope_fp8_quant(num_tokens: int, positions, iters: int = 20, warmup: int = 3) -> dict:
+    """Event-timed inv_rope_fp8_quant on the attention output (128 heads x 576, rope 64,
+    16 groups of 8 heads; two input sets alternated).  Algorithmic bytes: 2 in and 1 out
+    per value, 4 per 128-value scale; per token its position and cos/sin row."""
+    H, Dh, R, G, P = 128, 576, 64, 16, 65536
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    sets = [(torch.randn(num_tokens, H, Dh, device="cuda", generator=gen).mul_(0.03).bfloat16(),
+             torch.as_tensor(positions if positions is not None else
+                             torch.randint(0, P, (num_tokens,), device="cuda", generator=gen),
+                             dtype=torch.int32, device="cuda"),
+             WL.rope_table(P, R).cuda()) for _ in range(2)]
+    D = H // G * Dh
+    outs = [(torch.empty((G, num_tokens, D), dtype=torch.uint8, device="cuda"),
+             torch.empty((G, num_tokens, D // 128), dtype=torch.float32, device="cuda")) for _ in range(2)]
+
+    def call(i):
+        o, pos, cs = sets[i % 2]
+        sad.inv_rope_fp8_quant(o, pos, cs, G, out_fp8=outs[i % 2][0], out_scales=outs[i % 2][1])
+
+    us = _time_launches(call, iters, warmup)
+    vals = num_tokens * H * Dh
+    nbytes = vals * 3 + (vals // 128) * 4 + num_tokens * (4 + 4 * R)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del sets, outs
+    return {"tokens": num_tokens, "us_per_launch": us, "algorithmic_bytes": nbytes, "achieved_gbs": gbs,
+            "hbm_frac": gbs / PEAK_HBM_GBS}
+
+
+def bench_cache_writes(num_rows: int, iters: int = 30, warmup: int = 3) -> dict:
+    """Event-timed insert_kv_rows and insert_index_keys of ``num_rows`` compressed rows into
+    pools shaped like the 64K workload's (KV rows 512 fp8 + 64 bf16, pages of 64; indexer
+    keys 128 MXFP4), at distinct random slots.  Algorithmic bytes per KV row: 2*576 in,
+    672 out, 4 + 4 slot and position, 4*64 cos/sin; per key: 256 in, 68 out, 8, 4*64."""
+    g = torch.Generator(device="cuda").manual_seed(9)
+    pages = 4096
+    kv_pool = torch.zeros((pages, 64 * (640 + 32)), dtype=torch.uint8, device="cuda")
+    idx_pool = torch.zeros((pages, 64 * 68), dtype=torch.uint8, device="cuda")
+    kv = sad.KvCache(kv_pool, 64, 512, 64)
+    idx = sad.IndexerCache(idx_pool, 64, 128)
+    rows = torch.randn(num_rows, 576, device="cuda", generator=g).bfloat16()
+    keys = torch.randn(num_rows, 128, device="cuda", generator=g).bfloat16()
+    pos = torch.randint(0, 65536, (num_rows,), device="cuda", generator=g, dtype=torch.int32)
+    slots = torch.randperm(pages * 64, device="cuda", generator=g)[:num_rows].to(torch.int32)
+    cs = WL.rope_table(65536, 64).cuda()
+    us_kv = _time_launches(lambda i: sad.insert_kv_rows(rows, pos, cs, 4, slots, kv), iters, warmup)
+    us_idx = _time_launches(lambda i: sad.insert_index_keys(keys, pos, cs, 4, slots, idx), iters, warmup)
+    b_kv = num_rows * (2 * 576 + 672 + 8 + 256)
+    b_idx = num_rows * (256 + 68 + 8 + 256)
+    del kv_pool, idx_pool
+    return {"rows": num_rows,
+            "insert_kv_rows": {"us_per_launch": us_kv, "algorithmic_bytes": b_kv,
+                               "hbm_frac": b_kv / (us_kv * 1e-6) / 1e9 / PEAK_HBM_GBS},
+            "insert_index_keys": {"us_per_launch": us_idx, "algorithmic_bytes": b_idx,
+                                  "hbm_frac": b_idx / (us_idx * 1e-6) / 1e9 / PEAK_HBM_GBS}}
+
+
 def bench_prepare_indexer_q(num_tokens: int, positions, iters: int = 30, warmup: int = 5) -> dict:
     """Event-timed prepare_indexer_q_mxfp4 on 64 heads x 128 dims, rope 64 (two input
     sets alternated).  Algorithmic bytes: per row 2*D in, D/2 + D/32 out, 4 + 4 for the
@@ -267,19 +339,7 @@ def bench_prepare_indexer_q(num_tokens: int, positions, iters: int = 30, warmup:
         sad.prepare_indexer_q_mxfp4(a.index_q, a.positions, a.cos_sin, a.weights, a.softmax_scale,
                                     a.head_scale, q_values=o[0], q_scales=o[1], weights_out=o[2])
 
-    for i in range(warmup):
-        call(i)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    # A spin kernel holds the stream while the launches are queued, so the events
-    # time the kernels back to back rather than the host's submission rate.
-    torch.cuda._sleep(4_000_000)
-    e0.record()
-    for i in range(iters):
-        call(i)
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / iters
+    us = _time_launches(call, iters, warmup)
     rows = num_tokens * H
     nbytes = rows * (2 * D + D // 2 + D // 32 + 8) + num_tokens * (4 + 4 * R)
     gbs = nbytes / (us * 1e-6) / 1e9
@@ -376,12 +436,19 @@ def main() -> int:
         "indexer_hbm_gbs": idx_gbs,
         "step_hbm_frac": (ab["attention"] + ab["indexer"] + ab["build"]) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
-    log("[bench] indexer query preparation (outside the step)")
+    log("[bench] indexer query preparation and output quantization (outside the step)")
     del steps
     result["next_rows"] = {"prepare_indexer_q_mxfp4": {
         "bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
         "decode_128_tokens": bench_prepare_indexer_q(T, [65535] * T),
-        "prefill_16448_tokens": bench_prepare_indexer_q(16448, None)}}
+        "prefill_16448_tokens": bench_prepare_indexer_q(16448, None)},
+        "inv_rope_fp8_quant": {
+        "bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "decode_128_tokens": bench_inv_rope_fp8_quant(T, [65535] * T),
+        "prefill_16448_tokens": bench_inv_rope_fp8_quant(16448, None)},
+        "cache_writes": {"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "decode_128_rows": bench_cache_writes(T),
+                         "prefill_4112_rows": bench_cache_writes(16448 // 4)}}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
