@@ -19,7 +19,8 @@ Readings taken where the pages are silent (each is listed in the design doc):
 
 * indexer score  = sum_h w[t,h] * ReLU(q[t,h] . k_s)      (parity unpinned vs pages)
 * top-k ties go to the lower row id; output is ascending by row id, -1 padded
-* KV scales are fp32 per 64 nope elements (the pages use ue8m0 there)
+* KV scales are fp32 per 64 nope elements (the pages use ue8m0 there); the
+  pages' native ue8m0 record (448 + 64, 8 scale bytes per row) is the second form
 * sparse_topk_lens counts the valid compressed entries, which are packed to
   the left of the compressed segment in top-k order; the rest is -1
 * a row whose page id is negative, past the table or past the pool is invalid
@@ -228,18 +229,29 @@ def build_sparse_indices(
 # ---------------------------------------------------------------------------
 
 
-def dequant_rows(kv_pages: dict, slots, block_size: int, d_nope: int, d_rope: int) -> np.ndarray:
+def kv_scale_bytes(d_nope: int, scale_format: str = "f32") -> int:
+    """Bytes of one row's scales: d_nope/64 fp32 (the fp32 form), or the pages' native
+    ue8m0 form, one byte per 64 nope values padded to 8 bytes ([ops]
+    ``deepseek_v4_swa_scale_dim``: 448 nope values -> 7 scales + 1 pad byte)."""
+    return 4 * (d_nope // 64) if scale_format == "f32" else 8
+
+
+def dequant_rows(kv_pages: dict, slots, block_size: int, d_nope: int, d_rope: int,
+                 scale_format: str = "f32") -> np.ndarray:
     """bf16 bits [n, Dn+Dr] of the rows at ``slots``; slot -1 gives a zero row.
 
     [ops] ``dequantize_deepseek_v4_fp8_ds_mla_cache``: values of row ``o`` of
     page ``g`` start at ``g*stride + o*(Dn + 2*Dr)``; its scales start at
     ``g*stride + B*(Dn + 2*Dr) + o*scale_bytes``.  Each nope element is
     ``bf16_rne(fp32(e4m3(v)) * scale[d // 64])`` (one binary32 multiply); the
-    rope tail is stored bf16 and copied.  Scales here are fp32 (4 bytes each).
+    rope tail is stored bf16 and copied.  Scales are fp32 (4 bytes each) in the
+    "f32" form, or the pages' ue8m0 bytes, scale = 2^(b - 127), in the "ue8m0"
+    form (where the product is exact).
     """
     slots = np.asarray(slots, dtype=np.int64)
     row_b = d_nope + 2 * d_rope
     nsc = d_nope // 64
+    sbytes = kv_scale_bytes(d_nope, scale_format)
     out = np.zeros((slots.shape[0], d_nope + d_rope), dtype=np.uint16)
     for i, s in enumerate(slots):
         if s < 0:
@@ -247,8 +259,11 @@ def dequant_rows(kv_pages: dict, slots, block_size: int, d_nope: int, d_rope: in
         page = kv_pages[int(s) // block_size]
         o = int(s) % block_size
         vals = page[o * row_b: (o + 1) * row_b]
-        sbase = block_size * row_b + o * 4 * nsc
-        scales = page[sbase: sbase + 4 * nsc].view(np.float32)
+        sbase = block_size * row_b + o * sbytes
+        if scale_format == "f32":
+            scales = page[sbase: sbase + 4 * nsc].view(np.float32)
+        else:
+            scales = np.ldexp(np.float32(1.0), page[sbase: sbase + nsc].astype(np.int32) - 127).astype(np.float32)
         nope32 = E4M3_VALUES[vals[:d_nope]].astype(np.float32)
         prod = nope32 * np.repeat(scales, 64)  # binary32 multiply
         out[i, :d_nope] = float32_to_bf16_bits(prod)
@@ -257,7 +272,8 @@ def dequant_rows(kv_pages: dict, slots, block_size: int, d_nope: int, d_rope: in
 
 
 def gather_dequant(kv_swa: dict, kv_comp: dict, sparse_indices, sparse_topk_lens,
-                   window_size, block_size_swa, block_size_comp, d_nope, d_rope) -> np.ndarray:
+                   window_size, block_size_swa, block_size_comp, d_nope, d_rope,
+                   scale_format: str = "f32") -> np.ndarray:
     """[T, W+P, Dn+Dr] bf16 bits: every attended column dequantized, others zero.
 
     Window columns read the window cache; compressed columns ``W..W+lens-1``
@@ -268,9 +284,10 @@ def gather_dequant(kv_swa: dict, kv_comp: dict, sparse_indices, sparse_topk_lens
     W = int(window_size)
     out = np.zeros((T, width, d_nope + d_rope), dtype=np.uint16)
     for t in range(T):
-        out[t, :W] = dequant_rows(kv_swa, si[t, :W], block_size_swa, d_nope, d_rope)
+        out[t, :W] = dequant_rows(kv_swa, si[t, :W], block_size_swa, d_nope, d_rope, scale_format)
         n = int(min(max(sparse_topk_lens[t], 0), width - W))
-        out[t, W: W + n] = dequant_rows(kv_comp, si[t, W: W + n], block_size_comp, d_nope, d_rope)
+        out[t, W: W + n] = dequant_rows(kv_comp, si[t, W: W + n], block_size_comp, d_nope, d_rope,
+                                        scale_format)
     return out
 
 
@@ -414,7 +431,7 @@ def attend(q_bits: np.ndarray, row_bits: np.ndarray, softmax_scale: float, sink=
 
 def sparse_mla_decode(q_bits, kv_swa, kv_comp, sparse_indices, sparse_topk_lens, window_size,
                       block_size_swa, block_size_comp, d_nope, d_rope, softmax_scale,
-                      attn_sink=None, tokens=None, return_mass=False):
+                      attn_sink=None, tokens=None, return_mass=False, scale_format="f32"):
     """Attention of every head of each token over its attended columns.
 
     Attended columns: window columns ``0..W-1`` with slot >= 0 and compressed
@@ -437,8 +454,8 @@ def sparse_mla_decode(q_bits, kv_swa, kv_comp, sparse_indices, sparse_topk_lens,
         n = int(min(max(int(sparse_topk_lens[t]), 0), si.shape[1] - W))
         comp = si[t, W: W + n]
         rows = np.concatenate([
-            dequant_rows(kv_swa, swa[swa >= 0], block_size_swa, d_nope, d_rope),
-            dequant_rows(kv_comp, comp[comp >= 0], block_size_comp, d_nope, d_rope),
+            dequant_rows(kv_swa, swa[swa >= 0], block_size_swa, d_nope, d_rope, scale_format),
+            dequant_rows(kv_comp, comp[comp >= 0], block_size_comp, d_nope, d_rope, scale_format),
         ])
         if return_mass:
             o[i], lse[i], mass[i] = attend(q_bits[t], rows, softmax_scale, attn_sink, return_mass=True)
@@ -833,5 +850,6 @@ def step(view, cfg, padded_topk, kv_num_pages, idx_num_pages, softmax_scale, tok
         tk, cfg.topk, cfg.window, cfg.ratio, padded_topk)
     o, lse = sparse_mla_decode(view.q, view.kv_pages, view.kv_pages, si, lens, cfg.window,
                                cfg.block, cfg.block, cfg.d_nope, cfg.d_rope, softmax_scale,
-                               attn_sink=attn_sink, tokens=all_tokens)
+                               attn_sink=attn_sink, tokens=all_tokens,
+                               scale_format=getattr(cfg, "kv_format", "f32"))
     return {"topk": tk, "sparse_indices": si, "lens": lens, "out": o, "lse": lse, "tokens": all_tokens}

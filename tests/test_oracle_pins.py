@@ -158,6 +158,29 @@ def test_dequant_reads_the_addressed_row_and_scale_block():
     assert np.all(got[2, :64] == 1.0) and np.all(got[2, 64:Dn] == 2.0)
 
 
+def test_dequant_native_ue8m0_record():
+    # The pages' native record: 448 e4m3 + 64 bf16 per row (576 bytes), then per row 8
+    # scale bytes (7 ue8m0 + 1 pad).  Row o, block b: byte 0x38 (= 1.0) with scale byte
+    # 120 + b + o % 3, so element d is exactly 2^(d // 64 + o % 3 - 7); the pad byte is
+    # 0xFF and must be ignored; the rope part is copied.
+    B, Dn, Dr = 16, 448, 64
+    row_b = Dn + 2 * Dr
+    assert O.kv_scale_bytes(Dn, "ue8m0") == 8 and row_b == 576
+    page = np.zeros(B * (row_b + 8), np.uint8)
+    rope = (np.arange(Dr, dtype=np.float32) - 20.5).astype(np.float32)
+    for o in range(B):
+        page[o * row_b: o * row_b + Dn] = 0x38
+        page[o * row_b + Dn: (o + 1) * row_b] = O.float32_to_bf16_bits(rope * (o + 1)).view(np.uint8)
+        page[B * row_b + 8 * o: B * row_b + 8 * o + 7] = 120 + np.arange(7) + o % 3
+        page[B * row_b + 8 * o + 7] = 0xFF
+    got = O.bf16_bits_to_float(O.dequant_rows({1: page}, [B + 4, -1, B + 8], B, Dn, Dr, "ue8m0"))
+    for r, o in ((0, 4), (2, 8)):
+        want = np.exp2(np.arange(Dn) // 64 + o % 3 - 7.0)
+        assert np.array_equal(got[r, :Dn], want)
+        assert np.array_equal(got[r, Dn:], O.bf16_bits_to_float(O.float32_to_bf16_bits(rope * (o + 1))))
+    assert not got[1].any()
+
+
 # --------------------------------------------------------------------------- geometry / indices
 
 
