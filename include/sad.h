@@ -50,7 +50,10 @@
  *   bf16.  Row o's scales are at byte block_size*(d_nope + 2*d_rope) + o*4*(d_nope/64):
  *   d_nope/64 fp32, one per 64 nope elements.  Row value: nope[d] =
  *   bf16_rne(float(e4m3(v[d])) * scale[d/64]), rope copied.  A slot is
- *   page*block_size + row.
+ *   page*block_size + row.  In the pages' native form (SAD_KV_SCALE_UE8M0,
+ *   d_nope 448, d_rope 64: a 576-byte value row) row o's scales are 8 bytes at
+ *   block_size*(d_nope + 2*d_rope) + o*8: 7 ue8m0 bytes, scale 2^(b-127), and
+ *   one pad byte ([ops] deepseek_v4_swa_scale_dim); the product is exact.
  *
  *   sad_mxfp4_cache (indexer keys; [ops] read_deepseek_v4_indexer_mxfp4_cache):
  *   page g holds block_size rows: first block_size*dim/2 bytes of packed E2M1
@@ -75,16 +78,21 @@ enum {
   SAD_ELAUNCH = 4
 };
 
-/* Paged FP8 latent KV cache (see "Cache formats").  Supported (d_nope, d_rope):
- * (128, 32) and (512, 64); block_size 16 or 64; page_stride a multiple of 16 and
- * >= block_size*(d_nope + 2*d_rope + 4*d_nope/64); num_pages*block_size < 2^31. */
+/* Scale forms of sad_kv_cache (see "Cache formats"). */
+enum { SAD_KV_SCALE_F32 = 0, SAD_KV_SCALE_UE8M0 = 1 };
+
+/* Paged FP8 latent KV cache (see "Cache formats").  Supported (d_nope, d_rope,
+ * scale_format): (128, 32, F32), (512, 64, F32) and the pages' native record
+ * (448, 64, UE8M0); block_size 16 or 64; page_stride a multiple of 16 and
+ * >= block_size*(d_nope + 2*d_rope + scale bytes per row); num_pages*block_size < 2^31. */
 typedef struct {
-  const void* pool;    /* device, uint8 [num_pages * page_stride] */
-  int64_t page_stride; /* bytes between consecutive pages */
-  int64_t num_pages;   /* page ids outside [0, num_pages) are invalid */
-  int32_t block_size;  /* rows per page */
-  int32_t d_nope;      /* FP8 part of the row */
-  int32_t d_rope;      /* bf16 part of the row */
+  const void* pool;     /* device, uint8 [num_pages * page_stride] */
+  int64_t page_stride;  /* bytes between consecutive pages */
+  int64_t num_pages;    /* page ids outside [0, num_pages) are invalid */
+  int32_t block_size;   /* rows per page */
+  int32_t d_nope;       /* FP8 part of the row */
+  int32_t d_rope;       /* bf16 part of the row */
+  int32_t scale_format; /* SAD_KV_SCALE_F32 or SAD_KV_SCALE_UE8M0 */
 } sad_kv_cache;
 
 /* Paged MXFP4 indexer-key cache.  dim 64 or 128; block_size 16 or 64;

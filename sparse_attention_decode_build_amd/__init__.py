@@ -6,6 +6,8 @@ workloads used by the benchmark.
 """
 
 from ._lib import (  # noqa: F401
+    KV_SCALE_F32,
+    KV_SCALE_UE8M0,
     IndexerCache,
     KvCache,
     build_sparse_indices,

@@ -24,9 +24,12 @@ c_i32, c_i64, c_ptr, c_size, c_f32 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_v
                                       ctypes.c_size_t, ctypes.c_float)
 
 
+KV_SCALE_F32, KV_SCALE_UE8M0 = 0, 1
+
+
 class SadKvCache(ctypes.Structure):
     _fields_ = [("pool", c_ptr), ("page_stride", c_i64), ("num_pages", c_i64),
-                ("block_size", c_i32), ("d_nope", c_i32), ("d_rope", c_i32)]
+                ("block_size", c_i32), ("d_nope", c_i32), ("d_rope", c_i32), ("scale_format", c_i32)]
 
 
 class SadMxfp4Cache(ctypes.Structure):
@@ -116,17 +119,19 @@ def _need(t, dtype, name, dim=None, device=None):
 
 @dataclass
 class KvCache:
-    """A paged FP8 latent cache: uint8 pool [pages, page_bytes] + its geometry."""
+    """A paged FP8 latent cache: uint8 pool [pages, page_bytes] + its geometry and scale
+    form (KV_SCALE_F32, or KV_SCALE_UE8M0 for the pages' native 448 + 64 record)."""
 
     pool: torch.Tensor
     block_size: int
     d_nope: int
     d_rope: int
+    scale_format: int = KV_SCALE_F32
 
     def c(self) -> SadKvCache:
         _need(self.pool, torch.uint8, "kv pool", dim=2)
         return SadKvCache(self.pool.data_ptr(), self.pool.stride(0), self.pool.shape[0],
-                          self.block_size, self.d_nope, self.d_rope)
+                          self.block_size, self.d_nope, self.d_rope, self.scale_format)
 
 
 @dataclass

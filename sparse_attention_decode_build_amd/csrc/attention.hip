@@ -136,24 +136,31 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
 
 template <int DN, int DR>
 struct Shape {
+  // The pages' native record (448 nope + 64 rope) is told apart by its nope width: its
+  // scales are 8 ue8m0 bytes per row (7 + 1 pad) and its fp8 part ends half way into
+  // a 128-byte line; the other rows carry fp32 scales and whole fp8 lines.
+  static constexpr bool NATIVE = DN % 128 != 0;
   static constexpr int DQK = DN + DR;
   static constexpr int ROWB = DN + 2 * DR;  // value bytes per cached row
-  static constexpr int NSC = DN / 64;       // fp32 scales per row
+  static constexpr int NSC = DN / 64;       // scale blocks per row
+  static constexpr int SCB = NATIVE ? 8 : 4 * NSC;  // scale bytes per row
   static constexpr int MT = DQK / 32;       // PV MFMA m-tiles (output dims / 32)
   static constexpr int MT0 = (MT + 1) / 2;  // m-tiles of dim half 0 (half 1 gets the rest)
   static constexpr int MT1 = MT - MT0;
   static constexpr int KS0 = 2 * MT0;       // QK k-steps (16 dims) of dim half 0
   static constexpr int KS1 = 2 * MT1;
   static constexpr int KCH = DQK / 8 + 1;  // 16-byte chunks per K row in LDS (odd: one pad chunk)
-  static constexpr int CPR = ROWB / 16;          // 16-byte chunks of a cached row
-  static constexpr int LINES = (CPR + 7) / 8;    // 128-byte lines of a cached row
-  static constexpr int FP8_LINES = DN / 128;     // lines holding fp8 values (the rest: rope)
-  static constexpr int ROPE_CH = DR / 8;         // 16-byte bf16 chunks of the rope part
+  static constexpr int FP8_LINES = (DN + 127) / 128;  // 128-byte lines holding fp8 values
+  static constexpr int FP8_TAIL = DN % 128 == 0 ? 8 : (DN % 128) / 16;  // fp8 chunks of the last one
+  static constexpr int ROPE_CH = DR / 8;              // 16-byte bf16 chunks of the rope part
+  // fp8 lines, then one line read from byte DN of the row: the rope part
+  static constexpr int LINES = FP8_LINES + 1;
   static constexpr int DMA_PER_TILE = LINES + 1;  // value loads + one scale load per wave
   static constexpr int RAW_V = kWaves * LINES * 1024;  // [wave][line][row%8][chunk%8][16 B]
-  static constexpr int RAW_S = kThreads;               // fp32 [row][8], padded
-  static_assert(ROWB % 16 == 0 && DN % 128 == 0, "rows are whole chunks; fp8 part is whole lines");
-  static_assert(ROPE_CH <= 8 && NSC <= 8, "rope part within one line, at most 8 scales per row");
+  static constexpr int RAW_S = kThreads;               // [row][32 bytes] of scales, padded
+  static_assert(ROWB % 16 == 0 && DN % 64 == 0, "rows are whole chunks, fp8 part whole scale blocks");
+  static_assert(128 * FP8_LINES <= ROWB, "every fp8 line lies inside the row");
+  static_assert(ROPE_CH <= 8 && SCB <= 32, "rope part within one line, scales within 32 bytes");
   static_assert(kTile == 8 * kWaves, "each wave carries 8 rows of a tile");
   static_assert(DQK % 32 == 0, "output dims in 32-row MFMA tiles");
 };
@@ -173,7 +180,7 @@ __device__ inline int kt_off(int key, int dim) {
 // compressed columns read the same cache (wave-uniform descriptor).
 template <bool ONE>
 __device__ inline void slot_row(int slot, int col, int window, const KvDesc& swa, const KvDesc& comp, int rowb,
-                                int nsc, const uint8_t* zrow, const uint8_t** vals, const uint8_t** scales) {
+                                int scb, const uint8_t* zrow, const uint8_t** vals, const uint8_t** scales) {
   const KvDesc& kv = (ONE || col < window) ? swa : comp;
   // branch-free, so it can sit between other work without splitting it into blocks
   const bool ok = slot >= 0 && (slot >> kv.block_shift) < (int)kv.num_pages;  // num_pages * block fits in int32
@@ -182,7 +189,7 @@ __device__ inline void slot_row(int slot, int col, int window, const KvDesc& swa
   const int ro = s2 & (kv.block - 1);
   const uint8_t* pg = kv.pool + (int64_t)page * kv.stride;
   const uint8_t* v = pg + ro * rowb;
-  const uint8_t* sc = pg + (kv.block * rowb + ro * 4 * nsc);
+  const uint8_t* sc = pg + (kv.block * rowb + ro * scb);
   asm("" : "+v"(v), "+v"(sc));  // computed on every lane (no branch around them)
   *vals = ok ? v : zrow;
   *scales = ok ? sc : zrow;
@@ -191,7 +198,8 @@ __device__ inline void slot_row(int slot, int col, int window, const KvDesc& swa
 // Copy one tile's raw rows HBM -> LDS.  Wave w carries rows 8w..8w+7 of the tile:
 // lane l handles row 8w + l/8 (address vrow/srow, from slot_row) and 16-byte chunk l%8 of
 // each 128-byte line, so every load reads whole lines (8 rows x 128 contiguous bytes).
-// Values land as [wave][line][row%8][chunk%8] (16 B each), scales as [row][8] fp32.
+// Values land as [wave][line][row%8][chunk%8] (16 B each): the fp8 lines, then the rope
+// part read from byte DN of the row; scales as [row][32 bytes].
 // Every wave issues exactly DMA_PER_TILE loads with all lanes active (lanes past the
 // row read the zero row into padding LDS), so a wave's vmcnt advances by a known
 // amount per tile.  Returns the wave's 8-bit validity (bit r: row 8w + r attended).
@@ -206,12 +214,14 @@ __device__ inline uint32_t dma_issue(int lane, int wave, uint8_t (&raw_v)[Shape<
   static_for<S::LINES>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(vbase + j * 1024);
-    if constexpr (8 * j + 8 <= S::CPR)
-      dma_x4_off<128 * j>(vsrc, dst);  // every chunk of this line exists
+    if constexpr (j < S::FP8_LINES)
+      dma_x4_off<128 * j>(vsrc, dst);  // inside the row (a half fp8 line reads rope bytes too)
+    else if constexpr (S::ROPE_CH == 8)
+      dma_x4_off<DN>(vsrc, dst);
     else
-      dma_x4_off<0>(8 * j + c < S::CPR ? vsrc + 128 * j : zrow, dst);
+      dma_x4_off<0>(c < S::ROPE_CH ? vsrc + DN : zrow, dst);
   });
-  dma_x1(c < S::NSC ? srow + 4 * c : zrow, __builtin_amdgcn_readfirstlane(lds_addr(raw_s) + wave * 256));
+  dma_x1(c < S::SCB / 4 ? srow + 4 * c : zrow, __builtin_amdgcn_readfirstlane(lds_addr(raw_s) + wave * 256));
   // lane 8r carries row 8w + r: gather ballot bits 0, 8, .., 56 into one byte
   const uint64_t b = __ballot(vrow != zrow) & 0x0101010101010101ull;
   return (uint32_t)((b * 0x0102040810204080ull) >> 56);
@@ -227,12 +237,14 @@ __device__ inline void dma_one(int lane, int wave, uint8_t (&raw_v)[Shape<DN, DR
   const int c = lane & 7;
   if constexpr (J < S::LINES) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(raw_v) + wave * S::LINES * 1024 + J * 1024);
-    if constexpr (8 * J + 8 <= S::CPR)
+    if constexpr (J < S::FP8_LINES)
       dma_x4_off<128 * J>(vrow + 16 * c, dst);
+    else if constexpr (S::ROPE_CH == 8)
+      dma_x4_off<DN>(vrow + 16 * c, dst);
     else
-      dma_x4_off<0>(8 * J + c < S::CPR ? vrow + 16 * c + 128 * J : zrow, dst);
+      dma_x4_off<0>(c < S::ROPE_CH ? vrow + 16 * c + DN : zrow, dst);
   } else {
-    dma_x1(c < S::NSC ? srow + 4 * c : zrow, __builtin_amdgcn_readfirstlane(lds_addr(raw_s) + wave * 256));
+    dma_x1(c < S::SCB / 4 ? srow + 4 * c : zrow, __builtin_amdgcn_readfirstlane(lds_addr(raw_s) + wave * 256));
   }
 }
 __device__ inline uint32_t row_mask(const uint8_t* vrow, const uint8_t* zrow) {
@@ -242,6 +254,18 @@ __device__ inline uint32_t row_mask(const uint8_t* vrow, const uint8_t* zrow) {
 template <int N>
 __device__ inline void wait_lgkm() {
   asm volatile("s_waitcnt lgkmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Scale of block `blk` of tile row `key` from the raw scale slot: an fp32 value, or in
+// the native record a ue8m0 byte, 2^(b - 127) (byte 0 is the subnormal 2^-127).
+template <int DN, int DR>
+__device__ inline float scale_at(const float (&raw_s)[Shape<DN, DR>::RAW_S], int key, int blk) {
+  if constexpr (Shape<DN, DR>::NATIVE) {
+    const uint32_t b = reinterpret_cast<const uint8_t*>(raw_s)[key * 32 + blk];
+    return b != 0 ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+  } else {
+    return raw_s[key * 8 + blk];
+  }
 }
 
 // Dequantize fp8 lines [J0, J1) (and the rope line when ROPE) of this wave's 8 rows of
@@ -263,7 +287,7 @@ __device__ inline void dequant_lines(int lane, int wave, const uint8_t (&raw_v)[
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     raw[j] = *reinterpret_cast<const uint4*>(src + (J0 + j) * 1024);
-    sc[j] = raw_s[key * 8 + 2 * (J0 + j) + (c >> 2)];  // dims 128j + 16c .. +16: scale block 2j + c/4
+    sc[j] = scale_at<DN, DR>(raw_s, key, 2 * (J0 + j) + (c >> 2));  // dims 128j + 16c .. +16: block 2j + c/4
   }
   uint4 rope = make_uint4(0u, 0u, 0u, 0u);
   if (ROPE && c < S::ROPE_CH) rope = *reinterpret_cast<const uint4*>(src + S::FP8_LINES * 1024);
@@ -279,8 +303,11 @@ __device__ inline void dequant_lines(int lane, int wave, const uint8_t (&raw_v)[
       o[2 * q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
       o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
     }
-    *reinterpret_cast<uint4*>(dst + 128 * (J0 + j)) = make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4*>(dst + 128 * (J0 + j) + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+    // the chunks of a half fp8 line past the fp8 part hold rope bytes: not stored
+    if (J0 + j < S::FP8_LINES - 1 || c < S::FP8_TAIL) {
+      *reinterpret_cast<uint4*>(dst + 128 * (J0 + j)) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(dst + 128 * (J0 + j) + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
   }
   if (ROPE && c < S::ROPE_CH) *reinterpret_cast<uint4*>(kt + kt_off<S::KCH>(key, DN + 8 * c)) = rope;
 }
@@ -308,7 +335,7 @@ __device__ inline void raw_load(int lane, int wave, const uint8_t (&raw_v)[Shape
 #pragma unroll
   for (int j = 0; j < S::FP8_LINES; ++j) {
     r.v[j] = *reinterpret_cast<const u32x4_t*>(src + j * 1024);
-    r.sc[j] = raw_s[key * 8 + 2 * j + (c >> 2)];  // dims 128j + 16c .. +16: scale block 2j + c/4
+    r.sc[j] = scale_at<DN, DR>(raw_s, key, 2 * j + (c >> 2));  // dims 128j + 16c .. +16: block 2j + c/4
   }
   r.rope = *reinterpret_cast<const u32x4_t*>(src + S::FP8_LINES * 1024);
 }
@@ -446,7 +473,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   };
   auto row_addr_of = [&](int tile, int slot, const uint8_t** vrow, const uint8_t** srow)
       __attribute__((always_inline)) {
-    slot_row<ONE>(slot, tile * kTile + 8 * wave + (lane >> 3), window, swa, comp, S::ROWB, S::NSC, zrow, vrow,
+    slot_row<ONE>(slot, tile * kTile + 8 * wave + (lane >> 3), window, swa, comp, S::ROWB, S::SCB, zrow, vrow,
                   srow);
   };
   // ids of the wave's 8 rows of a tile -> the LDS ring (lanes 0..7; the others read the
@@ -658,8 +685,14 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
       const int c = lane_s & 7;
       uint16_t* sdst = kt[b ^ 1] + kt_off<S::KCH>(key, 16 * c);
 #pragma unroll
-      for (int kk = 0; kk < 2 * S::FP8_LINES; ++kk)
+      for (int kk = 0; kk < 2 * S::FP8_LINES - 2; ++kk)
         *reinterpret_cast<u32x4_t*>(sdst + 128 * (kk >> 1) + 8 * (kk & 1)) = dq[kk];
+      // the last fp8 line: in the native record only its first FP8_TAIL chunks
+      if (S::FP8_TAIL == 8 || c < S::FP8_TAIL) {
+        constexpr int kl = 2 * S::FP8_LINES - 2;
+        *reinterpret_cast<u32x4_t*>(sdst + 128 * (kl >> 1)) = dq[kl];
+        *reinterpret_cast<u32x4_t*>(sdst + 128 * (kl >> 1) + 8) = dq[kl + 1];
+      }
       if (c < S::ROPE_CH) *reinterpret_cast<u32x4_t*>(kt[b ^ 1] + kt_off<S::KCH>(key, DN + 8 * c)) = rr.rope;
       if (lane_s == 0) reinterpret_cast<uint8_t*>(&kt_mask[b ^ 1])[wave] = (uint8_t)mask_a;
       mask_a = mask_b;
@@ -947,8 +980,9 @@ extern "C" int sparse_mla_decode(const uint16_t* q_bf16, int32_t num_tokens, int
   if (rc != SAD_OK) return rc;
   rc = check_kv_cache(comp, "sparse_mla_decode(comp)");
   if (rc != SAD_OK) return rc;
-  SAD_CHECK(swa->d_nope == comp->d_nope && swa->d_rope == comp->d_rope, SAD_EINVAL,
-            "sparse_mla_decode: swa and comp caches must share (d_nope, d_rope)");
+  SAD_CHECK(swa->d_nope == comp->d_nope && swa->d_rope == comp->d_rope &&
+                swa->scale_format == comp->scale_format,
+            SAD_EINVAL, "sparse_mla_decode: swa and comp caches must share (d_nope, d_rope, scale_format)");
   SAD_CHECK(num_tokens >= 0 && window_size >= 0 && padded_topk >= 0, SAD_EINVAL,
             "sparse_mla_decode: negative size");
   SAD_CHECK(num_heads >= 8 && num_heads <= 128 && num_heads % 8 == 0, SAD_EUNSUPPORTED,
@@ -968,6 +1002,10 @@ extern "C" int sparse_mla_decode(const uint16_t* q_bf16, int32_t num_tokens, int
   hipStream_t st = (hipStream_t)stream;
   if (swa->d_nope == 512)
     return launch<512, 64>(q_bf16, num_tokens, num_heads, s, c, sparse_indices, sparse_topk_lens,
+                           window_size, padded_topk, softmax_scale, attn_sink, out_bf16, lse,
+                           workspace, workspace_bytes, st);
+  if (swa->d_nope == 448)
+    return launch<448, 64>(q_bf16, num_tokens, num_heads, s, c, sparse_indices, sparse_topk_lens,
                            window_size, padded_topk, softmax_scale, attn_sink, out_bf16, lse,
                            workspace, workspace_bytes, st);
   return launch<128, 32>(q_bf16, num_tokens, num_heads, s, c, sparse_indices, sparse_topk_lens,

@@ -106,6 +106,8 @@ extern "C" int insert_kv_rows(const uint16_t* rows, const int32_t* positions,
   clear_error();
   const int rc = check_kv_cache(cache, "insert_kv_rows");
   if (rc != SAD_OK) return rc;
+  SAD_CHECK(cache->scale_format == SAD_KV_SCALE_F32, SAD_EUNSUPPORTED,
+            "insert_kv_rows: only the fp32 scale form is written");
   SAD_CHECK(num_rows >= 0 && max_pos >= 0 && compress_ratio >= 1, SAD_EINVAL,
             "insert_kv_rows: bad size");
   if (num_rows == 0) return SAD_OK;

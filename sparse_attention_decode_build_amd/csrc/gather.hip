@@ -19,12 +19,20 @@ struct KvDesc {
   int block;
 };
 
+// 2^(b - 127) for a ue8m0 byte (byte 0 is the subnormal 2^-127).
+__device__ inline float ue8m0_scale(uint32_t b) {
+  return b != 0 ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
 template <int DN, int DR>
 __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(
     KvDesc swa, KvDesc comp, const int32_t* __restrict__ si, const int32_t* __restrict__ lens,
     int64_t num_rows, int window, int padded, uint16_t* __restrict__ out) {
-  constexpr int ROWB = DN + 2 * DR;  // value bytes per row
-  constexpr int EPL = DN / 64;       // FP8 elements per lane (8 or 2)
+  constexpr int ROWB = DN + 2 * DR;       // value bytes per row
+  constexpr bool NATIVE = DN % 128 != 0;  // the native record (448 + 64): ue8m0 scale bytes
+  constexpr int EPL = NATIVE ? 8 : DN / 64;  // FP8 elements per lane (8 or 2)
+  constexpr int NLANES = DN / EPL;           // lanes holding nope values
+  constexpr int SCB = NATIVE ? 8 : 4 * (DN / 64);  // scale bytes per row
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (r >= num_rows) return;
@@ -47,23 +55,28 @@ __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(
     const int ro = slot - page * kv.block;
     const uint8_t* pg = kv.pool + (int64_t)page * kv.stride;
     const uint8_t* vals = pg + (int64_t)ro * ROWB;
-    const float* scales = reinterpret_cast<const float*>(pg + (int64_t)kv.block * ROWB +
-                                                         (int64_t)ro * 4 * (DN / 64));
-    const float sc = scales[(lane * EPL) / 64];
-    if constexpr (EPL == 8) {
-      const uint2 w = *reinterpret_cast<const uint2*>(vals + lane * 8);
-      res[0] = f32_to_bf16_bits(e4m3_to_f32<0>(w.x) * sc);
-      res[1] = f32_to_bf16_bits(e4m3_to_f32<1>(w.x) * sc);
-      res[2] = f32_to_bf16_bits(e4m3_to_f32<2>(w.x) * sc);
-      res[3] = f32_to_bf16_bits(e4m3_to_f32<3>(w.x) * sc);
-      res[4] = f32_to_bf16_bits(e4m3_to_f32<0>(w.y) * sc);
-      res[5] = f32_to_bf16_bits(e4m3_to_f32<1>(w.y) * sc);
-      res[6] = f32_to_bf16_bits(e4m3_to_f32<2>(w.y) * sc);
-      res[7] = f32_to_bf16_bits(e4m3_to_f32<3>(w.y) * sc);
-    } else {
-      const uint32_t w = *reinterpret_cast<const uint16_t*>(vals + lane * 2);
-      res[0] = f32_to_bf16_bits(e4m3_to_f32<0>(w) * sc);
-      res[1] = f32_to_bf16_bits(e4m3_to_f32<1>(w) * sc);
+    const uint8_t* srow = pg + (int64_t)kv.block * ROWB + (int64_t)ro * SCB;
+    if (lane < NLANES) {
+      float sc;
+      if constexpr (NATIVE)
+        sc = ue8m0_scale(srow[(lane * EPL) / 64]);
+      else
+        sc = reinterpret_cast<const float*>(srow)[(lane * EPL) / 64];
+      if constexpr (EPL == 8) {
+        const uint2 w = *reinterpret_cast<const uint2*>(vals + lane * 8);
+        res[0] = f32_to_bf16_bits(e4m3_to_f32<0>(w.x) * sc);
+        res[1] = f32_to_bf16_bits(e4m3_to_f32<1>(w.x) * sc);
+        res[2] = f32_to_bf16_bits(e4m3_to_f32<2>(w.x) * sc);
+        res[3] = f32_to_bf16_bits(e4m3_to_f32<3>(w.x) * sc);
+        res[4] = f32_to_bf16_bits(e4m3_to_f32<0>(w.y) * sc);
+        res[5] = f32_to_bf16_bits(e4m3_to_f32<1>(w.y) * sc);
+        res[6] = f32_to_bf16_bits(e4m3_to_f32<2>(w.y) * sc);
+        res[7] = f32_to_bf16_bits(e4m3_to_f32<3>(w.y) * sc);
+      } else {
+        const uint32_t w = *reinterpret_cast<const uint16_t*>(vals + lane * 2);
+        res[0] = f32_to_bf16_bits(e4m3_to_f32<0>(w) * sc);
+        res[1] = f32_to_bf16_bits(e4m3_to_f32<1>(w) * sc);
+      }
     }
     // rope: DR bf16 = 2*DR bytes copied by the first DR/2 lanes (4 bytes each)
     if (lane < DR / 2) {
@@ -75,6 +88,7 @@ __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(
     for (int i = 0; i < EPL; ++i) res[i] = 0;
     if (lane < DR / 2) *reinterpret_cast<uint32_t*>(o + DN + lane * 2) = 0u;
   }
+  if (lane >= NLANES) return;
   if constexpr (EPL == 8) {
     uint4 v;
     v.x = res[0] | ((uint32_t)res[1] << 16);
@@ -89,14 +103,21 @@ __global__ __launch_bounds__(kThreads) void gather_dequant_kernel(
 
 }  // namespace
 
+int kv_scale_bytes(const sad_kv_cache* c) {
+  return c->scale_format == SAD_KV_SCALE_UE8M0 ? 8 : 4 * (c->d_nope / 64);
+}
+
 int check_kv_cache(const sad_kv_cache* c, const char* what) {
   SAD_CHECK(c != nullptr && c->pool != nullptr, SAD_EINVAL, "%s: cache or pool is NULL", what);
-  SAD_CHECK((c->d_nope == 512 && c->d_rope == 64) || (c->d_nope == 128 && c->d_rope == 32),
-            SAD_EUNSUPPORTED, "%s: (d_nope, d_rope) = (%d, %d) unsupported", what, c->d_nope,
-            c->d_rope);
+  const bool f32 = c->scale_format == SAD_KV_SCALE_F32;
+  const bool native = c->scale_format == SAD_KV_SCALE_UE8M0;
+  SAD_CHECK((f32 && c->d_nope == 512 && c->d_rope == 64) || (f32 && c->d_nope == 128 && c->d_rope == 32) ||
+                (native && c->d_nope == 448 && c->d_rope == 64),
+            SAD_EUNSUPPORTED, "%s: (d_nope, d_rope, scale_format) = (%d, %d, %d) unsupported", what,
+            c->d_nope, c->d_rope, c->scale_format);
   SAD_CHECK(c->block_size == 16 || c->block_size == 64, SAD_EUNSUPPORTED,
             "%s: block_size %d unsupported", what, c->block_size);
-  const int64_t need = (int64_t)c->block_size * (c->d_nope + 2 * c->d_rope + 4 * (c->d_nope / 64));
+  const int64_t need = (int64_t)c->block_size * (c->d_nope + 2 * c->d_rope + kv_scale_bytes(c));
   SAD_CHECK(c->page_stride >= need && c->page_stride % 16 == 0, SAD_EINVAL,
             "%s: page_stride %lld must be a multiple of 16 and >= %lld", what,
             (long long)c->page_stride, (long long)need);
@@ -119,8 +140,9 @@ extern "C" int gather_dequant_kv(const sad_kv_cache* swa, const sad_kv_cache* co
   if (rc != SAD_OK) return rc;
   rc = check_kv_cache(comp, "gather_dequant_kv(comp)");
   if (rc != SAD_OK) return rc;
-  SAD_CHECK(swa->d_nope == comp->d_nope && swa->d_rope == comp->d_rope, SAD_EINVAL,
-            "gather_dequant_kv: swa and comp caches must share (d_nope, d_rope)");
+  SAD_CHECK(swa->d_nope == comp->d_nope && swa->d_rope == comp->d_rope &&
+                swa->scale_format == comp->scale_format,
+            SAD_EINVAL, "gather_dequant_kv: swa and comp caches must share (d_nope, d_rope, scale_format)");
   SAD_CHECK(num_tokens >= 0 && window_size >= 0 && padded_topk >= 0, SAD_EINVAL,
             "gather_dequant_kv: negative size");
   if (num_tokens == 0 || window_size + padded_topk == 0) return SAD_OK;
@@ -135,6 +157,10 @@ extern "C" int gather_dequant_kv(const sad_kv_cache* swa, const sad_kv_cache* co
   KvDesc c{(const uint8_t*)comp->pool, comp->page_stride, comp->num_pages, comp->block_size};
   if (swa->d_nope == 512) {
     hipLaunchKernelGGL((gather_dequant_kernel<512, 64>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       (hipStream_t)stream, s, c, sparse_indices, sparse_topk_lens, rows,
+                       window_size, padded_topk, out_bf16);
+  } else if (swa->d_nope == 448) {
+    hipLaunchKernelGGL((gather_dequant_kernel<448, 64>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        (hipStream_t)stream, s, c, sparse_indices, sparse_topk_lens, rows,
                        window_size, padded_topk, out_bf16);
   } else {

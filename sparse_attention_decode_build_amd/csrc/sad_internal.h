@@ -15,6 +15,8 @@ void clear_error();
 int check_launch(const char* what);
 // Host-side validation of a latent KV cache descriptor (SAD_OK or an error code).
 int check_kv_cache(const sad_kv_cache* c, const char* what);
+// Bytes of one row's scales: 4*d_nope/64 (fp32 form) or 8 (native ue8m0 form).
+int kv_scale_bytes(const sad_kv_cache* c);
 
 #define SAD_CHECK(cond, code, ...)   \
   do {                               \

@@ -64,6 +64,7 @@ class Config:
     idx_pool_pages: int = 0
     swa_backing: str = "window"  # "window" | "all"
     pin_first_prefill_seq: int = 0  # config 4 pins one prefill request's seq len
+    kv_format: str = "f32"  # "f32": fp32 scale per 64 nope values; "ue8m0": the pages' native record
 
     @property
     def dqk(self) -> int:
@@ -79,7 +80,8 @@ class Config:
 
     @property
     def kv_scale_bytes(self) -> int:
-        return 4 * (self.d_nope // FP8_BLOCK)
+        # native record: one ue8m0 byte per 64 nope values, padded to 8 bytes per row
+        return 8 if self.kv_format == "ue8m0" else 4 * (self.d_nope // FP8_BLOCK)
 
     @property
     def kv_page_bytes(self) -> int:
@@ -129,6 +131,24 @@ CONFIGS = {
         groups=((64, 1, 16384, 0), (4, 4096, (4096, 32768), "half")),
         pin_first_prefill_seq=4096,
     ),
+    # the pages' native KV record (448 fp8 + 64 bf16, ue8m0 scales): small and 64K shapes
+    "tiny_native": Config(
+        name="tiny_native", seed=10, window=32, ratio=4, topk=16, heads=8, d_nope=448, d_rope=64,
+        idx_heads=4, idx_dim=64, block=16, idx_block=16,
+        groups=((1, 1, 256, 0),), kv_pool_pages=64, idx_pool_pages=8, swa_backing="all",
+        kv_format="ue8m0",
+    ),
+    "b32_8k_native": Config(
+        name="b32_8k_native", seed=11, window=128, ratio=4, topk=512, heads=64, d_nope=448, d_rope=64,
+        idx_heads=64, idx_dim=128, block=64, idx_block=64, groups=((32, 1, 8192, 0),),
+        kv_format="ue8m0",
+    ),
+    "b128_64k_native": Config(
+        name="b128_64k_native", seed=12, window=128, ratio=4, topk=2048, heads=128, d_nope=448,
+        d_rope=64, idx_heads=64, idx_dim=128, block=64, idx_block=64,
+        groups=((128, 1, 65536, 0),), kv_pool_pages=4_560_000, idx_pool_pages=900_000,
+        kv_format="ue8m0",
+    ),
     # 8 requests at seq 1M, ratio 128 (8192 compressed rows, all attended), W=128
     "dense_1m": Config(
         name="dense_1m", seed=4, window=128, ratio=128, topk=0, heads=128, d_nope=512,
@@ -139,6 +159,11 @@ CONFIGS = {
 
 # The headline workload (128 requests at 64K context).
 HEADLINE = "b128_64k"
+
+
+def kv_scale_format(cfg: Config) -> int:
+    """The C ABI's scale_format of the config's KV cache (0: fp32 scales, 1: ue8m0 bytes)."""
+    return 1 if cfg.kv_format == "ue8m0" else 0
 
 
 def padded_topk(cfg: Config, max_seq: int) -> int:
@@ -161,6 +186,21 @@ def encode_fp8_rows(x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
     y = torch.clamp(blocks / scale.unsqueeze(-1), -FP8_MAX, FP8_MAX)
     codes = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(n, dn)
     return codes, scale.contiguous()
+
+
+def encode_fp8_rows_ue8m0(x: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """bf16-valued rows [N, Dn] -> (e4m3fn bytes [N, Dn], ue8m0 scale bytes [N, 8]): the
+    pages' native writer rule, exponent = ceil(log2(max(amax, 1e-4) / 448)) per 64 values,
+    values x * 2^-exponent, byte = exponent + 127, padded with zeros to 8 bytes."""
+    n, dn = x.shape
+    blocks = x.float().reshape(n, dn // FP8_BLOCK, FP8_BLOCK)
+    amax = blocks.abs().amax(dim=-1).clamp_min(1.0e-4)
+    exponent = torch.ceil(torch.log2(amax / FP8_MAX))
+    y = torch.clamp(blocks * torch.pow(2.0, -exponent).unsqueeze(-1), -FP8_MAX, FP8_MAX)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(n, dn)
+    sb = torch.zeros((n, 8), dtype=torch.uint8, device=x.device)
+    sb[:, : dn // FP8_BLOCK] = torch.clamp(exponent + 127.0, 0.0, 255.0).to(torch.uint8)
+    return codes, sb.contiguous()
 
 
 # Round-to-nearest-even thresholds on the E2M1 magnitude grid
@@ -263,7 +303,10 @@ def _kv_page_bytes(cfg: Config, rows: torch.Tensor) -> torch.Tensor:
     npages = n // B
     nope = rows[:, : cfg.d_nope]
     rope = rows[:, cfg.d_nope:].contiguous()
-    codes, scales = encode_fp8_rows(nope.float())
+    if cfg.kv_format == "ue8m0":
+        codes, scales = encode_fp8_rows_ue8m0(nope.float())
+    else:
+        codes, scales = encode_fp8_rows(nope.float())
     vals = torch.cat([codes, rope.view(torch.uint8).reshape(n, 2 * cfg.d_rope)], dim=1)
     vals = vals.reshape(npages, B * cfg.kv_row_bytes)
     sc = scales.view(torch.uint8).reshape(npages, B * cfg.kv_scale_bytes)

@@ -21,7 +21,7 @@ def log(msg: str) -> None:
 
 def caches(wl: WL.Workload):
     cfg = wl.cfg
-    kv = sad.KvCache(wl.kv_pool, cfg.block, cfg.d_nope, cfg.d_rope)
+    kv = sad.KvCache(wl.kv_pool, cfg.block, cfg.d_nope, cfg.d_rope, WL.kv_scale_format(cfg))
     idx = sad.IndexerCache(wl.idx_pool, cfg.idx_block, cfg.idx_dim)
     return kv, idx
 
@@ -80,7 +80,7 @@ def oracle_attention(wl: WL.Workload, view, si, lens, tokens, sink=None, q_bits=
     q_bits = view.q if q_bits is None else q_bits
     return O.sparse_mla_decode(q_bits, view.kv_pages, view.kv_pages, si, lens, cfg.window, cfg.block,
                                cfg.block, cfg.d_nope, cfg.d_rope, wl.softmax_scale, attn_sink=sink,
-                               tokens=tokens, return_mass=return_mass)
+                               tokens=tokens, return_mass=return_mass, scale_format=cfg.kv_format)
 
 
 def check_topk(gpu_row: np.ndarray, scores: np.ndarray, valid: np.ndarray, k: int, rel: float = 1e-5):

@@ -110,7 +110,7 @@ def _full_check(wl, view, tokens, sink=None, check_gather=True, bf16_ulp_allowan
         rows_g = sad.gather_dequant_kv(kv, kv, si_sub, lens_sub, cfg.window, wl.padded_topk)
         torch.cuda.synchronize()
         rows_o = O.gather_dequant(view.kv_pages, view.kv_pages, si_o[: len(sub)], lens_o[: len(sub)],
-                                  cfg.window, cfg.block, cfg.block, cfg.d_nope, cfg.d_rope)
+                                  cfg.window, cfg.block, cfg.block, cfg.d_nope, cfg.d_rope, cfg.kv_format)
         got = rows_g.view(torch.int16).cpu().numpy().view(np.uint16)
         assert np.array_equal(got, rows_o)
         log(f"[ok] gather_dequant_kv bit-exact on {len(sub)} tokens")
@@ -141,14 +141,14 @@ def _bf16_ulp(x):
 
 def _caches(wl):
     cfg = wl.cfg
-    return (sad.KvCache(wl.kv_pool, cfg.block, cfg.d_nope, cfg.d_rope),
+    return (sad.KvCache(wl.kv_pool, cfg.block, cfg.d_nope, cfg.d_rope, WL.kv_scale_format(cfg)),
             sad.IndexerCache(wl.idx_pool, cfg.idx_block, cfg.idx_dim))
 
 
 # ---------------------------------------------------------------------------- small
 
 
-@pytest.mark.parametrize("name", ["tiny", "b32_8k"])
+@pytest.mark.parametrize("name", ["tiny", "b32_8k", "tiny_native", "b32_8k_native"])
 def test_small_config_every_step(name):
     wl = _wl(name)
     view = WL.host_view(wl)
@@ -164,7 +164,7 @@ def test_tiny_sparse_equals_dense_selfcheck():
     assert int(lens[0]) == 64
 
 
-@pytest.mark.parametrize("name", ["tiny", "b32_8k"])
+@pytest.mark.parametrize("name", ["tiny", "b32_8k", "tiny_native"])
 def test_peaky_queries(name):
     wl = _wl(name, q_scale=4.0)
     view = WL.host_view(wl)
@@ -322,6 +322,17 @@ def test_b128_64k_full_size_sampled():
     view = WL.host_view(wl, reqs=tokens)
     all_view = view
     _full_check(wl, all_view, tokens)
+    free(wl)
+
+
+@pytest.mark.slow
+def test_b128_64k_native_record_full_size_sampled():
+    """The pages' native KV record (448 fp8 + 64 bf16, ue8m0 scales) at 128 requests x
+    64K context over a ~170 GB pool, in the benchmark's launch configuration."""
+    wl = _wl("b128_64k_native")
+    tokens = [0, 45, 127]
+    view = WL.host_view(wl, reqs=tokens)
+    _full_check(wl, view, tokens)
     free(wl)
 
 
