@@ -57,7 +57,7 @@ class Step:
         self.batch = L.SadBatch(wl.query_start_loc.data_ptr(), wl.seq_lens.data_ptr(),
                                 wl.token_to_req.data_ptr(), wl.num_reqs, T)
         self.kv = L.SadKvCache(wl.kv_pool.data_ptr(), wl.kv_pool.stride(0), wl.kv_pool.shape[0],
-                               cfg.block, cfg.d_nope, cfg.d_rope)
+                               cfg.block, cfg.d_nope, cfg.d_rope, WL.kv_scale_format(cfg))
         self.idx = L.SadMxfp4Cache(wl.idx_pool.data_ptr(), wl.idx_pool.stride(0), wl.idx_pool.shape[0],
                                    cfg.idx_block, cfg.idx_dim)
         self.topk = torch.empty((T, cfg.topk), dtype=torch.int32, device=dev)
@@ -110,7 +110,7 @@ def algorithmic_bytes(wl: WL.Workload) -> dict:
     pos = seq[t2r] - (qsl[t2r + 1] - qsl[t2r]) + (np.arange(len(t2r)) - qsl[t2r])
     nc = (pos + 1) // cfg.ratio
     rows = np.minimum(pos + 1, cfg.window) + np.minimum(nc, cfg.topk)  # attended rows per token
-    row_b = cfg.d_nope + 2 * cfg.d_rope + 4 * (cfg.d_nope // 64)
+    row_b = cfg.d_nope + 2 * cfg.d_rope + cfg.kv_scale_bytes
     idx_row = cfg.idx_dim // 2 + cfg.idx_dim // 32
     W, P, H, D = cfg.window, wl.padded_topk, cfg.heads, cfg.dqk
     attn = rows * row_b + (W + P) * 4 + 4 + 2 * H * D + 2 * H * D
@@ -348,6 +348,48 @@ def bench_prepare_indexer_q(num_tokens: int, positions, iters: int = 30, warmup:
             "hbm_frac": gbs / PEAK_HBM_GBS}
 
 
+def time_steps(wl: WL.Workload, layers: int, K: int, warmup: int):
+    """Wall-clock ms per step over K steps (layers rotated) and the mean HIP-event ms of
+    the three entry points."""
+    steps = [Step(wl, i) for i in range(layers)]
+    for i in range(warmup):
+        steps[i % layers].run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        steps[i % layers].run(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    seg = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(K)])
+    return wall * 1e3 / K, seg.mean(axis=0)
+
+
+def bench_native_record(layers: int, K: int, warmup: int) -> dict:
+    """The same 128 x 64K step on the pages' native KV record (448 fp8 + 64 bf16, ue8m0
+    scales, 584-byte rows): step rate, and the attention kernel against both peaks."""
+    wl = WL.make_workload("b128_64k_native", "cuda", num_layers=layers)
+    torch.cuda.synchronize()
+    ms_step, (ms_idx, ms_build, ms_attn) = time_steps(wl, layers, K, warmup)
+    ab = algorithmic_bytes(wl)
+    T = wl.num_tokens
+    gbs = ab["attention"] / (ms_attn * 1e-3) / 1e9
+    tf = ab["attention_flops"] / (ms_attn * 1e-3) / 1e12
+    res = {"workload": "b128_64k_native: as b128_64k, latent 448 fp8 + 64 bf16, ue8m0 scales, "
+                       f"kv pool {wl.kv_pool.numel() / 1e9:.1f} GB",
+           "tokens_per_s": T / (ms_step * 1e-3), "ms_per_step": ms_step,
+           "kernels_ms": {"indexer_score_topk": ms_idx, "build_sparse_indices": ms_build,
+                          "sparse_mla_decode": ms_attn},
+           "attention_algorithmic_bytes": ab["attention"], "attention_gbs": gbs,
+           "attention_hbm_frac": gbs / PEAK_HBM_GBS, "attention_tflops": tf,
+           "attention_mfma_frac": tf / PEAK_BF16_TFLOPS}
+    del wl
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -382,21 +424,8 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"[bench] workload {WORKLOAD} built in {time.perf_counter() - t0:.1f} s "
         f"(kv pool {wl.kv_pool.numel() / 1e9:.1f} GB, {args.layers} layers)")
-    steps = [Step(wl, i) for i in range(args.layers)]
-    for i in range(args.warmup):
-        steps[i % args.layers].run()
-    torch.cuda.synchronize()
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(K):
-        steps[i % args.layers].run(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    seg = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(K)])
-    ms_step = wall * 1e3 / K
-    ms_idx, ms_build, ms_attn = seg.mean(axis=0)
+    ms_step, (ms_idx, ms_build, ms_attn) = time_steps(wl, args.layers, K, args.warmup)
     T = wl.num_tokens
     ab = algorithmic_bytes(wl)
     attn_gbs = ab["attention"] / (ms_attn * 1e-3) / 1e9
@@ -436,9 +465,15 @@ def main() -> int:
         "indexer_hbm_gbs": idx_gbs,
         "step_hbm_frac": (ab["attention"] + ab["indexer"] + ab["build"]) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
-    log("[bench] indexer query preparation and output quantization (outside the step)")
-    del steps
-    result["next_rows"] = {"prepare_indexer_q_mxfp4": {
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    log("[bench] next rows: native KV record, indexer query preparation, output quantization, cache writes")
+    del wl
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    native = bench_native_record(args.layers, K, args.warmup)
+    result["next_rows"] = {"native_kv_record": native, "prepare_indexer_q_mxfp4": {
         "bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
         "decode_128_tokens": bench_prepare_indexer_q(T, [65535] * T),
         "prefill_16448_tokens": bench_prepare_indexer_q(16448, None)},
@@ -449,9 +484,6 @@ def main() -> int:
         "cache_writes": {"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "decode_128_rows": bench_cache_writes(T),
                          "prefill_4112_rows": bench_cache_writes(16448 // 4)}}
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(result), flush=True)
     return 0
 
