@@ -761,34 +761,68 @@ def encode_kv_nope(x: np.ndarray):
     return e4m3_encode(y.astype(np.float64)).reshape(n, dn), scale
 
 
+def encode_kv_nope_ue8m0(x: np.ndarray):
+    """bf16-valued nope rows [n, Dn] -> (e4m3fn bytes [n, Dn], scale bytes [n, 8]).
+
+    [ops] ``_fp8_ds_mla_cache_rows`` (the pages' native record): per 64 values,
+    exponent = ceil(log2(max(amax, 1e-4) / 448)), written exactly as the smallest
+    integer e with 448 * 2^e >= max(amax, 1e-4); codes e4m3(clamp(x * 2^-e, +-448));
+    scale byte = clamp(e + 127, 0, 255); the row's 8th scale byte is a zero pad.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n, dn = x.shape
+    blocks = x.reshape(n, dn // 64, 64)
+    a = np.maximum(np.abs(blocks).max(axis=-1), float(np.float32(1.0e-4)))
+    e = np.empty(a.shape, dtype=np.int64)
+    for idx, v in np.ndenumerate(a):
+        k = math.ceil(math.log2(v / 448.0))
+        while 448.0 * 2.0 ** (k - 1) >= v:
+            k -= 1
+        while 448.0 * 2.0 ** k < v:
+            k += 1
+        e[idx] = k
+    y = np.clip(blocks * np.ldexp(1.0, -e)[..., None], -448.0, 448.0)
+    sb = np.zeros((n, 8), dtype=np.uint8)
+    sb[:, : dn // 64] = np.clip(e + 127, 0, 255).astype(np.uint8)
+    return e4m3_encode(y).reshape(n, dn), sb
+
+
 def insert_kv_rows(kv_pages: dict, rows_bits, positions, cos_sin_cache, ratio: int, slots,
-                   block_size: int, d_nope: int, d_rope: int, num_pages: int, page_bytes: int) -> dict:
+                   block_size: int, d_nope: int, d_rope: int, num_pages: int, page_bytes: int,
+                   scale_format: str = "f32") -> dict:
     """Write compressed KV rows into the paged latent cache; returns the updated pages.
 
     [ops] ``_write_fp8_ds_mla_cache_rows_capturable`` / ``_fp8_ds_mla_cache_rows``:
     the rope tail is rotated (GPT-J) at the compressed position and stored bf16;
     the nope part is stored FP8 with one scale per 64 (``encode_kv_nope``); row
     ``o`` of page ``g`` holds its values at ``g*stride + o*(Dn + 2*Dr)`` and its
-    scales at ``g*stride + B*(Dn + 2*Dr) + o*4*Dn/64``.  A slot that is negative
-    or whose page is past the pool is skipped.  Pages not yet in ``kv_pages`` start
-    as zero bytes.
+    scales at ``g*stride + B*(Dn + 2*Dr) + o*scale_bytes``.  In the native "ue8m0"
+    form the nope part takes ``encode_kv_nope_ue8m0``.  A slot that is negative or
+    whose page is past the pool is skipped.  Pages not yet in ``kv_pages`` start as
+    zero bytes.
     """
     x = bf16_bits_to_float(rows_bits).astype(np.float32)
     cs = np.asarray(cos_sin_cache, dtype=np.float32)
     cp = compressed_position(positions, ratio)
     out = {k: v.copy() for k, v in kv_pages.items()}
-    row_b, nsc = d_nope + 2 * d_rope, d_nope // 64
+    row_b = d_nope + 2 * d_rope
+    sbytes = kv_scale_bytes(d_nope, scale_format)
     for i, s in enumerate(np.asarray(slots, dtype=np.int64)):
         if s < 0 or s // block_size >= num_pages or not (0 <= cp[i] < cs.shape[0]):
             continue
         roped = rope_gptj_tail(x[i], cs[cp[i], : d_rope // 2], cs[cp[i], d_rope // 2:], d_rope)
-        codes, scale = encode_kv_nope(x[i: i + 1, :d_nope])
+        if scale_format == "f32":
+            codes, scale = encode_kv_nope(x[i: i + 1, :d_nope])
+            scale_row = scale[0].astype(np.float32).view(np.uint8)
+        else:
+            codes, sb8 = encode_kv_nope_ue8m0(x[i: i + 1, :d_nope])
+            scale_row = sb8[0]
         g, o = int(s) // block_size, int(s) % block_size
         page = out.setdefault(g, np.zeros(page_bytes, dtype=np.uint8))
         page[o * row_b: o * row_b + d_nope] = codes[0]
         page[o * row_b + d_nope: (o + 1) * row_b] = float32_to_bf16_bits(roped[d_nope:]).view(np.uint8)
-        sb = block_size * row_b + o * 4 * nsc
-        page[sb: sb + 4 * nsc] = scale[0].astype(np.float32).view(np.uint8)
+        sb = block_size * row_b + o * sbytes
+        page[sb: sb + sbytes] = scale_row
     return out
 
 

@@ -705,3 +705,27 @@ def test_insert_index_keys_matches_the_rotated_key():
         step = np.repeat(np.ldexp(1.0, pages[s // B][B * D // 2 + (s % B) * 4: B * D // 2 + (s % B) * 4 + 4]
                                   .astype(np.int64) - 127), 32)
         assert (np.abs(got[s] - ideal) <= step + 2.0 ** -7 * np.abs(ideal)).all()
+
+
+def test_native_kv_encoder_matches_harness_and_round_trips():
+    # The oracle's native writer rule against the harness's separately written one (torch
+    # ops of the pages' formula), and write -> read through the pinned native reader:
+    # power-of-two scales make every block's largest value land on a binade of e4m3.
+    g = torch.Generator().manual_seed(29)
+    x = (torch.randn(12, 448, generator=g) * torch.exp2(torch.randint(-20, 20, (12, 1), generator=g).float()))
+    x[2] = 0.0
+    x = x.bfloat16().float()
+    codes, sb = O.encode_kv_nope_ue8m0(x.numpy())
+    hc, hs = WL.encode_fp8_rows_ue8m0(x)
+    assert np.array_equal(codes, hc.numpy()) and np.array_equal(sb, hs.numpy())
+    B, Dn, Dr = 16, 448, 64
+    page_bytes = B * (Dn + 2 * Dr + 8)
+    rows = torch.cat([x, torch.randn(12, Dr, generator=g)], 1).bfloat16()
+    bits = rows.view(torch.int16).numpy().view(np.uint16)
+    cs = WL.rope_table(8, Dr).numpy()
+    pages = O.insert_kv_rows({}, bits, [0] * 12, cs, 4, list(range(12)), B, Dn, Dr, 1, page_bytes, "ue8m0")
+    back = O.bf16_bits_to_float(O.dequant_rows(pages, list(range(12)), B, Dn, Dr, "ue8m0"))
+    xf = x.numpy().astype(np.float64)
+    sc = np.repeat(np.ldexp(1.0, sb[:, :7].astype(np.int64) - 127), 64, axis=1)
+    assert (np.abs(back[:, :Dn] - xf) <= np.maximum(np.abs(xf) * 2.0 ** -4, sc * 2.0 ** -10)).all()
+    assert np.array_equal(back[:, Dn:], rows[:, Dn:].float().numpy())  # position 0: rope is the identity
