@@ -342,6 +342,10 @@ int inv_rope_fp8_quant(const uint16_t* attn_out, const int32_t* positions,
  *     e4m3fn(clamp(x / scale, +-448)) (correctly rounded fp32 divisions, nearest even);
  *   - row s % B of page s / B: values at page*page_stride + (s % B)*(Dn + 2*Dr), scales
  *     at page*page_stride + B*(Dn + 2*Dr) + (s % B)*4*Dn/64.
+ * In the native form (SAD_KV_SCALE_UE8M0, 448 + 64) the nope part takes the pages' own
+ * rule ([ops] _fp8_ds_mla_cache_rows): per 64 values e = the smallest integer with
+ * 448 * 2^e >= max(amax, 1e-4), code = e4m3fn(x * 2^-e), scale byte e + 127, and the
+ * row's 8th scale byte is a zero pad.
  * A negative slot, a page past num_pages or c outside [0, max_pos) writes nothing.  The
  * cache's pool is written in place; two rows with the same slot race.
  *

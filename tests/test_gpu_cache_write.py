@@ -40,12 +40,14 @@ def _slots(n, pages, block, seed):
     return s
 
 
-@pytest.mark.parametrize("Dn,Dr,B,N,ratio", [(512, 64, 64, 37, 4), (128, 32, 16, 20, 4), (512, 64, 64, 2048, 128)])
-def test_insert_kv_rows_pages_bit_exact(Dn, Dr, B, N, ratio):
-    log(f"[kvw] Dn={Dn} Dr={Dr} B={B} N={N} ratio={ratio}")
+@pytest.mark.parametrize("Dn,Dr,B,N,ratio,fmt", [(512, 64, 64, 37, 4, "f32"), (128, 32, 16, 20, 4, "f32"),
+                                                (512, 64, 64, 2048, 128, "f32"), (448, 64, 64, 45, 4, "ue8m0"),
+                                                (448, 64, 16, 900, 128, "ue8m0")])
+def test_insert_kv_rows_pages_bit_exact(Dn, Dr, B, N, ratio, fmt):
+    log(f"[kvw] Dn={Dn} Dr={Dr} B={B} N={N} ratio={ratio} {fmt}")
     pages, P = 64, 3000
     row_b = Dn + 2 * Dr
-    page_bytes = B * (row_b + 4 * (Dn // 64))
+    page_bytes = B * (row_b + O.kv_scale_bytes(Dn, fmt))
     g = torch.Generator().manual_seed(N)
     pool = torch.randint(0, 256, (pages, page_bytes), dtype=torch.uint8, generator=g)
     rows = (torch.randn(N, Dn + Dr, generator=g) * torch.exp2(torch.randint(-6, 6, (N, 1), generator=g).float())).bfloat16()
@@ -55,10 +57,11 @@ def test_insert_kv_rows_pages_bit_exact(Dn, Dr, B, N, ratio):
     cs = WL.rope_table(P, Dr)
     before = {p: pool[p].numpy().copy() for p in range(pages)}
     dev_pool = pool.cuda()
-    kv = sad.KvCache(dev_pool, B, Dn, Dr)
+    kv = sad.KvCache(dev_pool, B, Dn, Dr, sad.KV_SCALE_UE8M0 if fmt == "ue8m0" else sad.KV_SCALE_F32)
     sad.insert_kv_rows(rows.cuda(), pos.cuda(), cs.cuda(), ratio, torch.from_numpy(slots.astype(np.int32)).cuda(), kv)
     torch.cuda.synchronize()
-    want = O.insert_kv_rows(before, _bits(rows), pos.numpy(), cs.numpy(), ratio, slots, B, Dn, Dr, pages, page_bytes)
+    want = O.insert_kv_rows(before, _bits(rows), pos.numpy(), cs.numpy(), ratio, slots, B, Dn, Dr, pages,
+                            page_bytes, fmt)
     got = dev_pool.cpu().numpy()
     for p in range(pages):
         bad = np.flatnonzero(got[p] != want[p])
