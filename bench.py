@@ -233,7 +233,7 @@ def summarize_traffic(fetch_dir: str, write_dir: str) -> int:
     """Attention kernel HBM traffic per launch from two rocprofv3 --pmc runs of
     `bench.py --copy-calibration-gib 1 ...` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
     each scaled by the same counter on the 1 GiB copy kernel."""
-    copy_pat, attn_pat = "MulFunctor", "sparse_mla_kernel"
+    copy_pat, attn_pat = "MulFunctor", "sparse_mla_kernel<512, 64"
     cal = float(1 << 30)
     cf, _ = _pmc_mean(fetch_dir, "FETCH_SIZE", copy_pat, largest=True)
     cw, _ = _pmc_mean(write_dir, "WRITE_SIZE", copy_pat, largest=True)
@@ -398,6 +398,9 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=4, help="independent layers rotated per step")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the extra legs (native record, query preparation, output quantization, cache "
+                         "writes); counter runs use this so only the calibration copy and the step run")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="first run a plain copy of this many GiB (rocprofv3 counter calibration)")
     ap.add_argument("--summarize-stats", metavar="DIR", help="print a rocprofv3 kernel-stats CSV as markdown")
@@ -468,6 +471,9 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    if args.no_next_rows:
+        print(json.dumps(result), flush=True)
+        return 0
     log("[bench] next rows: native KV record, indexer query preparation, output quantization, cache writes")
     del wl
     torch.cuda.synchronize()
