@@ -498,6 +498,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
       wait_vmem<0>();
   };
   RawRows<DN, DR> rr;             // this wave's raw rows of the tile being dequantized
+  u32x4_t rope_keep;  // rope chunk of the tile whose K rows are stored in phase C
   u32x4_t dq[2 * S::FP8_LINES];  // ... and their fp8 part as bf16 (rope part: rr.rope)
   // One fp8 word of the raw rows (4 e4m3 values) -> 4 bf16 in dq: word w of line j holds
   // elements 16c + 4(w%4) .. +4 of that line.
@@ -664,11 +665,10 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     static_for<(kLdsAhead < NREAD ? kLdsAhead : NREAD)>([&](auto jc) { vread(jc, vbase); });
   };
 
-  // Phase B: this wave's rows of tile j+1 stored into the free K buffer; both dim halves
-  // of S^T summed, unattended columns -inf, row maximum, lazy rescale decision, phase
-  // C's first LDS reads, and the weights of keys 0..15 (pb[0]; keys 16..31 follow
-  // between the first PV MFMAs).  Returns whether any head of the wave needs its O
-  // rescaled.
+  // Phase B: both dim halves of S^T summed, unattended columns -inf, row maximum, lazy
+  // rescale decision, phase C's first LDS reads, and the weights of keys 0..15 (pb[0];
+  // keys 16..31 follow between the first PV MFMAs).  Returns whether any head of the
+  // wave needs its O rescaled.
   auto phase_b = [&](int tile, int b, int rs2, const f32x16_t& s, bf16x8_t (&pb)[2], float& alpha)
                      __attribute__((always_inline)) -> bool {
     int lane_s = lane;
@@ -677,23 +677,9 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     float4 ox[4];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) ox[q4] = xr[64 * q4];
-    // this wave's rows of tile j+1 (dequantized in registers during the previous step)
-    // and its mask byte into the other K buffer, free since the step began; LDS is
-    // otherwise idle here, while phase A's fragment reads kept it busy
+    // this wave's mask byte of tile j+1 beside the other K buffer (its rows go there
+    // during phase C)
     {
-      const int key = 8 * wave + (lane_s >> 3);
-      const int c = lane_s & 7;
-      uint16_t* sdst = kt[b ^ 1] + kt_off<S::KCH>(key, 16 * c);
-#pragma unroll
-      for (int kk = 0; kk < 2 * S::FP8_LINES - 2; ++kk)
-        *reinterpret_cast<u32x4_t*>(sdst + 128 * (kk >> 1) + 8 * (kk & 1)) = dq[kk];
-      // the last fp8 line: in the native record only its first FP8_TAIL chunks
-      if (S::FP8_TAIL == 8 || c < S::FP8_TAIL) {
-        constexpr int kl = 2 * S::FP8_LINES - 2;
-        *reinterpret_cast<u32x4_t*>(sdst + 128 * (kl >> 1)) = dq[kl];
-        *reinterpret_cast<u32x4_t*>(sdst + 128 * (kl >> 1) + 8) = dq[kl + 1];
-      }
-      if (c < S::ROPE_CH) *reinterpret_cast<u32x4_t*>(kt[b ^ 1] + kt_off<S::KCH>(key, DN + 8 * c)) = rr.rope;
       if (lane_s == 0) reinterpret_cast<uint8_t*>(&kt_mask[b ^ 1])[wave] = (uint8_t)mask_a;
       mask_a = mask_b;
       mask_b = mask_c;
@@ -728,14 +714,17 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     m_run = m_new;
     l_run *= alpha;
     if (LSE) l_lse *= alpha;
+    rope_keep = rr.rope;
     c_reads(tile, b, rs2, lane_s);
     static_for<4>([&](auto pc) { weight_pair(std::integral_constant<int, 2 * decltype(pc)::value>{}, pb); });
     return __ballot(upd) != 0ull;
   };
 
-  // Phase C: O^T += V^T P^T on tile j while this wave's rows of tile j+2 (read from their
-  // raw slot in phase B) are dequantized into registers and this wave's DMA of tile j+5
-  // into that raw slot is issued.
+  // Phase C: O^T += V^T P^T on tile j while this wave's rows of tile j+1 (dequantized in
+  // registers during the previous step) are stored into the other K buffer, free since
+  // the step began, each 16-byte chunk just before the words that overwrite its registers
+  // with tile j+2 (read from its raw slot in phase B) are converted, and this wave's DMA
+  // of tile j+5 into that raw slot is issued.
   auto phase_c = [&](int tile, int b, int rs2, bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
     int lane_s = lane;
     asm volatile("" : "+v"(lane_s));
@@ -777,8 +766,23 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
       static_for<NWORD>([&](auto wc) {
         constexpr int w = decltype(wc)::value;
         constexpr int slot = w < 2 * MTMAX ? w : 2 * MTMAX - 1;
-        if constexpr (slot == i) convert_word(wc);
+        if constexpr (slot == i) {
+          if constexpr (w % 2 == 0) {
+            constexpr int kk = w >> 1;
+            const int key = 8 * wave + (lane_s >> 3);
+            const int c = lane_s & 7;
+            uint16_t* sdst = kt[b ^ 1] + kt_off<S::KCH>(key, 16 * c) + 128 * (kk >> 1) + 8 * (kk & 1);
+            if ((kk >> 1) < S::FP8_LINES - 1 || S::FP8_TAIL == 8 || c < S::FP8_TAIL)
+              *reinterpret_cast<u32x4_t*>(sdst) = dq[kk];
+          }
+          convert_word(wc);
+        }
       });
+      if constexpr (i == 0) {
+        const int key = 8 * wave + (lane_s >> 3);
+        const int c = lane_s & 7;
+        if (c < S::ROPE_CH) *reinterpret_cast<u32x4_t*>(kt[b ^ 1] + kt_off<S::KCH>(key, DN + 8 * c)) = rope_keep;
+      }
       // the DMA of tile j+5 into the raw slot just read, one load per second slot, so a stall
       // of the memory pipeline overlaps the MFMAs already issued
       if constexpr (i == DSLOT0 - 1) {
