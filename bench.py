@@ -49,7 +49,7 @@ def log(*a):
 class Step:
     """Pre-marshalled C-ABI calls for one layer (no Python work in the timed loop)."""
 
-    def __init__(self, wl: WL.Workload, layer: int):
+    def __init__(self, wl: WL.Workload, layer: int, stream=None):
         cfg = wl.cfg
         lay = wl.layers[layer]
         self.lib = L.load()
@@ -69,7 +69,7 @@ class Step:
         self.ws_i = torch.empty((max(ws_i, 16),), dtype=torch.uint8, device=dev)
         ws_a = self.lib.sparse_mla_decode_workspace_size(T, cfg.heads, cfg.window + wl.padded_topk, cfg.dqk)
         self.ws_a = torch.empty((max(ws_a, 16),), dtype=torch.uint8, device=dev)
-        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        stream = ctypes.c_void_p((stream if stream is not None else torch.cuda.current_stream()).cuda_stream)
         p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
         n_pages = wl.kv_pool.shape[0]
         self.args_idx = (ctypes.byref(self.batch), p(lay.idx_q_values), p(lay.idx_q_scales),
@@ -366,6 +366,49 @@ def time_steps(wl: WL.Workload, layers: int, K: int, warmup: int):
     return wall * 1e3 / K, seg.mean(axis=0)
 
 
+def time_steps_graph(wl: WL.Workload, layers: int, K: int, warmup: int):
+    """Wall-clock ms per step when the steps of all layers are captured once into a HIP
+    graph and replayed (every kernel of every step runs on each replay; only the host's
+    launch work is replaced).  Before timing, each layer's outputs after a replay are
+    checked bit for bit against an eager run of the same step."""
+    s = torch.cuda.Stream()
+    steps = [Step(wl, i, stream=s) for i in range(layers)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for i in range(warmup):
+            steps[i % layers].run()
+    torch.cuda.synchronize()
+    eager = []
+    for st in steps:
+        with torch.cuda.stream(s):
+            st.run()
+        torch.cuda.synchronize()
+        eager.append((st.topk.clone(), st.si.clone(), st.lens.clone(), st.out.clone()))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for st in steps:
+            st.run()
+    for st in steps:  # clear the outputs, so the check below sees the replay's writes
+        for t in (st.topk, st.si, st.lens, st.out):
+            t.zero_()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    for st, ref in zip(steps, eager):
+        for a, b in zip((st.topk, st.si, st.lens, st.out), ref):
+            if not torch.equal(a, b):
+                raise RuntimeError("graph replay differs from the eager step")
+    reps = max(1, K // layers)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del g
+    return wall * 1e3 / (reps * layers)
+
+
 def bench_native_record(layers: int, K: int, warmup: int) -> dict:
     """The same 128 x 64K step on the pages' native KV record (448 fp8 + 64 bf16, ue8m0
     scales, 584-byte rows): step rate, and the attention kernel against both peaks."""
@@ -429,6 +472,7 @@ def main() -> int:
         f"(kv pool {wl.kv_pool.numel() / 1e9:.1f} GB, {args.layers} layers)")
     K = args.steps
     ms_step, (ms_idx, ms_build, ms_attn) = time_steps(wl, args.layers, K, args.warmup)
+    ms_graph = time_steps_graph(wl, args.layers, K, args.warmup)
     T = wl.num_tokens
     ab = algorithmic_bytes(wl)
     attn_gbs = ab["attention"] / (ms_attn * 1e-3) / 1e9
@@ -465,6 +509,7 @@ def main() -> int:
                        "sparse_mla_decode": ms_attn},
         "algorithmic_bytes_per_step": {"attention": ab["attention"], "indexer": ab["indexer"],
                                        "build": ab["build"]},
+        "graph_replay": {"ms_per_step": ms_graph, "tokens_per_s": T / (ms_graph * 1e-3)},
         "indexer_hbm_gbs": idx_gbs,
         "step_hbm_frac": (ab["attention"] + ab["indexer"] + ab["build"]) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
