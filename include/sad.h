@@ -196,6 +196,27 @@ int indexer_score_topk(const sad_batch* batch, const uint8_t* q_values, const ui
 size_t indexer_score_topk_workspace_size(int32_t num_tokens, int32_t max_ctx_rows, int32_t topk);
 
 /*
+ * indexer_topk_sparse_indices - indexer_score_topk and build_sparse_indices in one call
+ * (the index build runs inside the top-k kernel, so the step takes one launch fewer).
+ *
+ * Exactly indexer_score_topk(batch, q_values, ..., topk, topk_local, NULL, 0, workspace,
+ * workspace_bytes) followed by build_sparse_indices(batch, replay_start, swa_bt, ...,
+ * comp_num_pages, topk_local, topk_stride = topk, topk, window_size, compress_ratio,
+ * padded_topk, sparse_indices, sparse_topk_lens): the same outputs, bit for bit, and
+ * the union of both calls' argument rules and errors.  Each argument means what it
+ * means there (see both declarations above and below).
+ */
+int indexer_topk_sparse_indices(
+    const sad_batch* batch, const uint8_t* q_values, const uint8_t* q_scales, const float* weights,
+    int32_t num_idx_heads, const sad_mxfp4_cache* keys, const int32_t* idx_bt, int64_t idx_bt_stride,
+    int32_t idx_bt_cols, int32_t compress_ratio, int32_t topk, int32_t* topk_local,
+    const int32_t* replay_start, const int32_t* swa_bt, int64_t swa_bt_stride, int32_t swa_bt_cols,
+    int32_t swa_block_size, int64_t swa_num_pages, const int32_t* comp_bt, int64_t comp_bt_stride,
+    int32_t comp_bt_cols, int32_t comp_block_size, int64_t comp_num_pages, int32_t window_size,
+    int32_t padded_topk, int32_t* sparse_indices, int32_t* sparse_topk_lens, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/*
  * prepare_indexer_q_mxfp4 - the indexer query in the form indexer_score_topk takes.
  *
  * Defined by [ops] deepseek_v4_prepare_indexer_q_mxfp4 with

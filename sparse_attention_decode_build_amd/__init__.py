@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     indexer_score_topk,
     prepare_indexer_q_mxfp4,
     indexer_score_topk_workspace_size,
+    indexer_topk_sparse_indices,
     insert_index_keys,
     insert_kv_rows,
     inv_rope_fp8_quant,

@@ -50,6 +50,10 @@ _SIGNATURES = {
                                    ctypes.POINTER(SadMxfp4Cache), c_ptr, c_i64, c_i32, c_i32, c_i32,
                                    c_ptr, c_ptr, c_i64, c_ptr, c_size, c_ptr]),
     "indexer_score_topk_workspace_size": (c_size, [c_i32, c_i32, c_i32]),
+    "indexer_topk_sparse_indices": (c_i32, [ctypes.POINTER(SadBatch), c_ptr, c_ptr, c_ptr, c_i32,
+                                            ctypes.POINTER(SadMxfp4Cache), c_ptr, c_i64, c_i32, c_i32, c_i32,
+                                            c_ptr, c_ptr, c_ptr, c_i64, c_i32, c_i32, c_i64, c_ptr, c_i64, c_i32,
+                                            c_i32, c_i64, c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_size, c_ptr]),
     "prepare_indexer_q_mxfp4": (c_i32, [c_ptr, c_ptr, c_ptr, c_i32, c_i32, c_ptr, c_f32, c_f32, c_i32,
                                         c_i32, c_i32, c_ptr, c_ptr, c_ptr, c_ptr]),
     "gather_dequant_kv": (c_i32, [ctypes.POINTER(SadKvCache), ctypes.POINTER(SadKvCache), c_ptr, c_ptr,
@@ -184,6 +188,44 @@ def build_sparse_indices(query_start_loc, seq_lens, token_to_req, replay_start, 
         padded_topk, _p(out), _p(lens), _stream(stream))
     _check("build_sparse_indices", rc)
     return out, lens
+
+
+def indexer_topk_sparse_indices(query_start_loc, seq_lens, token_to_req, q_values, q_scales, weights,
+                                keys: IndexerCache, idx_bt, compress_ratio, topk, replay_start, swa_bt,
+                                swa_block_size, swa_num_pages, comp_bt, comp_block_size, comp_num_pages,
+                                window_size, padded_topk, topk_local=None, out=None, lens=None,
+                                workspace=None, stream=None):
+    """indexer_score_topk then build_sparse_indices in one call -> (topk_local, sparse_indices, lens)."""
+    lib = load()
+    b = _batch(query_start_loc, seq_lens, token_to_req)
+    T = b.num_tokens
+    _need(q_values, torch.uint8, "q_values", dim=3)
+    _need(q_scales, torch.uint8, "q_scales", dim=3)
+    _need(weights, torch.float32, "weights", dim=2)
+    for t, nm in ((idx_bt, "idx_bt"), (swa_bt, "swa_bt"), (comp_bt, "comp_bt")):
+        _need(t, torch.int32, nm, dim=2)
+    if replay_start is not None:
+        _need(replay_start, torch.int32, "replay_start", dim=1)
+    dev = q_values.device
+    if topk_local is None:
+        topk_local = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((T, window_size + padded_topk), dtype=torch.int32, device=dev)
+    if lens is None:
+        lens = torch.empty((T,), dtype=torch.int32, device=dev)
+    max_rows = idx_bt.shape[1] * keys.block_size
+    if workspace is None:
+        ws = lib.indexer_score_topk_workspace_size(T, max_rows, topk)
+        workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)
+    kc = keys.c()
+    rc = lib.indexer_topk_sparse_indices(
+        ctypes.byref(b), _p(q_values), _p(q_scales), _p(weights), q_values.shape[1], ctypes.byref(kc),
+        _p(idx_bt), idx_bt.stride(0), idx_bt.shape[1], compress_ratio, topk, _p(topk_local), _p(replay_start),
+        _p(swa_bt), swa_bt.stride(0), swa_bt.shape[1], swa_block_size, swa_num_pages, _p(comp_bt),
+        comp_bt.stride(0), comp_bt.shape[1], comp_block_size, comp_num_pages, window_size, padded_topk,
+        _p(out), _p(lens), _p(workspace), workspace.numel(), _stream(stream))
+    _check("indexer_topk_sparse_indices", rc)
+    return topk_local, out, lens
 
 
 def prepare_indexer_q_mxfp4(index_q, positions, cos_sin_cache, weights, softmax_scale, head_scale,

@@ -104,6 +104,45 @@ __global__ __launch_bounds__(kThreads) void build_sparse_indices_kernel(
 }
 
 }  // namespace
+
+int check_build_args(const char* what, const sad_batch* batch, const int32_t* swa_bt,
+                     int64_t swa_bt_stride, int32_t swa_bt_cols, int32_t swa_block_size,
+                     int64_t swa_num_pages, const int32_t* comp_bt, int64_t comp_bt_stride,
+                     int32_t comp_bt_cols, int32_t comp_block_size, int64_t comp_num_pages,
+                     bool has_topk, int64_t topk_stride, int32_t topk, int32_t window_size,
+                     int32_t compress_ratio, int32_t padded_topk, const int32_t* sparse_indices,
+                     const int32_t* sparse_topk_lens) {
+  SAD_CHECK(batch != nullptr, SAD_EINVAL, "%s: batch is NULL", what);
+  const int T = batch->num_tokens;
+  SAD_CHECK(T >= 0 && batch->num_reqs >= 0, SAD_EINVAL, "%s: negative num_tokens/num_reqs", what);
+  SAD_CHECK(window_size >= 0 && padded_topk >= 0 && topk >= 0, SAD_EINVAL,
+            "%s: negative window_size/padded_topk/topk", what);
+  SAD_CHECK(padded_topk % 64 == 0, SAD_EINVAL, "%s: padded_topk (%d) must be a multiple of 64", what,
+            padded_topk);
+  SAD_CHECK(compress_ratio >= 1, SAD_EINVAL, "%s: compress_ratio must be >= 1", what);
+  SAD_CHECK(!has_topk || (topk <= padded_topk && topk_stride >= topk), SAD_EINVAL,
+            "%s: need topk <= padded_topk and topk_stride >= topk", what);
+  SAD_CHECK(swa_block_size >= 1 && comp_block_size >= 1, SAD_EINVAL, "%s: block sizes must be >= 1",
+            what);
+  SAD_CHECK(swa_bt_cols >= 0 && comp_bt_cols >= 0 && swa_num_pages >= 0 && comp_num_pages >= 0,
+            SAD_EINVAL, "%s: negative table/pool size", what);
+  SAD_CHECK(swa_num_pages * (int64_t)swa_block_size <= INT32_MAX &&
+                comp_num_pages * (int64_t)comp_block_size <= INT32_MAX,
+            SAD_EINVAL, "%s: slots must fit int32 (num_pages*block_size)", what);
+  SAD_CHECK(swa_bt_stride >= swa_bt_cols && comp_bt_stride >= comp_bt_cols, SAD_EINVAL,
+            "%s: table stride smaller than its column count", what);
+  SAD_CHECK((int64_t)T * (window_size + padded_topk) < ((int64_t)1 << 40), SAD_EINVAL,
+            "%s: output too large", what);
+  if (T == 0) return SAD_OK;
+  SAD_CHECK(batch->query_start_loc && batch->seq_lens && batch->token_to_req, SAD_EINVAL,
+            "%s: batch arrays must be non-NULL", what);
+  SAD_CHECK(swa_bt != nullptr && comp_bt != nullptr, SAD_EINVAL, "%s: block tables must be non-NULL",
+            what);
+  SAD_CHECK(sparse_indices != nullptr && sparse_topk_lens != nullptr, SAD_EINVAL,
+            "%s: outputs must be non-NULL", what);
+  return SAD_OK;
+}
+
 }  // namespace sad
 
 using namespace sad;
@@ -119,35 +158,13 @@ extern "C" int build_sparse_indices(const sad_batch* batch, const int32_t* repla
                                     int32_t padded_topk, int32_t* sparse_indices,
                                     int32_t* sparse_topk_lens, void* stream) {
   clear_error();
-  SAD_CHECK(batch != nullptr, SAD_EINVAL, "build_sparse_indices: batch is NULL");
+  const int rc = check_build_args("build_sparse_indices", batch, swa_bt, swa_bt_stride, swa_bt_cols,
+                                  swa_block_size, swa_num_pages, comp_bt, comp_bt_stride, comp_bt_cols,
+                                  comp_block_size, comp_num_pages, topk_local != nullptr, topk_stride,
+                                  topk, window_size, compress_ratio, padded_topk, sparse_indices,
+                                  sparse_topk_lens);
+  if (rc != SAD_OK || batch->num_tokens == 0) return rc;
   const int T = batch->num_tokens;
-  SAD_CHECK(T >= 0 && batch->num_reqs >= 0, SAD_EINVAL,
-            "build_sparse_indices: negative num_tokens/num_reqs");
-  SAD_CHECK(window_size >= 0 && padded_topk >= 0 && topk >= 0, SAD_EINVAL,
-            "build_sparse_indices: negative window_size/padded_topk/topk");
-  SAD_CHECK(padded_topk % 64 == 0, SAD_EINVAL,
-            "build_sparse_indices: padded_topk (%d) must be a multiple of 64", padded_topk);
-  SAD_CHECK(compress_ratio >= 1, SAD_EINVAL, "build_sparse_indices: compress_ratio must be >= 1");
-  SAD_CHECK(topk_local == nullptr || (topk <= padded_topk && topk_stride >= topk), SAD_EINVAL,
-            "build_sparse_indices: need topk <= padded_topk and topk_stride >= topk");
-  SAD_CHECK(swa_block_size >= 1 && comp_block_size >= 1, SAD_EINVAL,
-            "build_sparse_indices: block sizes must be >= 1");
-  SAD_CHECK(swa_bt_cols >= 0 && comp_bt_cols >= 0 && swa_num_pages >= 0 && comp_num_pages >= 0,
-            SAD_EINVAL, "build_sparse_indices: negative table/pool size");
-  SAD_CHECK(swa_num_pages * (int64_t)swa_block_size <= INT32_MAX &&
-                comp_num_pages * (int64_t)comp_block_size <= INT32_MAX,
-            SAD_EINVAL, "build_sparse_indices: slots must fit int32 (num_pages*block_size)");
-  SAD_CHECK(swa_bt_stride >= swa_bt_cols && comp_bt_stride >= comp_bt_cols, SAD_EINVAL,
-            "build_sparse_indices: table stride smaller than its column count");
-  SAD_CHECK((int64_t)T * (window_size + padded_topk) < ((int64_t)1 << 40), SAD_EINVAL,
-            "build_sparse_indices: output too large");
-  if (T == 0) return SAD_OK;
-  SAD_CHECK(batch->query_start_loc && batch->seq_lens && batch->token_to_req, SAD_EINVAL,
-            "build_sparse_indices: batch arrays must be non-NULL");
-  SAD_CHECK(swa_bt != nullptr && comp_bt != nullptr, SAD_EINVAL,
-            "build_sparse_indices: block tables must be non-NULL");
-  SAD_CHECK(sparse_indices != nullptr && sparse_topk_lens != nullptr, SAD_EINVAL,
-            "build_sparse_indices: outputs must be non-NULL");
   hipLaunchKernelGGL(build_sparse_indices_kernel, dim3(T), dim3(kThreads), 0,
                      (hipStream_t)stream, *batch, replay_start, swa_bt, swa_bt_stride, swa_bt_cols,
                      swa_block_size, swa_num_pages, comp_bt, comp_bt_stride, comp_bt_cols,

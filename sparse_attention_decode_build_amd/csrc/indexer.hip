@@ -251,10 +251,33 @@ __device__ inline int select_bin(const int* hist, int kk, int* sh, int* pick, in
   return pick[0];
 }
 
-template <int KPT>
+// Index-build arguments of the fused path (build_sparse_indices on the top-k output).
+struct BuildArgs {
+  const int32_t* replay;
+  const int32_t* swa_bt;
+  int64_t swa_stride;
+  int swa_cols;
+  int swa_block;
+  int64_t swa_pages;
+  const int32_t* comp_bt;
+  int64_t comp_stride;
+  int comp_cols;
+  int comp_block;
+  int64_t comp_pages;
+  int window;
+  int padded;
+  int32_t* si;
+  int32_t* lens;
+};
+
+// BUILD: the workgroup also writes the token's sparse_indices row and length, as
+// build_sparse_indices would from this top-k row: window columns lo..p through the
+// window table, then the winners' slots through the compressed table (ascending, the
+// ones whose page is not in the pool dropped), then -1.
+template <int KPT, bool BUILD>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     sad_batch b, int ratio, int max_rows, const float* __restrict__ logits, int64_t logits_stride,
-    int k, int32_t* __restrict__ out) {
+    int k, int32_t* __restrict__ out, BuildArgs ba) {
   // logits staged in row order (coalesced global loads), then read back thread-contiguous
   constexpr int kStride = KPT <= 16 ? KPT + 4 : KPT;  // padded rows: conflict-free 16-byte reads
   __shared__ __align__(16) float stage[kTopkThreads * kStride];
@@ -267,8 +290,26 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   TokenGeom g;
   const bool ok = token_geometry(b, t, ratio, g);
   const int n = ok ? min(g.n_comp, max_rows) : 0;
+  int32_t* si_row = BUILD ? ba.si + (int64_t)t * (ba.window + ba.padded) : nullptr;
+  if constexpr (BUILD) {
+    int lo = 0;
+    if (ok) {
+      lo = g.pos - ba.window + 1;
+      if (ba.replay != nullptr) lo = max(lo, ba.replay[g.req]);
+      lo = max(lo, 0);
+    }
+    const int32_t* swa_row = ok ? ba.swa_bt + (int64_t)g.req * ba.swa_stride : nullptr;
+    for (int j = tid; j < ba.window; j += kTopkThreads) {
+      const int p = lo + j;
+      si_row[j] = ok && p <= g.pos ? page_slot(swa_row, ba.swa_cols, ba.swa_block, ba.swa_pages, p) : -1;
+    }
+  }
   if (n == 0) {
     for (int j = tid; j < k; j += kTopkThreads) orow[j] = -1;
+    if constexpr (BUILD) {
+      for (int j = tid; j < ba.padded; j += kTopkThreads) si_row[ba.window + j] = -1;
+      if (tid == 0) ba.lens[t] = 0;
+    }
     return;
   }
   const float* lrow = logits + (int64_t)t * logits_stride;
@@ -352,6 +393,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   }
   int total;
   int pos = block_excl_scan(sel_local, scan_sh, &total);
+  uint32_t sel_bits = 0;  // bit i: row base + i is a winner
   {
     int run = eq_before;
 #pragma unroll
@@ -362,9 +404,31 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         ++run;
       }
       if (s) orow[pos++] = base + i;
+      sel_bits |= (s ? 1u : 0u) << i;
     }
   }
   for (int j = total + tid; j < k; j += kTopkThreads) orow[j] = -1;
+  if constexpr (BUILD) {
+    // the winners' slots in row order; those whose compressed page is not in the pool
+    // are dropped (fail closed), the rest packed left
+    const int32_t* comp_row = ba.comp_bt + (int64_t)g.req * ba.comp_stride;
+    int nvalid_local = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if ((sel_bits >> i) & 1u)
+        nvalid_local += page_slot(comp_row, ba.comp_cols, ba.comp_block, ba.comp_pages, base + i) >= 0;
+    int vtotal;
+    int vpos = block_excl_scan(nvalid_local, scan_sh, &vtotal);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      if ((sel_bits >> i) & 1u) {
+        const int sl = page_slot(comp_row, ba.comp_cols, ba.comp_block, ba.comp_pages, base + i);
+        if (sl >= 0) si_row[ba.window + vpos++] = sl;
+      }
+    }
+    for (int j = vtotal + tid; j < ba.padded; j += kTopkThreads) si_row[ba.window + j] = -1;
+    if (tid == 0) ba.lens[t] = vtotal;
+  }
 }
 
 }  // namespace
@@ -382,14 +446,15 @@ extern "C" size_t indexer_score_topk_workspace_size(int32_t num_tokens, int32_t 
   return align256((size_t)num_tokens * stride * sizeof(float));
 }
 
-extern "C" int indexer_score_topk(const sad_batch* batch, const uint8_t* q_values,
-                                  const uint8_t* q_scales, const float* weights,
-                                  int32_t num_idx_heads, const sad_mxfp4_cache* keys,
-                                  const int32_t* idx_bt, int64_t idx_bt_stride, int32_t idx_bt_cols,
-                                  int32_t compress_ratio, int32_t topk, int32_t* topk_local,
-                                  float* logits_debug, int64_t logits_stride, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
-  clear_error();
+namespace {
+
+// Scoring + top-k (+ the index build when ba != nullptr; its arguments already checked).
+int run_indexer(const sad_batch* batch, const uint8_t* q_values, const uint8_t* q_scales,
+                const float* weights, int32_t num_idx_heads, const sad_mxfp4_cache* keys,
+                const int32_t* idx_bt, int64_t idx_bt_stride, int32_t idx_bt_cols,
+                int32_t compress_ratio, int32_t topk, int32_t* topk_local, float* logits_debug,
+                int64_t logits_stride, void* workspace, size_t workspace_bytes, void* stream,
+                const BuildArgs* ba) {
   SAD_CHECK(batch != nullptr && keys != nullptr, SAD_EINVAL, "indexer_score_topk: NULL batch/keys");
   const int T = batch->num_tokens;
   SAD_CHECK(T >= 0 && batch->num_reqs >= 0, SAD_EINVAL, "indexer_score_topk: negative sizes");
@@ -447,15 +512,55 @@ extern "C" int indexer_score_topk(const sad_batch* batch, const uint8_t* q_value
     int rc = check_launch("indexer_score_topk(score)");
     if (rc != SAD_OK) return rc;
   }
-  if (max_rows <= 4 * kTopkThreads) {
-    hipLaunchKernelGGL((topk_kernel<4>), dim3(T), dim3(kTopkThreads), 0, st, *batch,
-                       compress_ratio, max_rows, logits, ws_stride, topk, topk_local);
-  } else if (max_rows <= 16 * kTopkThreads) {
-    hipLaunchKernelGGL((topk_kernel<16>), dim3(T), dim3(kTopkThreads), 0, st, *batch,
-                       compress_ratio, max_rows, logits, ws_stride, topk, topk_local);
-  } else {
-    hipLaunchKernelGGL((topk_kernel<32>), dim3(T), dim3(kTopkThreads), 0, st, *batch,
-                       compress_ratio, max_rows, logits, ws_stride, topk, topk_local);
-  }
+  const BuildArgs bargs = ba != nullptr ? *ba : BuildArgs{};
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(T), dim3(kTopkThreads), 0, st, *batch, compress_ratio, max_rows,
+                       logits, ws_stride, topk, topk_local, bargs);
+  };
+  if (max_rows <= 4 * kTopkThreads)
+    ba != nullptr ? go(topk_kernel<4, true>) : go(topk_kernel<4, false>);
+  else if (max_rows <= 16 * kTopkThreads)
+    ba != nullptr ? go(topk_kernel<16, true>) : go(topk_kernel<16, false>);
+  else
+    ba != nullptr ? go(topk_kernel<32, true>) : go(topk_kernel<32, false>);
   return check_launch("indexer_score_topk(topk)");
+}
+
+}  // namespace
+
+extern "C" int indexer_score_topk(const sad_batch* batch, const uint8_t* q_values,
+                                  const uint8_t* q_scales, const float* weights,
+                                  int32_t num_idx_heads, const sad_mxfp4_cache* keys,
+                                  const int32_t* idx_bt, int64_t idx_bt_stride, int32_t idx_bt_cols,
+                                  int32_t compress_ratio, int32_t topk, int32_t* topk_local,
+                                  float* logits_debug, int64_t logits_stride, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  clear_error();
+  return run_indexer(batch, q_values, q_scales, weights, num_idx_heads, keys, idx_bt, idx_bt_stride,
+                     idx_bt_cols, compress_ratio, topk, topk_local, logits_debug, logits_stride,
+                     workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" int indexer_topk_sparse_indices(
+    const sad_batch* batch, const uint8_t* q_values, const uint8_t* q_scales, const float* weights,
+    int32_t num_idx_heads, const sad_mxfp4_cache* keys, const int32_t* idx_bt, int64_t idx_bt_stride,
+    int32_t idx_bt_cols, int32_t compress_ratio, int32_t topk, int32_t* topk_local,
+    const int32_t* replay_start, const int32_t* swa_bt, int64_t swa_bt_stride, int32_t swa_bt_cols,
+    int32_t swa_block_size, int64_t swa_num_pages, const int32_t* comp_bt, int64_t comp_bt_stride,
+    int32_t comp_bt_cols, int32_t comp_block_size, int64_t comp_num_pages, int32_t window_size,
+    int32_t padded_topk, int32_t* sparse_indices, int32_t* sparse_topk_lens, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  clear_error();
+  const int rc = check_build_args("indexer_topk_sparse_indices", batch, swa_bt, swa_bt_stride,
+                                  swa_bt_cols, swa_block_size, swa_num_pages, comp_bt, comp_bt_stride,
+                                  comp_bt_cols, comp_block_size, comp_num_pages, true, topk, topk,
+                                  window_size, compress_ratio, padded_topk, sparse_indices,
+                                  sparse_topk_lens);
+  if (rc != SAD_OK) return rc;
+  const BuildArgs ba{replay_start, swa_bt, swa_bt_stride, swa_bt_cols, swa_block_size, swa_num_pages,
+                     comp_bt, comp_bt_stride, comp_bt_cols, comp_block_size, comp_num_pages,
+                     window_size, padded_topk, sparse_indices, sparse_topk_lens};
+  return run_indexer(batch, q_values, q_scales, weights, num_idx_heads, keys, idx_bt, idx_bt_stride,
+                     idx_bt_cols, compress_ratio, topk, topk_local, nullptr, 0, workspace,
+                     workspace_bytes, stream, &ba);
 }

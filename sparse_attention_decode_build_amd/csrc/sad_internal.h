@@ -17,6 +17,15 @@ int check_launch(const char* what);
 int check_kv_cache(const sad_kv_cache* c, const char* what);
 // Bytes of one row's scales: 4*d_nope/64 (fp32 form) or 8 (native ue8m0 form).
 int kv_scale_bytes(const sad_kv_cache* c);
+// Host-side checks of build_sparse_indices' arguments (SAD_OK or an error code, the
+// message naming `what`); shared with the fused indexer + index build entry point.
+int check_build_args(const char* what, const sad_batch* batch, const int32_t* swa_bt,
+                     int64_t swa_bt_stride, int32_t swa_bt_cols, int32_t swa_block_size,
+                     int64_t swa_num_pages, const int32_t* comp_bt, int64_t comp_bt_stride,
+                     int32_t comp_bt_cols, int32_t comp_block_size, int64_t comp_num_pages,
+                     bool has_topk, int64_t topk_stride, int32_t topk, int32_t window_size,
+                     int32_t compress_ratio, int32_t padded_topk, const int32_t* sparse_indices,
+                     const int32_t* sparse_topk_lens);
 
 #define SAD_CHECK(cond, code, ...)   \
   do {                               \

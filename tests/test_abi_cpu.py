@@ -179,3 +179,20 @@ def test_insert_index_keys_errors(lib):
     assert call(ratio=0) == L.SAD_EINVAL
     assert call(stride=64) == L.SAD_EINVAL
     assert call(P=0) == L.SAD_EINVAL
+
+
+def test_indexer_topk_sparse_indices_errors(lib):
+    keys = L.SadMxfp4Cache(FAKE, 64 * 68, 10, 64, 128)
+
+    def call(T=2, padded=2048, topk=2048, dim=128, window=128, ratio=4):
+        k = keys if dim == 128 else L.SadMxfp4Cache(FAKE, 64 * 68, 10, 64, dim)
+        b = _batch(T)
+        return lib.indexer_topk_sparse_indices(ctypes.byref(b), FAKE, FAKE, FAKE, 64, ctypes.byref(k), FAKE, 4, 4,
+                                               ratio, topk, FAKE, None, FAKE, 4, 4, 64, 100, FAKE, 4, 4, 64, 100,
+                                               window, padded, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert call(T=0) == L.SAD_OK
+    assert call(padded=2000) == L.SAD_EINVAL  # not a multiple of 64
+    assert call(topk=4096) == L.SAD_EINVAL  # topk > padded
+    assert "indexer_topk_sparse_indices" in L.last_error()
+    assert call(dim=96) == L.SAD_EUNSUPPORTED
+    assert call(ratio=0) == L.SAD_EINVAL

@@ -352,3 +352,32 @@ def test_dense_1m_full():
     view = WL.host_view(wl)
     _full_check(wl, view, list(range(wl.num_tokens)))
     free(wl)
+
+
+@pytest.mark.parametrize("name", ["tiny", "b32_8k", "edge", "edge_holes", "b128_64k"])
+def test_fused_indexer_and_index_build_equal_the_two_calls(name):
+    # indexer_topk_sparse_indices is defined as indexer_score_topk then build_sparse_indices:
+    # all three outputs bit-identical to the two-call path (with holes in both block tables
+    # and a page past the pool in the "edge_holes" case).
+    cfg = EDGE if name.startswith("edge") else name
+    wl = _wl(cfg)
+    c = wl.cfg
+    L0 = wl.layers[0]
+    if name == "edge_holes":
+        g = torch.Generator(device="cpu").manual_seed(7)
+        L0.swa_bt[(torch.rand(L0.swa_bt.shape, generator=g) < 0.2).cuda()] = -1
+        L0.comp_bt[(torch.rand(L0.comp_bt.shape, generator=g) < 0.2).cuda()] = -1
+        L0.comp_bt[0, 0] = wl.kv_pool.shape[0] + 3
+    _, idx = _caches(wl)
+    n_pages = wl.kv_pool.shape[0]
+    tk_a, _ = gpu_indexer(wl, logits=False)
+    si_a, lens_a = gpu_build(wl, tk_a)
+    tk_b, si_b, lens_b = sad.indexer_topk_sparse_indices(
+        wl.query_start_loc, wl.seq_lens, wl.token_to_req, L0.idx_q_values, L0.idx_q_scales, L0.idx_weights, idx,
+        L0.idx_bt, c.ratio, c.topk, wl.replay_start, L0.swa_bt, c.block, n_pages, L0.comp_bt, c.block, n_pages,
+        c.window, wl.padded_topk)
+    torch.cuda.synchronize()
+    assert torch.equal(tk_a, tk_b)
+    assert torch.equal(si_a, si_b)
+    assert torch.equal(lens_a, lens_b)
+    free(wl)
