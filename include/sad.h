@@ -203,8 +203,9 @@ size_t indexer_score_topk_workspace_size(int32_t num_tokens, int32_t max_ctx_row
  * workspace_bytes) followed by build_sparse_indices(batch, replay_start, swa_bt, ...,
  * comp_num_pages, topk_local, topk_stride = topk, topk, window_size, compress_ratio,
  * padded_topk, sparse_indices, sparse_topk_lens): the same outputs, bit for bit, and
- * the union of both calls' argument rules and errors.  Each argument means what it
- * means there (see both declarations above and below).
+ * the union of both calls' argument rules and errors, plus comp_block_size a power of
+ * two >= 16 (else SAD_EUNSUPPORTED).  Each argument means what it means there (see
+ * both declarations above and below).
  */
 int indexer_topk_sparse_indices(
     const sad_batch* batch, const uint8_t* q_values, const uint8_t* q_scales, const float* weights,

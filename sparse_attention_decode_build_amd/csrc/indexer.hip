@@ -409,23 +409,35 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   }
   for (int j = total + tid; j < k; j += kTopkThreads) orow[j] = -1;
   if constexpr (BUILD) {
-    // the winners' slots in row order; those whose compressed page is not in the pool
-    // are dropped (fail closed), the rest packed left
+    // The winners' slots in row order; those whose compressed page is not in the pool
+    // are dropped (fail closed), the rest packed left.  The thread's KPT consecutive
+    // rows lie in at most two table columns (the block size is a power of two >= 16), so
+    // two unconditional loads give every page id.
     const int32_t* comp_row = ba.comp_bt + (int64_t)g.req * ba.comp_stride;
+    const int B = ba.comp_block;
+    const int c0 = base / B;
+    int pg0 = -1, pg1 = -1;
+    if (ba.comp_cols > 0) {
+      pg0 = comp_row[min(c0, ba.comp_cols - 1)];
+      pg1 = comp_row[min(c0 + 1, ba.comp_cols - 1)];
+    }
+    int sl[KPT];
     int nvalid_local = 0;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      if ((sel_bits >> i) & 1u)
-        nvalid_local += page_slot(comp_row, ba.comp_cols, ba.comp_block, ba.comp_pages, base + i) >= 0;
+    for (int i = 0; i < KPT; ++i) {
+      const int off = base + i - c0 * B;  // < 2B
+      const bool second = off >= B;
+      const int col = c0 + (second ? 1 : 0);
+      const int pg = second ? pg1 : pg0;
+      const bool v = ((sel_bits >> i) & 1u) && col < ba.comp_cols && pg >= 0 && (int64_t)pg < ba.comp_pages;
+      sl[i] = v ? pg * B + (second ? off - B : off) : -1;
+      nvalid_local += v;
+    }
     int vtotal;
     int vpos = block_excl_scan(nvalid_local, scan_sh, &vtotal);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      if ((sel_bits >> i) & 1u) {
-        const int sl = page_slot(comp_row, ba.comp_cols, ba.comp_block, ba.comp_pages, base + i);
-        if (sl >= 0) si_row[ba.window + vpos++] = sl;
-      }
-    }
+    for (int i = 0; i < KPT; ++i)
+      if (sl[i] >= 0) si_row[ba.window + vpos++] = sl[i];
     for (int j = vtotal + tid; j < ba.padded; j += kTopkThreads) si_row[ba.window + j] = -1;
     if (tid == 0) ba.lens[t] = vtotal;
   }
@@ -557,6 +569,9 @@ extern "C" int indexer_topk_sparse_indices(
                                   window_size, compress_ratio, padded_topk, sparse_indices,
                                   sparse_topk_lens);
   if (rc != SAD_OK) return rc;
+  SAD_CHECK(comp_block_size >= 16 && (comp_block_size & (comp_block_size - 1)) == 0, SAD_EUNSUPPORTED,
+            "indexer_topk_sparse_indices: comp_block_size must be a power of two >= 16 (got %d)",
+            comp_block_size);
   const BuildArgs ba{replay_start, swa_bt, swa_bt_stride, swa_bt_cols, swa_block_size, swa_num_pages,
                      comp_bt, comp_bt_stride, comp_bt_cols, comp_block_size, comp_num_pages,
                      window_size, padded_topk, sparse_indices, sparse_topk_lens};
