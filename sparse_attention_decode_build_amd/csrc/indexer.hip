@@ -38,9 +38,11 @@ __device__ inline void static_for(F&& f) {
 // ------------------------------------------------------------------ scoring
 
 constexpr int kScoreThreads = 256;
-constexpr int kRowsPerWave = 1024;                                 // 64 groups of 16 rows
+constexpr int kRowsPerWave = 512;                                  // 32 groups of 16 rows
 constexpr int kScoreChunk = kRowsPerWave * (kScoreThreads / 64);  // compressed rows per workgroup
-constexpr int kGroupBatch = 8;  // 16-row groups whose key loads are in flight together
+// 16-row groups whose key loads are in flight together: small batches and short waves
+// keep the registers low, so more waves per SIMD hide the random page reads
+constexpr int kGroupBatch = 4;
 
 typedef int gi32x4_t __attribute__((__vector_size__(4 * sizeof(int))));
 
@@ -54,14 +56,14 @@ struct IdxDesc {
   int block;
 };
 
-// Keys of one batch of 8 row groups: lane (m = lane%16, grp = lane/16) holds 16 packed
+// Keys of one batch of row groups: lane (m = lane%16, grp = lane/16) holds 16 packed
 // bytes (dims 32*grp .. +32) and the e8m0 exponent of row 16*u + m.
 struct KeyBatch {
   gi32x4_t v[kGroupBatch];
   int e[kGroupBatch];
 };
 
-// One wave scores 1024 consecutive compressed rows of one token, 8 groups of 16 rows at
+// One wave scores 512 consecutive compressed rows of one token, 4 groups of 16 rows at
 // a time; the loads of the next batch are issued before the current one is scored.  The
 // page ids of the wave's rows are loaded once up front (one per lane, at most 64 pages).
 template <int DIM>
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
 
   const int m = lane & 15;
   const int grp = lane >> 4;
-  // Issue the loads of groups gb .. gb+7 as buffer loads: a wave-uniform resource per
+  // Issue the loads of the batch's groups as buffer loads: a wave-uniform resource per
   // page (zero records for an absent or unbacked group, so its loads return zeros and
   // touch no memory), the group's first row as the scalar offset and a per-lane
   // constant offset.  Every load goes out unconditionally.
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
   float fmax_big = 3.402823466e+38f;
   asm volatile("" : "+s"(fmax_big));
 
-  // Score groups gb .. gb+7 from kb (absent groups are scored too, on the zero key;
+  // Score the batch's groups from kb (absent groups are scored too, on the zero key;
   // only rows before the end are stored).  The MFMAs of group u+1 are issued before the
   // results of group u are combined.
   auto mma = [&](const KeyBatch& kb, int u, f32x4_t (&acc)[4]) __attribute__((always_inline)) {
