@@ -13,10 +13,10 @@
 // scaled by powers of two are exact in fp32, so every per-head dot is exact.
 //
 // Top-k: one 1024-thread workgroup per token holds the token's keys in registers
-// (order-preserving uint32 transform), finds the exact k-th largest key with four
-// 8-bit radix passes over per-wave LDS histograms, then compacts the winners in
-// row order (ties at the threshold go to the lower row id), so the output is
-// ascending.
+// (order-preserving uint32 transform), finds the exact k-th largest key with radix
+// passes of 12, 12 and 8 bits over one LDS histogram (the later passes only when more
+// than k rows are candidates), then compacts the winners in row order (ties at the
+// threshold go to the lower row id), so the output is ascending.
 #include <type_traits>
 #include <utility>
 
@@ -210,36 +210,44 @@ __device__ inline uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the workgroup (all threads must call); returns the
-// exclusive prefix and writes the total to *total.
-__device__ inline int block_excl_scan(int v, int* sh, int* total) {
+// Exclusive prefix sum over the workgroup (every thread calls it, all lanes active), in
+// uint32 (sums wrap modulo 2^32); returns the exclusive prefix and writes the total to
+// *total.  It holds one barrier:
+// callers alternate between two `sh` buffers, so the reads of one scan are done before
+// the next-but-one scan writes the same buffer (the scan between them has a barrier).
+__device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int incl = wave_incl_scan(v);
+  const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) sh[wave] = incl;
   __syncthreads();
-  int off = 0;
-  int tot = 0;
+  uint32_t off = 0;
+  uint32_t tot = 0;
 #pragma unroll
   for (int w = 0; w < kTopkWaves; ++w) {
-    const int c = sh[w];
+    const uint32_t c = sh[w];
     if (w < wave) off += c;
     tot += c;
   }
-  __syncthreads();
   *total = tot;
   return off + incl - v;
 }
 
 // The digit bin holding the kk-th largest counted key (1-based), scanning the bins
 // from the top: returns it and the number of keys in higher bins (*above), and the
-// number of counted keys (*total).  Thread t owns bins 4095-4t .. 4092-4t.
-__device__ inline int select_bin(const int* hist, int kk, int* sh, int* pick, int* above, int* total) {
+// number of counted keys (*total).  Thread t owns bins 4095-4t .. 4092-4t; it clears
+// them after reading, so the histogram is zero for the next pass (the barriers of the
+// scan and of the pick order the clear before that pass's adds).
+__device__ inline int select_bin(int* hist, int kk, uint32_t* sh, int* pick, int* above, int* total) {
+  static_assert(kDigitBins == 4 * kTopkThreads, "four bins per thread");
   const int tid = threadIdx.x;
-  int c[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) c[q] = hist[kDigitBins - 1 - (4 * tid + q)];
-  int a = block_excl_scan(c[0] + c[1] + c[2] + c[3], sh, total);
+  int4* h4 = reinterpret_cast<int4*>(hist) + (kTopkThreads - 1 - tid);
+  const int4 hv = *h4;
+  *h4 = make_int4(0, 0, 0, 0);
+  const int c[4] = {hv.w, hv.z, hv.y, hv.x};  // bins 4095-4t, 4094-4t, 4093-4t, 4092-4t
+  uint32_t tot;
+  int a = (int)block_excl_scan((uint32_t)(c[0] + c[1] + c[2] + c[3]), sh, &tot);
+  *total = (int)tot;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (a < kk && kk <= a + c[q]) {
@@ -283,51 +291,80 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   // logits staged in row order (coalesced global loads), then read back thread-contiguous
   constexpr int kStride = KPT <= 16 ? KPT + 4 : KPT;  // padded rows: conflict-free 16-byte reads
   __shared__ __align__(16) float stage[kTopkThreads * kStride];
-  __shared__ int hist[kDigitBins];
-  __shared__ int scan_sh[kTopkWaves];
+  __shared__ __align__(16) int hist[kDigitBins];
+  __shared__ __align__(16) uint32_t scan_sh[2][kTopkWaves];
   __shared__ int pick[2];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  int32_t* orow = out + (int64_t)t * k;
+  const int base = tid * KPT;  // the thread's rows after staging: base .. base + KPT - 1
+
+  // The workspace row holds max_rows logits, so they are loaded before the token's
+  // length is known (at an index clamped into the row: none is conditional); rows past
+  // n become -inf below.
+  float lv[KPT];
+  if (max_rows > 0) {
+    const float* lrow = logits + (int64_t)t * logits_stride;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) lv[i] = lrow[min(i * kTopkThreads + tid, max_rows - 1)];
+  }
   TokenGeom g;
   const bool ok = token_geometry(b, t, ratio, g);
   const int n = ok ? min(g.n_comp, max_rows) : 0;
+  int32_t* orow = out + (int64_t)t * k;
+
+  // Index-build loads that need only the token, issued now and used at the end: the
+  // compressed-table page ids of the thread's rows (its KPT consecutive rows lie in at
+  // most two columns: the block size is a power of two >= 16), the replay bound, and
+  // the window page of position lo0 + tid (lo0 = max(p - window + 1, 0) is a lower
+  // bound of the window's first position).
+  int pg0 = -1, pg1 = -1, replay = 0, lo0 = 0, win_slot = -1;
   int32_t* si_row = BUILD ? ba.si + (int64_t)t * (ba.window + ba.padded) : nullptr;
+  const int32_t* swa_row = nullptr;
   if constexpr (BUILD) {
-    int lo = 0;
-    if (ok) {
-      lo = g.pos - ba.window + 1;
-      if (ba.replay != nullptr) lo = max(lo, ba.replay[g.req]);
-      lo = max(lo, 0);
+    if (n > 0 && ba.comp_cols > 0) {
+      const int32_t* comp_row = ba.comp_bt + (int64_t)g.req * ba.comp_stride;
+      const int c0 = base / ba.comp_block;
+      pg0 = comp_row[min(c0, ba.comp_cols - 1)];
+      pg1 = comp_row[min(c0 + 1, ba.comp_cols - 1)];
     }
-    const int32_t* swa_row = ok ? ba.swa_bt + (int64_t)g.req * ba.swa_stride : nullptr;
-    for (int j = tid; j < ba.window; j += kTopkThreads) {
-      const int p = lo + j;
-      si_row[j] = ok && p <= g.pos ? page_slot(swa_row, ba.swa_cols, ba.swa_block, ba.swa_pages, p) : -1;
+    if (ok) {
+      lo0 = max(g.pos - ba.window + 1, 0);
+      if (ba.replay != nullptr) replay = ba.replay[g.req];
+      swa_row = ba.swa_bt + (int64_t)g.req * ba.swa_stride;
+      if (tid < ba.window && lo0 + tid <= g.pos)
+        win_slot = page_slot(swa_row, ba.swa_cols, ba.swa_block, ba.swa_pages, lo0 + tid);
     }
   }
+  // Window columns: the slots of positions lo..p, lo = max(lo0, replay), then -1.
+  // Position lo0 + j goes to column lo0 + j - lo.
+  auto window_stores = [&]() __attribute__((always_inline)) {
+    const int lo = max(lo0, replay);
+    for (int j = tid; j < ba.window; j += kTopkThreads) {
+      const int p0 = lo0 + j;
+      int slot = win_slot;
+      if (j >= kTopkThreads)
+        slot = ok && p0 <= g.pos ? page_slot(swa_row, ba.swa_cols, ba.swa_block, ba.swa_pages, p0) : -1;
+      if (ok && p0 >= lo && p0 <= g.pos) si_row[p0 - lo] = slot;
+      if (j > g.pos - lo) si_row[j] = -1;  // columns past p - lo (all of them when !ok)
+    }
+  };
+
   if (n == 0) {
     for (int j = tid; j < k; j += kTopkThreads) orow[j] = -1;
     if constexpr (BUILD) {
+      window_stores();
       for (int j = tid; j < ba.padded; j += kTopkThreads) si_row[ba.window + j] = -1;
       if (tid == 0) ba.lens[t] = 0;
     }
     return;
   }
-  const float* lrow = logits + (int64_t)t * logits_stride;
-  // all loads first (at an index clamped into the row, so none is conditional and they
-  // are in flight together), then the rows past n become -inf
-  float lv[KPT];
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) lv[i] = lrow[min(i * kTopkThreads + tid, n - 1)];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int r = i * kTopkThreads + tid;  // row; thread r / KPT holds it
     stage[(r / KPT) * kStride + r % KPT] = r < n ? lv[i] : -INFINITY;
   }
-  for (int j = tid; j < kDigitBins; j += kTopkThreads) hist[j] = 0;
+  reinterpret_cast<int4*>(hist)[tid] = make_int4(0, 0, 0, 0);
   __syncthreads();
-  const int base = tid * KPT;
   uint32_t key[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; i += 4) {
@@ -339,109 +376,104 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   }
 
   // Pass 1: top 12 bits of every candidate key (this also counts the candidates).
+  // Each select_bin leaves the histogram cleared for the next pass.
 #pragma unroll
   for (int i = 0; i < KPT; ++i)
     if (key[i] != 0u) atomicAdd(&hist[key[i] >> 20], 1);
   __syncthreads();
   int above, nvalid;
-  const int d1 = select_bin(hist, k, scan_sh, pick, &above, &nvalid);
+  const int d1 = select_bin(hist, k, scan_sh[0], pick, &above, &nvalid);
 
   uint32_t thr = 0u;  // keys > thr are taken, plus `need` keys == thr in row order
   int need = 0;
   if (nvalid > k) {
     int kk = k - above;
     // Pass 2: next 12 bits of the keys in digit d1.
-    for (int j = tid; j < kDigitBins; j += kTopkThreads) hist[j] = 0;
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
       if ((int)(key[i] >> 20) == d1) atomicAdd(&hist[(key[i] >> 8) & 4095u], 1);
     __syncthreads();
     int dummy;
-    const int d2 = select_bin(hist, kk, scan_sh, pick, &above, &dummy);
+    const int d2 = select_bin(hist, kk, scan_sh[1], pick, &above, &dummy);
     kk -= above;
     const uint32_t prefix = ((uint32_t)d1 << 20) | ((uint32_t)d2 << 8);
     // Pass 3: last 8 bits of the keys in digits (d1, d2).
-    for (int j = tid; j < kDigitBins; j += kTopkThreads) hist[j] = 0;
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
       if ((key[i] >> 8) == (prefix >> 8)) atomicAdd(&hist[key[i] & 255u], 1);
     __syncthreads();
-    const int d3 = select_bin(hist, kk, scan_sh, pick, &above, &dummy);
+    const int d3 = select_bin(hist, kk, scan_sh[0], pick, &above, &dummy);
     kk -= above;
     thr = prefix | (uint32_t)d3;
     need = kk;
   }
+  const bool ties = thr != 0u;  // with thr == 0 every candidate is taken
 
-  // rank of equal keys in row order, then compaction of the winners in row order
-  int eq_local = 0;
+  // One scan gives both the keys above the threshold and the keys equal to it in the
+  // threads before this one (packed 16 + 16 bits; each count is at most 32768 and the
+  // equal-key count below 65536, so no carry crosses).  Equal keys are taken in row
+  // order, so min(equal before, need) of them precede this thread's winners.
+  uint32_t gt_local = 0, eq_local = 0;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) eq_local += (key[i] == thr && thr != 0u);
-  int dummy;
-  const int eq_before = block_excl_scan(eq_local, scan_sh, &dummy);
-  int sel_local = 0;
-  {
-    int run = eq_before;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      bool s = key[i] > thr;
-      if (key[i] == thr && thr != 0u) {
-        s = run < need;
-        ++run;
-      }
-      sel_local += s;
-    }
+  for (int i = 0; i < KPT; ++i) {
+    gt_local += key[i] > thr;
+    eq_local += ties && key[i] == thr;
   }
-  int total;
-  int pos = block_excl_scan(sel_local, scan_sh, &total);
+  uint32_t packed_total;
+  const uint32_t packed = block_excl_scan((gt_local << 16) | eq_local, scan_sh[1], &packed_total);
+  const int eq_before = (int)(packed & 0xFFFFu);
+  const int total = (int)(packed_total >> 16) + min((int)(packed_total & 0xFFFFu), need);
+  int pos = (int)(packed >> 16) + min(eq_before, need);
+  // The winners go to LDS in output order (the staging buffer is free since pass 1:
+  // total <= n fits), then out as whole rows with coalesced stores.  The LDS stores
+  // are unconditional, losers writing to a word of the histogram (no longer read), so
+  // the loop has no branches.
+  int32_t* ostage = reinterpret_cast<int32_t*>(stage);
+  int32_t* trash = hist + tid;
   uint32_t sel_bits = 0;  // bit i: row base + i is a winner
   {
     int run = eq_before;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      bool s = key[i] > thr;
-      if (key[i] == thr && thr != 0u) {
-        s = run < need;
-        ++run;
-      }
-      if (s) orow[pos++] = base + i;
+      const bool eq = ties && key[i] == thr;
+      const bool s = key[i] > thr || (eq && run < need);
+      run += eq ? 1 : 0;
+      *(s ? ostage + pos : trash) = base + i;
+      pos += s ? 1 : 0;
       sel_bits |= (s ? 1u : 0u) << i;
     }
   }
-  for (int j = total + tid; j < k; j += kTopkThreads) orow[j] = -1;
-  if constexpr (BUILD) {
+  if constexpr (!BUILD) {
+    __syncthreads();
+    for (int j = tid; j < k; j += kTopkThreads) orow[j] = j < total ? ostage[j] : -1;
+  } else {
     // The winners' slots in row order; those whose compressed page is not in the pool
-    // are dropped (fail closed), the rest packed left.  The thread's KPT consecutive
-    // rows lie in at most two table columns (the block size is a power of two >= 16), so
-    // two unconditional loads give every page id.
-    const int32_t* comp_row = ba.comp_bt + (int64_t)g.req * ba.comp_stride;
-    const int B = ba.comp_block;
-    const int c0 = base / B;
-    int pg0 = -1, pg1 = -1;
-    if (ba.comp_cols > 0) {
-      pg0 = comp_row[min(c0, ba.comp_cols - 1)];
-      pg1 = comp_row[min(c0 + 1, ba.comp_cols - 1)];
-    }
-    int sl[KPT];
-    int nvalid_local = 0;
+    // are dropped (fail closed), the rest packed left.  Rows base + i with i < split lie
+    // in column c0, the others in column c0 + 1; slot = column's page * B + row % B.
+    const int lg_b = 31 - __builtin_clz(ba.comp_block);
+    const int c0 = base >> lg_b;
+    const int split = ((c0 + 1) << lg_b) - base;  // >= 1
+    const uint32_t in_first = split >= 32 ? 0xFFFFFFFFu : (1u << split) - 1u;
+    const bool ok0 = c0 < ba.comp_cols && pg0 >= 0 && (int64_t)pg0 < ba.comp_pages;
+    const bool ok1 = c0 + 1 < ba.comp_cols && pg1 >= 0 && (int64_t)pg1 < ba.comp_pages;
+    const uint32_t vbits = sel_bits & ((ok0 ? in_first : 0u) | (ok1 ? ~in_first : 0u));
+    const uint32_t d0 = ((uint32_t)pg0 << lg_b) - ((uint32_t)c0 << lg_b) + (uint32_t)base;
+    const uint32_t d1s = ((uint32_t)pg1 << lg_b) - ((uint32_t)(c0 + 1) << lg_b) + (uint32_t)base;
+    uint32_t vtotal_u;
+    int vpos = (int)block_excl_scan((uint32_t)__builtin_popcount(vbits), scan_sh[0], &vtotal_u);  // also orders ostage
+    const int vtotal = (int)vtotal_u;
+    for (int j = tid; j < k; j += kTopkThreads) orow[j] = j < total ? ostage[j] : -1;
+    __syncthreads();  // the winners are read out before their slots overwrite them
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int off = base + i - c0 * B;  // < 2B
-      const bool second = off >= B;
-      const int col = c0 + (second ? 1 : 0);
-      const int pg = second ? pg1 : pg0;
-      const bool v = ((sel_bits >> i) & 1u) && col < ba.comp_cols && pg >= 0 && (int64_t)pg < ba.comp_pages;
-      sl[i] = v ? pg * B + (second ? off - B : off) : -1;
-      nvalid_local += v;
+      const bool v = (vbits >> i) & 1u;
+      *(v ? ostage + vpos : trash) = (int)((i >= split ? d1s : d0) + (uint32_t)i);
+      vpos += v ? 1 : 0;
     }
-    int vtotal;
-    int vpos = block_excl_scan(nvalid_local, scan_sh, &vtotal);
-#pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      if (sl[i] >= 0) si_row[ba.window + vpos++] = sl[i];
-    for (int j = vtotal + tid; j < ba.padded; j += kTopkThreads) si_row[ba.window + j] = -1;
+    __syncthreads();
+    for (int j = tid; j < ba.padded; j += kTopkThreads) si_row[ba.window + j] = j < vtotal ? ostage[j] : -1;
     if (tid == 0) ba.lens[t] = vtotal;
+    window_stores();
   }
 }
 

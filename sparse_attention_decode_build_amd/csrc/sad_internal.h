@@ -94,13 +94,17 @@ __device__ inline bool slot_ok(int slot, int block, int64_t num_pages) {
 __device__ inline int wave_lane() { return __lane_id(); }
 
 // Inclusive prefix sum across the 64 lanes of a wave.
-__device__ inline int wave_incl_scan(int v) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active), modulo 2^32: DPP
+// row shifts by 1, 2, 4 and 8 scan each row of 16 lanes (lanes shifted in from outside
+// the row add zero), then the row broadcasts of lane 15 (into rows 1 and 3) and of
+// lane 31 (into rows 2 and 3) carry the row totals.
+__device__ inline uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
 }
 
