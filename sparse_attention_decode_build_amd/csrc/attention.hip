@@ -831,34 +831,53 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   // the direct-to-LDS loads issued past the last tile land before the workgroup ends
   wait_vmem<0>();
 
-  if (!block_active || head >= num_heads) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float l_exp = LSE ? l_lse + __shfl_xor(l_lse, 32, 64) : l_tot;
+  const bool lane_active = block_active && head < num_heads;
   // lane (n, h) holds O^T rows (dims) dim0 + 32mt + 8(r/4) + 4h + r%4 for head n
   if (num_splits == 1) {
-    const float s2 = sink != nullptr ? sink[head] * kLog2e : -INFINITY;
-    const float mm = fmaxf(m_run, s2);
-    const float mref = mm == -INFINITY ? 0.0f : mm;
-    const float so = exp2f(m_run - mref);
-    const float es = exp2f(s2 - mref);
-    const float den = l_tot * so + es;
-    const float den_lse = l_exp * so + es;
-    const float f = den > 0.0f ? so / den : 0.0f;
-    uint16_t* orow = out + ((int64_t)t * num_heads + head) * DQK + dim0;
+    // O goes through LDS (the two K buffers: 64 head rows of DQK bf16 plus one 16-byte
+    // chunk of padding, the K tiles' own row pitch) so that the workgroup's 64 heads,
+    // which are contiguous in out, leave as one linear copy of whole lines.
+    constexpr int RP = 2 * DQK + 16;  // bytes per staged head row
+    static_assert(64 * RP <= (int)sizeof(kt), "the staged output fits the K buffers");
+    uint8_t* ostage = reinterpret_cast<uint8_t*>(&kt[0][0]);
+    lds_barrier();  // every wave's last PV reads of the K buffers are done
+    if (lane_active) {
+      const float s2 = sink != nullptr ? sink[head] * kLog2e : -INFINITY;
+      const float mm = fmaxf(m_run, s2);
+      const float mref = mm == -INFINITY ? 0.0f : mm;
+      const float so = exp2f(m_run - mref);
+      const float es = exp2f(s2 - mref);
+      const float den = l_tot * so + es;
+      const float den_lse = l_exp * so + es;
+      const float f = den > 0.0f ? so / den : 0.0f;
+      uint8_t* srow = ostage + (hb * 32 + n) * RP + 2 * dim0;
 #pragma unroll
-    for (int mt = 0; mt < MTMAX; ++mt)
-      if (mt < mt_n) {
+      for (int mt = 0; mt < MTMAX; ++mt)
+        if (mt < mt_n) {
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          uint2 w;
-          w.x = pack_bf16(acc_o[mt][4 * gg + 0] * f, acc_o[mt][4 * gg + 1] * f);
-          w.y = pack_bf16(acc_o[mt][4 * gg + 2] * f, acc_o[mt][4 * gg + 3] * f);
-          *reinterpret_cast<uint2*>(orow + 32 * mt + 8 * gg + 4 * h) = w;
+          for (int gg = 0; gg < 4; ++gg) {
+            uint2 w;
+            w.x = pack_bf16(acc_o[mt][4 * gg + 0] * f, acc_o[mt][4 * gg + 1] * f);
+            w.y = pack_bf16(acc_o[mt][4 * gg + 2] * f, acc_o[mt][4 * gg + 3] * f);
+            *reinterpret_cast<uint2*>(srow + 2 * (32 * mt + 8 * gg + 4 * h)) = w;
+          }
         }
-      }
-    if (lse_out != nullptr && h == 0 && dh == 0)
-      lse_out[(int64_t)t * num_heads + head] = den_lse > 0.0f ? (mref + log2f(den_lse)) * kLn2 : -INFINITY;
+      if (lse_out != nullptr && h == 0 && dh == 0)
+        lse_out[(int64_t)t * num_heads + head] = den_lse > 0.0f ? (mref + log2f(den_lse)) * kLn2 : -INFINITY;
+    }
+    lds_barrier();
+    constexpr int CPR = DQK / 8;  // 16-byte chunks per head row
+    const int rows = min(64, num_heads - hg * 64);
+    uint8_t* obase = reinterpret_cast<uint8_t*>(out + ((int64_t)t * num_heads + hg * 64) * DQK);
+    for (int i = tid; i < rows * CPR; i += kThreads) {
+      const int r = i / CPR;
+      *reinterpret_cast<uint4*>(obase + 16 * (int64_t)i) =
+          *reinterpret_cast<const uint4*>(ostage + r * RP + 16 * (i - r * CPR));
+    }
   } else {
+    if (!lane_active) return;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     float* prow = part_o + (((int64_t)split * num_tokens + t) * num_heads + head) * DQK + dim0;
 #pragma unroll
