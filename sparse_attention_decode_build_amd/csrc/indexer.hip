@@ -77,23 +77,48 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int m = lane & 15;
+  const int grp = lane >> 4;
+  // A operands: 16 heads x 128 dims per tile; lane (m, grp) holds dims [32*grp, 32*grp+32)
+  // of head 16*ht + m and that block's exponent.  They need only the token, so they are
+  // loaded first, together with the token's request.
+  gi32x4_t qa[4];
+  int qsc[4];
+  float wl[4][4];
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const int h = ht * 16 + m;
+    qa[ht] = gi32x4_t{0, 0, 0, 0};
+    qsc[ht] = 127;
+    if (h < num_heads && grp < SB) {
+      qa[ht] = *reinterpret_cast<const gi32x4_t*>(qv + ((int64_t)t * num_heads + h) * VB + 16 * grp);
+      qsc[ht] = qs[((int64_t)t * num_heads + h) * SB + grp];
+    }
+    // this lane's outputs are heads 16*ht + 4*grp + j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ho = ht * 16 + 4 * grp + j;
+      wl[ht][j] = ho < num_heads ? wts[(int64_t)t * num_heads + ho] : 0.0f;
+    }
+  }
+  const int req = b.token_to_req[t];
+  if (req < 0 || req >= b.num_reqs || bt_cols <= 0) return;
+  // Page ids of this wave's rows: lane i holds table column col0 + i (a 16-row group
+  // never straddles a page, since 16 divides the page size).  The load needs only the
+  // request, so it goes out with the loads of the token's length (column clamped into
+  // the table; lanes past the wave's columns are cleared below).
+  const int w_begin = blockIdx.x * kScoreChunk + wave * kRowsPerWave;
+  const int32_t* bt_row = bt + (int64_t)req * bt_stride;
+  const int col0 = w_begin / kc.block;
+  const int pid_any = bt_row[min(col0 + lane, bt_cols - 1)];
   TokenGeom g;
   if (!token_geometry(b, t, ratio, g)) return;
   const int n_rows = min(g.n_comp, bt_cols * kc.block);
-  const int w_begin = blockIdx.x * kScoreChunk + wave * kRowsPerWave;
   if (w_begin >= n_rows) return;  // no barriers in this kernel: waves may leave early
   const int w_rows = min(kRowsPerWave, n_rows - w_begin);
   const int n_groups = (w_rows + 15) / 16;
-
-  // Page ids of this wave's rows: lane i holds table column col0 + i (a 16-row group
-  // never straddles a page, since 16 divides the page size).
-  const int32_t* bt_row = bt + (int64_t)g.req * bt_stride;
-  const int col0 = w_begin / kc.block;
   const int ncol = (w_begin + w_rows - 1) / kc.block - col0 + 1;  // <= 64
-  const int pid = lane < ncol ? bt_row[col0 + lane] : -1;
-
-  const int m = lane & 15;
-  const int grp = lane >> 4;
+  const int pid = lane < ncol ? pid_any : -1;
   // Issue the loads of the batch's groups as buffer loads: a wave-uniform resource per
   // page (zero records for an absent or unbacked group, so its loads return zeros and
   // touch no memory), the group's first row as the scalar offset and a per-lane
@@ -115,27 +140,6 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
       kb.e[u] = __builtin_amdgcn_raw_buffer_load_b8(rs, lane_soff, kc.block * VB + r0 * SB, 0);
     }
   };
-  // A operands: 16 heads x 128 dims per tile; lane (m, grp) holds dims [32*grp, 32*grp+32)
-  // of head 16*ht + m and that block's exponent.
-  gi32x4_t qa[4];
-  int qsc[4];
-  float wl[4][4];
-#pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const int h = ht * 16 + m;
-    qa[ht] = gi32x4_t{0, 0, 0, 0};
-    qsc[ht] = 127;
-    if (h < num_heads && grp < SB) {
-      qa[ht] = *reinterpret_cast<const gi32x4_t*>(qv + ((int64_t)t * num_heads + h) * VB + 16 * grp);
-      qsc[ht] = qs[((int64_t)t * num_heads + h) * SB + grp];
-    }
-    // this lane's outputs are heads 16*ht + 4*grp + j
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ho = ht * 16 + 4 * grp + j;
-      wl[ht][j] = ho < num_heads ? wts[(int64_t)t * num_heads + ho] : 0.0f;
-    }
-  }
   float* lrow = logits + (int64_t)t * logits_stride;
   float* drow = dbg != nullptr ? dbg + (int64_t)t * dbg_stride : nullptr;
   // the ReLU's upper clamp, kept opaque so the clamp stays one med3 instruction
