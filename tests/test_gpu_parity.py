@@ -187,6 +187,32 @@ def test_edge_batch():
     free(wl)
 
 
+@pytest.mark.parametrize("heads,requests", [(40, 256), (72, 128), (96, 128), (120, 128), (72, 4), (120, 3)])
+def test_head_counts_with_partial_head_groups(heads, requests):
+    """Head counts whose last group of 64 heads is partial: a head block with absent
+    heads (40, 72, 120) or an idle one (96).  With 256 or more (token, head group)
+    pairs one workgroup covers a token's columns and stages O through LDS; with a few
+    tokens the columns are split and merged.  The rows after the output are untouched."""
+    cfg = WL.with_overrides(WL.CONFIGS["b32_8k"], name=f"h{heads}_r{requests}", heads=heads,
+                            groups=((requests, 1, 512, 0),))
+    wl = _wl(cfg)
+    view = WL.host_view(wl)
+    tokens = list(range(0, wl.num_tokens, max(1, wl.num_tokens // 24)))
+    si, lens, out = _full_check(wl, view, tokens, check_gather=False)
+    # the same launch into a buffer with a guard region after the output
+    T, H, D = out.shape
+    guard = 4096
+    buf = torch.full((T * H * D + guard,), -7, dtype=torch.int16, device="cuda")
+    kv, _ = _caches(wl)
+    out2 = buf[: T * H * D].view(torch.bfloat16).view(T, H, D)
+    sad.sparse_mla_decode(wl.layers[0].q, kv, kv, si, lens, cfg.window, wl.padded_topk, wl.softmax_scale,
+                          out=out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16)), "same launch, same bits"
+    assert bool((buf[T * H * D:] == -7).all()), "a store past the output"
+    free(wl)
+
+
 def test_edge_fail_closed_tables():
     """Unbacked pages, ids past the pool and random local ids (incl. -1 and >= n_c)."""
     wl = _wl(EDGE)
