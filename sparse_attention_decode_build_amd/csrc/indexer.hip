@@ -238,11 +238,12 @@ __device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* t
 }
 
 // The digit bin holding the kk-th largest counted key (1-based), scanning the bins
-// from the top: returns it and the number of keys in higher bins (*above), and the
-// number of counted keys (*total).  Thread t owns bins 4095-4t .. 4092-4t; it clears
+// from the top: returns it, the number of keys in higher bins (*above) and in the bin
+// itself (*count), and the number of counted keys (*total).  Thread t owns bins 4095-4t .. 4092-4t; it clears
 // them after reading, so the histogram is zero for the next pass (the barriers of the
 // scan and of the pick order the clear before that pass's adds).
-__device__ inline int select_bin(int* hist, int kk, uint32_t* sh, int* pick, int* above, int* total) {
+__device__ inline int select_bin(int* hist, int kk, uint32_t* sh, int* pick, int* above, int* count,
+                                 int* total) {
   static_assert(kDigitBins == 4 * kTopkThreads, "four bins per thread");
   const int tid = threadIdx.x;
   int4* h4 = reinterpret_cast<int4*>(hist) + (kTopkThreads - 1 - tid);
@@ -257,11 +258,13 @@ __device__ inline int select_bin(int* hist, int kk, uint32_t* sh, int* pick, int
     if (a < kk && kk <= a + c[q]) {
       pick[0] = kDigitBins - 1 - (4 * tid + q);
       pick[1] = a;
+      pick[2] = c[q];
     }
     a += c[q];
   }
   __syncthreads();
   *above = pick[1];
+  *count = pick[2];
   return pick[0];
 }
 
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   __shared__ __align__(16) float stage[kTopkThreads * kStride];
   __shared__ __align__(16) int hist[kDigitBins];
   __shared__ __align__(16) uint32_t scan_sh[2][kTopkWaves];
-  __shared__ int pick[2];
+  __shared__ int pick[3];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int base = tid * KPT;  // the thread's rows after staging: base .. base + KPT - 1
@@ -385,31 +388,43 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   for (int i = 0; i < KPT; ++i)
     if (key[i] != 0u) atomicAdd(&hist[key[i] >> 20], 1);
   __syncthreads();
-  int above, nvalid;
-  const int d1 = select_bin(hist, k, scan_sh[0], pick, &above, &nvalid);
+  int above, count, nvalid;
+  const int d1 = select_bin(hist, k, scan_sh[0], pick, &above, &count, &nvalid);
 
-  uint32_t thr = 0u;  // keys > thr are taken, plus `need` keys == thr in row order
+  // Keys > thr are taken, plus `need` keys == thr in row order.  When every key of the
+  // selected bin is taken, the threshold is just below the bin and the later passes are
+  // skipped (the smallest candidate key, that of the most negative float, is in bin 8 of
+  // the first digit, so thr stays above 0, the mark of the non-candidates).
+  uint32_t thr = 0u;
   int need = 0;
   if (nvalid > k) {
     int kk = k - above;
-    // Pass 2: next 12 bits of the keys in digit d1.
+    if (kk == count) {
+      thr = ((uint32_t)d1 << 20) - 1u;
+    } else {
+      // Pass 2: next 12 bits of the keys in digit d1.
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      if ((int)(key[i] >> 20) == d1) atomicAdd(&hist[(key[i] >> 8) & 4095u], 1);
-    __syncthreads();
-    int dummy;
-    const int d2 = select_bin(hist, kk, scan_sh[1], pick, &above, &dummy);
-    kk -= above;
-    const uint32_t prefix = ((uint32_t)d1 << 20) | ((uint32_t)d2 << 8);
-    // Pass 3: last 8 bits of the keys in digits (d1, d2).
+      for (int i = 0; i < KPT; ++i)
+        if ((int)(key[i] >> 20) == d1) atomicAdd(&hist[(key[i] >> 8) & 4095u], 1);
+      __syncthreads();
+      int dummy;
+      const int d2 = select_bin(hist, kk, scan_sh[1], pick, &above, &count, &dummy);
+      kk -= above;
+      const uint32_t prefix = ((uint32_t)d1 << 20) | ((uint32_t)d2 << 8);
+      if (kk == count) {
+        thr = prefix - 1u;
+      } else {
+        // Pass 3: last 8 bits of the keys in digits (d1, d2).
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      if ((key[i] >> 8) == (prefix >> 8)) atomicAdd(&hist[key[i] & 255u], 1);
-    __syncthreads();
-    const int d3 = select_bin(hist, kk, scan_sh[0], pick, &above, &dummy);
-    kk -= above;
-    thr = prefix | (uint32_t)d3;
-    need = kk;
+        for (int i = 0; i < KPT; ++i)
+          if ((key[i] >> 8) == (prefix >> 8)) atomicAdd(&hist[key[i] & 255u], 1);
+        __syncthreads();
+        const int d3 = select_bin(hist, kk, scan_sh[0], pick, &above, &count, &dummy);
+        kk -= above;
+        thr = prefix | (uint32_t)d3;
+        need = kk;
+      }
+    }
   }
   const bool ties = thr != 0u;  // with thr == 0 every candidate is taken
 
