@@ -220,21 +220,21 @@ __device__ inline uint32_t order_key(float f) {
 // callers alternate between two `sh` buffers, so the reads of one scan are done before
 // the next-but-one scan writes the same buffer (the scan between them has a barrier).
 __device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t* total) {
+  static_assert(kTopkWaves == 16, "the wave totals fill one 16-lane DPP row");
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) sh[wave] = incl;
   __syncthreads();
-  uint32_t off = 0;
-  uint32_t tot = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
-    const uint32_t c = sh[w];
-    if (w < wave) off += c;
-    tot += c;
-  }
-  *total = tot;
-  return off + incl - v;
+  // the wave totals, scanned within each 16-lane row (every row holds all 16)
+  uint32_t w = sh[lane & 15];
+  w += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0x111, 0xF, 0xF, false);  // row_shr:1
+  w += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0x112, 0xF, 0xF, false);  // row_shr:2
+  w += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0x114, 0xF, 0xF, false);  // row_shr:4
+  w += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0x118, 0xF, 0xF, false);  // row_shr:8
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)w, 15);
+  const uint32_t before = (uint32_t)__builtin_amdgcn_readlane((int)w, max(wave - 1, 0));
+  return (wave == 0 ? 0u : before) + incl - v;
 }
 
 // The digit bin holding the kk-th largest counted key (1-based), scanning the bins
@@ -251,16 +251,14 @@ __device__ inline int select_bin(int* hist, int kk, uint32_t* sh, int* pick, int
   *h4 = make_int4(0, 0, 0, 0);
   const int c[4] = {hv.w, hv.z, hv.y, hv.x};  // bins 4095-4t, 4094-4t, 4093-4t, 4092-4t
   uint32_t tot;
-  int a = (int)block_excl_scan((uint32_t)(c[0] + c[1] + c[2] + c[3]), sh, &tot);
+  const int a0 = (int)block_excl_scan((uint32_t)(c[0] + c[1] + c[2] + c[3]), sh, &tot);
   *total = (int)tot;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (a < kk && kk <= a + c[q]) {
-      pick[0] = kDigitBins - 1 - (4 * tid + q);
-      pick[1] = a;
-      pick[2] = c[q];
-    }
-    a += c[q];
+  const int a1 = a0 + c[0], a2 = a1 + c[1], a3 = a2 + c[2], a4 = a3 + c[3];
+  if (a0 < kk && kk <= a4) {  // the one thread whose bins hold the kk-th key
+    const int q = kk <= a1 ? 0 : kk <= a2 ? 1 : kk <= a3 ? 2 : 3;
+    pick[0] = kDigitBins - 1 - (4 * tid + q);
+    pick[1] = q == 0 ? a0 : q == 1 ? a1 : q == 2 ? a2 : a3;
+    pick[2] = c[q];
   }
   __syncthreads();
   *above = pick[1];
@@ -462,9 +460,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
       sel_bits |= (s ? 1u : 0u) << i;
     }
   }
+  constexpr int kCap = kTopkThreads * kStride;  // words of the staging buffer
   if constexpr (!BUILD) {
     __syncthreads();
-    for (int j = tid; j < k; j += kTopkThreads) orow[j] = j < total ? ostage[j] : -1;
+    for (int j = tid; j < k; j += kTopkThreads) {
+      const int v = ostage[min(j, kCap - 1)];
+      orow[j] = j < total ? v : -1;
+    }
   } else {
     // The winners' slots in row order; those whose compressed page is not in the pool
     // are dropped (fail closed), the rest packed left.  Rows base + i with i < split lie
@@ -481,7 +483,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     uint32_t vtotal_u;
     int vpos = (int)block_excl_scan((uint32_t)__builtin_popcount(vbits), scan_sh[0], &vtotal_u);  // also orders ostage
     const int vtotal = (int)vtotal_u;
-    for (int j = tid; j < k; j += kTopkThreads) orow[j] = j < total ? ostage[j] : -1;
+    for (int j = tid; j < k; j += kTopkThreads) {
+      const int v = ostage[min(j, kCap - 1)];
+      orow[j] = j < total ? v : -1;
+    }
     __syncthreads();  // the winners are read out before their slots overwrite them
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -490,7 +495,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
       vpos += v ? 1 : 0;
     }
     __syncthreads();
-    for (int j = tid; j < ba.padded; j += kTopkThreads) si_row[ba.window + j] = j < vtotal ? ostage[j] : -1;
+    for (int j = tid; j < ba.padded; j += kTopkThreads) {
+      const int v = ostage[min(j, kCap - 1)];
+      si_row[ba.window + j] = j < vtotal ? v : -1;
+    }
     if (tid == 0) ba.lens[t] = vtotal;
     window_stores();
   }
