@@ -93,25 +93,23 @@ class Step:
 
     def run(self, ev=None, fused=True):
         """One step: the indexer, top-k and index build (one call, or two when not fused),
-        then the attention.  ev: 4 events around the calls (ev[1] == ev[2] when fused)."""
+        then the attention.  ev (optional): events recorded after the indexer call (two-call
+        step only), just before the attention and just after it.  Each record costs the
+        step a few microseconds, so no event precedes the indexer: its segment is taken
+        from the previous step's last event."""
         lib = self.lib
-        if ev is not None:
-            ev[0].record()
         if fused:
             rc = lib.indexer_topk_sparse_indices(*self.args_fused)
-            if ev is not None:
-                ev[1].record()
-                ev[2].record()
         else:
             rc = lib.indexer_score_topk(*self.args_idx)
             if ev is not None:
-                ev[1].record()
+                ev[0].record()
             rc |= lib.build_sparse_indices(*self.args_build)
-            if ev is not None:
-                ev[2].record()
+        if ev is not None:
+            ev[-2].record()
         rc |= lib.sparse_mla_decode(*self.args_attn)
         if ev is not None:
-            ev[3].record()
+            ev[-1].record()
         if rc:
             raise RuntimeError(f"step failed: {L.last_error()}")
 
@@ -365,21 +363,30 @@ def bench_prepare_indexer_q(num_tokens: int, positions, iters: int = 30, warmup:
 
 def time_steps(wl: WL.Workload, layers: int, K: int, warmup: int, fused: bool = True):
     """Wall-clock ms per step over K steps (layers rotated) and the mean HIP-event ms of
-    the segments: indexer + top-k, index build (0 when fused into the top-k kernel),
-    attention."""
+    the segments: indexer + top-k (from the previous step's end, so launch gaps
+    included), index build (0 when fused into the top-k kernel), attention.  The events
+    are recorded inside the timed steps (two per step, three for the two-call step)."""
     steps = [Step(wl, i) for i in range(layers)]
     for i in range(warmup):
         steps[i % layers].run(fused=fused)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    n_ev = 2 if fused else 3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(K):
         steps[i % layers].run(evs[i], fused=fused)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    seg = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(K)])
-    return wall * 1e3 / K, seg.mean(axis=0)
+    attn = [evs[i][-2].elapsed_time(evs[i][-1]) for i in range(K)]
+    if fused:
+        idx = [evs[i - 1][-1].elapsed_time(evs[i][-2]) for i in range(1, K)]
+        build = [0.0]
+    else:
+        idx = [evs[i - 1][-1].elapsed_time(evs[i][0]) for i in range(1, K)]
+        build = [evs[i][0].elapsed_time(evs[i][1]) for i in range(K)]
+    ms_idx = float(np.mean(idx)) if idx else float("nan")  # needs two steps
+    return wall * 1e3 / K, np.array([ms_idx, np.mean(build), np.mean(attn)])
 
 
 def time_steps_graph(wl: WL.Workload, layers: int, K: int, warmup: int):
