@@ -65,8 +65,10 @@ struct KeyBatch {
 
 // One wave scores 512 consecutive compressed rows of one token, 4 groups of 16 rows at
 // a time; the loads of the next batch are issued before the current one is scored.  The
-// page ids of the wave's rows are loaded once up front (one per lane, at most 64 pages).
-template <int DIM>
+// page ids of the wave's rows are loaded once up front (one per lane, at most 64 pages),
+// with a wave mask of the ones that are pool pages.  BLOCK (rows per page, 16 or 64) is
+// a template argument, so a row's page column is a shift.
+template <int DIM, int BLOCK>
 __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
     sad_batch b, const uint8_t* __restrict__ qv, const uint8_t* __restrict__ qs,
     const float* __restrict__ wts, int num_heads, IdxDesc kc, const int32_t* __restrict__ bt,
@@ -74,6 +76,8 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
     float* __restrict__ dbg, int64_t dbg_stride) {
   constexpr int VB = DIM / 2;    // packed value bytes per row
   constexpr int SB = DIM / 32;   // exponent bytes per row
+  constexpr int LGB = BLOCK == 16 ? 4 : 6;
+  static_assert(BLOCK == 16 || BLOCK == 64, "16 or 64 rows per page");
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -109,16 +113,17 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
   // the table; lanes past the wave's columns are cleared below).
   const int w_begin = blockIdx.x * kScoreChunk + wave * kRowsPerWave;
   const int32_t* bt_row = bt + (int64_t)req * bt_stride;
-  const int col0 = w_begin / kc.block;
+  const int col0 = w_begin >> LGB;
   const int pid_any = bt_row[min(col0 + lane, bt_cols - 1)];
   TokenGeom g;
   if (!token_geometry(b, t, ratio, g)) return;
-  const int n_rows = min(g.n_comp, bt_cols * kc.block);
+  const int n_rows = min(g.n_comp, bt_cols * BLOCK);
   if (w_begin >= n_rows) return;  // no barriers in this kernel: waves may leave early
   const int w_rows = min(kRowsPerWave, n_rows - w_begin);
   const int n_groups = (w_rows + 15) / 16;
-  const int ncol = (w_begin + w_rows - 1) / kc.block - col0 + 1;  // <= 64
+  const int ncol = ((w_begin + w_rows - 1) >> LGB) - col0 + 1;  // <= 64
   const int pid = lane < ncol ? pid_any : -1;
+  const uint64_t pool_cols = __ballot(pid >= 0 && (int64_t)pid < kc.num_pages);  // bit i: column col0 + i
   // Issue the loads of the batch's groups as buffer loads: a wave-uniform resource per
   // page (zero records for an absent or unbacked group, so its loads return zeros and
   // touch no memory), the group's first row as the scalar offset and a per-lane
@@ -130,18 +135,20 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
 #pragma unroll
     for (int u = 0; u < kGroupBatch; ++u) {
       const int sg = w_begin + 16 * (gb + u);
-      const int page = __builtin_amdgcn_readlane(pid, min(sg / kc.block - col0, 63));  // wave-uniform
-      const bool ok = gb + u < n_groups && page >= 0 && (int64_t)page < kc.num_pages;
-      const int r0 = sg & (kc.block - 1);  // first row of the group in its page
+      const int ci = min((sg >> LGB) - col0, 63);  // the group's table column - col0
+      const int page = __builtin_amdgcn_readlane(pid, ci);  // wave-uniform
+      const bool ok = gb + u < n_groups && ((pool_cols >> ci) & 1ull);
+      const int r0 = sg & (BLOCK - 1);  // first row of the group in its page
       const uint8_t* pg = kc.pool + (int64_t)(ok ? page : 0) * kc.stride;
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)pg, (short)0, ok ? (int)kc.stride : 0, kRawBufferFlags);
       kb.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_voff, r0 * VB, 0);
-      kb.e[u] = __builtin_amdgcn_raw_buffer_load_b8(rs, lane_soff, kc.block * VB + r0 * SB, 0);
+      kb.e[u] = __builtin_amdgcn_raw_buffer_load_b8(rs, lane_soff, BLOCK * VB + r0 * SB, 0);
     }
   };
-  float* lrow = logits + (int64_t)t * logits_stride;
-  float* drow = dbg != nullptr ? dbg + (int64_t)t * dbg_stride : nullptr;
+  // this lane's first logit (lanes 0..15 store row w_begin + 16 g + lane of group g)
+  float* lrow = logits + (int64_t)t * logits_stride + w_begin + lane;
+  float* drow = dbg != nullptr ? dbg + (int64_t)t * dbg_stride + w_begin + lane : nullptr;
   // the ReLU's upper clamp, kept opaque so the clamp stays one med3 instruction
   float fmax_big = 3.402823466e+38f;
   asm volatile("" : "+s"(fmax_big));
@@ -162,8 +169,7 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
   };
   auto combine = [&](int gb, int u, const f32x4_t (&acc)[4]) __attribute__((always_inline)) {
     const int sg = w_begin + 16 * (gb + u);
-    const int page = __builtin_amdgcn_readlane(pid, min(sg / kc.block - col0, 63));
-    const bool ok = page >= 0 && (int64_t)page < kc.num_pages;
+    const bool ok = (pool_cols >> min((sg >> LGB) - col0, 63)) & 1ull;
     float part = 0.0f;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
@@ -173,10 +179,10 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
     // lanes m, m+16, m+32, m+48 hold the 4 head groups of row sg + m
     part += __shfl_xor(part, 16, 64);
     part += __shfl_xor(part, 32, 64);
-    if (lane < 16 && sg + lane < w_begin + w_rows) {
+    if (lane < 16 && 16 * (gb + u) + lane < w_rows) {
       const float v = ok ? part : -INFINITY;
-      lrow[sg + lane] = v;
-      if (drow != nullptr) drow[sg + lane] = v;
+      lrow[16 * (gb + u)] = v;
+      if (drow != nullptr) drow[16 * (gb + u)] = v;
     }
   };
   auto score = [&](int gb, const KeyBatch& kb) __attribute__((always_inline)) {
@@ -571,17 +577,15 @@ int run_indexer(const sad_batch* batch, const uint8_t* q_values, const uint8_t* 
   hipStream_t st = (hipStream_t)stream;
   if (max_rows > 0) {
     const dim3 grid((max_rows + kScoreChunk - 1) / kScoreChunk, T);
-    if (keys->dim == 128) {
-      hipLaunchKernelGGL((indexer_score_kernel<128>), grid, dim3(kScoreThreads), 0, st, *batch,
-                         q_values, q_scales, weights, num_idx_heads, kd, idx_bt, idx_bt_stride,
-                         idx_bt_cols, compress_ratio, logits, ws_stride, logits_debug,
-                         logits_stride);
-    } else {
-      hipLaunchKernelGGL((indexer_score_kernel<64>), grid, dim3(kScoreThreads), 0, st, *batch,
-                         q_values, q_scales, weights, num_idx_heads, kd, idx_bt, idx_bt_stride,
-                         idx_bt_cols, compress_ratio, logits, ws_stride, logits_debug,
-                         logits_stride);
-    }
+    auto score = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, grid, dim3(kScoreThreads), 0, st, *batch, q_values, q_scales, weights,
+                         num_idx_heads, kd, idx_bt, idx_bt_stride, idx_bt_cols, compress_ratio, logits,
+                         ws_stride, logits_debug, logits_stride);
+    };
+    if (keys->dim == 128)
+      keys->block_size == 64 ? score(indexer_score_kernel<128, 64>) : score(indexer_score_kernel<128, 16>);
+    else
+      keys->block_size == 64 ? score(indexer_score_kernel<64, 64>) : score(indexer_score_kernel<64, 16>);
     int rc = check_launch("indexer_score_topk(score)");
     if (rc != SAD_OK) return rc;
   }
