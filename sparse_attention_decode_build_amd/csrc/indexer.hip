@@ -176,9 +176,13 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j)  // ReLU as one med3 (clamp to [0, FLT_MAX])
         part = __builtin_fmaf(wl[ht][j], __builtin_amdgcn_fmed3f(acc[ht][j], 0.0f, fmax_big), part);
-    // lanes m, m+16, m+32, m+48 hold the 4 head groups of row sg + m
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
+    // lanes m, m+16, m+32, m+48 hold the 4 head groups of row sg + m: the row swaps of
+    // v_permlane16_swap / v_permlane32_swap hand each lane the value of lane ^ 16, then
+    // of lane ^ 32 (the same sums as two xor shuffles, without the LDS)
+    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    part = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    part = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
     if (lane < 16 && 16 * (gb + u) + lane < w_rows) {
       const float v = ok ? part : -INFINITY;
       lrow[16 * (gb + u)] = v;
