@@ -78,6 +78,7 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
   constexpr int SB = DIM / 32;   // exponent bytes per row
   constexpr int LGB = BLOCK == 16 ? 4 : 6;
   static_assert(BLOCK == 16 || BLOCK == 64, "16 or 64 rows per page");
+  static_assert(kRowsPerWave % BLOCK == 0, "every wave starts on a page boundary");
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -134,12 +135,16 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
   auto load = [&](int gb, KeyBatch& kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kGroupBatch; ++u) {
-      const int sg = w_begin + 16 * (gb + u);
-      const int ci = min((sg >> LGB) - col0, 63);  // the group's table column - col0
+      // the wave starts on a page boundary, so the group's table column (minus col0)
+      // and its first row in the page are constants
+      const int ci = (16 * (gb + u)) >> LGB;
+      const int r0 = (16 * (gb + u)) & (BLOCK - 1);
       const int page = __builtin_amdgcn_readlane(pid, ci);  // wave-uniform
-      const bool ok = gb + u < n_groups && ((pool_cols >> ci) & 1ull);
-      const int r0 = sg & (BLOCK - 1);  // first row of the group in its page
-      const uint8_t* pg = kc.pool + (int64_t)(ok ? page : 0) * kc.stride;
+      const bool page_ok = (pool_cols >> ci) & 1ull;
+      const bool ok = gb + u < n_groups && page_ok;
+      // the base depends on the page only (shared by its groups); a group past the
+      // wave's rows gets zero records instead
+      const uint8_t* pg = kc.pool + (int64_t)(page_ok ? page : 0) * kc.stride;
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)pg, (short)0, ok ? (int)kc.stride : 0, kRawBufferFlags);
       kb.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane_voff, r0 * VB, 0);
@@ -168,15 +173,14 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
     }
   };
   auto combine = [&](int gb, int u, const f32x4_t (&acc)[4]) __attribute__((always_inline)) {
-    const int sg = w_begin + 16 * (gb + u);
-    const bool ok = (pool_cols >> min((sg >> LGB) - col0, 63)) & 1ull;
+    const bool ok = (pool_cols >> ((16 * (gb + u)) >> LGB)) & 1ull;
     float part = 0.0f;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
       for (int j = 0; j < 4; ++j)  // ReLU as one med3 (clamp to [0, FLT_MAX])
         part = __builtin_fmaf(wl[ht][j], __builtin_amdgcn_fmed3f(acc[ht][j], 0.0f, fmax_big), part);
-    // lanes m, m+16, m+32, m+48 hold the 4 head groups of row sg + m: the row swaps of
+    // lanes m, m+16, m+32, m+48 hold the 4 head groups of the group's row m: the row swaps of
     // v_permlane16_swap / v_permlane32_swap hand each lane the value of lane ^ 16, then
     // of lane ^ 32 (the same sums as two xor shuffles, without the LDS)
     const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
