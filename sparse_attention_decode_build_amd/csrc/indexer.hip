@@ -319,7 +319,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 
   // The workspace row holds max_rows logits, so they are loaded before the token's
   // length is known (at an index clamped into the row: none is conditional); rows past
-  // n become -inf below.
+  // n become -inf below.  The token's geometry comes through scalar loads, which the
+  // wait for them does not serialize behind the logits loads.
   float lv[KPT];
   if (max_rows > 0) {
     const float* lrow = logits + (int64_t)t * logits_stride;
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     for (int i = 0; i < KPT; ++i) lv[i] = lrow[min(i * kTopkThreads + tid, max_rows - 1)];
   }
   TokenGeom g;
-  const bool ok = token_geometry(b, t, ratio, g);
+  const bool ok = token_geometry_uniform(b, t, ratio, g);
   const int n = ok ? min(g.n_comp, max_rows) : 0;
   int32_t* orow = out + (int64_t)t * k;
 

@@ -58,8 +58,8 @@ struct TokenGeom {
 };
 
 // Returns false when the token sees nothing (bad request id or negative position).
-__device__ inline bool token_geometry(const sad_batch& b, int t, int ratio, TokenGeom& g) {
-  const int r = b.token_to_req[t];
+// The same from the token's request id r = token_to_req[t], already loaded.
+__device__ inline bool token_geometry_of(const sad_batch& b, int t, int r, int ratio, TokenGeom& g) {
   g.req = r;
   g.pos = -1;
   g.n_comp = 0;
@@ -67,6 +67,35 @@ __device__ inline bool token_geometry(const sad_batch& b, int t, int ratio, Toke
   const int q0 = b.query_start_loc[r];
   const int q1 = b.query_start_loc[r + 1];
   const int p = b.seq_lens[r] - (q1 - q0) + (t - q0);
+  if (p < 0) return false;
+  g.pos = p;
+  g.n_comp = (p + 1) / ratio;
+  return true;
+}
+
+__device__ inline bool token_geometry(const sad_batch& b, int t, int ratio, TokenGeom& g) {
+  return token_geometry_of(b, t, b.token_to_req[t], ratio, g);
+}
+
+// A read of a batch word at a workgroup-uniform index through the constant address
+// space: a scalar-cache load (these arrays are inputs no kernel writes during a launch),
+// counted apart from the vector memory loads, so a vector load issued earlier is not
+// waited for when its value is needed.
+__device__ inline int uniform_ro_load(const int32_t* p) {
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  return *(const_i32*)p;
+}
+
+// token_geometry for a workgroup-uniform token t, with scalar-cache loads.
+__device__ inline bool token_geometry_uniform(const sad_batch& b, int t, int ratio, TokenGeom& g) {
+  const int r = uniform_ro_load(b.token_to_req + t);
+  g.req = r;
+  g.pos = -1;
+  g.n_comp = 0;
+  if (r < 0 || r >= b.num_reqs) return false;
+  const int q0 = uniform_ro_load(b.query_start_loc + r);
+  const int q1 = uniform_ro_load(b.query_start_loc + r + 1);
+  const int p = uniform_ro_load(b.seq_lens + r) - (q1 - q0) + (t - q0);
   if (p < 0) return false;
   g.pos = p;
   g.n_comp = (p + 1) / ratio;
