@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
       wl[ht][j] = ho < num_heads ? wts[(int64_t)t * num_heads + ho] : 0.0f;
     }
   }
-  const int req = b.token_to_req[t];
+  const int req = uniform_ro_load(b.token_to_req + t);  // scalar load: not behind the Q loads
   if (req < 0 || req >= b.num_reqs || bt_cols <= 0) return;
   // Page ids of this wave's rows: lane i holds table column col0 + i (a 16-row group
   // never straddles a page, since 16 divides the page size).  The load needs only the
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_score_kernel(
   const int col0 = w_begin >> LGB;
   const int pid_any = bt_row[min(col0 + lane, bt_cols - 1)];
   TokenGeom g;
-  if (!token_geometry(b, t, ratio, g)) return;
+  if (!token_geometry_uniform(b, t, ratio, g)) return;
   const int n_rows = min(g.n_comp, bt_cols * BLOCK);
   if (w_begin >= n_rows) return;  // no barriers in this kernel: waves may leave early
   const int w_rows = min(kRowsPerWave, n_rows - w_begin);

@@ -58,8 +58,8 @@ struct TokenGeom {
 };
 
 // Returns false when the token sees nothing (bad request id or negative position).
-// The same from the token's request id r = token_to_req[t], already loaded.
-__device__ inline bool token_geometry_of(const sad_batch& b, int t, int r, int ratio, TokenGeom& g) {
+__device__ inline bool token_geometry(const sad_batch& b, int t, int ratio, TokenGeom& g) {
+  const int r = b.token_to_req[t];
   g.req = r;
   g.pos = -1;
   g.n_comp = 0;
@@ -71,10 +71,6 @@ __device__ inline bool token_geometry_of(const sad_batch& b, int t, int r, int r
   g.pos = p;
   g.n_comp = (p + 1) / ratio;
   return true;
-}
-
-__device__ inline bool token_geometry(const sad_batch& b, int t, int ratio, TokenGeom& g) {
-  return token_geometry_of(b, t, b.token_to_req[t], ratio, g);
 }
 
 // A read of a batch word at a workgroup-uniform index through the constant address
