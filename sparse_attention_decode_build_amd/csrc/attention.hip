@@ -502,15 +502,27 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   u32x4_t dq[2 * S::FP8_LINES];  // ... and their fp8 part as bf16 (rope part: rr.rope)
   // One fp8 word of the raw rows (4 e4m3 values) -> 4 bf16 in dq: word w of line j holds
   // elements 16c + 4(w%4) .. +4 of that line.
+  // The native record's scales are powers of two (ue8m0): the scaled conversion does the
+  // multiply and the bf16 rounding in one instruction per pair, with the same result as
+  // bf16_rne(float(e4m3) * 2^(b - 127)) for every code and scale byte 0 .. 254.  (Byte
+  // 255, which the pages' writer never produces and ue8m0 reserves for NaN, decodes as
+  // NaN here instead of inf; a row holding it makes the output non-finite either way.)
   auto convert_word = [&](auto wc) __attribute__((always_inline)) {
     constexpr int w = decltype(wc)::value;
     constexpr int j = w >> 2;
     constexpr int qw = w & 3;
     const uint32_t word = rr.v[j][qw];
-    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false) * rr.sc[j];
-    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true) * rr.sc[j];
-    dq[2 * j + (qw >> 1)][2 * (qw & 1)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
-    dq[2 * j + (qw >> 1)][2 * (qw & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
+    if constexpr (S::NATIVE) {
+      dq[2 * j + (qw >> 1)][2 * (qw & 1)] =
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, rr.sc[j], false));
+      dq[2 * j + (qw >> 1)][2 * (qw & 1) + 1] =
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, rr.sc[j], true));
+    } else {
+      const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false) * rr.sc[j];
+      const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true) * rr.sc[j];
+      dq[2 * j + (qw >> 1)][2 * (qw & 1)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
+      dq[2 * j + (qw >> 1)][2 * (qw & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
+    }
   };
   constexpr int NWORD = 4 * S::FP8_LINES;
 
