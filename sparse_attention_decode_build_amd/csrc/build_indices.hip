@@ -26,13 +26,13 @@ __global__ __launch_bounds__(kThreads) void build_sparse_indices_kernel(
   int32_t* row = out + (int64_t)t * (window + padded);
 
   TokenGeom g;
-  const bool ok = token_geometry(b, t, ratio, g);
+  const bool ok = token_geometry_uniform(b, t, ratio, g);  // scalar-cache loads
 
   // Window columns: positions lo..pos ascending, then -1.
   int lo = 0;
   if (ok) {
     lo = g.pos - window + 1;
-    if (replay != nullptr) lo = max(lo, replay[g.req]);
+    if (replay != nullptr) lo = max(lo, uniform_ro_load(replay + g.req));
     lo = max(lo, 0);
   }
   const int32_t* swa_row = ok ? swa_bt + (int64_t)g.req * swa_stride : nullptr;

@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     }
     if (ok) {
       lo0 = max(g.pos - ba.window + 1, 0);
-      if (ba.replay != nullptr) replay = ba.replay[g.req];
+      if (ba.replay != nullptr) replay = uniform_ro_load(ba.replay + g.req);
       swa_row = ba.swa_bt + (int64_t)g.req * ba.swa_stride;
       if (tid < ba.window && lo0 + tid <= g.pos)
         win_slot = page_slot(swa_row, ba.swa_cols, ba.swa_block, ba.swa_pages, lo0 + tid);

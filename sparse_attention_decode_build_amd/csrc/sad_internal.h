@@ -57,22 +57,6 @@ struct TokenGeom {
   int n_comp;
 };
 
-// Returns false when the token sees nothing (bad request id or negative position).
-__device__ inline bool token_geometry(const sad_batch& b, int t, int ratio, TokenGeom& g) {
-  const int r = b.token_to_req[t];
-  g.req = r;
-  g.pos = -1;
-  g.n_comp = 0;
-  if (r < 0 || r >= b.num_reqs) return false;
-  const int q0 = b.query_start_loc[r];
-  const int q1 = b.query_start_loc[r + 1];
-  const int p = b.seq_lens[r] - (q1 - q0) + (t - q0);
-  if (p < 0) return false;
-  g.pos = p;
-  g.n_comp = (p + 1) / ratio;
-  return true;
-}
-
 // A read of a batch word at a workgroup-uniform index through the constant address
 // space: a scalar-cache load (these arrays are inputs no kernel writes during a launch),
 // counted apart from the vector memory loads, so a vector load issued earlier is not
@@ -82,7 +66,8 @@ __device__ inline int uniform_ro_load(const int32_t* p) {
   return *(const_i32*)p;
 }
 
-// token_geometry for a workgroup-uniform token t, with scalar-cache loads.
+// Geometry of a workgroup-uniform token t, read with scalar-cache loads.  Returns false
+// when the token sees nothing (bad request id or negative position).
 __device__ inline bool token_geometry_uniform(const sad_batch& b, int t, int ratio, TokenGeom& g) {
   const int r = uniform_ro_load(b.token_to_req + t);
   g.req = r;
