@@ -93,23 +93,24 @@ class Step:
 
     def run(self, ev=None, fused=True):
         """One step: the indexer, top-k and index build (one call, or two when not fused),
-        then the attention.  ev (optional): events recorded after the indexer call (two-call
-        step only), just before the attention and just after it.  Each record costs the
-        step a few microseconds, so no event precedes the indexer: its segment is taken
-        from the previous step's last event."""
+        then the attention.  ev (optional): [after the indexer call (two-call step only),
+        just before the attention, just after it], each an event or None.  Each record
+        costs the step a few microseconds, so no event precedes the indexer: its segment
+        is taken from the previous step's last event."""
         lib = self.lib
+        ev = ev if ev is not None else [None, None, None]
         if fused:
             rc = lib.indexer_topk_sparse_indices(*self.args_fused)
         else:
             rc = lib.indexer_score_topk(*self.args_idx)
-            if ev is not None:
+            if ev[0] is not None:
                 ev[0].record()
             rc |= lib.build_sparse_indices(*self.args_build)
-        if ev is not None:
-            ev[-2].record()
+        if ev[1] is not None:
+            ev[1].record()
         rc |= lib.sparse_mla_decode(*self.args_attn)
-        if ev is not None:
-            ev[-1].record()
+        if ev[2] is not None:
+            ev[2].record()
         if rc:
             raise RuntimeError(f"step failed: {L.last_error()}")
 
@@ -365,27 +366,30 @@ def time_steps(wl: WL.Workload, layers: int, K: int, warmup: int, fused: bool = 
     """Wall-clock ms per step over K steps (layers rotated) and the mean HIP-event ms of
     the segments: indexer + top-k (from the previous step's end, so launch gaps
     included), index build (0 when fused into the top-k kernel), attention.  The events
-    are recorded inside the timed steps (two per step, three for the two-call step)."""
+    are recorded inside the timed steps, on every EVERY-th step (and the end of the step
+    before it), so their cost is spread thin over the timed region."""
     steps = [Step(wl, i) for i in range(layers)]
     for i in range(warmup):
         steps[i % layers].run(fused=fused)
     torch.cuda.synchronize()
-    n_ev = 2 if fused else 3
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K)]
+    EVERY = 4
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    evs = []
+    for i in range(K):
+        sampled = i % EVERY == 0
+        evs.append([mk() if sampled and not fused else None, mk() if sampled else None,
+                    mk() if sampled or (i + 1) % EVERY == 0 else None])
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(K):
         steps[i % layers].run(evs[i], fused=fused)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    attn = [evs[i][-2].elapsed_time(evs[i][-1]) for i in range(K)]
-    if fused:
-        idx = [evs[i - 1][-1].elapsed_time(evs[i][-2]) for i in range(1, K)]
-        build = [0.0]
-    else:
-        idx = [evs[i - 1][-1].elapsed_time(evs[i][0]) for i in range(1, K)]
-        build = [evs[i][0].elapsed_time(evs[i][1]) for i in range(K)]
-    ms_idx = float(np.mean(idx)) if idx else float("nan")  # needs two steps
+    samples = [i for i in range(0, K, EVERY)]
+    attn = [evs[i][1].elapsed_time(evs[i][2]) for i in samples]
+    idx = [evs[i - 1][2].elapsed_time(evs[i][0] if not fused else evs[i][1]) for i in samples if i > 0]
+    build = [evs[i][0].elapsed_time(evs[i][1]) for i in samples] if not fused else [0.0]
+    ms_idx = float(np.mean(idx)) if idx else float("nan")  # needs EVERY + 1 steps
     return wall * 1e3 / K, np.array([ms_idx, np.mean(build), np.mean(attn)])
 
 
