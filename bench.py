@@ -426,6 +426,8 @@ def time_steps_graph(wl: WL.Workload, layers: int, K: int, warmup: int):
             if not torch.equal(a, b):
                 raise RuntimeError("graph replay differs from the eager step")
     reps = max(1, K // layers)
+    for _ in range(2):  # the first replays after capture run slower
+        g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(reps):
