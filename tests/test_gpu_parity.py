@@ -40,6 +40,11 @@ EDGE = WL.Config(
     swa_backing="all",
 )
 
+# Contexts past 64K positions (131072, 100003 and 96000): more than 16384 compressed rows,
+# so the top-k kernel runs with 32 keys per thread; the middle one leaves a ragged tail.
+LONG = WL.with_overrides(WL.CONFIGS["b32_8k"], name="long_ctx",
+                         groups=((1, 1, 131072, 0), (1, 1, 100003, 0), (1, 1, 96000, 0)))
+
 
 @pytest.fixture(scope="module", autouse=True)
 def gpu():
@@ -213,6 +218,14 @@ def test_head_counts_with_partial_head_groups(heads, requests):
     free(wl)
 
 
+def test_long_context_32_keys_per_thread():
+    wl = _wl(LONG)
+    view = WL.host_view(wl)
+    assert wl.layers[0].idx_bt.shape[1] * wl.cfg.idx_block > 16 * 1024
+    _full_check(wl, view, list(range(wl.num_tokens)), check_gather=False)
+    free(wl)
+
+
 def test_edge_fail_closed_tables():
     """Unbacked pages, ids past the pool and random local ids (incl. -1 and >= n_c)."""
     wl = _wl(EDGE)
@@ -380,12 +393,12 @@ def test_dense_1m_full():
     free(wl)
 
 
-@pytest.mark.parametrize("name", ["tiny", "b32_8k", "edge", "edge_holes", "b128_64k"])
+@pytest.mark.parametrize("name", ["tiny", "b32_8k", "edge", "edge_holes", "b128_64k", "long_ctx"])
 def test_fused_indexer_and_index_build_equal_the_two_calls(name):
     # indexer_topk_sparse_indices is defined as indexer_score_topk then build_sparse_indices:
     # all three outputs bit-identical to the two-call path (with holes in both block tables
     # and a page past the pool in the "edge_holes" case).
-    cfg = EDGE if name.startswith("edge") else name
+    cfg = EDGE if name.startswith("edge") else LONG if name == "long_ctx" else name
     wl = _wl(cfg)
     c = wl.cfg
     L0 = wl.layers[0]
