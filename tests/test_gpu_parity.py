@@ -226,6 +226,19 @@ def test_long_context_32_keys_per_thread():
     free(wl)
 
 
+@pytest.mark.parametrize("base,idx_dim,idx_block", [("tiny", 128, 16), ("b32_8k", 64, 64)])
+def test_indexer_key_dim_and_page_size(base, idx_dim, idx_block):
+    """The scoring kernel's other two (key dim, rows per page) forms: 128 x 16 and 64 x 64."""
+    cfg = WL.with_overrides(WL.CONFIGS[base], name=f"{base}_i{idx_dim}_b{idx_block}", idx_dim=idx_dim,
+                            idx_block=idx_block)
+    if base == "b32_8k":
+        cfg = WL.with_overrides(cfg, groups=((6, 1, 8192, 0),))
+    wl = _wl(cfg)
+    view = WL.host_view(wl)
+    _full_check(wl, view, list(range(wl.num_tokens)), check_gather=False)
+    free(wl)
+
+
 def test_edge_fail_closed_tables():
     """Unbacked pages, ids past the pool and random local ids (incl. -1 and >= n_c)."""
     wl = _wl(EDGE)
