@@ -375,9 +375,17 @@ def indexer_topk(query_start_loc, seq_lens, token_to_req, q_values, q_scales, we
     tokens = range(req.shape[0]) if tokens is None else tokens
     out = np.full((len(tokens), topk), -1, dtype=np.int32)
     scores_out = []
+    # a request's keys are read once, for its widest token (rows 0..n-1 of a read of
+    # more rows are the same rows)
+    widest = {}
+    for t in tokens:
+        widest[int(req[t])] = max(widest.get(int(req[t]), 0), int(nc[t]))
+    keys_of = {r: read_index_keys(idx_pages, idx_bt[r], n, idx_block_size, idx_dim, idx_num_pages)
+               for r, n in widest.items()}
     for i, t in enumerate(tokens):
         n = int(nc[t])
-        keys, valid = read_index_keys(idx_pages, idx_bt[req[t]], n, idx_block_size, idx_dim, idx_num_pages)
+        all_keys, all_valid = keys_of[int(req[t])]
+        keys, valid = all_keys[:n], all_valid[:n]
         sc = indexer_scores(q_values[t], q_scales[t], weights[t], keys) if n else np.zeros(0)
         out[i] = topk_select(sc, valid, topk)
         scores_out.append((sc, valid))
@@ -429,6 +437,52 @@ def attend(q_bits: np.ndarray, row_bits: np.ndarray, softmax_scale: float, sink=
     return o, lse
 
 
+def attention_spread(q_bits: np.ndarray, row_bits: np.ndarray, softmax_scale: float, sink,
+                     heads, dims) -> np.ndarray:
+    """``sum_j p_j |x_j[d] - o[h, d]|`` for each given (head h, dim d) pair, float64.
+
+    ``p_j`` are the normalized softmax weights of ``attend`` (the sink included in the
+    denominator) and ``o`` its output.  A relative change ``d_j`` of every weight,
+    renormalized, moves ``o[h, d]`` by ``sum_j p_j d_j (x_j[d] - o[h, d])``, so one
+    rounding of every weight to a format with unit roundoff u moves it by at most u
+    times this sum.  Zero where nothing is attended.
+    """
+    heads = np.asarray(heads, dtype=np.int64)
+    dims = np.asarray(dims, dtype=np.int64)
+    out = np.zeros(heads.shape[0], np.float64)
+    if row_bits.shape[0] == 0:
+        return out
+    q = bf16_bits_to_float(q_bits)
+    x = bf16_bits_to_float(row_bits)
+    o, _ = attend(q_bits, row_bits, softmax_scale, sink)
+    for i, (h, d) in enumerate(zip(heads, dims)):
+        logits = softmax_scale * (x @ q[h])
+        m = logits.max()
+        if sink is not None:
+            m = max(m, float(sink[h]))
+        e = np.exp(logits - m)
+        z = e.sum() + (math.exp(float(sink[h]) - m) if sink is not None else 0.0)
+        out[i] = float(e @ np.abs(x[:, d] - o[h, d])) / z
+    return out
+
+
+def attended_rows(kv_swa, kv_comp, si_row, topk_len, window_size, block_size_swa, block_size_comp,
+                  d_nope, d_rope, scale_format="f32") -> np.ndarray:
+    """bf16 bits [n, Dn+Dr] of one token's attended rows: window columns ``0..W-1`` with
+    a slot >= 0 read from the window cache, then compressed columns ``W..W+lens-1`` with
+    a slot >= 0 read from the compressed cache ([backend] ``forward_deepseek_v4_decode``:
+    ``k_cache`` is the window cache, ``extra_k_cache`` the compressed one)."""
+    si_row = np.asarray(si_row)
+    W = int(window_size)
+    swa = si_row[:W]
+    n = int(min(max(int(topk_len), 0), si_row.shape[0] - W))
+    comp = si_row[W: W + n]
+    return np.concatenate([
+        dequant_rows(kv_swa, swa[swa >= 0], block_size_swa, d_nope, d_rope, scale_format),
+        dequant_rows(kv_comp, comp[comp >= 0], block_size_comp, d_nope, d_rope, scale_format),
+    ])
+
+
 def sparse_mla_decode(q_bits, kv_swa, kv_comp, sparse_indices, sparse_topk_lens, window_size,
                       block_size_swa, block_size_comp, d_nope, d_rope, softmax_scale,
                       attn_sink=None, tokens=None, return_mass=False, scale_format="f32"):
@@ -450,13 +504,8 @@ def sparse_mla_decode(q_bits, kv_swa, kv_comp, sparse_indices, sparse_topk_lens,
     lse = np.zeros((len(tokens), H), np.float64)
     mass = np.zeros((len(tokens), H, D), np.float64) if return_mass else None
     for i, t in enumerate(tokens):
-        swa = si[t, :W]
-        n = int(min(max(int(sparse_topk_lens[t]), 0), si.shape[1] - W))
-        comp = si[t, W: W + n]
-        rows = np.concatenate([
-            dequant_rows(kv_swa, swa[swa >= 0], block_size_swa, d_nope, d_rope, scale_format),
-            dequant_rows(kv_comp, comp[comp >= 0], block_size_comp, d_nope, d_rope, scale_format),
-        ])
+        rows = attended_rows(kv_swa, kv_comp, si[t], sparse_topk_lens[t], W, block_size_swa,
+                             block_size_comp, d_nope, d_rope, scale_format)
         if return_mass:
             o[i], lse[i], mass[i] = attend(q_bits[t], rows, softmax_scale, attn_sink, return_mass=True)
         else:
@@ -472,23 +521,29 @@ def sparse_mla_decode(q_bits, kv_swa, kv_comp, sparse_indices, sparse_topk_lens,
 def rope_gptj_tail(x: np.ndarray, cos: np.ndarray, sin: np.ndarray, rope_dim: int) -> np.ndarray:
     """GPT-J (interleaved) rotary embedding of the last ``rope_dim`` elements, float32.
 
-    [ops] ``_apply_gptj_rope_tail_rows``: the row is taken to float32; each pair
-    (e, o) = (x[n + 2i], x[n + 2i + 1]) of the tail (n = D - rope_dim) becomes
-    (e*cos_i - o*sin_i, e*sin_i + o*cos_i), every product and sum a separate
-    float32 operation.  ``x`` [..., D]; ``cos``/``sin`` [..., rope_dim/2]
-    broadcast over the middle axes.  The leading part is returned unchanged.
+    [ops] rotary tail of the indexer query (GPT-J style, ``is_neox_style=False`` on the
+    [model] page): element pair i of the tail, (e, o) at positions (n + 2i, n + 2i + 1)
+    with n = D - rope_dim, is the complex number e + i*o, and it is multiplied by
+    cos_i + i*sin_i, giving (e*cos_i - o*sin_i, e*sin_i + o*cos_i).  Every real product
+    and sum of that complex multiply is a separate float32 operation (no fused
+    multiply-add).  ``x`` [..., D]; ``cos``/``sin`` [..., rope_dim/2] share ``x``'s
+    leading axes and broadcast over any axes between them and the last.  The leading
+    part of each row is returned unchanged.
     """
-    out = np.array(x, dtype=np.float32, copy=True)
+    f32 = np.float32
+    out = np.array(x, dtype=f32, copy=True)
     n = out.shape[-1] - rope_dim
-    e = out[..., n::2].copy()
-    o = out[..., n + 1::2].copy()
-    c = np.asarray(cos, dtype=np.float32)
-    s = np.asarray(sin, dtype=np.float32)
-    while c.ndim < e.ndim:
-        c = c[..., None, :]
-        s = s[..., None, :]
-    out[..., n::2] = (e * c).astype(np.float32) - (o * s).astype(np.float32)
-    out[..., n + 1::2] = (e * s).astype(np.float32) + (o * c).astype(np.float32)
+    c = np.asarray(cos, dtype=f32)
+    s = np.asarray(sin, dtype=f32)
+    extra = out.ndim - c.ndim  # axes of x between cos/sin's leading axes and the last one
+    lead = c.shape[:-1]
+    for i in range(rope_dim // 2):
+        ci = c[..., i].reshape(lead + (1,) * extra)
+        si = s[..., i].reshape(lead + (1,) * extra)
+        re = out[..., n + 2 * i].copy()
+        im = out[..., n + 2 * i + 1].copy()
+        out[..., n + 2 * i] = f32(re * ci) - f32(im * si)
+        out[..., n + 2 * i + 1] = f32(re * si) + f32(im * ci)
     return out
 
 

@@ -65,6 +65,11 @@ class Config:
     swa_backing: str = "window"  # "window" | "all"
     pin_first_prefill_seq: int = 0  # config 4 pins one prefill request's seq len
     kv_format: str = "f32"  # "f32": fp32 scale per 64 nope values; "ue8m0": the pages' native record
+    # 0: window rows share the compressed rows' pool and page size; else the window rows
+    # live in a pool of their own with this many rows per page (two caches, as the
+    # attention backend keeps them)
+    swa_block: int = 0
+    swa_pool_pages: int = 0  # 0 = 4x the window pages used (two-cache form only)
 
     @property
     def dqk(self) -> int:
@@ -86,6 +91,18 @@ class Config:
     @property
     def kv_page_bytes(self) -> int:
         return self.block * (self.kv_row_bytes + self.kv_scale_bytes)
+
+    @property
+    def two_cache(self) -> bool:
+        return self.swa_block != 0
+
+    @property
+    def swa_block_size(self) -> int:
+        return self.swa_block or self.block
+
+    @property
+    def swa_page_bytes(self) -> int:
+        return self.swa_block_size * (self.kv_row_bytes + self.kv_scale_bytes)
 
     @property
     def idx_row_bytes(self) -> int:
@@ -148,6 +165,18 @@ CONFIGS = {
         d_rope=64, idx_heads=64, idx_dim=128, block=64, idx_block=64,
         groups=((128, 1, 65536, 0),), kv_pool_pages=4_560_000, idx_pool_pages=900_000,
         kv_format="ue8m0",
+    ),
+    # two caches (the attention backend's window cache and compressed cache, each with its
+    # own pool and page size): window pages of 64 rows, compressed pages of 16 rows
+    "two_cache_tiny": Config(
+        name="two_cache_tiny", seed=20, window=32, ratio=4, topk=16, heads=8, d_nope=128, d_rope=32,
+        idx_heads=4, idx_dim=64, block=16, idx_block=16, groups=((1, 1, 256, 0), (1, 40, 300, 12)),
+        swa_backing="all", swa_block=64,
+    ),
+    "two_cache_b8_8k": Config(
+        name="two_cache_b8_8k", seed=21, window=128, ratio=4, topk=512, heads=64, d_nope=512,
+        d_rope=64, idx_heads=64, idx_dim=128, block=16, idx_block=64, groups=((8, 1, 8192, 0),),
+        swa_block=64,
     ),
     # 8 requests at seq 1M, ratio 128 (8192 compressed rows, all attended), W=128
     "dense_1m": Config(
@@ -264,9 +293,10 @@ class Workload:
     replay_start: torch.Tensor  # [R] int32
     padded_topk: int
     softmax_scale: float
-    kv_pool: torch.Tensor  # [pages, page_bytes] u8 (SWA and compressed rows share it)
+    kv_pool: torch.Tensor  # [pages, page_bytes] u8 (compressed rows; window rows too unless two-cache)
     idx_pool: torch.Tensor  # [pages, idx_page_bytes] u8 (1 page when dense)
     layers: list
+    swa_pool: torch.Tensor = None  # window rows' pool: kv_pool itself unless cfg.two_cache
 
     @property
     def max_seq(self) -> int:
@@ -296,9 +326,9 @@ def _geometry(cfg: Config, gen: torch.Generator):
     return q_lens, seq_lens, replay
 
 
-def _kv_page_bytes(cfg: Config, rows: torch.Tensor) -> torch.Tensor:
+def _kv_page_bytes(cfg: Config, rows: torch.Tensor, B: int = 0) -> torch.Tensor:
     """Encode rows [npages*B, Dqk] (bf16) into page images [npages, page_bytes]."""
-    B = cfg.block
+    B = B or cfg.block
     n = rows.shape[0]
     npages = n // B
     nope = rows[:, : cfg.d_nope]
@@ -353,28 +383,32 @@ def make_workload(
     max_seq = max(seq_lens)
     P = padded_topk(cfg, max_seq)
     B, Bi, W = cfg.block, cfg.idx_block, cfg.window
+    Bs = cfg.swa_block_size
 
     # Which logical pages each request needs.
     n_comp = [s // cfg.ratio for s in seq_lens]
     comp_pages = [(nc + B - 1) // B for nc in n_comp]
     idx_pages = [0 if cfg.dense else (nc + Bi - 1) // Bi for nc in n_comp]
-    swa_cols = (max_seq + B - 1) // B
+    swa_cols = (max_seq + Bs - 1) // Bs
     swa_needed = []
     for r in range(R):
         first_pos = seq_lens[r] - q_lens[r]
         lo = max(first_pos - W + 1, replay[r], 0)
         if cfg.swa_backing == "all":
             lo = 0
-        lo_page = lo // B
-        hi_page = (seq_lens[r] - 1) // B
+        lo_page = lo // Bs
+        hi_page = (seq_lens[r] - 1) // Bs
         swa_needed.append(list(range(lo_page, hi_page + 1)) if lo <= seq_lens[r] - 1 else [])
-    kv_used = sum(comp_pages) + sum(len(x) for x in swa_needed)
+    swa_used = sum(len(x) for x in swa_needed)
+    kv_used = sum(comp_pages) + (0 if cfg.two_cache else swa_used)
     idx_used = sum(idx_pages)
     n_kv_pages = kv_pool_pages or cfg.kv_pool_pages or 4 * kv_used * num_layers
     n_idx_pages = idx_pool_pages or cfg.idx_pool_pages or max(1, 4 * idx_used * num_layers)
-    if kv_used * num_layers > n_kv_pages or idx_used * num_layers > n_idx_pages:
+    n_swa_pages = (cfg.swa_pool_pages or max(1, 4 * swa_used * num_layers)) if cfg.two_cache else 0
+    if (kv_used * num_layers > n_kv_pages or idx_used * num_layers > n_idx_pages
+            or (cfg.two_cache and swa_used * num_layers > n_swa_pages)):
         raise ValueError("pool too small for the requested layers")
-    if n_kv_pages * B >= 2**31 or n_idx_pages * Bi >= 2**31:
+    if n_kv_pages * B >= 2**31 or n_idx_pages * Bi >= 2**31 or n_swa_pages * Bs >= 2**31:
         raise ValueError("slot ids must fit int32")
 
     # Device-side generator for the bulk data.
@@ -389,6 +423,12 @@ def make_workload(
     idx_perm_l = idx_perm.cpu().tolist()
     kv_next = 0
     idx_next = 0
+    if cfg.two_cache:
+        swa_pool = torch.empty((n_swa_pages, cfg.swa_page_bytes), dtype=torch.uint8, device=device)
+        swa_perm_l = torch.randperm(n_swa_pages, generator=dgen, device=device)[: swa_used * num_layers].cpu().tolist()
+        swa_next = 0
+    else:
+        swa_pool = kv_pool
 
     comp_cols = max(1, max(comp_pages))
     idx_cols = max(1, max(idx_pages))
@@ -409,14 +449,19 @@ def make_workload(
                 kv_pool[torch.tensor(pages, device=device)] = _kv_page_bytes(cfg, rows)
                 kv_written += pages
             # window rows: one latent row per token position
-            spages = kv_perm_l[kv_next: kv_next + len(swa_needed[r])]
-            kv_next += len(swa_needed[r])
+            if cfg.two_cache:
+                spages = swa_perm_l[swa_next: swa_next + len(swa_needed[r])]
+                swa_next += len(swa_needed[r])
+            else:
+                spages = kv_perm_l[kv_next: kv_next + len(swa_needed[r])]
+                kv_next += len(swa_needed[r])
             for lp, pp in zip(swa_needed[r], spages):
                 swa_bt[r, lp] = pp
             if spages:
-                rows = _bf16_round(torch.randn((len(spages) * B, cfg.dqk), generator=dgen, device=device))
-                kv_pool[torch.tensor(spages, device=device)] = _kv_page_bytes(cfg, rows)
-                kv_written += spages
+                rows = _bf16_round(torch.randn((len(spages) * Bs, cfg.dqk), generator=dgen, device=device))
+                swa_pool[torch.tensor(spages, device=device)] = _kv_page_bytes(cfg, rows, Bs)
+                if not cfg.two_cache:
+                    kv_written += spages
             # indexer keys (MXFP4), one per compressed row
             if not cfg.dense:
                 ipages = idx_perm_l[idx_next: idx_next + idx_pages[r]]
@@ -466,6 +511,7 @@ def make_workload(
         kv_pool=kv_pool,
         idx_pool=idx_pool,
         layers=layers,
+        swa_pool=swa_pool,
     )
 
 
@@ -489,8 +535,20 @@ class HostView:
     idx_q_values: object
     idx_q_scales: object
     idx_weights: object
-    kv_pages: dict
+    kv_pages: dict  # pages of the compressed rows' pool (and of the window rows' unless two-cache)
     idx_pages: dict
+    swa_pages: dict = None  # pages of the window rows' pool (kv_pages itself unless two-cache)
+
+
+def _copy_pages(pool: torch.Tensor, ids, device) -> dict:
+    pages = {}
+    chunk = 4096
+    for i in range(0, len(ids), chunk):
+        part = ids[i: i + chunk]
+        data = pool[torch.tensor(part, device=device)].detach().cpu().numpy()
+        for j, pid in enumerate(part):
+            pages[pid] = data[j]
+    return pages
 
 
 def host_view(wl: Workload, layer: int = 0, reqs=None) -> HostView:
@@ -505,24 +563,17 @@ def host_view(wl: Workload, layer: int = 0, reqs=None) -> HostView:
         return t.detach().cpu().numpy()
 
     rows = slice(None) if reqs is None else torch.as_tensor(sorted(set(reqs)), device=L.swa_bt.device)
-    # only ids that name a page of the pool (tables may hold -1 or stale ids past it)
-    kv_ids = torch.cat([L.swa_bt[rows].flatten(), L.comp_bt[rows].flatten()])
-    kv_ids = sorted(set(kv_ids[(kv_ids >= 0) & (kv_ids < wl.kv_pool.shape[0])].cpu().tolist()))
-    idx_ids = L.idx_bt[rows].flatten()
-    idx_ids = sorted(set(idx_ids[(idx_ids >= 0) & (idx_ids < wl.idx_pool.shape[0])].cpu().tolist()))
-    kv_pages = {}
-    idx_pages = {}
-    chunk = 4096
-    for i in range(0, len(kv_ids), chunk):
-        ids = kv_ids[i: i + chunk]
-        data = np_(wl.kv_pool[torch.tensor(ids, device=wl.device)])
-        for j, pid in enumerate(ids):
-            kv_pages[pid] = data[j]
-    for i in range(0, len(idx_ids), chunk):
-        ids = idx_ids[i: i + chunk]
-        data = np_(wl.idx_pool[torch.tensor(ids, device=wl.device)])
-        for j, pid in enumerate(ids):
-            idx_pages[pid] = data[j]
+
+    def ids_in(tables, pool):
+        # only ids that name a page of the pool (tables may hold -1 or stale ids past it)
+        ids = torch.cat([t[rows].flatten() for t in tables])
+        return sorted(set(ids[(ids >= 0) & (ids < pool.shape[0])].cpu().tolist()))
+
+    two = wl.swa_pool is not None and wl.swa_pool is not wl.kv_pool
+    kv_tables = [L.comp_bt] if two else [L.swa_bt, L.comp_bt]
+    kv_pages = _copy_pages(wl.kv_pool, ids_in(kv_tables, wl.kv_pool), wl.device)
+    idx_pages = _copy_pages(wl.idx_pool, ids_in([L.idx_bt], wl.idx_pool), wl.device)
+    swa_pages = _copy_pages(wl.swa_pool, ids_in([L.swa_bt], wl.swa_pool), wl.device) if two else kv_pages
     return HostView(
         query_start_loc=np_(wl.query_start_loc),
         seq_lens=np_(wl.seq_lens),
@@ -537,6 +588,7 @@ def host_view(wl: Workload, layer: int = 0, reqs=None) -> HostView:
         idx_weights=np_(L.idx_weights),
         kv_pages=kv_pages,
         idx_pages=idx_pages,
+        swa_pages=swa_pages,
     )
 
 

@@ -267,6 +267,78 @@ def _mx_query(rng, H, D):
     return v.numpy(), e.numpy()
 
 
+# E2M1 magnitudes as the [ops] page prints them (codes 0..7; bit 3 is the sign)
+_E2M1_PRINTED = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _mx_page(B, dim, code_of, exp_of):
+    """A hand-built indexer key page: B rows of dim/2 packed bytes (element 2k in the low
+    nibble of byte k), then B rows of dim/32 exponent bytes."""
+    vb, sb = dim // 2, dim // 32
+    page = np.zeros(B * (vb + sb), np.uint8)
+    for o in range(B):
+        for k in range(vb):
+            page[o * vb + k] = code_of(o, 2 * k) | (code_of(o, 2 * k + 1) << 4)
+        for b in range(sb):
+            page[B * vb + o * sb + b] = exp_of(o, b)
+    return page
+
+
+def test_read_index_keys_hand_built_page_and_unbacked_rows():
+    """[ops] read_deepseek_v4_indexer_mxfp4_cache: the value region (B x dim/2 bytes, low
+    nibble = even element) comes before the exponent region (B x dim/32 e8m0 bytes).  Row o,
+    element d of the page holds code (d + 3o) % 8 with the sign bit where (d + o) % 5 == 0,
+    and block b of row o the exponent byte 120 + o + 3b, so the key is
+    +-E2M1[(d + 3o) % 8] * 2^(o + 3b - 7).  The table names an unbacked page (-1), a page
+    past the pool and (by its length) no page for the last rows: those rows are invalid
+    and read as zero."""
+    B, dim = 16, 64
+    code = lambda o, d: ((d + 3 * o) % 8) | (0x8 if (d + o) % 5 == 0 else 0)  # noqa: E731
+    expo = lambda o, b: 120 + o + 3 * b  # noqa: E731
+    page = _mx_page(B, dim, code, expo)
+    num_pages = 10
+    bt_row = np.array([-1, 5, 99, 5], np.int32)  # logical pages 0..3; 99 is past the pool
+    rows = 4 * B + 6  # 6 rows past the table
+    keys, valid = O.read_index_keys({5: page}, bt_row, rows, B, dim, num_pages)
+    want_valid = np.zeros(rows, bool)
+    want_valid[B: 2 * B] = True
+    want_valid[3 * B: 4 * B] = True
+    assert np.array_equal(valid, want_valid)
+    for lp in (1, 3):
+        for o in range(B):
+            want = np.array([(-1.0 if (d + o) % 5 == 0 else 1.0) * _E2M1_PRINTED[(d + 3 * o) % 8]
+                             * 2.0 ** (o + 3 * (d // 32) - 7) for d in range(dim)])
+            assert np.array_equal(keys[lp * B + o], want), (lp, o)
+    assert not keys[~valid].any()
+    # a row past n_c is never read: fewer rows than the table covers
+    k2, v2 = O.read_index_keys({5: page}, bt_row, B + 3, B, dim, num_pages)
+    assert k2.shape == (B + 3, dim) and np.array_equal(v2, want_valid[: B + 3])
+    assert np.array_equal(k2[B:], keys[B: B + 3])
+
+
+def test_indexer_topk_never_selects_unbacked_rows():
+    """Rows whose key page is unbacked score nothing: top-k draws only from backed rows and
+    pads with -1 when fewer than k are backed ([backend] safe_page_ids, fail closed)."""
+    B, dim, H = 16, 64, 2
+    rng = np.random.default_rng(12)
+    pages = {}
+    for pid in (2, 7):
+        keys = torch.from_numpy(rng.standard_normal((B, dim)).astype(np.float32))
+        v, e = WL.encode_mxfp4(keys)
+        pages[pid] = np.concatenate([v.numpy().reshape(-1), e.numpy().reshape(-1)])
+    idx_bt = np.array([[2, -1, 7, 40]], np.int32)  # 40: past a pool of 10 pages
+    qv, qe = _mx_query(rng, H, dim)
+    w = np.abs(rng.standard_normal(H))
+    seq = 4 * B * 4  # n_c = 64 rows: logical pages 0..3
+    out, sc = O.indexer_topk(np.array([0, 1]), np.array([seq]), np.array([0]), qv[None], qe[None], w[None],
+                             pages, idx_bt, B, dim, 10, 4, 40, return_scores=True)
+    scores, valid = sc[0]
+    assert np.array_equal(np.nonzero(valid)[0], np.r_[0:B, 2 * B:3 * B])
+    got = out[0]
+    assert np.all(got[:2 * B] >= 0) and np.all(got[2 * B:] == -1)  # 32 backed rows < k = 40
+    assert set(got[:2 * B].tolist()) == set(range(B)) | set(range(2 * B, 3 * B))
+
+
 def test_scores_one_hot_query_reads_single_key_element():
     rng = np.random.default_rng(5)
     D = 64
@@ -404,6 +476,89 @@ def test_sparse_attention_ignores_padding_and_invalid_columns():
     o2, _ = O.sparse_mla_decode(v.q, v.kv_pages, v.kv_pages, si2, lens, W, cfg.block, cfg.block,
                                 cfg.d_nope, cfg.d_rope, wl.softmax_scale)
     assert np.array_equal(o2, res["out"])
+
+
+def _const_kv_page(B, Dn, Dr, byte, scale, rope_val):
+    """A KV page whose every row is byte `byte` (e4m3) with fp32 scale `scale` per block and
+    rope elements `rope_val` (bf16)."""
+    row_b = Dn + 2 * Dr
+    page = np.zeros(B * (row_b + 4 * (Dn // 64)), np.uint8)
+    rope = O.float32_to_bf16_bits(np.full(Dr, rope_val, np.float32)).view(np.uint8)
+    for o in range(B):
+        page[o * row_b: o * row_b + Dn] = byte
+        page[o * row_b + Dn: (o + 1) * row_b] = rope
+        page[B * row_b + o * 4 * (Dn // 64): B * row_b + (o + 1) * 4 * (Dn // 64)] = \
+            np.full(Dn // 64, scale, np.float32).view(np.uint8)
+    return page
+
+
+def test_window_and_compressed_columns_read_their_own_caches():
+    """[backend] forward_deepseek_v4_decode passes the window cache as k_cache and the
+    compressed cache as extra_k_cache, each with its own page size.  Window columns must
+    read the window cache and compressed columns the compressed one: page 3 exists in both
+    with different bytes (x = 1 / rope 0.5 in the window cache, x = -2 / rope -0.25 in the
+    compressed one)."""
+    Dn, Dr = 128, 32
+    for Bs, Bc in ((16, 16), (64, 16), (16, 64)):
+        swa = {3: _const_kv_page(Bs, Dn, Dr, 0x38, 1.0, 0.5)}    # e4m3 0x38 = 1.0
+        comp = {3: _const_kv_page(Bc, Dn, Dr, 0xB8, 2.0, -0.25)}  # e4m3 0xB8 = -1.0
+        W, P = 4, 4
+        si = np.array([[3 * Bs + 1, -1, 3 * Bs + Bs - 1, 3 * Bs,
+                        3 * Bc + 2, 3 * Bc + 5, 3 * Bc, 3 * Bc + 7]], np.int32)
+        lens = np.array([2], np.int32)  # compressed columns past lens are not attended
+        got = O.bf16_bits_to_float(O.gather_dequant(swa, comp, si, lens, W, Bs, Bc, Dn, Dr))[0]
+        for c in (0, 2, 3):
+            assert np.all(got[c, :Dn] == 1.0) and np.all(got[c, Dn:] == 0.5), (Bs, Bc, c)
+        for c in (4, 5):
+            assert np.all(got[c, :Dn] == -2.0) and np.all(got[c, Dn:] == -0.25), (Bs, Bc, c)
+        for c in (1, 6, 7):
+            assert not got[c].any()
+        # attention: 3 window rows u and 2 compressed rows v, so
+        # o = (3 e^{l_u} u + 2 e^{l_v} v) / (3 e^{l_u} + 2 e^{l_v})
+        rng = np.random.default_rng(Bs + Bc)
+        H = 4
+        q = _bf16_bits(rng.standard_normal((1, H, Dn + Dr)))
+        c_s = 0.05
+        o, lse = O.sparse_mla_decode(q, swa, comp, si, lens, W, Bs, Bc, Dn, Dr, c_s)
+        u = np.r_[np.full(Dn, 1.0), np.full(Dr, 0.5)]
+        v = np.r_[np.full(Dn, -2.0), np.full(Dr, -0.25)]
+        qf = O.bf16_bits_to_float(q[0])
+        lu, lv = c_s * (qf @ u), c_s * (qf @ v)
+        m = np.maximum(lu, lv)
+        wu, wv = 3 * np.exp(lu - m), 2 * np.exp(lv - m)
+        want = (wu[:, None] * u + wv[:, None] * v) / (wu + wv)[:, None]
+        assert np.allclose(o[0], want, rtol=1e-13, atol=1e-13)
+        assert np.allclose(lse[0], m + np.log(wu + wv), rtol=1e-13)
+
+
+def test_attention_spread_bounds_a_rounding_of_every_weight():
+    """attention_spread(h, d) = sum_j p_j |x_j[d] - o[h, d]|: zero for one row, the closed
+    form p(1-p)|x_0 - x_1| * 2 for two rows, and rounding every normalized weight to bf16
+    (then renormalizing) moves the output by at most 2^-8 of it (brute force)."""
+    rng = np.random.default_rng(21)
+    H, D, n = 3, 16, 40
+    q = _bf16_bits(rng.standard_normal((H, D)) * 3)
+    x = _bf16_bits(rng.standard_normal((n, D)))
+    c = 0.5
+    heads = np.repeat(np.arange(H), D)
+    dims = np.tile(np.arange(D), H)
+    assert not O.attention_spread(q, x[:1], c, None, heads, dims).any()
+    two = O.attention_spread(q, x[:2], c, None, heads, dims).reshape(H, D)
+    xf = O.bf16_bits_to_float(x[:2])
+    qf = O.bf16_bits_to_float(q)
+    l = c * (qf @ xf.T)
+    p0 = 1.0 / (1.0 + np.exp(l[:, 1] - l[:, 0]))
+    want = 2 * (p0 * (1 - p0))[:, None] * np.abs(xf[0] - xf[1])[None, :]
+    assert np.allclose(two, want, rtol=1e-12, atol=1e-15)
+    sp = O.attention_spread(q, x, c, None, heads, dims).reshape(H, D)
+    o, _ = O.attend(q, x, c)
+    xf = O.bf16_bits_to_float(x)
+    lg = c * (O.bf16_bits_to_float(q) @ xf.T)
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    pb = O.bf16_bits_to_float(O.float32_to_bf16_bits(p.astype(np.float32)))
+    ob = (pb @ xf) / pb.sum(axis=1, keepdims=True)
+    assert np.all(np.abs(ob - o) <= 2.0 ** -8 * sp + 1e-15)
 
 
 # --------------------------------------------------------------------------- indexer query preparation
