@@ -301,8 +301,10 @@ int gather_dequant_kv(const sad_kv_cache* swa, const sad_kv_cache* comp,
  *            when window_size + padded_topk = 0); sparse_topk_lens [num_tokens]
  *   workspace >= sparse_mla_decode_workspace_size(num_tokens, num_heads,
  *                window_size + padded_topk, d_nope + d_rope)
- * num_heads in {8, 16, ..., 128} (a multiple of 8, <= 128); (d_nope, d_rope)
- * = (512, 64) or (128, 32); page sizes (block_size) of both caches are powers of two.
+ * num_heads in {8, 16, ..., 128} (a multiple of 8, <= 128); (d_nope, d_rope,
+ * scale_format) = (512, 64, F32), (128, 32, F32) or the pages' native (448, 64, UE8M0),
+ * the same for both caches; page sizes (block_size) of both caches are powers of two
+ * and may differ (the window cache and the compressed cache are separate pools).
  * With few tokens a token's columns are split over several workgroups; the partial
  * results are merged through the workspace.
  */
@@ -315,7 +317,6 @@ int sparse_mla_decode(const uint16_t* q_bf16, int32_t num_tokens, int32_t num_he
 size_t sparse_mla_decode_workspace_size(int32_t num_tokens, int32_t num_heads,
                                         int32_t max_row_width, int32_t dv);
 
-/* Description of the last non-OK return on the calling thread ("" if none). */
 /*
  * inv_rope_fp8_quant - the attention output in the form the output projection takes.
  *
@@ -407,6 +408,7 @@ int insert_index_keys(const uint16_t* keys, const int32_t* positions, const floa
                       const int32_t* slot_mapping, int32_t num_rows, const sad_mxfp4_cache* cache,
                       void* stream);
 
+/* Description of the last non-OK return on the calling thread ("" if none). */
 const char* sad_last_error(void);
 
 #ifdef __cplusplus

@@ -916,12 +916,19 @@ def insert_index_keys(idx_pages: dict, keys_bits, positions, cos_sin_cache, rati
 # ---------------------------------------------------------------------------
 
 
-def step(view, cfg, padded_topk, kv_num_pages, idx_num_pages, softmax_scale, tokens=None, attn_sink=None):
+def step(view, cfg, padded_topk, kv_num_pages, idx_num_pages, softmax_scale, tokens=None, attn_sink=None,
+         swa_num_pages=None):
     """Indexer -> top-k -> index build -> attention for one layer.
 
     ``view`` holds numpy inputs (see the workload host view); ``cfg`` gives
-    the shape parameters.  Returns a dict of every intermediate.
+    the shape parameters.  The window rows are read from ``view.swa_pages`` with
+    ``cfg.swa_block_size`` rows per page when the view has a window cache of its own
+    (``swa_num_pages`` pages), else from the compressed rows' pages.  Returns a dict of
+    every intermediate.
     """
+    swa_pages = getattr(view, "swa_pages", None) or view.kv_pages
+    swa_block = getattr(cfg, "swa_block_size", cfg.block)
+    swa_num_pages = kv_num_pages if swa_num_pages is None else swa_num_pages
     T = len(view.token_to_req)
     all_tokens = list(range(T)) if tokens is None else list(tokens)
     if cfg.topk > 0:
@@ -935,10 +942,10 @@ def step(view, cfg, padded_topk, kv_num_pages, idx_num_pages, softmax_scale, tok
         tk = None
     si, lens = build_sparse_indices(
         view.query_start_loc, view.seq_lens, view.token_to_req, view.replay_start,
-        view.swa_bt, cfg.block, kv_num_pages, view.comp_bt, cfg.block, kv_num_pages,
+        view.swa_bt, swa_block, swa_num_pages, view.comp_bt, cfg.block, kv_num_pages,
         tk, cfg.topk, cfg.window, cfg.ratio, padded_topk)
-    o, lse = sparse_mla_decode(view.q, view.kv_pages, view.kv_pages, si, lens, cfg.window,
-                               cfg.block, cfg.block, cfg.d_nope, cfg.d_rope, softmax_scale,
+    o, lse = sparse_mla_decode(view.q, swa_pages, view.kv_pages, si, lens, cfg.window,
+                               swa_block, cfg.block, cfg.d_nope, cfg.d_rope, softmax_scale,
                                attn_sink=attn_sink, tokens=all_tokens,
                                scale_format=getattr(cfg, "kv_format", "f32"))
     return {"topk": tk, "sparse_indices": si, "lens": lens, "out": o, "lse": lse, "tokens": all_tokens}

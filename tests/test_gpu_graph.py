@@ -9,7 +9,7 @@ import torch
 import sparse_attention_decode_build_amd as sad
 from sparse_attention_decode_build_amd import workloads as WL
 
-from gpu_helpers import caches, free, log
+from gpu_helpers import free, idx_cache, kv_caches, log
 
 pytestmark = pytest.mark.gpu
 
@@ -25,14 +25,14 @@ def gpu():
 def _step(wl, layer, outs, stream):
     c = wl.cfg
     L = wl.layers[layer]
-    kv, idx = caches(wl)
-    n_pages = wl.kv_pool.shape[0]
+    swa, comp = kv_caches(wl)
     topk, si, lens, out, ws_i, ws_a = outs
     sad.indexer_topk_sparse_indices(
-        wl.query_start_loc, wl.seq_lens, wl.token_to_req, L.idx_q_values, L.idx_q_scales, L.idx_weights, idx,
-        L.idx_bt, c.ratio, c.topk, wl.replay_start, L.swa_bt, c.block, n_pages, L.comp_bt, c.block, n_pages,
-        c.window, wl.padded_topk, topk_local=topk, out=si, lens=lens, workspace=ws_i, stream=stream)
-    sad.sparse_mla_decode(L.q, kv, kv, si, lens, c.window, wl.padded_topk, wl.softmax_scale, out=out,
+        wl.query_start_loc, wl.seq_lens, wl.token_to_req, L.idx_q_values, L.idx_q_scales, L.idx_weights,
+        idx_cache(wl), L.idx_bt, c.ratio, c.topk, wl.replay_start, L.swa_bt, c.swa_block_size,
+        wl.swa_pool.shape[0], L.comp_bt, c.block, wl.kv_pool.shape[0], c.window, wl.padded_topk,
+        topk_local=topk, out=si, lens=lens, workspace=ws_i, stream=stream)
+    sad.sparse_mla_decode(L.q, swa, comp, si, lens, c.window, wl.padded_topk, wl.softmax_scale, out=out,
                           workspace=ws_a, stream=stream)
 
 
@@ -49,7 +49,7 @@ def _outs(wl):
             torch.empty((T, c.heads, c.dqk), dtype=torch.bfloat16, device=dev), ws_i, ws_a)
 
 
-@pytest.mark.parametrize("name", ["tiny", "b32_8k"])
+@pytest.mark.parametrize("name", ["tiny", "b32_8k", "two_cache_b8_8k"])
 def test_graph_replays_equal_the_eager_step(name):
     log(f"[graph] {name}")
     wl = WL.make_workload(name, "cuda", num_layers=2)

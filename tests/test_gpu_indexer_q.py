@@ -4,7 +4,8 @@ weight fold) against the CPU oracle on the same seeded inputs.
 Bar: bit-exact on the packed E2M1 codes, the e8m0 scale bytes and the folded fp32
 weights.  The codes are integers decided by floating point; both sides take every
 decision in the same precision (fp32 RoPE with separately rounded products, bf16
-rounding, exact Hadamard sums rounded once to fp32, exact exponent rule).
+rounding, the fp32 radix-2 fast Hadamard transform with index bit 0 first, one fp32
+multiply by the scale, exact exponent rule).
 """
 
 import numpy as np

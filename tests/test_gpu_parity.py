@@ -1,18 +1,20 @@
 """GPU parity: every step of the HIP path, called through the C ABI, against the CPU
 oracle on the same seeded input bytes.
 
-Bars: bit-exact for sparse_indices, lens and dequantized rows; top-k sets equal except
-swaps among scores within 1e-5 relative of the oracle's k-th score; indexer logits
-within 1e-5 relative (the per-head dots are exact, only the fp32 head sum rounds);
-attention output within max-abs 5e-3 (bf16 out, fp32 accumulate) and lse within 1e-3.
-Where one bf16 ulp of the exact output exceeds 5e-3 (|o| >= 1, e.g. a token that
-attends to one row, so o = x), the output format alone cannot meet 5e-3 and the bar
-there is one bf16 ulp of the oracle value.
-The "peaky" variant (queries x4) drives outputs towards one or two rows with |x| up to
-~4: there one bf16 rounding of a probability (2^-9 relative, as the PV MFMA takes
-bf16 operands) or of the output (2^-9 |o|) alone exceeds 5e-3.  It is reported
-(max-abs, relative RMS) and held to 5e-3 + 2^-8 * sum_j p_j |x_j|, the bound of one
-bf16 rounding of every weight plus one of the output.
+Bars:
+- sparse_indices and lens: bit-exact on every token, built from the GPU's own top-k (the
+  build is a function of the top-k row, so the two sides see the same input);
+- dequantized rows: bit-exact;
+- top-k: sets equal to the oracle's except swaps among scores within 1e-5 relative of
+  the oracle's k-th score; indexer logits within 1e-5 relative (the per-head dots are
+  exact, only the fp32 head sum rounds);
+- attention output: max(5e-3, half an ulp of the bf16 output + 2^-8 (1 + 2^-6) spread +
+  2^-11 (|o| + spread)) per element, spread = sum_j p_j |x_j - o| (see
+  gpu_helpers.check_attention): beyond the bf16 rounding of the output, the PV MFMA takes
+  every softmax weight rounded to bf16, which moves o by at most 2^-8 spread (bf16's unit roundoff).  Each case
+  reports how many elements exceed the plain 5e-3; lse within 1e-3.
+The "peaky" variant (queries x4) concentrates the weights on a few rows (|x| up to ~4),
+where the weight rounding is the largest term; it is reported separately.
 """
 
 import numpy as np
@@ -23,13 +25,11 @@ import sparse_attention_decode_build_amd as sad
 from oracle import sad_oracle as O
 from sparse_attention_decode_build_amd import workloads as WL
 
-from gpu_helpers import (bf16_to_f64, check_topk, free, gpu_attention, gpu_build, gpu_indexer, log,
-                         oracle_attention, oracle_build, oracle_topk, sample_tokens)
+from gpu_helpers import (ATOL_LSE, bf16_to_f64, check_attention, check_topk, free, gpu_attention, gpu_build,
+                         gpu_fused, gpu_indexer, kv_caches, log, oracle_attention, oracle_build, oracle_gather,
+                         oracle_topk, sample_tokens)
 
 pytestmark = pytest.mark.gpu
-
-ATOL_OUT = 5e-3
-ATOL_LSE = 1e-3
 
 EDGE = WL.Config(
     name="edge", seed=5, window=32, ratio=4, topk=16, heads=16, d_nope=128, d_rope=32, idx_heads=4,
@@ -61,19 +61,23 @@ def _wl(cfg, **kw):
     return WL.make_workload(cfg, "cuda", **kw)
 
 
-def _full_check(wl, view, tokens, sink=None, check_gather=True, bf16_ulp_allowance=False):
-    """Indexer/top-k, index build, gather and attention of `tokens` vs the oracle."""
+def _full_check(wl, view, tokens, sink=None, check_gather=True, label=None):
+    """Every step vs the oracle: indexer logits and top-k on `tokens`; the index build on
+    every token (from the GPU's own top-k), and the fused indexer + build call equal to
+    the two calls on every token; gather on up to 16 of `tokens`; attention on `tokens`."""
     cfg = wl.cfg
+    label = label or cfg.name
     T = wl.num_tokens
     torch.cuda.synchronize()
+    topk_dev = None
     # ---- indexer + top-k
     if not cfg.dense:
         log("[step] indexer_score_topk")
-        topk_g, logits = gpu_indexer(wl)
+        topk_dev, logits = gpu_indexer(wl)
         torch.cuda.synchronize()
-        topk_g = topk_g.cpu().numpy()
+        topk_g = topk_dev.cpu().numpy()
         logits = logits.cpu().numpy()
-        tk_o, scores = oracle_topk(wl, view, tokens)
+        _, scores = oracle_topk(wl, view, tokens)
         swaps = 0
         for i, t in enumerate(tokens):
             sc, valid = scores[i]
@@ -86,51 +90,42 @@ def _full_check(wl, view, tokens, sink=None, check_gather=True, bf16_ulp_allowan
                 assert np.max(np.abs(lg[valid] - ref)) <= 1e-5 * scale, f"logits token {t}"
             swaps += check_topk(topk_g[t], sc, valid, cfg.topk)
         log(f"[ok] indexer/top-k on {len(tokens)} tokens, {swaps} near-tie swaps")
-        # oracle top-k for every token feeds the index build (tokens not sampled get
-        # the GPU-independent oracle result too when cheap)
-        tk_full = np.full((T, cfg.topk), -1, np.int32)
-        tk_full[tokens] = tk_o
-    else:
-        tk_full = None
-    # ---- build_sparse_indices on the oracle's top-k: bit-exact
+    # ---- build_sparse_indices on the GPU's top-k: bit-exact on every token
     log("[step] build_sparse_indices")
-    tk_dev = torch.from_numpy(tk_full).cuda() if tk_full is not None else None
-    si_g, lens_g = gpu_build(wl, tk_dev)
+    si_g, lens_g = gpu_build(wl, topk_dev)
     torch.cuda.synchronize()
-    si_o, lens_o = oracle_build(wl, view, tk_full, tokens=tokens)
-    assert np.array_equal(si_g.cpu().numpy()[tokens], si_o)
-    assert np.array_equal(lens_g.cpu().numpy()[tokens], lens_o)
-    log("[ok] build_sparse_indices bit-exact")
-    si_full = np.full((T, si_o.shape[1]), -1, np.int32)
-    lens_full = np.zeros(T, np.int32)
-    si_full[tokens] = si_o
-    lens_full[tokens] = lens_o
+    si_o, lens_o = oracle_build(wl, view, topk_dev.cpu().numpy() if topk_dev is not None else None)
+    si_np, lens_np = si_g.cpu().numpy(), lens_g.cpu().numpy()
+    assert np.array_equal(si_np, si_o), "sparse_indices differ from the oracle"
+    assert np.array_equal(lens_np, lens_o), "sparse_topk_lens differ from the oracle"
+    log(f"[ok] build_sparse_indices bit-exact on all {T} tokens")
+    # ---- the fused call: the same three outputs, bit for bit, on every token
+    if not cfg.dense:
+        log("[step] indexer_topk_sparse_indices")
+        tk_f, si_f, lens_f = gpu_fused(wl)
+        torch.cuda.synchronize()
+        assert torch.equal(tk_f, topk_dev) and torch.equal(si_f, si_g) and torch.equal(lens_f, lens_g)
+        log("[ok] fused indexer + index build equal to the two calls")
     # ---- gather + dequant: bit-exact
     if check_gather:
         log("[step] gather_dequant_kv")
-        kv, _ = _caches(wl)
+        swa, comp = kv_caches(wl)
         sub = tokens[: min(len(tokens), 16)]
-        si_sub = si_g[torch.as_tensor(sub, device="cuda")].contiguous()
-        lens_sub = lens_g[torch.as_tensor(sub, device="cuda")].contiguous()
-        rows_g = sad.gather_dequant_kv(kv, kv, si_sub, lens_sub, cfg.window, wl.padded_topk)
+        sub_dev = torch.as_tensor(sub, device="cuda")
+        rows_g = sad.gather_dequant_kv(swa, comp, si_g[sub_dev].contiguous(), lens_g[sub_dev].contiguous(),
+                                       cfg.window, wl.padded_topk)
         torch.cuda.synchronize()
-        rows_o = O.gather_dequant(view.kv_pages, view.kv_pages, si_o[: len(sub)], lens_o[: len(sub)],
-                                  cfg.window, cfg.block, cfg.block, cfg.d_nope, cfg.d_rope, cfg.kv_format)
-        got = rows_g.view(torch.int16).cpu().numpy().view(np.uint16)
-        assert np.array_equal(got, rows_o)
+        rows_o = oracle_gather(wl, view, si_o[sub], lens_o[sub])
+        assert np.array_equal(rows_g.view(torch.int16).cpu().numpy().view(np.uint16), rows_o)
         log(f"[ok] gather_dequant_kv bit-exact on {len(sub)} tokens")
     # ---- attention on the (bit-identical) index rows
     log("[step] sparse_mla_decode")
     sink_dev = None if sink is None else torch.from_numpy(sink.astype(np.float32)).cuda()
     out_g, lse_g = gpu_attention(wl, si_g, lens_g, sink=sink_dev, with_lse=True)
     torch.cuda.synchronize()
-    o_o, lse_o, mass = oracle_attention(wl, view, si_full, lens_full, tokens, sink=sink, return_mass=True)
+    o_o, lse_o = oracle_attention(wl, view, si_o, lens_o, tokens, sink=sink)
     got = bf16_to_f64(out_g)[tokens]
-    err = np.abs(got - o_o)
-    rms = float(np.sqrt(np.mean((got - o_o) ** 2)) / max(np.sqrt(np.mean(o_o ** 2)), 1e-30))
-    log(f"[report] attention max-abs {err.max():.3e} rel-rms {rms:.3e} max|o| {np.abs(o_o).max():.3f}")
-    tol = np.maximum(ATOL_OUT, _bf16_ulp(o_o)) + (2.0 ** -8 * mass if bf16_ulp_allowance else 0.0)
-    assert np.all(err <= tol)
+    check_attention(wl, view, tokens, got, o_o, si_o, lens_o, sink=sink, label=label)
     lg = lse_g.cpu().numpy()[tokens]
     fin = np.isfinite(lse_o)
     assert np.array_equal(np.isfinite(lg), fin)
@@ -138,23 +133,16 @@ def _full_check(wl, view, tokens, sink=None, check_gather=True, bf16_ulp_allowan
     return si_g, lens_g, out_g
 
 
-def _bf16_ulp(x):
-    """Spacing of bfloat16 numbers at |x| (8 significant bits)."""
-    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
-    return np.ldexp(1.0, (e - 7).astype(np.int64))
-
-
-def _caches(wl):
-    cfg = wl.cfg
-    return (sad.KvCache(wl.kv_pool, cfg.block, cfg.d_nope, cfg.d_rope, WL.kv_scale_format(cfg)),
-            sad.IndexerCache(wl.idx_pool, cfg.idx_block, cfg.idx_dim))
-
-
 # ---------------------------------------------------------------------------- small
 
 
-@pytest.mark.parametrize("name", ["tiny", "b32_8k", "tiny_native", "b32_8k_native"])
+@pytest.mark.parametrize("name", ["tiny", "b32_8k", "tiny_native", "b32_8k_native", "two_cache_tiny",
+                                  "two_cache_b8_8k"])
 def test_small_config_every_step(name):
+    """Every step on every token.  The two_cache_* workloads keep the window rows in a pool
+    of their own with 64-row pages and the compressed rows in 16-row pages ([backend]
+    forward_deepseek_v4_decode: k_cache / extra_k_cache), so the index build maps the two
+    segments through different page sizes and the gather and attention read two pools."""
     wl = _wl(name)
     view = WL.host_view(wl)
     _full_check(wl, view, list(range(wl.num_tokens)))
@@ -169,11 +157,11 @@ def test_tiny_sparse_equals_dense_selfcheck():
     assert int(lens[0]) == 64
 
 
-@pytest.mark.parametrize("name", ["tiny", "b32_8k", "tiny_native"])
+@pytest.mark.parametrize("name", ["tiny", "b32_8k", "tiny_native", "two_cache_tiny"])
 def test_peaky_queries(name):
     wl = _wl(name, q_scale=4.0)
     view = WL.host_view(wl)
-    _full_check(wl, view, list(range(wl.num_tokens)), check_gather=False, bf16_ulp_allowance=True)
+    _full_check(wl, view, list(range(wl.num_tokens)), check_gather=False, label=f"{name} peaky")
     free(wl)
 
 
@@ -195,9 +183,9 @@ def test_edge_batch():
 @pytest.mark.parametrize("heads,requests", [(40, 256), (72, 128), (96, 128), (120, 128), (72, 4), (120, 3)])
 def test_head_counts_with_partial_head_groups(heads, requests):
     """Head counts whose last group of 64 heads is partial: a head block with absent
-    heads (40, 72, 120) or an idle one (96).  With 256 or more (token, head group)
-    pairs one workgroup covers a token's columns and stages O through LDS; with a few
-    tokens the columns are split and merged.  The rows after the output are untouched."""
+    heads (40, 72, 120) or an idle one (96).  With many (token, head group) pairs one
+    workgroup covers a token's columns; with a few tokens the columns are split and
+    merged.  The rows after the output are untouched."""
     cfg = WL.with_overrides(WL.CONFIGS["b32_8k"], name=f"h{heads}_r{requests}", heads=heads,
                             groups=((requests, 1, 512, 0),))
     wl = _wl(cfg)
@@ -208,9 +196,9 @@ def test_head_counts_with_partial_head_groups(heads, requests):
     T, H, D = out.shape
     guard = 4096
     buf = torch.full((T * H * D + guard,), -7, dtype=torch.int16, device="cuda")
-    kv, _ = _caches(wl)
+    swa, comp = kv_caches(wl)
     out2 = buf[: T * H * D].view(torch.bfloat16).view(T, H, D)
-    sad.sparse_mla_decode(wl.layers[0].q, kv, kv, si, lens, cfg.window, wl.padded_topk, wl.softmax_scale,
+    sad.sparse_mla_decode(wl.layers[0].q, swa, comp, si, lens, cfg.window, wl.padded_topk, wl.softmax_scale,
                           out=out2)
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16)), "same launch, same bits"
@@ -239,19 +227,24 @@ def test_indexer_key_dim_and_page_size(base, idx_dim, idx_block):
     free(wl)
 
 
+def _punch(table, frac, seed, past_pool):
+    """Set a seeded fraction of a block table's entries to -1 and one to a page past the pool."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    holes = torch.rand(table.shape, generator=g) < frac
+    table[holes.to(table.device)] = -1
+    table[0, 0] = past_pool
+
+
 def test_edge_fail_closed_tables():
     """Unbacked pages, ids past the pool and random local ids (incl. -1 and >= n_c)."""
     wl = _wl(EDGE)
     cfg = wl.cfg
     L = wl.layers[0]
-    g = torch.Generator(device="cpu").manual_seed(3)
-    holes = torch.rand(L.swa_bt.shape, generator=g) < 0.2
-    L.swa_bt[holes.cuda()] = -1
-    holes = torch.rand(L.comp_bt.shape, generator=g) < 0.2
-    L.comp_bt[holes.cuda()] = -1
-    L.comp_bt[0, 0] = wl.kv_pool.shape[0] + 3  # past the pool
+    _punch(L.swa_bt, 0.2, 3, wl.swa_pool.shape[0] + 3)
+    _punch(L.comp_bt, 0.2, 4, wl.kv_pool.shape[0] + 3)
     view = WL.host_view(wl)
     T = wl.num_tokens
+    g = torch.Generator(device="cpu").manual_seed(5)
     tk = torch.randint(-3, 80, (T, cfg.topk + 5), generator=g, dtype=torch.int32)
     si_g, lens_g = sad.build_sparse_indices(
         wl.query_start_loc, wl.seq_lens, wl.token_to_req, wl.replay_start, L.swa_bt, cfg.block,
@@ -265,7 +258,26 @@ def test_edge_fail_closed_tables():
     out_g, _ = gpu_attention(wl, si_g, lens_g)
     torch.cuda.synchronize()
     o_o, _ = oracle_attention(wl, view, si_o, lens_o, list(range(T)))
-    assert np.all(np.abs(bf16_to_f64(out_g) - o_o) <= np.maximum(ATOL_OUT, _bf16_ulp(o_o)))
+    check_attention(wl, view, list(range(T)), bf16_to_f64(out_g), o_o, si_o, lens_o, label="edge holes")
+
+
+@pytest.mark.parametrize("name", ["edge", "b32_8k", "two_cache_b8_8k"])
+def test_indexer_table_holes(name):
+    """Unbacked indexer key pages (-1) and a page past the indexer pool inside n_c ([ops]
+    read_deepseek_v4_indexer_mxfp4_cache masks them; [backend] safe_page_ids fails closed):
+    their rows score -inf, are never chosen (top-k pads with -1 when fewer than k rows are
+    backed), and the fused call still equals the two calls; holes in the window and
+    compressed tables too."""
+    cfg = EDGE if name == "edge" else WL.with_overrides(WL.CONFIGS[name], groups=((6, 1, 8192, 0),))
+    wl = _wl(cfg)
+    L = wl.layers[0]
+    _punch(L.idx_bt, 0.3, 9, wl.idx_pool.shape[0] + 5)
+    if name == "edge":
+        _punch(L.swa_bt, 0.2, 10, wl.swa_pool.shape[0] + 1)
+        _punch(L.comp_bt, 0.2, 11, wl.kv_pool.shape[0] + 1)
+    view = WL.host_view(wl)
+    _full_check(wl, view, list(range(wl.num_tokens)), check_gather=name != "b32_8k", label=f"{name} idx holes")
+    free(wl)
 
 
 def test_nothing_attended_gives_zero_and_neg_inf_lse():
@@ -282,7 +294,7 @@ def test_nothing_attended_gives_zero_and_neg_inf_lse():
 
 @pytest.mark.parametrize("window,padded", [(3, 2), (0, 5), (7, 0), (0, 0), (5, 64)])
 def test_narrow_index_rows(window, padded):
-    """Index rows narrower than one wave's 8 slot ids (and an empty row)."""
+    """Index rows narrower than one tile's slot ids (and an empty row)."""
     wl = _wl("tiny")
     cfg = wl.cfg
     view = WL.host_view(wl)
@@ -293,17 +305,17 @@ def test_narrow_index_rows(window, padded):
           + rng.integers(0, cfg.block, (T, window + padded))).astype(np.int32)
     si[rng.random(si.shape) < 0.2] = -1
     lens = rng.integers(0, padded + 1, T).astype(np.int32)
-    kv, _ = _caches(wl)
+    swa, comp = kv_caches(wl)
     L = wl.layers[0]
     lse = torch.empty((T, cfg.heads), dtype=torch.float32, device="cuda")
-    out = sad.sparse_mla_decode(L.q, kv, kv, torch.from_numpy(si).cuda(), torch.from_numpy(lens).cuda(),
+    out = sad.sparse_mla_decode(L.q, swa, comp, torch.from_numpy(si).cuda(), torch.from_numpy(lens).cuda(),
                                 window, padded, wl.softmax_scale, lse=lse)
     torch.cuda.synchronize()
-    o_o, lse_o = O.sparse_mla_decode(view.q, view.kv_pages, view.kv_pages, si, lens, window, cfg.block,
+    o_o, lse_o = O.sparse_mla_decode(view.q, view.swa_pages, view.kv_pages, si, lens, window, cfg.block,
                                      cfg.block, cfg.d_nope, cfg.d_rope, wl.softmax_scale,
                                      tokens=list(range(T)))
-    err = np.abs(bf16_to_f64(out) - o_o)
-    assert np.all(err <= np.maximum(ATOL_OUT, _bf16_ulp(o_o)))
+    check_attention(wl, view, list(range(T)), bf16_to_f64(out), o_o, si, lens, label=f"narrow {window}+{padded}",
+                    window=window)
     lg = lse.cpu().numpy()
     fin = np.isfinite(lse_o)
     assert np.array_equal(np.isfinite(lg), fin)
@@ -319,8 +331,8 @@ def test_empty_batch_is_a_no_op():
                                         L.swa_bt[:0], cfg.block, 1, L.comp_bt[:0], cfg.block, 1, None, 0,
                                         cfg.window, cfg.ratio, wl.padded_topk)
     assert si.shape == (0, cfg.window + wl.padded_topk)
-    kv, _ = _caches(wl)
-    out = sad.sparse_mla_decode(L.q[:0], kv, kv, si, lens, cfg.window, wl.padded_topk, 0.1)
+    swa, comp = kv_caches(wl)
+    out = sad.sparse_mla_decode(L.q[:0], swa, comp, si, lens, cfg.window, wl.padded_topk, 0.1)
     assert out.shape[0] == 0
 
 
@@ -365,35 +377,30 @@ def test_deterministic():
 
 
 @pytest.mark.slow
-def test_b128_64k_full_size_sampled():
-    """128 requests at 64K context over a ~196 GB pool: all tokens run on the GPU in
-    the benchmark's launch configuration; index rows are compared on every token and
-    the oracle recomputes scores, top-k, rows and attention for sampled tokens."""
-    wl = _wl("b128_64k")
-    tokens = [0, 17, 63, 127]
-    view = WL.host_view(wl, reqs=tokens)
-    all_view = view
-    _full_check(wl, all_view, tokens)
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,q_scale", [("b128_64k", 1.0), ("b128_64k_native", 1.0), ("b128_64k", 4.0)])
+def test_b128_64k_full_size_every_token(name, q_scale):
+    """128 requests at 64K context over a ~196 GB pool (~170 GB for the native record), in
+    the benchmark's launch configuration: every token's logits, top-k, index row, fused
+    call and attention output against the oracle (rows of 16 tokens for the gather).
+    q_scale 4 is the peaky variant."""
+    wl = _wl(name, q_scale=q_scale)
+    view = WL.host_view(wl)
+    _full_check(wl, view, list(range(wl.num_tokens)), label=f"{name} q x{q_scale:g}")
     free(wl)
 
 
 @pytest.mark.slow
-def test_b128_64k_native_record_full_size_sampled():
-    """The pages' native KV record (448 fp8 + 64 bf16, ue8m0 scales) at 128 requests x
-    64K context over a ~170 GB pool, in the benchmark's launch configuration."""
-    wl = _wl("b128_64k_native")
-    tokens = [0, 45, 127]
-    view = WL.host_view(wl, reqs=tokens)
-    _full_check(wl, view, tokens)
-    free(wl)
-
-
-@pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_mixed_batch_sampled():
+    """The mixed batch (64 decode tokens, then 4 prefill chunks of 4096): the index build on
+    all 16,448 tokens; indexer, top-k and attention on all 64 decode tokens plus 256 seeded
+    prefill tokens and every prefill token at p = 0, with a window clipped by replay_start
+    or with fewer than k compressed rows."""
     wl = _wl("mixed")
-    tokens = sample_tokens(wl, n_decode=4, n_prefill=8)
-    reqs = sorted(set(wl.token_to_req.cpu().numpy()[tokens].tolist()))
-    view = WL.host_view(wl, reqs=reqs)
+    tokens = sample_tokens(wl, n_decode=64, n_prefill=256)
+    log(f"[case] mixed: {len(tokens)} sampled tokens")
+    view = WL.host_view(wl)
     _full_check(wl, view, tokens)
     free(wl)
 
@@ -406,28 +413,20 @@ def test_dense_1m_full():
     free(wl)
 
 
-@pytest.mark.parametrize("name", ["tiny", "b32_8k", "edge", "edge_holes", "b128_64k", "long_ctx"])
+@pytest.mark.parametrize("name", ["edge_holes", "long_ctx"])
 def test_fused_indexer_and_index_build_equal_the_two_calls(name):
     # indexer_topk_sparse_indices is defined as indexer_score_topk then build_sparse_indices:
     # all three outputs bit-identical to the two-call path (with holes in both block tables
     # and a page past the pool in the "edge_holes" case).
-    cfg = EDGE if name.startswith("edge") else LONG if name == "long_ctx" else name
+    cfg = EDGE if name.startswith("edge") else LONG
     wl = _wl(cfg)
-    c = wl.cfg
     L0 = wl.layers[0]
     if name == "edge_holes":
-        g = torch.Generator(device="cpu").manual_seed(7)
-        L0.swa_bt[(torch.rand(L0.swa_bt.shape, generator=g) < 0.2).cuda()] = -1
-        L0.comp_bt[(torch.rand(L0.comp_bt.shape, generator=g) < 0.2).cuda()] = -1
-        L0.comp_bt[0, 0] = wl.kv_pool.shape[0] + 3
-    _, idx = _caches(wl)
-    n_pages = wl.kv_pool.shape[0]
+        _punch(L0.swa_bt, 0.2, 7, wl.swa_pool.shape[0] + 3)
+        _punch(L0.comp_bt, 0.2, 8, wl.kv_pool.shape[0] + 3)
     tk_a, _ = gpu_indexer(wl, logits=False)
     si_a, lens_a = gpu_build(wl, tk_a)
-    tk_b, si_b, lens_b = sad.indexer_topk_sparse_indices(
-        wl.query_start_loc, wl.seq_lens, wl.token_to_req, L0.idx_q_values, L0.idx_q_scales, L0.idx_weights, idx,
-        L0.idx_bt, c.ratio, c.topk, wl.replay_start, L0.swa_bt, c.block, n_pages, L0.comp_bt, c.block, n_pages,
-        c.window, wl.padded_topk)
+    tk_b, si_b, lens_b = gpu_fused(wl)
     torch.cuda.synchronize()
     assert torch.equal(tk_a, tk_b)
     assert torch.equal(si_a, si_b)
