@@ -40,6 +40,9 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 WORKLOAD = WL.HEADLINE
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_b128_64k_traffic.md")
+# the headline attention kernel (512 fp8 + 64 bf16 latent rows) and its source file
+ATTN_KERNEL = "mla_dsplit_kernel"
+ATTN_SRC = "attention_dsplit.hip"
 
 
 def log(*a):
@@ -141,14 +144,14 @@ def measured_traffic():
     the kernel source changed since they were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    src = open(os.path.join(ROOT, "sparse_attention_decode_build_amd", "csrc", "attention.hip"), "rb").read()
+    src = open(os.path.join(ROOT, "sparse_attention_decode_build_amd", "csrc", ATTN_SRC), "rb").read()
     sha = hashlib.sha256(src).hexdigest()
     vals = {}
     for line in open(TRAFFIC_FILE):
         if ":" in line and line.strip().startswith("- "):
             k, v = line.strip()[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
-    if vals.get("attention.hip sha256") != sha:
+    if vals.get(f"{ATTN_SRC} sha256") != sha:
         return None
     try:
         return float(vals["bytes per launch"])
@@ -247,7 +250,7 @@ def summarize_traffic(fetch_dir: str, write_dir: str) -> int:
     """Attention kernel HBM traffic per launch from two rocprofv3 --pmc runs of
     `bench.py --copy-calibration-gib 1 ...` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
     each scaled by the same counter on the 1 GiB copy kernel."""
-    copy_pat, attn_pat = "MulFunctor", "sparse_mla_kernel<512, 64"
+    copy_pat, attn_pat = "MulFunctor", ATTN_KERNEL
     cal = float(1 << 30)
     cf, _ = _pmc_mean(fetch_dir, "FETCH_SIZE", copy_pat, largest=True)
     cw, _ = _pmc_mean(write_dir, "WRITE_SIZE", copy_pat, largest=True)
@@ -255,12 +258,12 @@ def summarize_traffic(fetch_dir: str, write_dir: str) -> int:
     aw, nw = _pmc_mean(write_dir, "WRITE_SIZE", attn_pat)
     kf, kw = cal / (cf * 1024.0), cal / (cw * 1024.0)
     fetch_b, write_b = af * 1024.0 * kf, aw * 1024.0 * kw
-    src = open(os.path.join(ROOT, "sparse_attention_decode_build_amd", "csrc", "attention.hip"), "rb").read()
-    print(f"- attention.hip sha256: `{hashlib.sha256(src).hexdigest()}`")
+    src = open(os.path.join(ROOT, "sparse_attention_decode_build_amd", "csrc", ATTN_SRC), "rb").read()
+    print(f"- {ATTN_SRC} sha256: `{hashlib.sha256(src).hexdigest()}`")
     print(f"- copy kernel (1 GiB read + 1 GiB written): FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB "
           f"-> scale factors {kf:.4f} (fetch), {kw:.4f} (write)")
-    print(f"- sparse_mla_kernel FETCH_SIZE mean {af:.0f} KiB over {nf} dispatches -> {fetch_b / 1e6:.2f} MB")
-    print(f"- sparse_mla_kernel WRITE_SIZE mean {aw:.0f} KiB over {nw} dispatches -> {write_b / 1e6:.2f} MB")
+    print(f"- {ATTN_KERNEL} FETCH_SIZE mean {af:.0f} KiB over {nf} dispatches -> {fetch_b / 1e6:.2f} MB")
+    print(f"- {ATTN_KERNEL} WRITE_SIZE mean {aw:.0f} KiB over {nw} dispatches -> {write_b / 1e6:.2f} MB")
     print(f"- bytes per launch: {fetch_b + write_b:.0f}")
     return 0
 
@@ -532,10 +535,10 @@ def main() -> int:
                    "tokens_per_step": T, "layers_rotated": args.layers},
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "kernel": "sparse_mla_decode (sparse_mla_kernel)"},
+                     "kernel": f"sparse_mla_decode ({ATTN_KERNEL})"},
         "roofline_hbm": {"bound": "hbm", "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": attn_gbs / PEAK_HBM_GBS, "traffic": traffic,
-                         "kernel": "sparse_mla_decode (sparse_mla_kernel)"},
+                         "kernel": f"sparse_mla_decode ({ATTN_KERNEL})"},
         "kernels_ms": {"indexer_topk_sparse_indices": ms_idx, "sparse_mla_decode": ms_attn},
         "unfused_step": {"ms_per_step": ms_step3, "tokens_per_s": T / (ms_step3 * 1e-3),
                          "kernels_ms": {"indexer_score_topk": seg3[0], "build_sparse_indices": seg3[1],

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsad.so")
 SOURCES = ("abi.hip", "build_indices.hip", "indexer.hip", "indexer_q.hip", "gather.hip", "attention.hip",
-           "out_quant.hip", "cache_write.hip")
+           "attention_dsplit.hip", "out_quant.hip", "cache_write.hip")
 ARCH = "gfx950"
 
 # hipcc flags: gfx950 only; packed-FP32 VALU ops disabled (hipcc's host pass warns
@@ -30,7 +30,8 @@ FLAGS = [
     f"-I{CSRC}",
 ]
 # Per-file extra flags.  The indexer's MFMA results feed VALU work right away, so its
-# MFMAs write VGPRs (the attention kernel keeps its long-lived accumulators in AGPRs).
+# MFMAs write VGPRs; the dim-split attention kernel keeps its accumulators in VGPRs and
+# its Q^T operand in AGPRs (the other attention kernel keeps its accumulators in AGPRs).
 EXTRA_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 

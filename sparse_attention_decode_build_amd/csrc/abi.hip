@@ -26,6 +26,23 @@ int check_launch(const char* what) {
   return SAD_OK;
 }
 
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();  // a failed query must not read as a later launch failure
+    return 256;
+  }
+  int n = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  __atomic_store_n(&cached[dev], n, __ATOMIC_RELAXED);
+  return n;
+}
+
 }  // namespace sad
 
 extern "C" const char* sad_last_error(void) { return sad::g_error; }

@@ -38,6 +38,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "lds_dma.h"
 #include "sad_internal.h"
 
 namespace sad {
@@ -63,30 +64,6 @@ __device__ inline void lds_barrier() {
 // dequantized rows exactly zero with no masking in the dequant.
 __device__ __align__(16) uint8_t kZeroRow[1024];
 
-// Direct global -> LDS loads.  They are issued as inline asm so that the compiler
-// neither tracks them nor inserts its own waits for them (its LDS-DMA alias tracking
-// is lost across the tile loop and would drain every in-flight tile); the kernel waits
-// for them explicitly with vmcnt, which counts vector-memory ops in issue order.  The
-// LDS destination of lane i is m0 + 16*i (dwordx4) or m0 + 4*i (dword).
-__device__ inline void dma_x4(const void* src, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds_wave_base), "v"(src) : "memory", "m0");
-}
-// Same with an immediate byte offset on the global address.  The instruction adds its
-// offset to the LDS address as well, so M0 is lowered by the same amount.
-template <int OFF>
-__device__ inline void dma_x4_off(const void* src, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%2"
-               :: "s"(lds_wave_base - OFF), "v"(src), "n"(OFF) : "memory", "m0");
-}
-__device__ inline void dma_x1(const void* src, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(lds_wave_base), "v"(src) : "memory", "m0");
-}
-template <int N>
-__device__ inline void wait_vmem() {
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
 // Scheduling hint for a chain of N MFMAs that each consume R LDS reads: keep
 // kLdsAhead reads in flight ahead of the chain, then one MFMA per R reads.
 constexpr int kLdsAhead = 8;
@@ -113,18 +90,6 @@ __device__ inline void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <typename T>
-__device__ inline uint32_t lds_addr(const T* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) T*)p;
-}
-
-struct KvDesc {
-  const uint8_t* pool;
-  int64_t stride;
-  int64_t num_pages;
-  int block;
-  int block_shift;  // log2(block)
-};
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
@@ -937,11 +902,19 @@ __global__ __launch_bounds__(DQK) void combine_kernel(const float* __restrict__ 
     lse_out[th] = den > 0.0f ? (mref + log2f(den)) * kLn2 : -INFINITY;
 }
 
-int choose_splits(int T, int num_heads, int max_cols, int dqk, int rowb) {
+// Bytes of one cached row (values and scales) of the latent shape whose row has dqk
+// values: 512+64 with fp32 scales, the native 448+64 with 8 scale bytes, 128+32 with fp32.
+int row_bytes_of(int dqk) {
+  return dqk == 576 ? 512 + 128 + 32 : dqk == 512 ? 448 + 128 + 8 : dqk == 160 ? 128 + 64 + 8 : 2 * dqk;
+}
+
+int choose_splits(int T, int num_heads, int max_cols, int dqk) {
+  const int cus = num_cus();
   const int units = T * ((num_heads + 63) / 64);  // workgroups without splitting
-  if (units <= 0 || units >= kNumCUs) return 1;
+  if (units <= 0 || units >= cus) return 1;
+  const int rowb = row_bytes_of(dqk);
   const int tiles = (max_cols + kTile - 1) / kTile;
-  int s = (kNumCUs + units - 1) / units;
+  int s = (cus + units - 1) / units;
   s = std::min(s, std::max(1, tiles / 4));
   // keep the partials' traffic (write + read of 128 heads x dqk fp32) below the rows'
   const int64_t row_bytes = (int64_t)max_cols * rowb;
@@ -950,12 +923,19 @@ int choose_splits(int T, int num_heads, int max_cols, int dqk, int rowb) {
   return std::max(1, s);
 }
 
+// Workspace bytes of `splits` column splits (0 without splitting): the partials o / l
+// (fp32 [splits, T, H, dqk]) and log2-sum-exp (fp32 [splits, T, H]).
+size_t split_workspace_bytes(int splits, int T, int H, int dqk) {
+  if (splits <= 1) return 0;
+  const size_t n = (size_t)splits * T * H;
+  return (n * dqk + n) * sizeof(float);
+}
+
 template <int DN, int DR>
 int launch(const uint16_t* q, int T, int H, const KvDesc& s, const KvDesc& c, const int32_t* si,
            const int32_t* lens, int W, int P, float scale, const float* sink, uint16_t* out,
-           float* lse, void* ws, size_t ws_bytes, hipStream_t st) {
+           float* lse, void* ws, size_t ws_bytes, int splits, hipStream_t st) {
   using Sh = Shape<DN, DR>;
-  const int splits = choose_splits(T, H, W + P, Sh::DQK, Sh::ROWB);
   float* part_o = nullptr;
   float* part_lse = nullptr;
   if (splits > 1) {
@@ -966,26 +946,79 @@ int launch(const uint16_t* q, int T, int H, const KvDesc& s, const KvDesc& c, co
     part_o = reinterpret_cast<float*>(ws);
     part_lse = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + po);
   }
-  const int head_groups = (H + 63) / 64;
-  const int pairs = T * splits;
-  const int blocks = (pairs + 7) / 8 * 8 * head_groups;
-  // one cache for both segments (the usual case): wave-uniform row descriptors
-  const bool one = s.pool == c.pool && s.stride == c.stride && s.num_pages == c.num_pages && s.block == c.block;
-  // the fp32 sum of the weights is only kept for the log-sum-exp outputs
-  const bool want_lse = lse != nullptr || splits > 1;
-  auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kThreads), 0, st, q, T, H, s, c, si, lens, W, P,
-                       scale * kLog2e, sink, out, lse, part_o, part_lse, splits, head_groups);
-  };
-  if (one)
-    want_lse ? go(sparse_mla_kernel<DN, DR, true, true>) : go(sparse_mla_kernel<DN, DR, true, false>);
-  else
-    want_lse ? go(sparse_mla_kernel<DN, DR, false, true>) : go(sparse_mla_kernel<DN, DR, false, false>);
-  int rc = check_launch("sparse_mla_decode(attention)");
+  int rc;
+  if constexpr (DN == 512) {
+    // the headline row: the dim-split kernel
+    rc = launch_mla_dsplit(q, T, H, s, c, si, lens, W, P, scale, sink, out, lse, part_o, part_lse, splits, st);
+  } else {
+    const int head_groups = (H + 63) / 64;
+    const int pairs = T * splits;
+    const int blocks = (pairs + 7) / 8 * 8 * head_groups;
+    // one cache for both segments (the usual case): wave-uniform row descriptors
+    const bool one = s.pool == c.pool && s.stride == c.stride && s.num_pages == c.num_pages && s.block == c.block;
+    // the fp32 sum of the weights is only kept for the log-sum-exp outputs
+    const bool want_lse = lse != nullptr || splits > 1;
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kThreads), 0, st, q, T, H, s, c, si, lens, W, P,
+                         scale * kLog2e, sink, out, lse, part_o, part_lse, splits, head_groups);
+    };
+    if (one)
+      want_lse ? go(sparse_mla_kernel<DN, DR, true, true>) : go(sparse_mla_kernel<DN, DR, true, false>);
+    else
+      want_lse ? go(sparse_mla_kernel<DN, DR, false, true>) : go(sparse_mla_kernel<DN, DR, false, false>);
+    rc = check_launch("sparse_mla_decode(attention)");
+  }
   if (rc != SAD_OK || splits == 1) return rc;
   hipLaunchKernelGGL((combine_kernel<Sh::DQK>), dim3(H, T), dim3(Sh::DQK), 0, st, part_o, part_lse,
                      splits, T, H, sink, out, lse);
   return check_launch("sparse_mla_decode(combine)");
+}
+
+// Body of sparse_mla_decode.
+int mla_decode_entry(const char* name, const uint16_t* q_bf16, int32_t num_tokens, int32_t num_heads,
+                     const sad_kv_cache* swa, const sad_kv_cache* comp, const int32_t* sparse_indices,
+                     const int32_t* sparse_topk_lens, int32_t window_size, int32_t padded_topk,
+                     float softmax_scale, const float* attn_sink, uint16_t* out_bf16, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  int rc = check_kv_cache(swa, "sparse_mla_decode(swa)");
+  if (rc != SAD_OK) return rc;
+  rc = check_kv_cache(comp, "sparse_mla_decode(comp)");
+  if (rc != SAD_OK) return rc;
+  SAD_CHECK(swa->d_nope == comp->d_nope && swa->d_rope == comp->d_rope &&
+                swa->scale_format == comp->scale_format,
+            SAD_EINVAL, "%s: swa and comp caches must share (d_nope, d_rope, scale_format)", name);
+  SAD_CHECK(num_tokens >= 0 && window_size >= 0 && padded_topk >= 0, SAD_EINVAL, "%s: negative size", name);
+  SAD_CHECK(num_heads >= 8 && num_heads <= 128 && num_heads % 8 == 0, SAD_EUNSUPPORTED,
+            "%s: num_heads %d unsupported (multiple of 8, <= 128)", name, num_heads);
+  SAD_CHECK(num_tokens < 65536, SAD_EINVAL, "%s: num_tokens must be < 65536", name);
+  if (num_tokens == 0) return SAD_OK;
+  SAD_CHECK(q_bf16 && (sparse_indices || window_size + padded_topk == 0) && sparse_topk_lens && out_bf16,
+            SAD_EINVAL, "%s: NULL pointer argument", name);
+  SAD_CHECK(((uintptr_t)q_bf16 & 15) == 0 && ((uintptr_t)out_bf16 & 15) == 0, SAD_EINVAL,
+            "%s: q and out must be 16-byte aligned", name);
+  SAD_CHECK(((uintptr_t)workspace & 15) == 0, SAD_EINVAL, "%s: workspace must be 16-byte aligned", name);
+  const int dqk = swa->d_nope + swa->d_rope;
+  const int splits = choose_splits(num_tokens, num_heads, window_size + padded_topk, dqk);
+  const size_t need = split_workspace_bytes(splits, num_tokens, num_heads, dqk);
+  SAD_CHECK(need == 0 || (workspace != nullptr && workspace_bytes >= need), SAD_EWORKSPACE,
+            "%s: workspace needs %zu bytes, got %zu", name, need, workspace_bytes);
+  KvDesc s{(const uint8_t*)swa->pool, swa->page_stride, swa->num_pages, swa->block_size,
+           __builtin_ctz(swa->block_size)};
+  KvDesc c{(const uint8_t*)comp->pool, comp->page_stride, comp->num_pages, comp->block_size,
+           __builtin_ctz(comp->block_size)};
+  hipStream_t st = (hipStream_t)stream;
+  if (swa->d_nope == 512)
+    return launch<512, 64>(q_bf16, num_tokens, num_heads, s, c, sparse_indices, sparse_topk_lens,
+                           window_size, padded_topk, softmax_scale, attn_sink, out_bf16, lse,
+                           workspace, workspace_bytes, splits, st);
+  if (swa->d_nope == 448)
+    return launch<448, 64>(q_bf16, num_tokens, num_heads, s, c, sparse_indices, sparse_topk_lens,
+                           window_size, padded_topk, softmax_scale, attn_sink, out_bf16, lse,
+                           workspace, workspace_bytes, splits, st);
+  return launch<128, 32>(q_bf16, num_tokens, num_heads, s, c, sparse_indices, sparse_topk_lens,
+                         window_size, padded_topk, softmax_scale, attn_sink, out_bf16, lse,
+                         workspace, workspace_bytes, splits, st);
 }
 
 }  // namespace
@@ -996,12 +1029,8 @@ using namespace sad;
 extern "C" size_t sparse_mla_decode_workspace_size(int32_t num_tokens, int32_t num_heads,
                                                    int32_t max_row_width, int32_t dv) {
   if (num_tokens <= 0 || num_heads <= 0 || max_row_width <= 0 || dv <= 0) return 0;
-  // value bytes per cached row for the supported latent shapes
-  const int rowb = dv == 576 ? 640 : (dv == 160 ? 192 : 2 * dv);
-  const int splits = choose_splits(num_tokens, num_heads, max_row_width, dv, rowb);
-  if (splits <= 1) return 0;
-  const size_t n = (size_t)splits * num_tokens * num_heads;
-  return (n * dv + n) * sizeof(float);
+  return split_workspace_bytes(choose_splits(num_tokens, num_heads, max_row_width, dv), num_tokens, num_heads,
+                               dv);
 }
 
 extern "C" int sparse_mla_decode(const uint16_t* q_bf16, int32_t num_tokens, int32_t num_heads,
@@ -1010,40 +1039,7 @@ extern "C" int sparse_mla_decode(const uint16_t* q_bf16, int32_t num_tokens, int
                                  int32_t window_size, int32_t padded_topk, float softmax_scale,
                                  const float* attn_sink, uint16_t* out_bf16, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream) {
-  clear_error();
-  int rc = check_kv_cache(swa, "sparse_mla_decode(swa)");
-  if (rc != SAD_OK) return rc;
-  rc = check_kv_cache(comp, "sparse_mla_decode(comp)");
-  if (rc != SAD_OK) return rc;
-  SAD_CHECK(swa->d_nope == comp->d_nope && swa->d_rope == comp->d_rope &&
-                swa->scale_format == comp->scale_format,
-            SAD_EINVAL, "sparse_mla_decode: swa and comp caches must share (d_nope, d_rope, scale_format)");
-  SAD_CHECK(num_tokens >= 0 && window_size >= 0 && padded_topk >= 0, SAD_EINVAL,
-            "sparse_mla_decode: negative size");
-  SAD_CHECK(num_heads >= 8 && num_heads <= 128 && num_heads % 8 == 0, SAD_EUNSUPPORTED,
-            "sparse_mla_decode: num_heads %d unsupported (multiple of 8, <= 128)", num_heads);
-  SAD_CHECK(num_tokens < 65536, SAD_EINVAL, "sparse_mla_decode: num_tokens must be < 65536");
-  if (num_tokens == 0) return SAD_OK;
-  SAD_CHECK(q_bf16 && (sparse_indices || window_size + padded_topk == 0) && sparse_topk_lens && out_bf16,
-            SAD_EINVAL, "sparse_mla_decode: NULL pointer argument");
-  SAD_CHECK(((uintptr_t)q_bf16 & 15) == 0 && ((uintptr_t)out_bf16 & 15) == 0, SAD_EINVAL,
-            "sparse_mla_decode: q and out must be 16-byte aligned");
-  SAD_CHECK(((uintptr_t)workspace & 15) == 0, SAD_EINVAL,
-            "sparse_mla_decode: workspace must be 16-byte aligned");
-  KvDesc s{(const uint8_t*)swa->pool, swa->page_stride, swa->num_pages, swa->block_size,
-           __builtin_ctz(swa->block_size)};
-  KvDesc c{(const uint8_t*)comp->pool, comp->page_stride, comp->num_pages, comp->block_size,
-           __builtin_ctz(comp->block_size)};
-  hipStream_t st = (hipStream_t)stream;
-  if (swa->d_nope == 512)
-    return launch<512, 64>(q_bf16, num_tokens, num_heads, s, c, sparse_indices, sparse_topk_lens,
-                           window_size, padded_topk, softmax_scale, attn_sink, out_bf16, lse,
-                           workspace, workspace_bytes, st);
-  if (swa->d_nope == 448)
-    return launch<448, 64>(q_bf16, num_tokens, num_heads, s, c, sparse_indices, sparse_topk_lens,
-                           window_size, padded_topk, softmax_scale, attn_sink, out_bf16, lse,
-                           workspace, workspace_bytes, st);
-  return launch<128, 32>(q_bf16, num_tokens, num_heads, s, c, sparse_indices, sparse_topk_lens,
-                         window_size, padded_topk, softmax_scale, attn_sink, out_bf16, lse,
-                         workspace, workspace_bytes, st);
+  return mla_decode_entry("sparse_mla_decode", q_bf16, num_tokens, num_heads, swa, comp, sparse_indices,
+                          sparse_topk_lens, window_size, padded_topk, softmax_scale, attn_sink, out_bf16, lse,
+                          workspace, workspace_bytes, stream);
 }

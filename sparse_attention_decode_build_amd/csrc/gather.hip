@@ -12,13 +12,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-struct KvDesc {
-  const uint8_t* pool;
-  int64_t stride;
-  int64_t num_pages;
-  int block;
-};
-
 // 2^(b - 127) for a ue8m0 byte (byte 0 is the subnormal 2^-127).
 __device__ inline float ue8m0_scale(uint32_t b) {
   return b != 0 ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
@@ -153,8 +146,10 @@ extern "C" int gather_dequant_kv(const sad_kv_cache* swa, const sad_kv_cache* co
   const int64_t rows = (int64_t)num_tokens * (window_size + padded_topk);
   const int64_t blocks = (rows + 3) / 4;
   SAD_CHECK(blocks < ((int64_t)1 << 31), SAD_EINVAL, "gather_dequant_kv: too many rows");
-  KvDesc s{(const uint8_t*)swa->pool, swa->page_stride, swa->num_pages, swa->block_size};
-  KvDesc c{(const uint8_t*)comp->pool, comp->page_stride, comp->num_pages, comp->block_size};
+  KvDesc s{(const uint8_t*)swa->pool, swa->page_stride, swa->num_pages, swa->block_size,
+           __builtin_ctz(swa->block_size)};
+  KvDesc c{(const uint8_t*)comp->pool, comp->page_stride, comp->num_pages, comp->block_size,
+           __builtin_ctz(comp->block_size)};
   if (swa->d_nope == 512) {
     hipLaunchKernelGGL((gather_dequant_kernel<512, 64>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        (hipStream_t)stream, s, c, sparse_indices, sparse_topk_lens, rows,

@@ -35,8 +35,24 @@ int check_build_args(const char* what, const sad_batch* batch, const int32_t* sw
     }                                \
   } while (0)
 
-// Number of compute units the launch heuristics assume (MI355X: 256 CUs in 8 XCDs).
-constexpr int kNumCUs = 256;
+// Compute units of the current device (read once per device; 256, MI355X's count, if the
+// query fails).  The launch heuristics size their grids with it.
+int num_cus();
+
+// A paged latent KV cache as the attention kernels address it.
+struct KvDesc {
+  const uint8_t* pool;
+  int64_t stride;
+  int64_t num_pages;
+  int block;
+  int block_shift;  // log2(block)
+};
+
+// The dim-split attention kernel of the (512 fp8 + 64 bf16, fp32 scales) row: out (or,
+// with splits > 1, the split partials part_o / part_lse) for every token and head.
+int launch_mla_dsplit(const uint16_t* q, int T, int H, const KvDesc& swa, const KvDesc& comp,
+                      const int32_t* si, const int32_t* lens, int W, int P, float scale, const float* sink,
+                      uint16_t* out, float* lse, float* part_o, float* part_lse, int splits, hipStream_t st);
 
 // ---- vector types -----------------------------------------------------------------
 
