@@ -318,6 +318,28 @@ size_t sparse_mla_decode_workspace_size(int32_t num_tokens, int32_t num_heads,
                                         int32_t max_row_width, int32_t dv);
 
 /*
+ * sparse_mla_decode_noalloc - sparse_mla_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same outputs and errors.
+ *
+ * The split partials go to a static 32 MiB scratch array inside the library, one per
+ * GPU, held until the process ends; its device address is resolved on the first call on
+ * each device that splits a token's columns (make such a first call outside graph
+ * capture).  No call allocates or frees memory.  When the partials of the column splits
+ * that sparse_mla_decode would use exceed 32 MiB, fewer splits are used (outputs then
+ * differ from sparse_mla_decode's only by the fp32 summation order), so no input is
+ * refused for its size.  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (on different streams or threads) race and must be
+ * serialized by the caller.  SAD_ELAUNCH if the array has no device address on the
+ * current device.
+ */
+int sparse_mla_decode_noalloc(const uint16_t* q_bf16, int32_t num_tokens, int32_t num_heads,
+                              const sad_kv_cache* swa, const sad_kv_cache* comp,
+                              const int32_t* sparse_indices, const int32_t* sparse_topk_lens,
+                              int32_t window_size, int32_t padded_topk, float softmax_scale,
+                              const float* attn_sink, uint16_t* out_bf16, float* lse, void* stream);
+
+/*
  * inv_rope_fp8_quant - the attention output in the form the output projection takes.
  *
  * Defined by [vllm] fused_inv_rope_fp8_quant and [model] _project_attention_output

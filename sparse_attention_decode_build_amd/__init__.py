@@ -23,4 +23,5 @@ from ._lib import (  # noqa: F401
     load,
     sparse_mla_decode,
     sparse_mla_decode_workspace_size,
+    sparse_mla_decode_noalloc,
 )

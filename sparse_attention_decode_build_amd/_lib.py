@@ -62,6 +62,9 @@ _SIGNATURES = {
                                   ctypes.POINTER(SadKvCache), c_ptr, c_ptr, c_i32, c_i32, c_f32, c_ptr,
                                   c_ptr, c_ptr, c_ptr, c_size, c_ptr]),
     "sparse_mla_decode_workspace_size": (c_size, [c_i32, c_i32, c_i32, c_i32]),
+    "sparse_mla_decode_noalloc": (c_i32, [c_ptr, c_i32, c_i32, ctypes.POINTER(SadKvCache),
+                                          ctypes.POINTER(SadKvCache), c_ptr, c_ptr, c_i32, c_i32, c_f32, c_ptr,
+                                          c_ptr, c_ptr, c_ptr]),
     "inv_rope_fp8_quant": (c_i32, [c_ptr, c_ptr, c_ptr, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_ptr,
                                    c_ptr, c_ptr]),
     "insert_kv_rows": (c_i32, [c_ptr, c_ptr, c_ptr, c_i32, c_i32, c_ptr, c_i32, ctypes.POINTER(SadKvCache),
@@ -346,6 +349,32 @@ def sparse_mla_decode(q, swa: KvCache, comp: KvCache, sparse_indices, sparse_top
                                _p(attn_sink), _p(out), _p(lse), _p(workspace),
                                workspace.numel() if workspace is not None else 0, _stream(stream))
     _check("sparse_mla_decode", rc)
+    return out
+
+
+def sparse_mla_decode_noalloc(q, swa: KvCache, comp: KvCache, sparse_indices, sparse_topk_lens, window_size,
+                              padded_topk, softmax_scale, attn_sink=None, out=None, lse=None, stream=None):
+    """sparse_mla_decode without a workspace: the split partials use the library's static
+    per-GPU scratch (no allocation by the library; `out` is allocated here if not given)."""
+    lib = load()
+    _need(q, torch.bfloat16, "q", dim=3)
+    _need(sparse_indices, torch.int32, "sparse_indices", dim=2)
+    _need(sparse_topk_lens, torch.int32, "sparse_topk_lens", dim=1)
+    T, H, D = q.shape
+    if tuple(sparse_indices.shape) != (T, window_size + padded_topk) or tuple(sparse_topk_lens.shape) != (T,):
+        raise ValueError("sparse_mla_decode_noalloc: sparse_indices must be [T, window_size + padded_topk] and "
+                         "sparse_topk_lens [T]")
+    if attn_sink is not None:
+        _need(attn_sink, torch.float32, "attn_sink", dim=1)
+    if out is None:
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=q.device)
+    if lse is not None:
+        _need(lse, torch.float32, "lse", dim=2)
+    s, c = swa.c(), comp.c()
+    rc = lib.sparse_mla_decode_noalloc(_p(q), T, H, ctypes.byref(s), ctypes.byref(c), _p(sparse_indices),
+                                       _p(sparse_topk_lens), window_size, padded_topk, softmax_scale,
+                                       _p(attn_sink), _p(out), _p(lse), _stream(stream))
+    _check("sparse_mla_decode_noalloc", rc)
     return out
 
 

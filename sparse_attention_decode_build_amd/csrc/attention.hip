@@ -974,12 +974,38 @@ int launch(const uint16_t* q, int T, int H, const KvDesc& s, const KvDesc& c, co
   return check_launch("sparse_mla_decode(combine)");
 }
 
-// Body of sparse_mla_decode.
+// The scratch buffer of sparse_mla_decode_noalloc: one per GPU the library runs on (each
+// device holds its own copy of this array, at its own address, until the process ends).
+constexpr size_t kNoAllocScratchBytes = 32ull << 20;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+// The device address of this device's copy of `scratch` (resolved once per device, with
+// that device current; the array's name is only a host-side stand-in), or NULL.
+void* noalloc_scratch() {
+  static void* ptrs[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* p = __atomic_load_n(&ptrs[dev], __ATOMIC_ACQUIRE);
+  if (p != nullptr) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  __atomic_store_n(&ptrs[dev], p, __ATOMIC_RELEASE);
+  return p;
+}
+
+// Shared body of sparse_mla_decode and sparse_mla_decode_noalloc.  With static_ws the
+// workspace is this device's copy of `scratch` (resolved only when splits need it) and
+// the column splits are reduced until their partials fit in it.
 int mla_decode_entry(const char* name, const uint16_t* q_bf16, int32_t num_tokens, int32_t num_heads,
                      const sad_kv_cache* swa, const sad_kv_cache* comp, const int32_t* sparse_indices,
                      const int32_t* sparse_topk_lens, int32_t window_size, int32_t padded_topk,
                      float softmax_scale, const float* attn_sink, uint16_t* out_bf16, float* lse,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     void* workspace, size_t workspace_bytes, bool static_ws, void* stream) {
   clear_error();
   int rc = check_kv_cache(swa, "sparse_mla_decode(swa)");
   if (rc != SAD_OK) return rc;
@@ -999,7 +1025,18 @@ int mla_decode_entry(const char* name, const uint16_t* q_bf16, int32_t num_token
             "%s: q and out must be 16-byte aligned", name);
   SAD_CHECK(((uintptr_t)workspace & 15) == 0, SAD_EINVAL, "%s: workspace must be 16-byte aligned", name);
   const int dqk = swa->d_nope + swa->d_rope;
-  const int splits = choose_splits(num_tokens, num_heads, window_size + padded_topk, dqk);
+  int splits = choose_splits(num_tokens, num_heads, window_size + padded_topk, dqk);
+  if (static_ws) {
+    while (splits > 1 && split_workspace_bytes(splits, num_tokens, num_heads, dqk) > kNoAllocScratchBytes)
+      --splits;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (splits > 1) {
+      workspace = noalloc_scratch();
+      SAD_CHECK(workspace != nullptr, SAD_ELAUNCH, "%s: the static scratch has no device address", name);
+      workspace_bytes = kNoAllocScratchBytes;
+    }
+  }
   const size_t need = split_workspace_bytes(splits, num_tokens, num_heads, dqk);
   SAD_CHECK(need == 0 || (workspace != nullptr && workspace_bytes >= need), SAD_EWORKSPACE,
             "%s: workspace needs %zu bytes, got %zu", name, need, workspace_bytes);
@@ -1041,5 +1078,16 @@ extern "C" int sparse_mla_decode(const uint16_t* q_bf16, int32_t num_tokens, int
                                  void* workspace, size_t workspace_bytes, void* stream) {
   return mla_decode_entry("sparse_mla_decode", q_bf16, num_tokens, num_heads, swa, comp, sparse_indices,
                           sparse_topk_lens, window_size, padded_topk, softmax_scale, attn_sink, out_bf16, lse,
-                          workspace, workspace_bytes, stream);
+                          workspace, workspace_bytes, false, stream);
+}
+
+extern "C" int sparse_mla_decode_noalloc(const uint16_t* q_bf16, int32_t num_tokens, int32_t num_heads,
+                                         const sad_kv_cache* swa, const sad_kv_cache* comp,
+                                         const int32_t* sparse_indices, const int32_t* sparse_topk_lens,
+                                         int32_t window_size, int32_t padded_topk, float softmax_scale,
+                                         const float* attn_sink, uint16_t* out_bf16, float* lse,
+                                         void* stream) {
+  return mla_decode_entry("sparse_mla_decode_noalloc", q_bf16, num_tokens, num_heads, swa, comp,
+                          sparse_indices, sparse_topk_lens, window_size, padded_topk, softmax_scale, attn_sink,
+                          out_bf16, lse, nullptr, 0, true, stream);
 }

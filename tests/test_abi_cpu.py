@@ -120,6 +120,24 @@ def test_attention_errors(lib):
     assert lib.sparse_mla_decode_workspace_size(16448, 128, 2176, 576) == 0
 
 
+def _call_attn_noalloc(lib, T=128, H=128, W=128, P=2048, d_nope=512):
+    s, c = _kv(d_nope=d_nope), _kv(d_nope=d_nope)
+    return lib.sparse_mla_decode_noalloc(FAKE, T, H, ctypes.byref(s), ctypes.byref(c), FAKE, FAKE, W, P, 0.04,
+                                         None, FAKE, None, None)
+
+
+def test_attention_noalloc_errors(lib):
+    """The entry point for callers that cannot allocate checks its arguments as
+    sparse_mla_decode does; it never asks for a workspace."""
+    assert _call_attn_noalloc(lib, T=0) == L.SAD_OK
+    assert L.last_error() == ""
+    assert _call_attn_noalloc(lib, H=7) == L.SAD_EUNSUPPORTED
+    assert "sparse_mla_decode_noalloc" in L.last_error()
+    assert _call_attn_noalloc(lib, T=-1) == L.SAD_EINVAL
+    assert _call_attn_noalloc(lib, T=70000) == L.SAD_EINVAL
+    assert _call_attn_noalloc(lib, d_nope=256) == L.SAD_EUNSUPPORTED
+
+
 def _call_qprep(lib, T=4, H=64, D=128, R=64, P=100, align=FAKE):
     return lib.prepare_indexer_q_mxfp4(align, FAKE, FAKE, P, R, FAKE, 0.088, 0.125, T, H, D,
                                        FAKE, FAKE, FAKE, None)
