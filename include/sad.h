@@ -185,7 +185,11 @@ int build_sparse_indices(const sad_batch* batch, const int32_t* replay_start,
  *     valid rows s < n_c(t), -inf for invalid rows s < n_c(t) (others untouched);
  *     requires logits_stride >= idx_bt_cols*block_size.
  *   workspace  >= indexer_score_topk_workspace_size(num_tokens, idx_bt_cols*block_size, topk)
- * num_idx_heads in [1, 64]; topk in [1, 65536]; idx_bt_cols*block_size <= 32768.
+ * num_idx_heads in [1, 64]; topk in [1, 65536].  Up to 32768 rows
+ * (idx_bt_cols*block_size) one workgroup per token selects the top-k; past that the
+ * rows go in chunks of 32768 whose own top-k are merged, which needs
+ * ceil(rows / 32768) * topk <= 32768 (else SAD_EUNSUPPORTED; e.g. topk 2048 allows
+ * 524288 rows, a 2M-token context at compress_ratio 4).
  */
 int indexer_score_topk(const sad_batch* batch, const uint8_t* q_values, const uint8_t* q_scales,
                        const float* weights, int32_t num_idx_heads, const sad_mxfp4_cache* keys,
@@ -197,7 +201,8 @@ size_t indexer_score_topk_workspace_size(int32_t num_tokens, int32_t max_ctx_row
 
 /*
  * indexer_topk_sparse_indices - indexer_score_topk and build_sparse_indices in one call
- * (the index build runs inside the top-k kernel, so the step takes one launch fewer).
+ * (up to 32768 rows the index build runs inside the top-k kernel, so the step takes one
+ * launch fewer; past that the call runs the build as its own launch).
  *
  * Exactly indexer_score_topk(batch, q_values, ..., topk, topk_local, NULL, 0, workspace,
  * workspace_bytes) followed by build_sparse_indices(batch, replay_start, swa_bt, ...,

@@ -299,14 +299,31 @@ struct BuildArgs {
   int32_t* lens;
 };
 
-// BUILD: the workgroup also writes the token's sparse_indices row and length, as
+// Rows past one workgroup's reach (32 keys per thread) go through chunks: each chunk
+// of kTopkChunk rows keeps its own top-k (value and row id, k slots per chunk, padded
+// with -inf / -1), then one workgroup per token selects the top-k of those candidates.
+// Every row of the token's top-k is in its chunk's top-k (fewer than k rows of the
+// chunk precede it in the order value desc, row asc), and the candidates keep row
+// order (chunks in order, each ascending), so the result equals the one-pass top-k.
+constexpr int kTopkChunk = 32 * kTopkThreads;
+struct ChunkIO {
+  float* vals;    // [T][nch * k]
+  int32_t* ids;   // [T][nch * k]
+  int nch;
+};
+enum TopkMode { kDirect = 0, kDirectBuild = 1, kChunk = 2, kMerge = 3 };
+
+// Mode kDirect: top-k of the token's first n_c logits.  kDirectBuild: the same, and the
+// workgroup also writes the token's sparse_indices row and length, as
 // build_sparse_indices would from this top-k row: window columns lo..p through the
 // window table, then the winners' slots through the compressed table (ascending, the
-// ones whose page is not in the pool dropped), then -1.
-template <int KPT, bool BUILD>
+// ones whose page is not in the pool dropped), then -1.  kChunk: chunk blockIdx.y of
+// the logits -> its k candidates.  kMerge: the candidates -> the token's top-k.
+template <int KPT, int MODE>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     sad_batch b, int ratio, int max_rows, const float* __restrict__ logits, int64_t logits_stride,
-    int k, int32_t* __restrict__ out, BuildArgs ba) {
+    int k, int32_t* __restrict__ out, BuildArgs ba, ChunkIO cio) {
+  constexpr bool BUILD = MODE == kDirectBuild;
   // logits staged in row order (coalesced global loads), then read back thread-contiguous
   constexpr int kStride = KPT <= 16 ? KPT + 4 : KPT;  // padded rows: conflict-free 16-byte reads
   __shared__ __align__(16) float stage[kTopkThreads * kStride];
@@ -317,20 +334,30 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   const int tid = threadIdx.x;
   const int base = tid * KPT;  // the thread's rows after staging: base .. base + KPT - 1
 
-  // The workspace row holds max_rows logits, so they are loaded before the token's
-  // length is known (at an index clamped into the row: none is conditional); rows past
-  // n become -inf below.  The token's geometry comes through scalar loads, which the
-  // wait for them does not serialize behind the logits loads.
+  // The workspace row holds max_rows logits (a chunk: its part of them; the merge: the
+  // token's nch * k candidates), so they are loaded before the token's length is known
+  // (at an index clamped into the row: none is conditional); rows past n become -inf
+  // below.  The token's geometry comes through scalar loads, which the wait for them
+  // does not serialize behind the logits loads.
+  const int chunk = MODE == kChunk ? (int)blockIdx.y : 0;
+  const int row_off = chunk * kTopkChunk;
+  const int span = MODE == kMerge ? cio.nch * k : max_rows - row_off;  // positions in the row
+  const float* lrow = MODE == kMerge ? cio.vals + (int64_t)t * cio.nch * k
+                                     : logits + (int64_t)t * logits_stride + row_off;
   float lv[KPT];
-  if (max_rows > 0) {
-    const float* lrow = logits + (int64_t)t * logits_stride;
+  if (span > 0) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) lv[i] = lrow[min(i * kTopkThreads + tid, max_rows - 1)];
+    for (int i = 0; i < KPT; ++i) lv[i] = lrow[min(i * kTopkThreads + tid, span - 1)];
   }
   TokenGeom g;
   const bool ok = token_geometry_uniform(b, t, ratio, g);
-  const int n = ok ? min(g.n_comp, max_rows) : 0;
+  const int n = MODE == kMerge ? span
+                : MODE == kChunk ? (ok ? max(0, min(min(g.n_comp, max_rows) - row_off, kTopkChunk)) : 0)
+                : (ok ? min(g.n_comp, max_rows) : 0);
   int32_t* orow = out + (int64_t)t * k;
+  // chunk outputs: k candidate slots of this chunk
+  float* cvals = MODE == kChunk ? cio.vals + ((int64_t)t * cio.nch + chunk) * k : nullptr;
+  int32_t* cids = MODE == kChunk ? cio.ids + ((int64_t)t * cio.nch + chunk) * k : nullptr;
 
   // Index-build loads that need only the token, issued now and used at the end: the
   // compressed-table page ids of the thread's rows (its KPT consecutive rows lie in at
@@ -370,6 +397,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   };
 
   if (n == 0) {
+    if constexpr (MODE == kChunk) {
+      for (int j = tid; j < k; j += kTopkThreads) {
+        cvals[j] = -INFINITY;
+        cids[j] = -1;
+      }
+      return;
+    }
     for (int j = tid; j < k; j += kTopkThreads) orow[j] = -1;
     if constexpr (BUILD) {
       window_stores();
@@ -476,7 +510,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     }
   }
   constexpr int kCap = kTopkThreads * kStride;  // words of the staging buffer
-  if constexpr (!BUILD) {
+  if constexpr (MODE == kChunk) {
+    __syncthreads();
+    for (int j = tid; j < k; j += kTopkThreads) {
+      const int v = ostage[min(j, kCap - 1)];
+      cvals[j] = j < total ? lrow[v] : -INFINITY;
+      cids[j] = j < total ? row_off + v : -1;
+    }
+  } else if constexpr (MODE == kMerge) {
+    __syncthreads();
+    const int32_t* crow = cio.ids + (int64_t)t * cio.nch * k;
+    for (int j = tid; j < k; j += kTopkThreads) {
+      const int v = ostage[min(j, kCap - 1)];
+      orow[j] = j < total ? crow[v] : -1;
+    }
+  } else if constexpr (!BUILD) {
     __syncthreads();
     for (int j = tid; j < k; j += kTopkThreads) {
       const int v = ostage[min(j, kCap - 1)];
@@ -526,12 +574,18 @@ using namespace sad;
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Chunks of the top-k for rows past one workgroup's reach (1 when it needs none).
+static int topk_chunks(int64_t max_rows) { return (int)((max_rows + kTopkChunk - 1) / kTopkChunk); }
+
 extern "C" size_t indexer_score_topk_workspace_size(int32_t num_tokens, int32_t max_ctx_rows,
                                                     int32_t topk) {
-  (void)topk;
   if (num_tokens <= 0 || max_ctx_rows <= 0) return 0;
   const size_t stride = (size_t)((max_ctx_rows + 3) / 4 * 4);
-  return align256((size_t)num_tokens * stride * sizeof(float));
+  size_t bytes = align256((size_t)num_tokens * stride * sizeof(float));
+  const int nch = topk_chunks(max_ctx_rows);
+  if (nch > 1 && topk > 0)  // the chunks' candidates: a value and a row id each
+    bytes += 2 * align256((size_t)num_tokens * nch * topk * sizeof(float));
+  return bytes;
 }
 
 namespace {
@@ -562,9 +616,12 @@ int run_indexer(const sad_batch* batch, const uint8_t* q_values, const uint8_t* 
             (long long)need_stride);
   SAD_CHECK(keys->num_pages >= 0, SAD_EINVAL, "indexer_score_topk: negative num_pages");
   const int64_t max_rows64 = (int64_t)idx_bt_cols * keys->block_size;
-  SAD_CHECK(max_rows64 <= 32 * kTopkThreads, SAD_EUNSUPPORTED,
-            "indexer_score_topk: idx_bt_cols*block_size = %lld exceeds 32768 rows",
-            (long long)max_rows64);
+  SAD_CHECK(max_rows64 <= INT32_MAX / 2, SAD_EINVAL, "indexer_score_topk: idx_bt_cols*block_size too large");
+  const int nch = topk_chunks(max_rows64);
+  SAD_CHECK(nch <= 1 || (int64_t)nch * topk <= kTopkChunk, SAD_EUNSUPPORTED,
+            "indexer_score_topk: %lld rows need %d chunks of the top-k, and %d x topk %d candidates "
+            "exceed %d",
+            (long long)max_rows64, nch, nch, topk, kTopkChunk);
   const int max_rows = (int)max_rows64;
   SAD_CHECK(logits_debug == nullptr || logits_stride >= max_rows, SAD_EINVAL,
             "indexer_score_topk: logits_stride must be >= idx_bt_cols*block_size");
@@ -599,17 +656,44 @@ int run_indexer(const sad_batch* batch, const uint8_t* q_values, const uint8_t* 
     if (rc != SAD_OK) return rc;
   }
   const BuildArgs bargs = ba != nullptr ? *ba : BuildArgs{};
-  auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(T), dim3(kTopkThreads), 0, st, *batch, compress_ratio, max_rows,
-                       logits, ws_stride, topk, topk_local, bargs);
+  if (nch <= 1) {
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3(T), dim3(kTopkThreads), 0, st, *batch, compress_ratio, max_rows,
+                         logits, ws_stride, topk, topk_local, bargs, ChunkIO{});
+    };
+    if (max_rows <= 4 * kTopkThreads)
+      ba != nullptr ? go(topk_kernel<4, kDirectBuild>) : go(topk_kernel<4, kDirect>);
+    else if (max_rows <= 16 * kTopkThreads)
+      ba != nullptr ? go(topk_kernel<16, kDirectBuild>) : go(topk_kernel<16, kDirect>);
+    else
+      ba != nullptr ? go(topk_kernel<32, kDirectBuild>) : go(topk_kernel<32, kDirect>);
+    return check_launch("indexer_score_topk(topk)");
+  }
+  // chunks, then the merge of their candidates (then the index build, as its own call)
+  uint8_t* cand = reinterpret_cast<uint8_t*>(workspace) + align256((size_t)T * ws_stride * sizeof(float));
+  const ChunkIO cio{reinterpret_cast<float*>(cand),
+                    reinterpret_cast<int32_t*>(cand + align256((size_t)T * nch * topk * sizeof(float))), nch};
+  hipLaunchKernelGGL((topk_kernel<32, kChunk>), dim3(T, nch), dim3(kTopkThreads), 0, st, *batch, compress_ratio,
+                     max_rows, logits, ws_stride, topk, topk_local, bargs, cio);
+  int rc = check_launch("indexer_score_topk(topk chunks)");
+  if (rc != SAD_OK) return rc;
+  auto merge = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(T), dim3(kTopkThreads), 0, st, *batch, compress_ratio, max_rows, logits,
+                       ws_stride, topk, topk_local, bargs, cio);
   };
-  if (max_rows <= 4 * kTopkThreads)
-    ba != nullptr ? go(topk_kernel<4, true>) : go(topk_kernel<4, false>);
-  else if (max_rows <= 16 * kTopkThreads)
-    ba != nullptr ? go(topk_kernel<16, true>) : go(topk_kernel<16, false>);
+  const int ncand = nch * topk;
+  if (ncand <= 4 * kTopkThreads)
+    merge(topk_kernel<4, kMerge>);
+  else if (ncand <= 16 * kTopkThreads)
+    merge(topk_kernel<16, kMerge>);
   else
-    ba != nullptr ? go(topk_kernel<32, true>) : go(topk_kernel<32, false>);
-  return check_launch("indexer_score_topk(topk)");
+    merge(topk_kernel<32, kMerge>);
+  rc = check_launch("indexer_score_topk(topk merge)");
+  if (rc != SAD_OK || ba == nullptr) return rc;
+  return build_sparse_indices(batch, ba->replay, ba->swa_bt, ba->swa_stride, ba->swa_cols, ba->swa_block,
+                              ba->swa_pages, ba->comp_bt, ba->comp_stride, ba->comp_cols, ba->comp_block,
+                              ba->comp_pages, topk_local, topk, topk, ba->window, compress_ratio, ba->padded,
+                              ba->si, ba->lens, stream);
 }
 
 }  // namespace

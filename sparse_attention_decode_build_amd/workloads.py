@@ -179,6 +179,13 @@ CONFIGS = {
         swa_block=64,
     ),
     # 8 requests at seq 1M, ratio 128 (8192 compressed rows, all attended), W=128
+    # 4 requests x 1 token at seq 2^20, ratio 4: 262144 compressed rows, past one top-k
+    # workgroup's reach (8 chunks of 32768 rows, merged)
+    "csa_1m": Config(
+        name="csa_1m", seed=22, window=128, ratio=4, topk=2048, heads=128, d_nope=512,
+        d_rope=64, idx_heads=64, idx_dim=128, block=64, idx_block=64,
+        groups=((4, 1, 1 << 20, 0),),
+    ),
     "dense_1m": Config(
         name="dense_1m", seed=4, window=128, ratio=128, topk=0, heads=128, d_nope=512,
         d_rope=64, idx_heads=64, idx_dim=128, block=64, idx_block=64,

@@ -80,12 +80,16 @@ def test_indexer_errors(lib):
     assert _call_indexer(lib, dim=96) == L.SAD_EUNSUPPORTED
     assert _call_indexer(lib, heads=65) == L.SAD_EUNSUPPORTED
     assert _call_indexer(lib, block=32) == L.SAD_EUNSUPPORTED
-    assert _call_indexer(lib, cols=1024) == L.SAD_EUNSUPPORTED  # 65536 rows > 32768
+    # 1M rows: 32 chunks of 32768 rows x topk 2048 candidates > 32768
+    assert _call_indexer(lib, cols=16384, topk=2048) == L.SAD_EUNSUPPORTED
+    assert "chunks" in L.last_error()
     assert _call_indexer(lib, topk=0) == L.SAD_EINVAL
     assert _call_indexer(lib, ws_bytes=16) == L.SAD_EWORKSPACE
     assert "workspace" in L.last_error()
     need = lib.indexer_score_topk_workspace_size(128, 16384, 2048)
     assert need == 128 * 16384 * 4
+    # past 32768 rows: the logits plus the chunks' candidates (value and row id)
+    assert lib.indexer_score_topk_workspace_size(128, 262144, 2048) == 128 * 262144 * 4 + 2 * 128 * 8 * 2048 * 4
     assert lib.indexer_score_topk_workspace_size(0, 16384, 2048) == 0
 
 

@@ -406,6 +406,17 @@ def test_mixed_batch_sampled():
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_csa_1m_top_k_past_one_workgroup():
+    """262144 compressed rows per token (1M context at ratio 4): the top-k runs in 8
+    chunks whose candidates are merged; every step on all 4 tokens vs the oracle."""
+    wl = _wl("csa_1m")
+    view = WL.host_view(wl)
+    _full_check(wl, view, list(range(wl.num_tokens)))
+    free(wl)
+
+
+@pytest.mark.slow
 def test_dense_1m_full():
     wl = _wl("dense_1m")
     view = WL.host_view(wl)
