@@ -63,7 +63,8 @@ class Step:
                                cfg.block, cfg.d_nope, cfg.d_rope, WL.kv_scale_format(cfg))
         self.idx = L.SadMxfp4Cache(wl.idx_pool.data_ptr(), wl.idx_pool.stride(0), wl.idx_pool.shape[0],
                                    cfg.idx_block, cfg.idx_dim)
-        self.topk = torch.empty((T, cfg.topk), dtype=torch.int32, device=dev)
+        self.dense = cfg.dense
+        self.topk = torch.empty((T, max(cfg.topk, 1)), dtype=torch.int32, device=dev)
         self.si = torch.empty((T, cfg.window + wl.padded_topk), dtype=torch.int32, device=dev)
         self.lens = torch.empty((T,), dtype=torch.int32, device=dev)
         self.out = torch.empty((T, cfg.heads, cfg.dqk), dtype=torch.bfloat16, device=dev)
@@ -81,8 +82,9 @@ class Step:
                          None, 0, p(self.ws_i), self.ws_i.numel(), stream)
         self.args_build = (ctypes.byref(self.batch), p(wl.replay_start), p(lay.swa_bt), lay.swa_bt.stride(0),
                            lay.swa_bt.shape[1], cfg.block, n_pages, p(lay.comp_bt), lay.comp_bt.stride(0),
-                           lay.comp_bt.shape[1], cfg.block, n_pages, p(self.topk), self.topk.stride(0),
-                           cfg.topk, cfg.window, cfg.ratio, wl.padded_topk, p(self.si), p(self.lens), stream)
+                           lay.comp_bt.shape[1], cfg.block, n_pages, None if self.dense else p(self.topk),
+                           self.topk.stride(0), cfg.topk, cfg.window, cfg.ratio, wl.padded_topk, p(self.si),
+                           p(self.lens), stream)
         self.args_fused = (ctypes.byref(self.batch), p(lay.idx_q_values), p(lay.idx_q_scales),
                            p(lay.idx_weights), cfg.idx_heads, ctypes.byref(self.idx), p(lay.idx_bt),
                            lay.idx_bt.stride(0), lay.idx_bt.shape[1], cfg.ratio, cfg.topk, p(self.topk),
@@ -102,7 +104,9 @@ class Step:
         is taken from the previous step's last event."""
         lib = self.lib
         ev = ev if ev is not None else [None, None, None]
-        if fused:
+        if self.dense:  # every compressed row attended: no indexer
+            rc = lib.build_sparse_indices(*self.args_build)
+        elif fused:
             rc = lib.indexer_topk_sparse_indices(*self.args_fused)
         else:
             rc = lib.indexer_score_topk(*self.args_idx)
@@ -126,13 +130,14 @@ def algorithmic_bytes(wl: WL.Workload) -> dict:
     t2r = wl.token_to_req.cpu().numpy().astype(np.int64)
     pos = seq[t2r] - (qsl[t2r + 1] - qsl[t2r]) + (np.arange(len(t2r)) - qsl[t2r])
     nc = (pos + 1) // cfg.ratio
-    rows = np.minimum(pos + 1, cfg.window) + np.minimum(nc, cfg.topk)  # attended rows per token
+    # attended rows per token: the window, then the top-k (dense: every compressed row)
+    rows = np.minimum(pos + 1, cfg.window) + (nc if cfg.dense else np.minimum(nc, cfg.topk))
     row_b = cfg.d_nope + 2 * cfg.d_rope + cfg.kv_scale_bytes
     idx_row = cfg.idx_dim // 2 + cfg.idx_dim // 32
     W, P, H, D = cfg.window, wl.padded_topk, cfg.heads, cfg.dqk
     attn = rows * row_b + (W + P) * 4 + 4 + 2 * H * D + 2 * H * D
     indexer = (nc * idx_row + (nc + cfg.idx_block - 1) // cfg.idx_block * 4
-               + cfg.idx_heads * idx_row + 4 * cfg.idx_heads + 4 * cfg.topk)
+               + cfg.idx_heads * idx_row + 4 * cfg.idx_heads + 4 * cfg.topk) * (0 if cfg.dense else 1)
     build = 4 * cfg.topk + 4 * (W + P)
     flops = 2 * H * (D + D) * rows  # QK + PV
     return {"attention": int(attn.sum()), "indexer": int(indexer.sum()), "build": int(build * len(t2r)),
@@ -428,8 +433,8 @@ def time_steps_graph(wl: WL.Workload, layers: int, K: int, warmup: int):
         for a, b in zip((st.topk, st.si, st.lens, st.out), ref):
             if not torch.equal(a, b):
                 raise RuntimeError("graph replay differs from the eager step")
-    reps = max(1, K // layers)
-    for _ in range(2):  # the first replays after capture run slower
+    reps = max(20, K // layers)
+    for _ in range(3):  # the first replays after capture run slower
         g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -439,6 +444,117 @@ def time_steps_graph(wl: WL.Workload, layers: int, K: int, warmup: int):
     wall = time.perf_counter() - t0
     del g
     return wall * 1e3 / (reps * layers)
+
+
+def per_step_ms(wl: WL.Workload, layers: int, n: int, warmup: int, cold: bool = False) -> dict:
+    """Per-step HIP-event times of n steps (layers rotated): warm (steps back to back,
+    queued behind a spin kernel so the host's launch rate does not show), or cold (a
+    1 GiB scratch write, untimed, before each step: the L2s and the 256 MB MALL hold
+    none of the step's data).  Median, mean, 10th and 90th percentiles in ms."""
+    steps = [Step(wl, i) for i in range(layers)]
+    for i in range(warmup):
+        steps[i % layers].run()
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    scratch = torch.empty((1 << 28,), dtype=torch.float32, device="cuda") if cold else None
+    torch.cuda.synchronize()
+    if cold:
+        pairs = [(mk(), mk()) for _ in range(n)]
+        for i in range(n):
+            scratch.fill_(float(i))
+            pairs[i][0].record()
+            steps[i % layers].run()
+            pairs[i][1].record()
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in pairs])
+    else:
+        ev = [mk() for _ in range(n + 1)]
+        torch.cuda._sleep(int(2e5) * n)  # ~0.1 ms of spinning per queued step
+        ev[0].record()
+        for i in range(n):
+            steps[i % layers].run()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+    del scratch
+    return {"steps": n, "median_ms": float(np.median(ms)), "mean_ms": float(ms.mean()),
+            "p10_ms": float(np.percentile(ms, 10)), "p90_ms": float(np.percentile(ms, 90))}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_rate(wl: WL.Workload, budget_s: float, tokens=None, threads=None) -> dict:
+    """The CPU oracle, as it stands, on a bounded sample of tokens of layer 0 (whole step
+    each: the indexer, top-k, index build and attention of those tokens); threads: cap the
+    BLAS pools (None: as configured)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import sad_oracle as O
+
+    cfg = wl.cfg
+    T = wl.num_tokens
+    cand = list(range(T)) if tokens is None else list(tokens)
+
+    def run(tok):
+        view = WL.host_view(wl, 0, reqs=sorted(set(wl.token_to_req[tok].cpu().tolist())))
+        t0 = time.perf_counter()
+        O.step(view, cfg, wl.padded_topk, wl.kv_pool.shape[0], wl.idx_pool.shape[0], wl.softmax_scale,
+               tokens=tok)
+        return time.perf_counter() - t0
+
+    with threadpool_limits(limits=threads):
+        t1 = run(cand[:1])
+        n = int(max(1, min(len(cand), budget_s / max(t1, 1e-3))))
+        tok = cand[:n]
+        dt = run(tok) if n > 1 else t1
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"whole step of {n} of {T} tokens (layer 0), float64 numpy oracle, {dt:.1f} s"
+                      + ("" if n == T else "; extrapolated to tokens/s from the sample")}
+
+
+# The other seeded configurations: (name, layers rotated, oracle sample budget in s)
+OTHER_CONFIGS = (("tiny", 1, 3.0), ("b32_8k", 4, 5.0), ("mixed", 1, 8.0), ("dense_1m", 1, 5.0),
+                 ("csa_1m", 1, 5.0))
+
+
+def bench_config(name: str, layers: int, steps: int, warmup: int, oracle_s: float, oracle: bool) -> dict:
+    """One seeded configuration: median step time over `steps` per-step events (warm),
+    its tokens/s, the attention kernel against both peaks, and the oracle's rate on a
+    sample (also single-threaded for the two small configurations)."""
+    wl = WL.make_workload(name, "cuda", num_layers=layers)
+    torch.cuda.synchronize()
+    cfg = wl.cfg
+    T = wl.num_tokens
+    st = per_step_ms(wl, layers, steps, warmup)
+    _, (ms_idx, ms_build, ms_attn) = time_steps(wl, layers, max(steps, 8), warmup)
+    ab = algorithmic_bytes(wl)
+    gbs = ab["attention"] / (ms_attn * 1e-3) / 1e9
+    tf = ab["attention_flops"] / (ms_attn * 1e-3) / 1e12
+    res = {"workload": f"{name}: {wl.num_reqs} requests, {T} tokens, max seq {int(wl.seq_lens.max())}, window "
+                       f"{cfg.window}, ratio {cfg.ratio}, " + ("dense" if cfg.dense else f"topk {cfg.topk}")
+                       + f", {cfg.heads} heads, latent {cfg.d_nope}+{cfg.d_rope}",
+           "tokens_per_step": T, "layers_rotated": layers,
+           "tokens_per_s": T / (st["median_ms"] * 1e-3), "step": st,
+           "kernels_ms": {"indexer_topk_sparse_indices" if not cfg.dense else "build_sparse_indices": ms_idx,
+                          "sparse_mla_decode": ms_attn},
+           "attention": {"algorithmic_bytes": ab["attention"], "gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+                         "tflops": tf, "mfma_frac": tf / PEAK_BF16_TFLOPS}}
+    if oracle:
+        res["cpu_oracle"] = oracle_rate(wl, oracle_s)
+        if name in ("tiny", "b32_8k"):
+            res["cpu_oracle_single_thread"] = oracle_rate(wl, oracle_s, threads=1)
+    del wl
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_native_record(layers: int, K: int, warmup: int) -> dict:
@@ -472,6 +588,9 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=4, help="independent layers rotated per step")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--protocol-steps", type=int, default=100,
+                    help="per-step median over this many warm and cold steps of the headline")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other seeded configurations")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the extra legs (native record, query preparation, output quantization, cache "
                          "writes); counter runs use this so only the calibration copy and the step run")
@@ -507,6 +626,8 @@ def main() -> int:
     ms_step3, seg3 = time_steps(wl, args.layers, K, args.warmup, fused=False)
     ms_step, (ms_idx, ms_build, ms_attn) = time_steps(wl, args.layers, K, args.warmup)
     ms_graph = time_steps_graph(wl, args.layers, K, args.warmup)
+    protocol = {"warm": per_step_ms(wl, args.layers, args.protocol_steps, args.warmup),
+                "cold_1gib_scratch_write": per_step_ms(wl, args.layers, args.protocol_steps, args.warmup, cold=True)}
     T = wl.num_tokens
     ab = algorithmic_bytes(wl)
     attn_gbs = ab["attention"] / (ms_attn * 1e-3) / 1e9
@@ -546,19 +667,29 @@ def main() -> int:
         "algorithmic_bytes_per_step": {"attention": ab["attention"], "indexer": ab["indexer"],
                                        "build": ab["build"]},
         "graph_replay": {"ms_per_step": ms_graph, "tokens_per_s": T / (ms_graph * 1e-3)},
+        "timing_protocol": dict(protocol, cpu_model=cpu_model(),
+                                tokens_per_s_warm_median=T / (protocol["warm"]["median_ms"] * 1e-3),
+                                tokens_per_s_cold_median=T / (protocol["cold_1gib_scratch_write"]["median_ms"] * 1e-3)),
         "indexer_hbm_gbs": idx_gbs,
         "step_hbm_frac": (ab["attention"] + ab["indexer"] + ab["build"]) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        result["cpu_baseline"]["cpu_model"] = cpu_model()
+    del wl
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        result["configs"] = {}
+        for name, layers, osec in OTHER_CONFIGS:
+            log(f"[bench] config {name}")
+            result["configs"][name] = bench_config(name, layers, args.protocol_steps, args.warmup, osec,
+                                                   not args.no_cpu_baseline)
     if args.no_next_rows:
         print(json.dumps(result), flush=True)
         return 0
     log("[bench] next rows: native KV record, indexer query preparation, output quantization, cache writes")
-    del wl
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
     native = bench_native_record(args.layers, K, args.warmup)
     result["next_rows"] = {"native_kv_record": native, "prepare_indexer_q_mxfp4": {
         "bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
