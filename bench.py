@@ -39,7 +39,7 @@ from sparse_attention_decode_build_amd import workloads as WL  # noqa: E402
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 WORKLOAD = WL.HEADLINE
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_b128_64k_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "counters_b128_64k.md")
 # the headline attention kernel (512 fp8 + 64 bf16 latent rows) and its source file
 ATTN_KERNEL = "mla_dsplit_kernel"
 ATTN_SRC = "attention_dsplit.hip"
@@ -159,7 +159,7 @@ def measured_traffic():
     if vals.get(f"{ATTN_SRC} sha256") != sha:
         return None
     try:
-        return float(vals["bytes per launch"])
+        return float(vals["attention bytes per launch"])
     except (KeyError, ValueError):
         return None
 
@@ -188,20 +188,6 @@ def cpu_baseline(wl: WL.Workload, budget_s: float) -> dict:
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"whole step (indexer, top-k, index build, attention) of tokens 0..{n - 1} "
                       f"of layer 0 of the same {WORKLOAD} workload, float64 numpy oracle, {dt:.1f} s"}
-
-
-def copy_calibration(gib: float) -> int:
-    """A plain device copy of known size (fp32 multiply by one: reads N bytes, writes N
-    bytes), run three times.  Under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE per
-    dispatch scale the counters of the other kernels to bytes."""
-    n = int(gib * (1 << 30)) // 4
-    src = torch.ones(n, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        torch.mul(src, 1.0, out=dst)
-    torch.cuda.synchronize()
-    log(f"[bench] copy calibration: {n * 4} bytes read and written per dispatch")
-    return 0
 
 
 def _read_csv(path):
@@ -236,40 +222,66 @@ def summarize_stats(directory: str) -> int:
     return 0
 
 
-def _pmc_mean(directory: str, counter: str, pattern: str, largest: bool = False) -> tuple:
-    """Mean counter value per dispatch of the kernels whose name contains `pattern`
-    (largest: only dispatches within 2x of the largest value, e.g. the 1 GiB copy among
-    smaller kernels of the same name)."""
-    rows = [r for r in _read_csv(_find(directory, "counter_collection.csv"))
-            if r["Counter_Name"] == counter and pattern in r["Kernel_Name"]]
-    if not rows:
-        raise RuntimeError(f"no {counter} rows for kernels matching {pattern!r} under {directory}")
-    vals = [float(r["Counter_Value"]) for r in rows]
-    if largest:
-        top = max(vals)
-        vals = [v for v in vals if v >= 0.5 * top]
-    return sum(vals) / len(vals), len(vals)
+# kernels of the step whose counters are summarized, and how their names start
+COUNTER_KERNELS = (("attention", ATTN_KERNEL), ("indexer scoring", "indexer_score_kernel"),
+                   ("top-k", "topk_kernel"))
 
 
-def summarize_traffic(fetch_dir: str, write_dir: str) -> int:
-    """Attention kernel HBM traffic per launch from two rocprofv3 --pmc runs of
-    `bench.py --copy-calibration-gib 1 ...` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
-    each scaled by the same counter on the 1 GiB copy kernel."""
-    copy_pat, attn_pat = "MulFunctor", ATTN_KERNEL
-    cal = float(1 << 30)
-    cf, _ = _pmc_mean(fetch_dir, "FETCH_SIZE", copy_pat, largest=True)
-    cw, _ = _pmc_mean(write_dir, "WRITE_SIZE", copy_pat, largest=True)
-    af, nf = _pmc_mean(fetch_dir, "FETCH_SIZE", attn_pat)
-    aw, nw = _pmc_mean(write_dir, "WRITE_SIZE", attn_pat)
-    kf, kw = cal / (cf * 1024.0), cal / (cw * 1024.0)
-    fetch_b, write_b = af * 1024.0 * kf, aw * 1024.0 * kw
+def summarize_counters(dirs) -> int:
+    """Markdown summary of rocprofv3 --pmc runs (one counter set per directory): for each
+    step kernel, the mean value per dispatch of every counter, then the derived figures
+    (MFMA busy share, bf16 / fp4 MFMA FLOPs, LDS bank-conflict share, HBM bytes from the
+    request counts by size)."""
+    vals = {}
+    for d in dirs:
+        if not os.path.isdir(d):
+            continue
+        for r in _read_csv(_find(d, "counter_collection.csv")):
+            name = r["Kernel_Name"]
+            for key, pat in COUNTER_KERNELS:
+                if pat in name:
+                    vals.setdefault(key, {}).setdefault(r["Counter_Name"], {}).setdefault(
+                        r.get("Dispatch_Id", ""), 0.0)
+                    vals[key][r["Counter_Name"]][r.get("Dispatch_Id", "")] += float(r["Counter_Value"])
     src = open(os.path.join(ROOT, "sparse_attention_decode_build_amd", "csrc", ATTN_SRC), "rb").read()
-    print(f"- {ATTN_SRC} sha256: `{hashlib.sha256(src).hexdigest()}`")
-    print(f"- copy kernel (1 GiB read + 1 GiB written): FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB "
-          f"-> scale factors {kf:.4f} (fetch), {kw:.4f} (write)")
-    print(f"- {ATTN_KERNEL} FETCH_SIZE mean {af:.0f} KiB over {nf} dispatches -> {fetch_b / 1e6:.2f} MB")
-    print(f"- {ATTN_KERNEL} WRITE_SIZE mean {aw:.0f} KiB over {nw} dispatches -> {write_b / 1e6:.2f} MB")
-    print(f"- bytes per launch: {fetch_b + write_b:.0f}")
+    print(f"- {ATTN_SRC} sha256: `{hashlib.sha256(src).hexdigest()}`\n")
+    for key, _ in COUNTER_KERNELS:
+        if key not in vals:
+            continue
+        m = {c: sum(v.values()) / len(v) for c, v in vals[key].items()}
+        n = {c: len(v) for c, v in vals[key].items()}
+        print(f"### {key}\n")
+        print("| counter | mean per dispatch | dispatches |")
+        print("|---|---|---|")
+        for c in sorted(m):
+            print(f"| `{c}` | {m[c]:.6g} | {n[c]} |")
+        print()
+        g = m.get
+        if g("SQ_BUSY_CU_CYCLES") and g("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+            print(f"- MFMA busy: {100 * g('SQ_VALU_MFMA_BUSY_CYCLES') / (4 * g('SQ_BUSY_CU_CYCLES')):.1f}% of the "
+                  "SIMD cycles of busy CUs (SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES))")
+        for c, label in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", "bf16"), ("SQ_INSTS_VALU_MFMA_MOPS_F6F4", "fp4/fp6/fp8")):
+            if g(c):
+                print(f"- {label} MFMA work: {g(c) * 512 / 1e9:.2f} GFLOP per dispatch ({c} x 512)")
+        if g("SQ_LDS_IDX_ACTIVE"):
+            print(f"- LDS bank conflicts: {100 * g('SQ_LDS_BANK_CONFLICT', 0.0) / g('SQ_LDS_IDX_ACTIVE'):.2f}% of the "
+                  "LDS-active cycles (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE)")
+        if g("TCC_EA0_RDREQ") is not None:
+            r32, r64, r128 = g("TCC_EA0_RDREQ_32B", 0.0), g("TCC_EA0_RDREQ_64B", 0.0), g("TCC_EA0_RDREQ_128B", 0.0)
+            rd = 32 * r32 + 64 * r64 + 128 * r128
+            print(f"- reads from memory: {rd / 1e6:.2f} MB per dispatch = 32 x RDREQ_32B + 64 x RDREQ_64B + "
+                  f"128 x RDREQ_128B (those three add up to {(r32 + r64 + r128) / max(g('TCC_EA0_RDREQ'), 1):.3f} "
+                  "of TCC_EA0_RDREQ)")
+            if g("TCC_EA0_RDREQ_DRAM") is not None:
+                print(f"- requests served by DRAM: {g('TCC_EA0_RDREQ_DRAM') / max(g('TCC_EA0_RDREQ'), 1):.3f} "
+                      "of the read requests (TCC_EA0_RDREQ_DRAM / TCC_EA0_RDREQ)")
+        if g("TCC_EA0_WRREQ") is not None:
+            w64 = g("TCC_EA0_WRREQ_64B", 0.0)
+            wr = 64 * w64 + 32 * (g("TCC_EA0_WRREQ") - w64)
+            print(f"- writes to memory: {wr / 1e6:.2f} MB per dispatch = 64 x WRREQ_64B + 32 x (WRREQ - WRREQ_64B)")
+            if key == "attention" and g("TCC_EA0_RDREQ") is not None:
+                print(f"- attention bytes per launch: {rd + wr:.0f}")
+        print()
     return 0
 
 
@@ -593,17 +605,15 @@ def main() -> int:
     ap.add_argument("--no-configs", action="store_true", help="skip the other seeded configurations")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the extra legs (native record, query preparation, output quantization, cache "
-                         "writes); counter runs use this so only the calibration copy and the step run")
-    ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
-                    help="first run a plain copy of this many GiB (rocprofv3 counter calibration)")
+                         "writes); counter runs use this so only the step runs")
     ap.add_argument("--summarize-stats", metavar="DIR", help="print a rocprofv3 kernel-stats CSV as markdown")
-    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="print attention traffic per launch from two rocprofv3 --pmc CSV runs")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="print the step kernels' counters from rocprofv3 --pmc CSV runs")
     args = ap.parse_args()
     if args.summarize_stats:
         return summarize_stats(args.summarize_stats)
-    if args.summarize_traffic:
-        return summarize_traffic(*args.summarize_traffic)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the step is data-parallel "
               "over requests and needs no collectives; run with --gpus 1", file=sys.stderr)
@@ -613,8 +623,6 @@ def main() -> int:
         return 2
     torch.cuda.set_device(0)
     sad.load()
-    if args.copy_calibration_gib > 0:
-        copy_calibration(args.copy_calibration_gib)
     t0 = time.perf_counter()
     wl = WL.make_workload(WORKLOAD, "cuda", num_layers=args.layers)
     torch.cuda.synchronize()
