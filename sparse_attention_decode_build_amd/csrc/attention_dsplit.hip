@@ -229,6 +229,41 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   auto read_id = [&](int b) __attribute__((always_inline)) -> int { return ids_lds[b * (IDS_SLOT / 4) + lane]; };
   // the raw loads of `tile` (this lane's key has slot id `id`) -> raw slot b; returns the
   // tile's validity mask (bit k: key k)
+  struct RowAddr {
+    const uint8_t* vrow;
+    const uint8_t* srow;
+  };
+  // the row and scale addresses of this lane's key in `tile` (slot id `id`); the tile's
+  // validity mask in *mask (bit k: key k)
+  auto row_addr = [&](int tile, int id, uint32_t* mask) __attribute__((always_inline)) -> RowAddr {
+    const int col = tile * kTile + key;
+    const bool inside = col < col_end;
+    const bool is_swa = ONE || col < window;
+    const uint8_t* pool = is_swa ? swa.pool : comp.pool;
+    const int64_t stride = is_swa ? swa.stride : comp.stride;
+    const int64_t npages = is_swa ? swa.num_pages : comp.num_pages;
+    const int blk = is_swa ? swa.block : comp.block;
+    const int shift = is_swa ? swa.block_shift : comp.block_shift;
+    const int slot = inside ? id : -1;
+    const bool ok = slot >= 0 && (int64_t)(slot >> shift) < npages;
+    const int s2 = ok ? slot : 0;
+    const int page = s2 >> shift;
+    const int ro = s2 & (blk - 1);
+    const uint8_t* pg = pool + (int64_t)page * stride;
+    *mask = (uint32_t)__ballot(ok);
+    return RowAddr{ok ? pg + ro * ROWB : zrow, ok ? pg + (blk * ROWB + ro * SCB) : zrow};
+  };
+  // load i (0..5) of a tile's rows into raw slot b
+  auto issue_load = [&](const RowAddr& ra, int i, int b) __attribute__((always_inline)) {
+    const uint32_t dst = lds_w + RAW_OFF + b * RAW_SLOT;
+    const uint8_t* vn = ra.vrow + 128 * w + 64 * hf;
+    if (i == 0) dma_x4_off<0>(vn, dst);
+    if (i == 1) dma_x4_off<16>(vn, dst + 1024);
+    if (i == 2) dma_x4_off<32>(vn, dst + 2048);
+    if (i == 3) dma_x4_off<48>(vn, dst + 3072);
+    if (i == 4) dma_x4_off<0>(ra.vrow + DN + 32 * w + 16 * hf, dst + 4096);
+    if (i == 5) dma_x1(ra.srow + 8 * w + 4 * hf, dst + 5120);
+  };
   auto issue_raw = [&](int tile, int id, int b) __attribute__((always_inline)) -> uint32_t {
     const int col = tile * kTile + key;
     const bool inside = col < col_end;
@@ -282,6 +317,17 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
       k[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{o0, o1, o2, o3});
     }
     k[8] = __builtin_bit_cast(bf16x8_t, x.rope);
+  };
+  // one k-step of dequant_regs (s < 8: nope values 8s..; s = 8: the rope values)
+  auto dequant_ks = [&](const RawRegs& x, bf16x8_t (&k)[KS], int s) __attribute__((always_inline)) {
+    if (s < 8) {
+      uint32_t o0, o1, o2, o3;
+      dequant_word(x.v[s >> 1][2 * (s & 1)], x.sc, o0, o1);
+      dequant_word(x.v[s >> 1][2 * (s & 1) + 1], x.sc, o2, o3);
+      k[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{o0, o1, o2, o3});
+    } else {
+      k[8] = __builtin_bit_cast(bf16x8_t, x.rope);
+    }
   };
   auto dequant = [&](int b, bf16x8_t (&k)[KS]) __attribute__((always_inline)) {
     RawRegs x;
@@ -485,7 +531,8 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   uint32_t mask_ring[NRAW];  // validity of the tile in each raw slot
   const int b0 = tile_begin;
   const bool any_tile = b0 < tile_end;
-  uint32_t mask_cur = 0;  // validity of tile j+1 (the tile of step j's softmax)
+  uint32_t mask_cur = 0;   // scratch: validity of tile j+2 while step j runs
+  uint32_t mask_prev = 0;  // validity of tile j+1 (the tile of step j's softmax)
   if (any_tile) {
     int id0[4];
 #pragma unroll
@@ -507,7 +554,7 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     wait_vmem<kLoadsPerStep>();  // tile b0+1 landed
     dequant(1, kf[1]);
     wait_lds();
-    mask_cur = mask_ring[1];
+    mask_prev = mask_ring[1];
     mask_ring[1] = issue_raw(b0 + 3, id0[3], 1);
     issue_ids(b0 + 5, 1);
     barrier();  // partial S^T of tile b0 published
@@ -530,51 +577,95 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   // unattended (fully masked) tiles.
   auto step = [&](int j, auto rc) __attribute__((always_inline)) {
     constexpr int R = decltype(rc)::value;
-    // P1
-    wait_vmem<kLoadsPerStep + 1>();  // rows of tile j+2 landed
+    // P1: the QK MFMAs of tile j+1, with the dequant of tile j+2 and the stores between
+    // them, and the seven loads of the rows of tile j+4 and the ids of tile j+6 spread
+    // between MFMA pairs (issued in a burst they stall the wave until the memory
+    // pipeline drains)
+    wait_vmem<kLoadsPerStep>();  // rows of tile j+2 and ids of tile j+4 landed
     RawRegs x;
     read_raw(R, x);
-    qk(kf[R ^ 1]);
+    const int id4 = read_id(R);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[nt][r] = 0.0f;
+    const bf16x8_t (&k1)[KS] = kf[R ^ 1];
+    auto qk_pair = [&](int s2) __attribute__((always_inline)) {
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1[s2], qf[0][s2], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1[s2], qf[1][s2], sacc[1], 0, 0, 0);
+    };
+    qk_pair(0);
+    qk_pair(1);
+    wait_lds();  // raw slot R and id slot R read (their data is in x and id4)
+    uint32_t mask_j4;
+    const RowAddr ra = row_addr(j + 4, id4, &mask_j4);
+    // seven sub-phases, each ending in one load: an MFMA pair, a k-step of the dequant
+    // and K-tile stores between them
+    qk_pair(2);
+    dequant_ks(x, kf[R], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_load(ra, 0, R);
+    __builtin_amdgcn_sched_barrier(0);
+    qk_pair(3);
+    dequant_ks(x, kf[R], 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_load(ra, 1, R);
+    __builtin_amdgcn_sched_barrier(0);
+    qk_pair(4);
+    dequant_ks(x, kf[R], 2);
     store_k(R ^ 1, kf[R ^ 1]);
-    dequant_regs(x, kf[R]);  // tile j+2
+    __builtin_amdgcn_sched_barrier(0);
+    issue_load(ra, 2, R);
+    __builtin_amdgcn_sched_barrier(0);
+    qk_pair(5);
+    dequant_ks(x, kf[R], 3);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_load(ra, 3, R);
+    __builtin_amdgcn_sched_barrier(0);
+    qk_pair(6);
+    dequant_ks(x, kf[R], 4);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_load(ra, 4, R);
+    __builtin_amdgcn_sched_barrier(0);
+    qk_pair(7);
+    dequant_ks(x, kf[R], 5);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_load(ra, 5, R);
+    __builtin_amdgcn_sched_barrier(0);
+    qk_pair(8);
+    dequant_ks(x, kf[R], 6);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_ids(j + 6, R);
+    __builtin_amdgcn_sched_barrier(0);
+    dequant_ks(x, kf[R], 7);
+    dequant_ks(x, kf[R], 8);
     store_s();
-    SCHED_GROUP(kSchedDsRead, 6);
-    static_for<2 * KS>([&](auto i) {
-      SCHED_GROUP(kSchedMfma, 1);
-      if constexpr (decltype(i)::value < 9) SCHED_GROUP(kSchedDsWrite, 1);
-      SCHED_GROUP(kSchedValu, 8);
-    });
-    // keep the dequant in this phase (the compiler would sink it to its use, the next
-    // step's QK)
 #pragma unroll
     for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(kf[R][s]));
+    mask_cur = mask_ring[R];  // tile j+2
+    mask_ring[R] = mask_j4;
     barrier();
     // P2
     if (__builtin_amdgcn_readfirstlane(flags[R]) != 0u) rescale(R);
-    wait_vmem<kLoadsPerStep>();  // ids of tile j+4 landed
     f32x4_t spa[kWaves], spb[kWaves];
     s_read(spa, spb);
-    const int id4 = read_id(R);
     bf16x8_t pf[4], vf[MT];
     pv_read(R, pf, vf);
     pv_mma(pf, vf);
     float sv[8];
     s_sum(spa, spb, sv);
-    s_mask(sv, mask_cur);
+    s_mask(sv, mask_prev);
     softmax(sv, R ^ 1);  // tile j+1
     // (the V^T reads two dim tiles ahead of their MFMAs: all of them up front would hold
     // 36 more VGPRs across the phase)
-    SCHED_GROUP(kSchedDsRead, 2 * kWaves + 1 + 4 + 4);
+    SCHED_GROUP(kSchedDsRead, 2 * kWaves + 4 + 4);
     static_for<MT * 4>([&](auto i) {
       constexpr int I = decltype(i)::value;
       if constexpr (I % 4 == 0 && I / 4 + 2 < MT) SCHED_GROUP(kSchedDsRead, 2);
       SCHED_GROUP(kSchedMfma, 1);
       SCHED_GROUP(kSchedValu, 3);
     });
-    wait_lds();  // raw slot R and id slot R read before they are refilled
-    mask_cur = mask_ring[R];  // tile j+2
-    mask_ring[R] = issue_raw(j + 4, id4, R);
-    issue_ids(j + 6, R);
+    mask_prev = mask_cur;
     barrier();
   };
   // An even number of steps, so that the loop body has no exit in its middle: a tile
