@@ -873,6 +873,10 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   }
 }
 
+// Most column splits of one (token, head group): the combine stages the splits' weights
+// in LDS.
+constexpr int kMaxSplits = 256;
+
 // Merge split partials: out = sum_s 2^(lse_s - M) o_s / (sum_s 2^(lse_s - M) + 2^(sink2 - M)).
 template <int DQK>
 __global__ __launch_bounds__(DQK) void combine_kernel(const float* __restrict__ part_o,
@@ -881,19 +885,25 @@ __global__ __launch_bounds__(DQK) void combine_kernel(const float* __restrict__ 
                                                       const float* __restrict__ sink,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ lse_out) {
+  __shared__ float lse_s[kMaxSplits];
   const int head = blockIdx.x;
   const int t = blockIdx.y;
   const int d = threadIdx.x;
   const int64_t th = (int64_t)t * num_heads + head;
   const int64_t plane = (int64_t)T * num_heads;
+  // the splits' log2-sum-exp values, one load per thread, then read from LDS
+  for (int s = d; s < num_splits; s += DQK) lse_s[s] = part_lse[s * plane + th];
+  __syncthreads();
   const float s2 = sink != nullptr ? sink[head] * kLog2e : -INFINITY;
   float mm = s2;
-  for (int s = 0; s < num_splits; ++s) mm = fmaxf(mm, part_lse[s * plane + th]);
+  for (int s = 0; s < num_splits; ++s) mm = fmaxf(mm, lse_s[s]);
   const float mref = mm == -INFINITY ? 0.0f : mm;
   float den = exp2f(s2 - mref);
   float acc = 0.0f;
+  // unrolled so that several splits' loads are in flight at once
+#pragma unroll 8
   for (int s = 0; s < num_splits; ++s) {
-    const float w = exp2f(part_lse[s * plane + th] - mref);
+    const float w = exp2f(lse_s[s] - mref);
     den += w;
     acc += w * part_o[(s * plane + th) * DQK + d];
   }
@@ -902,25 +912,17 @@ __global__ __launch_bounds__(DQK) void combine_kernel(const float* __restrict__ 
     lse_out[th] = den > 0.0f ? (mref + log2f(den)) * kLn2 : -INFINITY;
 }
 
-// Bytes of one cached row (values and scales) of the latent shape whose row has dqk
-// values: 512+64 with fp32 scales, the native 448+64 with 8 scale bytes, 128+32 with fp32.
-int row_bytes_of(int dqk) {
-  return dqk == 576 ? 512 + 128 + 32 : dqk == 512 ? 448 + 128 + 8 : dqk == 160 ? 128 + 64 + 8 : 2 * dqk;
-}
-
 int choose_splits(int T, int num_heads, int max_cols, int dqk) {
   const int cus = num_cus();
   const int units = T * ((num_heads + 63) / 64);  // workgroups without splitting
   if (units <= 0 || units >= cus) return 1;
-  const int rowb = row_bytes_of(dqk);
+  (void)dqk;
   const int tiles = (max_cols + kTile - 1) / kTile;
-  int s = (cus + units - 1) / units;
-  s = std::min(s, std::max(1, tiles / 4));
-  // keep the partials' traffic (write + read of 128 heads x dqk fp32) below the rows'
-  const int64_t row_bytes = (int64_t)max_cols * rowb;
-  const int64_t part_bytes = 2LL * 128 * dqk * 4;
-  s = (int)std::min<int64_t>(s, std::max<int64_t>(1, row_bytes / part_bytes));
-  return std::max(1, s);
+  // as many splits as keep one workgroup per compute unit, each with at least 4 tiles:
+  // with fewer workgroups than compute units the extra partials' traffic costs less
+  // than the idle units do
+  int s = std::min(cus / units, tiles / 4);
+  return std::max(1, std::min(s, kMaxSplits));
 }
 
 // Workspace bytes of `splits` column splits (0 without splitting): the partials o / l

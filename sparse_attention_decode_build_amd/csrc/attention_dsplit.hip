@@ -189,6 +189,16 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   const uint8_t* zrow = kZeroRow;
   asm volatile("" : "+s"(zrow));
 
+  // the slot ids of the first four tiles, requested together with Q (one memory round
+  // trip for both; the rows they name are the prologue's next request)
+  const int b0 = tile_begin;
+  const bool any_tile = b0 < tile_end;
+  int id0[4] = {0, 0, 0, 0};
+  if (any_tile) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) id0[k] = si_row[min((b0 + k) * kTile + key, width - 1)];
+  }
+
   // ---- Q^T fragments of this wave's slice: B operand of the 32x32x16 MFMA, lane (head
   // n = key, half hf) holds 8 dims of k-step s: nope 128w + 64hf + 8s (s < 8), rope
   // 512 + 16w + 8hf (s = 8).  Heads past num_heads load a copy of the last head (their
@@ -205,7 +215,7 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     }
   }
   // Q^T is an MFMA operand only: it lives in AGPRs, leaving the VGPRs to the rows in flight
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the Q loads landed
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the Q and first-id loads landed
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -239,11 +249,21 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     const int col = tile * kTile + key;
     const bool inside = col < col_end;
     const bool is_swa = ONE || col < window;
-    const uint8_t* pool = is_swa ? swa.pool : comp.pool;
-    const int64_t stride = is_swa ? swa.stride : comp.stride;
-    const int64_t npages = is_swa ? swa.num_pages : comp.num_pages;
-    const int blk = is_swa ? swa.block : comp.block;
-    const int shift = is_swa ? swa.block_shift : comp.block_shift;
+    // two caches: the per-lane choice between the descriptors is made here, from SGPR
+    // copies pinned at this point (else per-lane copies of both descriptors are hoisted
+    // out of the tile loop and spilled)
+    KvDesc sw = swa, cp = comp;
+    if (!ONE) {
+      asm volatile("" : "+s"(sw.pool), "+s"(sw.stride), "+s"(sw.num_pages), "+s"(sw.block), "+s"(sw.block_shift));
+      asm volatile("" : "+s"(cp.pool), "+s"(cp.stride), "+s"(cp.num_pages), "+s"(cp.block), "+s"(cp.block_shift));
+    } else if (LSE) {
+      asm volatile("" : "+s"(sw.pool));
+    }
+    const uint8_t* pool = is_swa ? sw.pool : cp.pool;
+    const int64_t stride = is_swa ? sw.stride : cp.stride;
+    const int64_t npages = is_swa ? sw.num_pages : cp.num_pages;
+    const int blk = is_swa ? sw.block : cp.block;
+    const int shift = is_swa ? sw.block_shift : cp.block_shift;
     const int slot = inside ? id : -1;
     const bool ok = slot >= 0 && (int64_t)(slot >> shift) < npages;
     const int s2 = ok ? slot : 0;
@@ -529,17 +549,11 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   //   kf[R ^ 1] holds tile j+1 dequantized; in flight, in this order: the rows of tile
   //   j+2 (raw slot R), the ids of j+4 (id slot R), the rows of j+3, the ids of j+5.
   uint32_t mask_ring[NRAW];  // validity of the tile in each raw slot
-  const int b0 = tile_begin;
-  const bool any_tile = b0 < tile_end;
   uint32_t mask_cur = 0;   // scratch: validity of tile j+2 while step j runs
   uint32_t mask_prev = 0;  // validity of tile j+1 (the tile of step j's softmax)
   if (any_tile) {
-    int id0[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) id0[k] = *id_src(b0 + k);
-    // (these are the only loads the compiler tracks: all of them land before the first
-    // direct load, so none of its own waits ever counts one of those)
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // (the Q and id loads are the only loads the compiler tracks: all of them landed
+    // before the first direct load, so none of its own waits ever counts one of those)
     mask_ring[0] = issue_raw(b0, id0[0], 0);
     mask_ring[1] = issue_raw(b0 + 1, id0[1], 1);
     wait_vmem<6>();  // tile b0 landed

@@ -19,10 +19,10 @@ from gpu_helpers import ATOL_LSE, ATOL_OUT, bf16_to_f64, gpu_build, kv_caches, l
 pytestmark = pytest.mark.gpu
 
 # dense compressed path (ratio 128, every compressed row attended): 8 requests with 16384
-# compressed rows each, then 4 requests with 4096
+# compressed rows each, then 4 requests with 2048
 BIG = WL.with_overrides(WL.CONFIGS["dense_1m"], name="dense_2m_x8", groups=((8, 1, 1 << 21, 0),),
                         kv_pool_pages=0)
-SMALL = WL.with_overrides(WL.CONFIGS["dense_1m"], name="dense_512k_x4", seed=7, groups=((4, 1, 1 << 19, 0),),
+SMALL = WL.with_overrides(WL.CONFIGS["dense_1m"], name="dense_256k_x4", seed=7, groups=((4, 1, 1 << 18, 0),),
                           kv_pool_pages=0)
 
 
