@@ -24,8 +24,8 @@
 //     of heads 16w .. 16w+15 and runs their online softmax; the bf16 weights go back
 //     through LDS to every wave for PV.  Two barriers per tile;
 //   * software pipeline (step j): phase 1 runs the QK MFMAs of tile j+1 with the dequant
-//     of tile j+2 between them; phase 2 runs the PV MFMAs of tile j with the softmax of
-//     tile j+1 between them, then requests the rows of tile j+4.  The weights, their
+//     of tile j+2 and, one by one, the row loads of tile j+4 between them; phase 2 runs
+//     the PV MFMAs of tile j with the softmax of tile j+1 between them.  The weights, their
 //     rescale factors and the K tiles are double-buffered so that the two phases of one
 //     step never wait on each other's data;
 //   * the two head groups of one (token, split) are numbered 8 workgroups apart, so
@@ -581,10 +581,10 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
 
   // ---- tile loop, step j (R = (j - b0) % 2):
   // P1: QK of tile j+1 (kf[R ^ 1]), tile j+1 -> K buffer R ^ 1 and its partial S^T
-  //     published; tile j+2 dequantized into kf[R] under the QK MFMAs; barrier.
+  //     published; tile j+2 dequantized into kf[R] and the rows of tile j+4 and the ids
+  //     of j+6 requested, all under the QK MFMAs; the PV operands of tile j read; barrier.
   // P2: PV of tile j (K buffer R, P buffer R, after the rescale its softmax asked for)
-  //     with the softmax of tile j+1 -> P buffer R ^ 1 under the PV MFMAs; the rows of
-  //     tile j+4 and the ids of j+6 requested; barrier.
+  //     with the softmax of tile j+1 -> P buffer R ^ 1 under the PV MFMAs; barrier.
   // Each phase is one scheduling region whose VALU and LDS work is spread between its
   // MFMAs (one wave per SIMD: its MFMAs hide nothing unless its own VALU instructions
   // sit between them); the steps past the last tile load zero rows and compute
@@ -658,24 +658,23 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(kf[R][s]));
     mask_cur = mask_ring[R];  // tile j+2
     mask_ring[R] = mask_j4;
+    // the PV operands of tile j (K buffer R and P buffer R, complete since the previous
+    // step): requested here so that their LDS latency passes under the barrier (the
+    // dequant registers of tile j+2 are dead by now, which leaves room for them)
+    bf16x8_t pf[4], vf[MT];
+    pv_read(R, pf, vf);
     barrier();
     // P2
     if (__builtin_amdgcn_readfirstlane(flags[R]) != 0u) rescale(R);
     f32x4_t spa[kWaves], spb[kWaves];
     s_read(spa, spb);
-    bf16x8_t pf[4], vf[MT];
-    pv_read(R, pf, vf);
     pv_mma(pf, vf);
     float sv[8];
     s_sum(spa, spb, sv);
     s_mask(sv, mask_prev);
     softmax(sv, R ^ 1);  // tile j+1
-    // (the V^T reads two dim tiles ahead of their MFMAs: all of them up front would hold
-    // 36 more VGPRs across the phase)
-    SCHED_GROUP(kSchedDsRead, 2 * kWaves + 4 + 4);
-    static_for<MT * 4>([&](auto i) {
-      constexpr int I = decltype(i)::value;
-      if constexpr (I % 4 == 0 && I / 4 + 2 < MT) SCHED_GROUP(kSchedDsRead, 2);
+    SCHED_GROUP(kSchedDsRead, 2 * kWaves);
+    static_for<MT * 4>([&](auto) {
       SCHED_GROUP(kSchedMfma, 1);
       SCHED_GROUP(kSchedValu, 3);
     });
