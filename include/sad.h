@@ -310,8 +310,10 @@ int gather_dequant_kv(const sad_kv_cache* swa, const sad_kv_cache* comp,
  * scale_format) = (512, 64, F32), (128, 32, F32) or the pages' native (448, 64, UE8M0),
  * the same for both caches; page sizes (block_size) of both caches are powers of two
  * and may differ (the window cache and the compressed cache are separate pools).
- * With few tokens a token's columns are split over several workgroups; the partial
- * results are merged through the workspace.
+ * With fewer (token, 64-head group) pairs than compute units a token's columns are
+ * split over several workgroups (as many as keep one workgroup per compute unit, each
+ * with at least 4 tiles of 32 columns, at most 256); the fp32 partial results are
+ * merged through the workspace.
  */
 int sparse_mla_decode(const uint16_t* q_bf16, int32_t num_tokens, int32_t num_heads,
                       const sad_kv_cache* swa, const sad_kv_cache* comp,
