@@ -237,8 +237,6 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     dma_x1(id_src(tile), ids_w + b * IDS_SLOT);
   };
   auto read_id = [&](int b) __attribute__((always_inline)) -> int { return ids_lds[b * (IDS_SLOT / 4) + lane]; };
-  // the raw loads of `tile` (this lane's key has slot id `id`) -> raw slot b; returns the
-  // tile's validity mask (bit k: key k)
   struct RowAddr {
     const uint8_t* vrow;
     const uint8_t* srow;
@@ -284,32 +282,13 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     if (i == 4) dma_x4_off<0>(ra.vrow + DN + 32 * w + 16 * hf, dst + 4096);
     if (i == 5) dma_x1(ra.srow + 8 * w + 4 * hf, dst + 5120);
   };
+  // all six loads of `tile` into raw slot b; returns the tile's validity mask
   auto issue_raw = [&](int tile, int id, int b) __attribute__((always_inline)) -> uint32_t {
-    const int col = tile * kTile + key;
-    const bool inside = col < col_end;
-    const bool is_swa = ONE || col < window;
-    const uint8_t* pool = is_swa ? swa.pool : comp.pool;
-    const int64_t stride = is_swa ? swa.stride : comp.stride;
-    const int64_t npages = is_swa ? swa.num_pages : comp.num_pages;
-    const int blk = is_swa ? swa.block : comp.block;
-    const int shift = is_swa ? swa.block_shift : comp.block_shift;
-    const int slot = inside ? id : -1;
-    const bool ok = slot >= 0 && (int64_t)(slot >> shift) < npages;
-    const int s2 = ok ? slot : 0;
-    const int page = s2 >> shift;
-    const int ro = s2 & (blk - 1);
-    const uint8_t* pg = pool + (int64_t)page * stride;
-    const uint8_t* vrow = ok ? pg + ro * ROWB : zrow;
-    const uint8_t* srow = ok ? pg + (blk * ROWB + ro * SCB) : zrow;
-    const uint8_t* vn = vrow + 128 * w + 64 * hf;
-    const uint32_t dst = lds_w + RAW_OFF + b * RAW_SLOT;
-    dma_x4_off<0>(vn, dst);
-    dma_x4_off<16>(vn, dst + 1024);
-    dma_x4_off<32>(vn, dst + 2048);
-    dma_x4_off<48>(vn, dst + 3072);
-    dma_x4_off<0>(vrow + DN + 32 * w + 16 * hf, dst + 4096);
-    dma_x1(srow + 8 * w + 4 * hf, dst + 5120);
-    return (uint32_t)__ballot(ok);  // lanes 0..31 = keys 0..31
+    uint32_t m;
+    const RowAddr ra = row_addr(tile, id, &m);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) issue_load(ra, i, b);
+    return m;
   };
   constexpr int kLoadsPerStep = 6 + 1;  // row loads of one tile + one tile's slot ids
 
@@ -663,9 +642,10 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     // dequant registers of tile j+2 are dead by now, which leaves room for them)
     bf16x8_t pf[4], vf[MT];
     pv_read(R, pf, vf);
+    const uint32_t rescale_flags = flags[R];  // set by tile j's softmax, in the previous step
     barrier();
     // P2
-    if (__builtin_amdgcn_readfirstlane(flags[R]) != 0u) rescale(R);
+    if (__builtin_amdgcn_readfirstlane(rescale_flags) != 0u) rescale(R);
     f32x4_t spa[kWaves], spb[kWaves];
     s_read(spa, spb);
     pv_mma(pf, vf);
