@@ -416,6 +416,23 @@ def test_csa_1m_top_k_past_one_workgroup():
     free(wl)
 
 
+def test_attention_at_the_split_cap():
+    # one request and one 64-head group: as many column splits as compute units (256 on
+    # MI355X), each of ~4 tiles, merged by the combine kernel (its LDS stage holds 256)
+    cfg = WL.with_overrides(WL.CONFIGS["dense_1m"], name="dense_128k_r4_h64", ratio=4, heads=64,
+                            groups=((1, 1, 1 << 17, 0),), kv_pool_pages=0)
+    wl = _wl(cfg)
+    c = wl.cfg
+    width = c.window + wl.padded_topk
+    need = sad.sparse_mla_decode_workspace_size(wl.num_tokens, c.heads, width, c.dqk)
+    splits = need // (wl.num_tokens * c.heads * (c.dqk + 1) * 4)
+    log(f"[report] {width} columns in {splits} splits")
+    assert splits == min(torch.cuda.get_device_properties(0).multi_processor_count, (width + 31) // 32 // 4, 256)
+    view = WL.host_view(wl)
+    _full_check(wl, view, list(range(wl.num_tokens)))
+    free(wl)
+
+
 @pytest.mark.slow
 def test_dense_1m_full():
     wl = _wl("dense_1m")
