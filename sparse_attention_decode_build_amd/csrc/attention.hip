@@ -949,9 +949,10 @@ int launch(const uint16_t* q, int T, int H, const KvDesc& s, const KvDesc& c, co
     part_lse = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + po);
   }
   int rc;
-  if constexpr (DN == 512) {
-    // the headline row: the dim-split kernel
-    rc = launch_mla_dsplit(q, T, H, s, c, si, lens, W, P, scale, sink, out, lse, part_o, part_lse, splits, st);
+  if constexpr (DN == 512 || DN == 448) {
+    // the 512 + 64 row and the pages' native 448 + 64 row: the dim-split kernel
+    rc = launch_mla_dsplit(q, T, H, s, c, si, lens, W, P, scale, sink, out, lse, part_o, part_lse, splits,
+                           DN == 448, st);
   } else {
     const int head_groups = (H + 63) / 64;
     const int pairs = T * splits;

@@ -51,7 +51,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;                  // attended columns per tile
 constexpr int DN = 512, DR = 64, DQK = DN + DR;
-constexpr int ROWB = DN + 2 * DR;          // value bytes per cached row
 constexpr int SCB = 4 * DN / 64;           // scale bytes per cached row (8 fp32)
 constexpr int KS = 9;                      // QK k-steps (16 dims) of a wave's slice
 constexpr int MT = 9;                      // PV m-tiles (16 dims) of a wave's slice
@@ -100,7 +99,7 @@ __device__ inline void static_for(F&& f) {
 }
 
 // Instruction classes of the scheduler's group barriers
-constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
 #define SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 // A load through the global address space (a plain pointer to a row or to the zero row
@@ -143,7 +142,7 @@ __device__ inline float sum_rows(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <bool ONE, bool LSE>
+template <bool ONE, bool LSE, bool NAT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads, KvDesc swa, KvDesc comp,
                   const int32_t* __restrict__ si, const int32_t* __restrict__ lens, int window, int padded,
@@ -169,6 +168,14 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   __builtin_assume(w >= 0 && w < kWaves);
   const int key = lane & 31;  // load / QK role: the tile row of this lane
   const int hf = lane >> 5;   // lane half: nope bytes 64hf.., rope values 8hf.. of the slice
+  // The cached record: 512 fp8 + 64 bf16 with 8 fp32 scales, or (NAT) the pages' native
+  // 448 fp8 + 64 bf16 with 8 ue8m0 bytes (7 used).  The slices keep the 576-dim layout
+  // either way; in the native form nope dims 448..511 (wave 3's lane half 1) are zero.
+  constexpr int R_NOPE = NAT ? 448 : DN;  // fp8 bytes of a row, and its rope's offset
+  constexpr int R_ROWB = R_NOPE + 2 * DR;  // value bytes per row
+  constexpr int R_SCB = NAT ? 8 : SCB;     // scale bytes per row
+  constexpr int IO_D = R_NOPE + DR;        // dims of a q and of an out row
+  const bool pad_lane = NAT && w == 3 && hf == 1;
   const int c16 = lane & 15;  // softmax / PV role: head (within 16) ...
   const int g = lane >> 4;    // ... and lane group (which 8 keys of the tile)
   // keys of the lane group's k-slots: slot 4r + a <-> key 8g + 4(r ^ (g & 1)) + a (the
@@ -201,17 +208,19 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
 
   // ---- Q^T fragments of this wave's slice: B operand of the 32x32x16 MFMA, lane (head
   // n = key, half hf) holds 8 dims of k-step s: nope 128w + 64hf + 8s (s < 8), rope
-  // 512 + 16w + 8hf (s = 8).  Heads past num_heads load a copy of the last head (their
-  // outputs are not written), so every load is unconditional.
+  // 512 + 16w + 8hf (s = 8) of the 576-dim layout (q's rope starts at R_NOPE).  Heads
+  // past num_heads load a copy of the last head (their outputs are not written), so
+  // every load is unconditional; the native form's padding dims load dim 0 and are zeroed.
   bf16x8_t qf[2][KS];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int head = min(hg * 64 + 32 * nt + key, num_heads - 1);
-    const uint16_t* qrow = q + ((int64_t)t * num_heads + head) * DQK;
+    const uint16_t* qrow = q + ((int64_t)t * num_heads + head) * IO_D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int d = s < 8 ? 128 * w + 64 * hf + 8 * s : DN + 16 * w + 8 * hf;
-      qf[nt][s] = *reinterpret_cast<const bf16x8_t*>(qrow + d);
+      const int d = s < 8 ? (pad_lane ? 0 : 128 * w + 64 * hf + 8 * s) : R_NOPE + 16 * w + 8 * hf;
+      const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qrow + d);
+      qf[nt][s] = s < 8 && pad_lane ? bf16x8_t{} : v;
     }
   }
   // Q^T is an MFMA operand only: it lives in AGPRs, leaving the VGPRs to the rows in flight
@@ -269,18 +278,19 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     const int ro = s2 & (blk - 1);
     const uint8_t* pg = pool + (int64_t)page * stride;
     *mask = (uint32_t)__ballot(ok);
-    return RowAddr{ok ? pg + ro * ROWB : zrow, ok ? pg + (blk * ROWB + ro * SCB) : zrow};
+    return RowAddr{ok ? pg + ro * R_ROWB : zrow, ok ? pg + (blk * R_ROWB + ro * R_SCB) : zrow};
   };
   // load i (0..5) of a tile's rows into raw slot b
   auto issue_load = [&](const RowAddr& ra, int i, int b) __attribute__((always_inline)) {
     const uint32_t dst = lds_w + RAW_OFF + b * RAW_SLOT;
-    const uint8_t* vn = ra.vrow + 128 * w + 64 * hf;
+    const uint8_t* vn = pad_lane ? zrow : ra.vrow + 128 * w + 64 * hf;
     if (i == 0) dma_x4_off<0>(vn, dst);
     if (i == 1) dma_x4_off<16>(vn, dst + 1024);
     if (i == 2) dma_x4_off<32>(vn, dst + 2048);
     if (i == 3) dma_x4_off<48>(vn, dst + 3072);
-    if (i == 4) dma_x4_off<0>(ra.vrow + DN + 32 * w + 16 * hf, dst + 4096);
-    if (i == 5) dma_x1(ra.srow + 8 * w + 4 * hf, dst + 5120);
+    if (i == 4) dma_x4_off<0>(ra.vrow + R_NOPE + 32 * w + 16 * hf, dst + 4096);
+    // the scale of nope block 2w + hf: its fp32 word, or (native) the word holding its byte
+    if (i == 5) dma_x1(NAT ? (pad_lane ? zrow : ra.srow + 4 * (w >> 1)) : ra.srow + 8 * w + 4 * hf, dst + 5120);
   };
   // all six loads of `tile` into raw slot b; returns the tile's validity mask
   auto issue_raw = [&](int tile, int id, int b) __attribute__((always_inline)) -> uint32_t {
@@ -306,27 +316,35 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     for (int i = 0; i < 4; ++i) x.v[i] = *reinterpret_cast<const u32x4_t*>(r + 1024 * i + 16 * lane);
     x.rope = *reinterpret_cast<const u32x4_t*>(r + 4096 + 16 * lane);
     x.sc = *reinterpret_cast<const float*>(r + 5120 + 4 * lane);
-  };
-  auto dequant_regs = [&](const RawRegs& x, bf16x8_t (&k)[KS]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      uint32_t o0, o1, o2, o3;
-      dequant_word(x.v[s >> 1][2 * (s & 1)], x.sc, o0, o1);
-      dequant_word(x.v[s >> 1][2 * (s & 1) + 1], x.sc, o2, o3);
-      k[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{o0, o1, o2, o3});
+    if (NAT) {  // ue8m0 byte b -> the fp32 2^(b - 127) (b = 0: the denormal 2^-127)
+      const uint32_t b = (__float_as_uint(x.sc) >> (8 * (2 * (w & 1) + hf))) & 255u;
+      x.sc = __uint_as_float(b != 0 ? b << 23 : 0x00400000u);
     }
-    k[8] = __builtin_bit_cast(bf16x8_t, x.rope);
   };
-  // one k-step of dequant_regs (s < 8: nope values 8s..; s = 8: the rope values)
+  // one k-step (s < 8: nope values 8s..; s = 8: the rope values).  The native form's
+  // power-of-two scales take the scaled conversion (v_cvt_scalef32_pk_bf16_fp8), whose
+  // product is exact before the one rounding to bf16: the same values as the multiply.
   auto dequant_ks = [&](const RawRegs& x, bf16x8_t (&k)[KS], int s) __attribute__((always_inline)) {
     if (s < 8) {
-      uint32_t o0, o1, o2, o3;
-      dequant_word(x.v[s >> 1][2 * (s & 1)], x.sc, o0, o1);
-      dequant_word(x.v[s >> 1][2 * (s & 1) + 1], x.sc, o2, o3);
-      k[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{o0, o1, o2, o3});
+      uint32_t o[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t word = x.v[s >> 1][2 * (s & 1) + h];
+        if (NAT) {
+          o[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, x.sc, false));
+          o[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, x.sc, true));
+        } else {
+          dequant_word(word, x.sc, o[2 * h], o[2 * h + 1]);
+        }
+      }
+      k[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
     } else {
       k[8] = __builtin_bit_cast(bf16x8_t, x.rope);
     }
+  };
+  auto dequant_regs = [&](const RawRegs& x, bf16x8_t (&k)[KS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) dequant_ks(x, k, s);
   };
   auto dequant = [&](int b, bf16x8_t (&k)[KS]) __attribute__((always_inline)) {
     RawRegs x;
@@ -704,26 +722,28 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     lse_out[(int64_t)t * num_heads + hg * 64 + tid] = lse_lds[tid];
   // slice dim d of m-tile m: nope 128w + 16m + 4g (m < 8), rope 512 + 16w + 4g (m = 8)
   if (num_splits == 1) {
-    // O goes through LDS (the K buffers: 64 head rows of DQK bf16, padded by 16 bytes)
+    // O goes through LDS (the K buffers: 64 head rows of IO_D bf16, padded by 16 bytes)
     // so that the workgroup's heads, contiguous in out, leave as one linear copy.
+    constexpr int OP = 2 * IO_D + 16;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int d = m < 8 ? 128 * w + 16 * m + 4 * g : DN + 16 * w + 4 * g;
+      if (NAT && m >= 4 && m < 8 && w == 3) continue;  // the native form's padding dims
+      const int d = m < 8 ? 128 * w + 16 * m + 4 * g : R_NOPE + 16 * w + 4 * g;
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         uint2 v;
         v.x = pack2(acc[m][n][0] * f[n], acc[m][n][1] * f[n]);
         v.y = pack2(acc[m][n][2] * f[n], acc[m][n][3] * f[n]);
-        *reinterpret_cast<uint2*>(smem + (16 * n + c16) * OPITCH + 2 * d) = v;
+        *reinterpret_cast<uint2*>(smem + (16 * n + c16) * OP + 2 * d) = v;
       }
     }
     barrier();
-    constexpr int CPR = DQK / 8;  // 16-byte chunks per head row
-    uint8_t* obase = reinterpret_cast<uint8_t*>(out + ((int64_t)t * num_heads + hg * 64) * DQK);
+    constexpr int CPR = IO_D / 8;  // 16-byte chunks per head row
+    uint8_t* obase = reinterpret_cast<uint8_t*>(out + ((int64_t)t * num_heads + hg * 64) * IO_D);
     for (int i = tid; i < rows * CPR; i += kThreads) {
       const int r = i / CPR;
       *reinterpret_cast<uint4*>(obase + 16 * (int64_t)i) =
-          *reinterpret_cast<const uint4*>(smem + r * OPITCH + 16 * (i - r * CPR));
+          *reinterpret_cast<const uint4*>(smem + r * OP + 16 * (i - r * CPR));
     }
   } else {
     const int64_t base = ((int64_t)split * num_tokens + t) * num_heads;
@@ -731,10 +751,11 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     for (int n = 0; n < 4; ++n) {
       const int head = hg * 64 + 16 * n + c16;
       if (head >= num_heads) continue;
-      float* prow = part_o + (base + head) * DQK;
+      float* prow = part_o + (base + head) * IO_D;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const int d = m < 8 ? 128 * w + 16 * m + 4 * g : DN + 16 * w + 4 * g;
+        if (NAT && m >= 4 && m < 8 && w == 3) continue;
+        const int d = m < 8 ? 128 * w + 16 * m + 4 * g : R_NOPE + 16 * w + 4 * g;
         *reinterpret_cast<float4*>(prow + d) =
             make_float4(acc[m][n][0] * f[n], acc[m][n][1] * f[n], acc[m][n][2] * f[n], acc[m][n][3] * f[n]);
       }
@@ -747,7 +768,7 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
 
 int launch_mla_dsplit(const uint16_t* q, int T, int H, const KvDesc& s, const KvDesc& c, const int32_t* si,
                       const int32_t* lens, int W, int P, float scale, const float* sink, uint16_t* out,
-                      float* lse, float* part_o, float* part_lse, int splits, hipStream_t st) {
+                      float* lse, float* part_o, float* part_lse, int splits, bool native, hipStream_t st) {
   const int head_groups = (H + 63) / 64;
   const int pairs = T * splits;
   const int blocks = (pairs + 7) / 8 * 8 * head_groups;
@@ -757,10 +778,14 @@ int launch_mla_dsplit(const uint16_t* q, int T, int H, const KvDesc& s, const Kv
     hipLaunchKernelGGL(kernel, dim3(blocks), dim3(kThreads), 0, st, q, T, H, s, c, si, lens, W, P,
                        scale * kLog2e, sink, out, lse, part_o, part_lse, splits, head_groups);
   };
-  if (one)
-    want_lse ? go(mla_dsplit_kernel<true, true>) : go(mla_dsplit_kernel<true, false>);
-  else
-    want_lse ? go(mla_dsplit_kernel<false, true>) : go(mla_dsplit_kernel<false, false>);
+  auto pick = [&](auto nat) {
+    constexpr bool N = decltype(nat)::value;
+    if (one)
+      want_lse ? go(mla_dsplit_kernel<true, true, N>) : go(mla_dsplit_kernel<true, false, N>);
+    else
+      want_lse ? go(mla_dsplit_kernel<false, true, N>) : go(mla_dsplit_kernel<false, false, N>);
+  };
+  native ? pick(std::true_type{}) : pick(std::false_type{});
   return check_launch("sparse_mla_decode(attention)");
 }
 

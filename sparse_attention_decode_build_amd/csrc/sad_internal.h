@@ -48,11 +48,13 @@ struct KvDesc {
   int block_shift;  // log2(block)
 };
 
-// The dim-split attention kernel of the (512 fp8 + 64 bf16, fp32 scales) row: out (or,
-// with splits > 1, the split partials part_o / part_lse) for every token and head.
+// The dim-split attention kernel of the (512 fp8 + 64 bf16, fp32 scales) row, or with
+// native = true of the pages' (448 fp8 + 64 bf16, ue8m0 scales) row: out (or, with
+// splits > 1, the split partials part_o / part_lse) for every token and head.
 int launch_mla_dsplit(const uint16_t* q, int T, int H, const KvDesc& swa, const KvDesc& comp,
                       const int32_t* si, const int32_t* lens, int W, int P, float scale, const float* sink,
-                      uint16_t* out, float* lse, float* part_o, float* part_lse, int splits, hipStream_t st);
+                      uint16_t* out, float* lse, float* part_o, float* part_lse, int splits, bool native,
+                      hipStream_t st);
 
 // ---- vector types -----------------------------------------------------------------
 
