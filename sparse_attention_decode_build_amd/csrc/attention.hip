@@ -101,14 +101,12 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
 
 template <int DN, int DR>
 struct Shape {
-  // The pages' native record (448 nope + 64 rope) is told apart by its nope width: its
-  // scales are 8 ue8m0 bytes per row (7 + 1 pad) and its fp8 part ends half way into
-  // a 128-byte line; the other rows carry fp32 scales and whole fp8 lines.
-  static constexpr bool NATIVE = DN % 128 != 0;
+  // Rows with fp32 scales and whole 128-byte fp8 lines (the pages' native 448 + 64 row
+  // runs on the dim-split kernel).
   static constexpr int DQK = DN + DR;
   static constexpr int ROWB = DN + 2 * DR;  // value bytes per cached row
   static constexpr int NSC = DN / 64;       // scale blocks per row
-  static constexpr int SCB = NATIVE ? 8 : 4 * NSC;  // scale bytes per row
+  static constexpr int SCB = 4 * NSC;       // scale bytes per row
   static constexpr int MT = DQK / 32;       // PV MFMA m-tiles (output dims / 32)
   static constexpr int MT0 = (MT + 1) / 2;  // m-tiles of dim half 0 (half 1 gets the rest)
   static constexpr int MT1 = MT - MT0;
@@ -221,16 +219,10 @@ __device__ inline void wait_lgkm() {
   asm volatile("s_waitcnt lgkmcnt(%0)" :: "n"(N) : "memory");
 }
 
-// Scale of block `blk` of tile row `key` from the raw scale slot: an fp32 value, or in
-// the native record a ue8m0 byte, 2^(b - 127) (byte 0 is the subnormal 2^-127).
+// Scale (fp32) of block `blk` of tile row `key` from the raw scale slot.
 template <int DN, int DR>
 __device__ inline float scale_at(const float (&raw_s)[Shape<DN, DR>::RAW_S], int key, int blk) {
-  if constexpr (Shape<DN, DR>::NATIVE) {
-    const uint32_t b = reinterpret_cast<const uint8_t*>(raw_s)[key * 32 + blk];
-    return b != 0 ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
-  } else {
-    return raw_s[key * 8 + blk];
-  }
+  return raw_s[key * 8 + blk];
 }
 
 // Dequantize fp8 lines [J0, J1) (and the rope line when ROPE) of this wave's 8 rows of
@@ -321,6 +313,7 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
                   uint16_t* __restrict__ out, float* __restrict__ lse_out,
                   float* __restrict__ part_o, float* __restrict__ part_lse, int num_splits,
                   int head_groups) {
+  static_assert(DN % 128 == 0, "whole fp8 lines with fp32 scales (the native row runs on the dim-split kernel)");
   using S = Shape<DN, DR>;
   constexpr int DQK = S::DQK;
   constexpr int KSMAX = S::KS0;
@@ -467,27 +460,15 @@ sparse_mla_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   u32x4_t dq[2 * S::FP8_LINES];  // ... and their fp8 part as bf16 (rope part: rr.rope)
   // One fp8 word of the raw rows (4 e4m3 values) -> 4 bf16 in dq: word w of line j holds
   // elements 16c + 4(w%4) .. +4 of that line.
-  // The native record's scales are powers of two (ue8m0): the scaled conversion does the
-  // multiply and the bf16 rounding in one instruction per pair, with the same result as
-  // bf16_rne(float(e4m3) * 2^(b - 127)) for every code and scale byte 0 .. 254.  (Byte
-  // 255, which the pages' writer never produces and ue8m0 reserves for NaN, decodes as
-  // NaN here instead of inf; a row holding it makes the output non-finite either way.)
   auto convert_word = [&](auto wc) __attribute__((always_inline)) {
     constexpr int w = decltype(wc)::value;
     constexpr int j = w >> 2;
     constexpr int qw = w & 3;
     const uint32_t word = rr.v[j][qw];
-    if constexpr (S::NATIVE) {
-      dq[2 * j + (qw >> 1)][2 * (qw & 1)] =
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, rr.sc[j], false));
-      dq[2 * j + (qw >> 1)][2 * (qw & 1) + 1] =
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, rr.sc[j], true));
-    } else {
-      const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false) * rr.sc[j];
-      const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true) * rr.sc[j];
-      dq[2 * j + (qw >> 1)][2 * (qw & 1)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
-      dq[2 * j + (qw >> 1)][2 * (qw & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
-    }
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false) * rr.sc[j];
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true) * rr.sc[j];
+    dq[2 * j + (qw >> 1)][2 * (qw & 1)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
+    dq[2 * j + (qw >> 1)][2 * (qw & 1) + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
   };
   constexpr int NWORD = 4 * S::FP8_LINES;
 

@@ -1,5 +1,5 @@
-// sparse_mla_decode for the 512 fp8 + 64 bf16 latent row with fp32 block scales:
-// the dim-split kernel.
+// sparse_mla_decode for the 512 fp8 + 64 bf16 latent row with fp32 block scales, and
+// for the pages' native 448 fp8 + 64 bf16 row with ue8m0 scales: the dim-split kernel.
 //
 // [backend] forward_deepseek_v4_decode (FlashMLA sparse decode: window ids bounded by
 // their lengths plus compressed ids bounded by extra_topk_length, FP8 cache,
@@ -322,8 +322,11 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     }
   };
   // one k-step (s < 8: nope values 8s..; s = 8: the rope values).  The native form's
-  // power-of-two scales take the scaled conversion (v_cvt_scalef32_pk_bf16_fp8), whose
-  // product is exact before the one rounding to bf16: the same values as the multiply.
+  // power-of-two scales take the scaled conversion (v_cvt_scalef32_pk_bf16_fp8): the
+  // multiply and the bf16 rounding in one instruction per pair, with the same result as
+  // bf16_rne(float(e4m3) * 2^(b - 127)) for every code and scale byte 0 .. 254.  (Byte
+  // 255, which the pages' writer never produces and ue8m0 reserves for NaN, decodes as
+  // NaN here instead of inf; a row holding it makes the output non-finite either way.)
   auto dequant_ks = [&](const RawRegs& x, bf16x8_t (&k)[KS], int s) __attribute__((always_inline)) {
     if (s < 8) {
       uint32_t o[4];
