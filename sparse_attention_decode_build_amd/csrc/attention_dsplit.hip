@@ -196,8 +196,8 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   const uint8_t* zrow = kZeroRow;
   asm volatile("" : "+s"(zrow));
 
-  // the slot ids of the first four tiles, requested together with Q (one memory round
-  // trip for both; the rows they name are the prologue's next request)
+  // the slot ids of the first four tiles, requested before Q: the rows they name go out
+  // (in the prologue) while Q is still in flight
   const int b0 = tile_begin;
   const bool any_tile = b0 < tile_end;
   int id0[4] = {0, 0, 0, 0};
@@ -223,12 +223,6 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
       qf[nt][s] = s < 8 && pad_lane ? bf16x8_t{} : v;
     }
   }
-  // Q^T is an MFMA operand only: it lives in AGPRs, leaving the VGPRs to the rows in flight
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the Q and first-id loads landed
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int s = 0; s < KS; ++s) asm volatile("" : "+a"(qf[nt][s]));
 
   // ---- row addressing and the LDS rings.  Every vector-memory operation of the tile
   // loop is a direct global -> LDS load issued here, so vmcnt counts exactly these:
@@ -551,12 +545,21 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
   uint32_t mask_ring[NRAW];  // validity of the tile in each raw slot
   uint32_t mask_cur = 0;   // scratch: validity of tile j+2 while step j runs
   uint32_t mask_prev = 0;  // validity of tile j+1 (the tile of step j's softmax)
+  // The Q and id loads are the only loads the compiler tracks.  The rows of the first two
+  // tiles go out as soon as the ids are in (the compiler waits for those), with Q still in
+  // flight; then everything lands (vmcnt(0)) before the tile loop, so none of the
+  // compiler's own waits ever counts a direct load after that.
   if (any_tile) {
-    // (the Q and id loads are the only loads the compiler tracks: all of them landed
-    // before the first direct load, so none of its own waits ever counts one of those)
     mask_ring[0] = issue_raw(b0, id0[0], 0);
     mask_ring[1] = issue_raw(b0 + 1, id0[1], 1);
-    wait_vmem<6>();  // tile b0 landed
+  }
+  // Q^T is an MFMA operand only: it lives in AGPRs, leaving the VGPRs to the rows in flight
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first two tiles landed
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" : "+a"(qf[nt][s]));
+  if (any_tile) {
     dequant(0, kf[0]);
     wait_lds();  // raw slot 0 read before it is refilled
     const uint32_t mask_b0 = mask_ring[0];
@@ -565,8 +568,7 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
     qk(kf[0]);
     store_k(0, kf[0]);
     store_s();
-    wait_vmem<kLoadsPerStep>();  // tile b0+1 landed
-    dequant(1, kf[1]);
+    dequant(1, kf[1]);  // (tile b0+1 landed with Q)
     wait_lds();
     mask_prev = mask_ring[1];
     mask_ring[1] = issue_raw(b0 + 3, id0[3], 1);
