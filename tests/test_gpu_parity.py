@@ -416,6 +416,18 @@ def test_csa_1m_top_k_past_one_workgroup():
     free(wl)
 
 
+def test_native_record_two_caches():
+    # the pages' native record (448 + 64, ue8m0) in the two-cache form: window pages of 64
+    # rows and compressed pages of 16 rows in pools of their own (the dim-split kernel's
+    # two-cache native instantiation), 3 requests, so the columns are split as well
+    cfg = WL.with_overrides(WL.CONFIGS["two_cache_b8_8k"], name="two_cache_b3_8k_native", d_nope=448,
+                            kv_format="ue8m0", groups=((3, 1, 8192, 0),))
+    wl = _wl(cfg)
+    view = WL.host_view(wl)
+    _full_check(wl, view, list(range(wl.num_tokens)))
+    free(wl)
+
+
 def test_attention_at_the_split_cap():
     # one request and one 64-head group: as many column splits as compute units (256 on
     # MI355X), each of ~4 tiles, merged by the combine kernel (its LDS stage holds 256)
