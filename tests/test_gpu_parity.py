@@ -428,6 +428,26 @@ def test_native_record_two_caches():
     free(wl)
 
 
+@pytest.mark.parametrize("native", [False, True])
+def test_two_caches_unsplit_with_and_without_lse(native):
+    # 256 requests of one 64-head group fill the GPU without column splits, so the
+    # two-cache kernels run in their one-pass form; asked without lse they must give the
+    # same output, bit for bit, as asked with it (which is checked against the oracle)
+    over = dict(d_nope=448, kv_format="ue8m0") if native else {}
+    cfg = WL.with_overrides(WL.CONFIGS["two_cache_b8_8k"], name=f"two_cache_b256_2k{'_native' if native else ''}",
+                            groups=((256, 1, 2048, 0),), **over)
+    wl = _wl(cfg)
+    c = wl.cfg
+    assert sad.sparse_mla_decode_workspace_size(wl.num_tokens, c.heads, c.window + wl.padded_topk, c.dqk) == 0
+    view = WL.host_view(wl)
+    si_g, lens_g, out_lse = _full_check(wl, view, list(range(wl.num_tokens)), check_gather=False)
+    out_nolse, _ = gpu_attention(wl, si_g, lens_g)
+    torch.cuda.synchronize()
+    assert torch.equal(out_nolse.view(torch.int16), out_lse.view(torch.int16))
+    log(f"[ok] {cfg.name}: output without lse identical to the checked one")
+    free(wl)
+
+
 def test_attention_at_the_split_cap():
     # one request and one 64-head group: as many column splits as compute units (256 on
     # MI355X), each of ~4 tiles, merged by the combine kernel (its LDS stage holds 256)
