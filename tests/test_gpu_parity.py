@@ -428,13 +428,14 @@ def test_native_record_two_caches():
     free(wl)
 
 
-@pytest.mark.parametrize("native", [False, True])
-def test_two_caches_unsplit_with_and_without_lse(native):
+@pytest.mark.parametrize("base,native", [("two_cache_b8_8k", False), ("two_cache_b8_8k", True),
+                                         ("b32_8k", True)])
+def test_unsplit_with_and_without_lse(base, native):
     # 256 requests of one 64-head group fill the GPU without column splits, so the
-    # two-cache kernels run in their one-pass form; asked without lse they must give the
-    # same output, bit for bit, as asked with it (which is checked against the oracle)
+    # kernels run in their one-pass form; asked without lse they must give the same
+    # output, bit for bit, as asked with it (which is checked against the oracle)
     over = dict(d_nope=448, kv_format="ue8m0") if native else {}
-    cfg = WL.with_overrides(WL.CONFIGS["two_cache_b8_8k"], name=f"two_cache_b256_2k{'_native' if native else ''}",
+    cfg = WL.with_overrides(WL.CONFIGS[base], name=f"{base}_b256_2k{'_native' if native else ''}",
                             groups=((256, 1, 2048, 0),), **over)
     wl = _wl(cfg)
     c = wl.cfg
