@@ -222,6 +222,37 @@ def summarize_stats(directory: str) -> int:
     return 0
 
 
+def summarize_trace(directory: str) -> int:
+    """Per-layer step of a rocprofv3 --kernel-trace run: for each occurrence of the fused
+    step's kernel sequence (scoring, fused top-k + build, attention), the medians of the
+    three kernels' durations and of the gaps between the end of one kernel and the start
+    of the next (the attention's to the next scoring)."""
+    import statistics
+    rows = sorted(_read_csv(_find(directory, "kernel_trace.csv")), key=lambda r: int(r["Start_Timestamp"]))
+    seq = ("indexer_score_kernel", "topk_kernel<16, 1>", ATTN_KERNEL)
+    dur = {k: [] for k in seq}
+    gaps = {"scoring -> top-k": [], "top-k -> attention": [], "attention -> next scoring": []}
+    for i in range(len(rows) - 2):
+        a, b, c = rows[i], rows[i + 1], rows[i + 2]
+        if not all(k in r["Kernel_Name"] for k, r in zip(seq, (a, b, c))):
+            continue
+        for k, r in zip(seq, (a, b, c)):
+            dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        gaps["scoring -> top-k"].append((int(b["Start_Timestamp"]) - int(a["End_Timestamp"])) / 1e3)
+        gaps["top-k -> attention"].append((int(c["Start_Timestamp"]) - int(b["End_Timestamp"])) / 1e3)
+        if i + 3 < len(rows) and seq[0] in rows[i + 3]["Kernel_Name"]:
+            gaps["attention -> next scoring"].append((int(rows[i + 3]["Start_Timestamp"]) -
+                                                      int(c["End_Timestamp"])) / 1e3)
+    n = len(dur[seq[0]])
+    print(f"{n} occurrences of the fused step's kernel sequence\n")
+    print("| kernel or gap | median (us) |")
+    print("|---|---|")
+    for k, v in list(dur.items()) + list(gaps.items()):
+        if v:
+            print(f"| {k} | {statistics.median(v):.2f} |")
+    return 0
+
+
 # kernels of the step whose counters are summarized, and how their names start
 COUNTER_KERNELS = (("attention", ATTN_KERNEL), ("indexer scoring", "indexer_score_kernel"),
                    ("top-k", "topk_kernel"))
@@ -607,6 +638,7 @@ def main() -> int:
                     help="skip the extra legs (native record, query preparation, output quantization, cache "
                          "writes); counter runs use this so only the step runs")
     ap.add_argument("--summarize-stats", metavar="DIR", help="print a rocprofv3 kernel-stats CSV as markdown")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="kernel durations and gaps of a rocprofv3 kernel trace")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                     help="print the step kernels' counters from rocprofv3 --pmc CSV runs")
     args = ap.parse_args()
@@ -614,6 +646,8 @@ def main() -> int:
         return summarize_stats(args.summarize_stats)
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters)
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the step is data-parallel "
               "over requests and needs no collectives; run with --gpus 1", file=sys.stderr)
