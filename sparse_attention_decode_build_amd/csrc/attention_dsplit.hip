@@ -30,7 +30,11 @@
 //     step never wait on each other's data;
 //   * the two head groups of one (token, split) are numbered 8 workgroups apart, so
 //     they run on the same XCD at the same time and the second read of each row hits
-//     that XCD's L2.
+//     that XCD's L2;
+//   * the native 448 + 64 row keeps the same slices, with nope dims 448..511 (wave 3's
+//     lane half 1) as zeros: those lanes load the zero row and a zero Q fragment, and
+//     their output dims are not written; its power-of-two scales dequantize with the
+//     scaled conversion instruction.
 // LDS layouts keep every store and read of the loop free of bank conflicts (with 32 or
 // 64 banks): a K tile row is 288 bytes and the two 16-byte halves of each of its
 // 32-byte blocks are swapped in the rows with fb(key) = 1 (fb below); the lane groups
