@@ -180,14 +180,17 @@ def test_edge_batch():
     free(wl)
 
 
-@pytest.mark.parametrize("heads,requests", [(40, 256), (72, 128), (96, 128), (120, 128), (72, 4), (120, 3)])
-def test_head_counts_with_partial_head_groups(heads, requests):
+@pytest.mark.parametrize("heads,requests,native", [(40, 256, False), (72, 128, False), (96, 128, False),
+                                                  (120, 128, False), (72, 4, False), (120, 3, False),
+                                                  (72, 128, True), (120, 3, True)])
+def test_head_counts_with_partial_head_groups(heads, requests, native):
     """Head counts whose last group of 64 heads is partial: a head block with absent
     heads (40, 72, 120) or an idle one (96).  With many (token, head group) pairs one
     workgroup covers a token's columns; with a few tokens the columns are split and
-    merged.  The rows after the output are untouched."""
-    cfg = WL.with_overrides(WL.CONFIGS["b32_8k"], name=f"h{heads}_r{requests}", heads=heads,
-                            groups=((requests, 1, 512, 0),))
+    merged.  The rows after the output are untouched.  Also for the native record."""
+    over = dict(d_nope=448, kv_format="ue8m0") if native else {}
+    cfg = WL.with_overrides(WL.CONFIGS["b32_8k"], name=f"h{heads}_r{requests}{'_native' if native else ''}",
+                            heads=heads, groups=((requests, 1, 512, 0),), **over)
     wl = _wl(cfg)
     view = WL.host_view(wl)
     tokens = list(range(0, wl.num_tokens, max(1, wl.num_tokens // 24)))
