@@ -42,15 +42,27 @@ def _hipcc() -> str:
     return exe
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libsad.so; returns its path."""
+# Host-code sanitizers (the device code is built as usual): AddressSanitizer and
+# UndefinedBehaviorSanitizer on the ABI's argument checks, workspace sizing and launch
+# set-up.  The library needs the clang ASan runtime loaded first (LD_PRELOAD of
+# libclang_rt.asan-x86_64.so, ASAN_OPTIONS=detect_leaks=0 under Python).
+HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                       "-Xarch_host", "-fno-omit-frame-pointer"]
+HOST_SANITIZED_LIB = os.path.join(PKG, "libsad_hostsan.so")
+
+
+def build(verbose: bool = False, host_sanitize: bool = False) -> str:
+    """Compile every source for gfx950 and link libsad.so (or, with host_sanitize, the
+    host-sanitized libsad_hostsan.so); returns its path."""
     hipcc = _hipcc()
-    obj_dir = os.path.join(ROOT, "_build")
+    obj_dir = os.path.join(ROOT, "_build_hostsan" if host_sanitize else "_build")
     os.makedirs(obj_dir, exist_ok=True)
+    san = HOST_SANITIZE_FLAGS if host_sanitize else []
+    lib = HOST_SANITIZED_LIB if host_sanitize else LIB
 
     def compile_one(src: str) -> str:
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
-        cmd = [hipcc, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *FLAGS, *san, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
@@ -60,14 +72,17 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    tmp = lib + ".tmp"
+    link_san = ["-fsanitize=address", "-fsanitize=undefined", "-shared-libasan"] if host_sanitize else []
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_san, *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"link of libsad.so failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n{res.stderr}")
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+
+    print(build(verbose=True, host_sanitize="--host-sanitize" in sys.argv[1:]))
