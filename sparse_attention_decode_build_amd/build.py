@@ -73,7 +73,7 @@ def build(verbose: bool = False, host_sanitize: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = lib + ".tmp"
-    link_san = ["-fsanitize=address", "-fsanitize=undefined", "-shared-libasan"] if host_sanitize else []
+    link_san = [*HOST_SANITIZE_FLAGS, "-shared-libasan"] if host_sanitize else []
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_san, *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
