@@ -165,12 +165,23 @@ def test_peaky_queries(name):
     free(wl)
 
 
-def test_attention_sink_and_lse():
-    wl = _wl("tiny")
+@pytest.mark.parametrize("base,requests,native", [("tiny", 0, False), ("b32_8k", 0, False),
+                                                 ("b32_8k", 256, False), ("b32_8k", 8, True),
+                                                 ("b32_8k", 256, True)])
+def test_attention_sink_and_lse(base, requests, native):
+    # a per-head sink: in the kernel's epilogue when one workgroup covers a token's
+    # columns (256 requests of one head group), in the combine when they are split
+    over = dict(d_nope=448, kv_format="ue8m0") if native else {}
+    if requests:
+        over["groups"] = ((requests, 1, 2048, 0),)
+    cfg = WL.with_overrides(WL.CONFIGS[base], name=f"{base}_sink_r{requests}{'_native' if native else ''}", **over)
+    wl = _wl(cfg)
     view = WL.host_view(wl)
     rng = np.random.default_rng(11)
     sink = rng.standard_normal(wl.cfg.heads) * 2.0
-    _full_check(wl, view, [0], sink=sink, check_gather=False)
+    tokens = list(range(0, wl.num_tokens, max(1, wl.num_tokens // 16)))
+    _full_check(wl, view, tokens, sink=sink, check_gather=False)
+    free(wl)
 
 
 def test_edge_batch():
