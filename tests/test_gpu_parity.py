@@ -165,6 +165,20 @@ def test_peaky_queries(name):
     free(wl)
 
 
+@pytest.mark.parametrize("requests", [8, 256])
+def test_lazy_rescale_under_very_peaky_queries(requests):
+    # queries x16: log2-unit logits span about +-100, so a 32-column tile's maximum
+    # passes the running maximum by more than the 2^8 slack on about 8% of the tiles
+    # (about 1% at x4, never at x1, counted on the CPU from the oracle's rows) and the O
+    # accumulators are rescaled often (split with 8 requests, unsplit with 256)
+    cfg = WL.with_overrides(WL.CONFIGS["b32_8k"], name=f"b32_8k_q16_r{requests}", groups=((requests, 1, 2048, 0),))
+    wl = _wl(cfg, q_scale=16.0)
+    view = WL.host_view(wl)
+    tokens = list(range(0, wl.num_tokens, max(1, wl.num_tokens // 16)))
+    _full_check(wl, view, tokens, check_gather=False, label=f"{cfg.name} peaky")
+    free(wl)
+
+
 @pytest.mark.parametrize("base,requests,native", [("tiny", 0, False), ("b32_8k", 0, False),
                                                  ("b32_8k", 256, False), ("b32_8k", 8, True),
                                                  ("b32_8k", 256, True)])
