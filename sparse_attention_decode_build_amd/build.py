@@ -30,9 +30,12 @@ FLAGS = [
     f"-I{CSRC}",
 ]
 # Per-file extra flags.  The indexer's MFMA results feed VALU work right away, so its
-# MFMAs write VGPRs; the dim-split attention kernel keeps its accumulators in VGPRs and
-# its Q^T operand in AGPRs (the other attention kernel keeps its accumulators in AGPRs).
-EXTRA_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# MFMAs write VGPRs.  The dim-split attention kernel runs two waves per SIMD (256
+# registers each): its PV waves' 144 accumulators and its QK waves' Q^T fragments only
+# fit one register split between the two roles when every MFMA operand is a VGPR (the
+# other attention kernel keeps its accumulators in AGPRs).
+EXTRA_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+               "attention_dsplit.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc() -> str:
