@@ -432,7 +432,9 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
       if constexpr (decltype(doA)::value) {
         float sv[8];
         s_reduce(sv);
-        s_mask(sv, mask_lds[(s - 1 - b0) & 3]);
+        // (most tiles have every column attended: no mask to apply)
+        const uint32_t vm = __builtin_amdgcn_readfirstlane(mask_lds[(s - 1 - b0) & 3]);
+        if (vm != 0xFFFFFFFFu) s_mask(sv, vm);
         softmax(sv);
       }
       barrier();  // A: weights of tile s-1 published; V^T of tile s-1 read
