@@ -445,12 +445,17 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
         for (int n2 = 0; n2 < 2; ++n2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) sacc[n2][r] = 0.0f;
+        // k-step by k-step: the dequant, its K-tile store and its MFMA pair, in this order
+        // (the scheduler otherwise sinks the K-tile stores behind the last MFMAs, where
+        // they lengthen the burst of stores the barrier waits for); the MFMAs of one
+        // k-step run while the next k-step's dequant issues
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const bf16x8_t k = dequant_ks(x, ks);
           store_k(ks, k);
           sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[0][ks], sacc[0], 0, 0, 0);
           sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, qf[1][ks], sacc[1], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
         store_s();
         slot = slot == NRAW - 1 ? 0 : slot + 1;
