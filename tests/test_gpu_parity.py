@@ -350,6 +350,56 @@ def test_narrow_index_rows(window, padded):
     assert np.max(np.abs(lg[fin] - lse_o[fin]), initial=0.0) <= ATOL_LSE
 
 
+@pytest.mark.parametrize("rep", [1, 8])
+def test_tile_counts_and_holes_on_the_headline_row(rep):
+    """The headline row (512 fp8 + 64 bf16, 64 heads) with index rows of 1 to 8 tiles per
+    token: widths at tile boundaries and one off either side, fully valid rows (no
+    mask to apply) and rows with -1 and past-pool ids in their tiles (masked).  With 32
+    tokens the columns are split in two, so splits hold 0 to 4 tiles (the loops' first,
+    steady and drain steps, and a split with nothing); with the tokens repeated 8 times
+    (256 units) nothing is split.  Every token against the oracle, lse included."""
+    wl = _wl("b32_8k")
+    cfg = wl.cfg
+    view = WL.host_view(wl)
+    T0 = wl.num_tokens
+    T = T0 * rep
+    window, padded = 0, 256
+    rng = np.random.default_rng(4242 + rep)
+    pages = np.array(sorted(view.kv_pages.keys()), np.int64)
+    si = (rng.choice(pages, (T, padded)) * cfg.block + rng.integers(0, cfg.block, (T, padded))).astype(np.int64)
+    widths = np.array([1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 128, 129, 160, 191, 224, 256], np.int32)
+    lens = widths[np.arange(T) % len(widths)].astype(np.int32)
+    holes = (np.arange(T) // len(widths)) % 2 == 1  # every other round of widths has holes
+    for t in np.nonzero(holes)[0]:
+        m = rng.random(padded) < 0.15
+        si[t, m] = -1
+        past = rng.random(padded) < 0.05
+        si[t, past] = (wl.kv_pool.shape[0] + 3) * cfg.block  # a page past the pool: masked
+    si = si.astype(np.int32)
+    # the kernel masks ids past the pool as it masks -1 (fail closed); the oracle's attention
+    # takes rows whose ids are already safe, so it gets those ids as -1
+    si_o = np.where(si >= wl.kv_pool.shape[0] * cfg.block, -1, si).astype(np.int32)
+    q = wl.layers[0].q
+    q_rep = q.repeat(rep, 1, 1).contiguous() if rep > 1 else q
+    q_bits = np.tile(view.q, (rep, 1, 1)) if rep > 1 else view.q
+    swa, comp = kv_caches(wl)
+    lse = torch.empty((T, cfg.heads), dtype=torch.float32, device="cuda")
+    out = sad.sparse_mla_decode(q_rep, swa, comp, torch.from_numpy(si).cuda(), torch.from_numpy(lens).cuda(),
+                                window, padded, wl.softmax_scale, lse=lse)
+    torch.cuda.synchronize()
+    tokens = list(range(T)) if rep == 1 else list(range(0, T, 3))
+    o_o, lse_o = O.sparse_mla_decode(q_bits, view.swa_pages, view.kv_pages, si_o, lens, window, cfg.block,
+                                     cfg.block, cfg.d_nope, cfg.d_rope, wl.softmax_scale, tokens=tokens)
+    got = bf16_to_f64(out[tokens])
+    check_attention(wl, view, tokens, got, o_o, si_o, lens, q_bits=q_bits, label=f"tile counts x{rep}",
+                    window=window)
+    lg = lse.cpu().numpy()[tokens]
+    fin = np.isfinite(lse_o)
+    assert np.array_equal(np.isfinite(lg), fin)
+    assert np.max(np.abs(lg[fin] - lse_o[fin]), initial=0.0) <= ATOL_LSE
+    free(wl)
+
+
 def test_empty_batch_is_a_no_op():
     wl = _wl("tiny")
     cfg = wl.cfg
