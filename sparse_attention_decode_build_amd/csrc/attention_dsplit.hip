@@ -390,21 +390,37 @@ mla_dsplit_kernel(const uint16_t* __restrict__ q, int num_tokens, int num_heads,
       }
     };
     auto softmax = [&](const float (&sv)[8]) __attribute__((always_inline)) {
-      float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      tmax = max_rows(tmax) * scale_log2;
       // the running maximum is kept until a tile exceeds it by 2^slack (also true while it
-      // is -inf); O needs rescaling only when it already holds weights (a finite maximum)
-      const bool upd = tmax > m_run + kRescaleSlack;
-      const bool resc = upd && m_run != -INFINITY;
-      const float m_new = upd ? tmax : m_run;
-      const float alpha = resc ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      m_run = m_new;
-      l_run *= alpha;
-      if (LSE) l_lse *= alpha;
+      // is -inf); O needs rescaling only when it already holds weights (a finite maximum).
+      // A head's maximum moves iff one of its keys has sv * scale_log2 > m_run + slack:
+      // rounding is monotone, so that is the test max(sv) * scale_log2 > m_run + slack
+      // key by key.  When no lane of the wave has such a key (the usual tile) the
+      // maximum, its cross-lane reduction and the rescale are skipped.
       float p[8];
+      bool resc = false;
+      float alpha = 1.0f;
+      bool over = false;
+      const float thr = m_run + kRescaleSlack;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], scale_log2, -m_use));
+      for (int i = 0; i < 8; ++i) over = over || sv[i] * scale_log2 > thr;
+      if (__ballot(over) == 0ull) {
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], scale_log2, -m_use));
+      } else {
+        float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        tmax = max_rows(tmax) * scale_log2;
+        const bool upd = tmax > thr;
+        resc = upd && m_run != -INFINITY;
+        const float m_new = upd ? tmax : m_run;
+        alpha = resc ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        m_run = m_new;
+        l_run *= alpha;
+        if (LSE) l_lse *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], scale_log2, -m_use));
+      }
       // (scalars, not elements of a vector: a bit_cast of a vector element compiled to the
       // first element every time)
       uint32_t pw[4];
